@@ -1,0 +1,303 @@
+"""Pins of the oracle against what the pages and the mathematics fix.
+
+Each pin takes an oracle module `orc` and raises AssertionError when it
+disagrees.  They are written against facts that do not come from the oracle
+itself: worked examples derived by hand from the pages' rule (tests/golden),
+counts the pages print, closed forms through a plain library matrix product,
+the structure of a tensor-product algebra (numpy.kron), associativity, the
+unit, and composition.  test_oracle_pins.py runs them on the real oracle and
+on copies of it with planted mistakes, each of which some pin must catch.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+from scipy.special import expit
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL = 1e-11
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, tol=TOL):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"max abs err {err} > {tol * scale}"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- golden ---
+
+def pin_golden_q2(orc):
+    g = _load("q2_hand_examples.json")
+    ex = g["scalar_full_product"]
+    _close(orc.star(ex["X"], ex["W"], ex["law"], ex["q"]), ex["star"], 0)
+    dense = np.asarray(ex["X"], float) @ np.asarray(ex["W"], float)
+    _close(dense, ex["dense"], 0)
+    ex = g["rowtyped_rectangular"]
+    _close(orc.project(ex["X"], ex["W"], ex["law"], ex["q"], ex["types"]), ex["Y"], 0)
+    ex = g["decode_positions"]
+    _close(orc.decode(ex["x"], ex["W"], ex["law"], ex["q"], ex["positions"]), ex["y"], 0)
+
+
+def pin_golden_q2xq2_triples(orc):
+    g = _load("q2xq2_triples.json")
+    for t in g["triples"]:
+        got = orc.in_table("Q2xQ2", 4, t["g"], t["g1"], t["g2"])
+        assert got == t["kept"], t
+        got4 = orc.in_table("Qq", 4, t["g"], t["g1"], t["g2"])
+        assert got4 == t["q4_kept"], t
+
+
+def pin_counts(orc):
+    c = _load("page_counts.json")
+    assert orc.count_block_products("Qq", 2) == c["q2_block_products"]
+    assert orc.count_block_products("Qq", 2) < c["q2_dense_block_products"]
+    for q in c["rank_formula_qs"]:
+        assert orc.count_block_products("Qq", q) == 2 * q * q - q, q
+        for i in range(min(q, 8)):
+            assert Fraction(orc.count_row_block_products("Qq", q, i), q * q) == Fraction(2 * q - 1, q * q)
+    assert orc.count_block_products("Q2xQ2", 4) == c["q2xq2_block_products"]
+    # 16 coordinates = a 4x4 grid of groups
+    assert 4 * 4 == c["q2xq2_coordinates"]
+    r = Fraction(*c["q2xq2_ffn_mac_ratio"])
+    for i in range(4):
+        assert Fraction(orc.count_row_block_products("Q2xQ2", 4, i), 16) == r
+    # not isomorphic to Q4: a different number of structure constants
+    assert orc.count_block_products("Qq", 4) == 28 != c["q2xq2_block_products"]
+    # projection share of one pilot decoder block: four dense d x d attention
+    # projections plus three FFN projections at the law's MAC ratio
+    d, F = c["pilot_width"], c["pilot_ffn_width"]
+    share = (4 * d * d + r * 3 * d * F) / Fraction(4 * d * d + 3 * d * F)
+    assert share == Fraction(*c["pilot_block_projection_share"])
+
+
+# ---------------------------------------------------- library reductions ---
+
+def pin_q1_is_matmul(orc):
+    rng = _rng(1)
+    A = rng.standard_normal((5, 7))
+    B = rng.standard_normal((7, 3))
+    _close(orc.star(A, B, "Qq", 1), A @ B)
+    _close(orc.project(A, B, "Qq", 1, np.zeros(5, int)), A @ B)
+
+
+def _off_qq(A, q):
+    """Zero the diagonal blocks of a q x q block matrix (rectangular blocks)."""
+    A = np.array(A, dtype=np.float64)
+    r, c = A.shape[0] // q, A.shape[1] // q
+    for i in range(q):
+        A[i * r:(i + 1) * r, i * c:(i + 1) * c] = 0
+    return A
+
+
+def pin_closed_form_qq(orc):
+    # The edge-times-edge products are exactly off(A) off(B), so the algebra
+    # product is the ordinary product minus that.
+    rng = _rng(2)
+    for q, (ra, ca, cb) in [(2, (3, 2, 4)), (3, (2, 3, 2)), (4, (1, 2, 3)), (5, (2, 1, 1))]:
+        A = rng.standard_normal((q * ra, q * ca))
+        B = rng.standard_normal((q * ca, q * cb))
+        _close(orc.star(A, B, "Qq", q), A @ B - _off_qq(A, q) @ _off_qq(B, q))
+        # row-typed: y_t = x_t W - off_tau(x_t) off(W), off_tau zeroing group tau
+        M = 11
+        X = rng.standard_normal((M, q * ca))
+        types = rng.integers(0, q, M)
+        ref = X @ B
+        offB = _off_qq(B, q)
+        for t in range(M):
+            xo = X[t].copy()
+            xo[types[t] * ca:(types[t] + 1) * ca] = 0
+            ref[t] -= xo @ offB
+        _close(orc.project(X, B, "Qq", q, types), ref)
+
+
+def _proj_q2xq2(A, keep):
+    """Keep the blocks (g, g') of a 4 x 4 block matrix where keep(a, b, a1, b1)."""
+    A = np.array(A, dtype=np.float64)
+    r, c = A.shape[0] // 4, A.shape[1] // 4
+    out = np.zeros_like(A)
+    for g in range(4):
+        for g1 in range(4):
+            a, b = divmod(g, 2)
+            a1, b1 = divmod(g1, 2)
+            if keep(a, b, a1, b1):
+                out[g * r:(g + 1) * r, g1 * c:(g1 + 1) * c] = A[g * r:(g + 1) * r, g1 * c:(g1 + 1) * c]
+    return out
+
+
+def pin_closed_form_q2xq2(orc):
+    # Inclusion-exclusion: a triple is dropped when the first factor's middle
+    # index leaves {a, a''} or the second factor's leaves {b, b''}.
+    rng = _rng(3)
+    Pa = lambda A: _proj_q2xq2(A, lambda a, b, a1, b1: a != a1)
+    Pb = lambda A: _proj_q2xq2(A, lambda a, b, a1, b1: b != b1)
+    Pab = lambda A: _proj_q2xq2(A, lambda a, b, a1, b1: a != a1 and b != b1)
+    for (ra, ca, cb) in [(1, 1, 1), (2, 3, 2), (3, 2, 1)]:
+        A = rng.standard_normal((4 * ra, 4 * ca))
+        B = rng.standard_normal((4 * ca, 4 * cb))
+        ref = A @ B - Pa(A) @ Pa(B) - Pb(A) @ Pb(B) + Pab(A) @ Pab(B)
+        _close(orc.star(A, B, "Q2xQ2", 4), ref)
+
+
+def pin_kronecker_q2xq2(orc):
+    # The tensor square of Q2: (P1 (x) P2) * (R1 (x) R2) = (P1 *2 R1) (x) (P2 *2 R2)
+    # with g = 2a + b, which is numpy.kron's index order.  The second factor may
+    # carry matrix blocks.
+    rng = _rng(4)
+    for b in (1, 2, 3):
+        P1, R1 = rng.standard_normal((2, 2)), rng.standard_normal((2, 2))
+        P2, R2 = rng.standard_normal((2 * b, 2 * b)), rng.standard_normal((2 * b, 2 * b))
+        lhs = orc.star(np.kron(P1, P2), np.kron(R1, R2), "Q2xQ2", 4)
+        rhs = np.kron(orc.star(P1, R1, "Qq", 2), orc.star(P2, R2, "Qq", 2))
+        _close(lhs, rhs)
+
+
+def pin_basis_products_qq(orc):
+    # Structure constants at block size 1 for q = 3: e_ij * e_lk is e_ik when
+    # l == j and j is i or k, else 0.  The matrix-unit product in star must
+    # follow that orientation (rows of A, columns of B).
+    q = 3
+    E = lambda i, j: np.eye(q)[:, [i]] @ np.eye(q)[[j], :]
+    for i in range(q):
+        for j in range(q):
+            for l in range(q):
+                for k in range(q):
+                    got = orc.star(E(i, j), E(l, k), "Qq", q)
+                    want = E(i, k) if (l == j and j in (i, k)) else np.zeros((q, q))
+                    _close(got, want, 0)
+
+
+# ------------------------------------------------------------- algebra ---
+
+def pin_associativity(orc):
+    rng = _rng(5)
+    for law, q in [("Qq", 2), ("Qq", 3), ("Qq", 4), ("Q2xQ2", 4)]:
+        for (r0, r1, r2, r3) in [(1, 1, 1, 1), (2, 3, 1, 2)]:
+            A = rng.standard_normal((q * r0, q * r1))
+            B = rng.standard_normal((q * r1, q * r2))
+            C = rng.standard_normal((q * r2, q * r3))
+            _close(orc.star(orc.star(A, B, law, q), C, law, q), orc.star(A, orc.star(B, C, law, q), law, q), 1e-10)
+
+
+def pin_unit(orc):
+    rng = _rng(6)
+    for law, q in [("Qq", 2), ("Qq", 5), ("Q2xQ2", 4)]:
+        A = rng.standard_normal((2 * q, 2 * q))
+        I = np.eye(2 * q)
+        _close(orc.star(I, A, law, q), A)
+        _close(orc.star(A, I, law, q), A)
+
+
+def pin_composition(orc):
+    # Phi_W2(Phi_W1(X)) = Phi_{W1 * W2}(X) for row-typed inputs.
+    rng = _rng(7)
+    for law, q in [("Qq", 2), ("Qq", 4), ("Q2xQ2", 4)]:
+        d0, d1, d2 = 3 * q, 2 * q, 5 * q
+        X = rng.standard_normal((13, d0))
+        W1 = rng.standard_normal((d0, d1))
+        W2 = rng.standard_normal((d1, d2))
+        types = orc.types_pos_mod(13, q, 3)
+        lhs = orc.project(orc.project(X, W1, law, q, types), W2, law, q, types)
+        rhs = orc.project(X, orc.star(W1, W2, law, q), law, q, types)
+        _close(lhs, rhs, 1e-10)
+
+
+def pin_rowtyped_equals_full_rows(orc):
+    rng = _rng(8)
+    for law, q in [("Qq", 2), ("Qq", 3), ("Q2xQ2", 4)]:
+        A = rng.standard_normal((2 * q, 3 * q))
+        B = rng.standard_normal((3 * q, 2 * q))
+        _close(orc.project(A, B, law, q, orc.types_block_rows(2 * q, q)), orc.star(A, B, law, q))
+        # a single token of type i equals the matching row of a full product
+        # whose block-row i holds it
+        x = rng.standard_normal((1, 3 * q))
+        for i in range(q):
+            Asq = np.zeros((q, 3 * q))
+            Asq[i] = x[0]
+            full = orc.star(Asq, B, law, q)
+            _close(orc.project(x, B, law, q, [i]), full[[i]])
+
+
+def pin_row_locality(orc):
+    rng = _rng(9)
+    q = 4
+    X = rng.standard_normal((9, 8))
+    W = rng.standard_normal((8, 12))
+    types = orc.types_pos_mod(9, q)
+    Y = orc.project(X, W, "Qq", q, types)
+    X2 = X.copy()
+    X2[[0, 2, 5]] = rng.standard_normal((3, 8))
+    Y2 = orc.project(X2, W, "Qq", q, types)
+    keep = [1, 3, 4, 6, 7, 8]
+    _close(Y[keep], Y2[keep])
+
+
+def pin_types(orc):
+    q = 4
+    t0 = orc.types_pos_mod(10, q, 5)
+    assert list(t0) == [(5 + t) % 4 for t in range(10)]
+    assert list(orc.types_pos_mod(10, q, 5 + q)) == list(t0)
+    assert list(orc.types_pos_mod(10, q, 6)) == list(t0[1:]) + [(6 + 9) % 4]
+    # two sequences of length 8 laid end to end: positions restart
+    assert list(orc.types_pos_mod(16, q, 0, 8)) == [p % 4 for p in list(range(8)) * 2]
+    assert list(orc.types_pos_mod(12, 3, 0, 6)) == [0, 1, 2] * 4
+    # a sequence length that q does not divide: types restart with each sequence
+    assert list(orc.types_pos_mod(12, 4, 0, 6)) == [0, 1, 2, 3, 0, 1] * 2
+    assert list(orc.types_pos_mod(6, 4, 4, 6)) == [0, 1, 0, 1, 2, 3]
+    assert list(orc.types_block_rows(8, 4)) == [0, 0, 1, 1, 2, 2, 3, 3]
+
+
+def pin_decode(orc):
+    rng = _rng(10)
+    for law, q in [("Qq", 4), ("Q2xQ2", 4)]:
+        X = rng.standard_normal((12, 8))
+        W = rng.standard_normal((8, 16))
+        full = orc.project(X, W, law, q, orc.types_pos_mod(12, q, 7))
+        for t in (0, 5, 11):
+            _close(orc.decode(X[[t]], W, law, q, [7 + t]), full[[t]])
+
+
+def pin_swiglu(orc):
+    # silu against the library logistic function
+    g = np.linspace(-30, 30, 241)
+    _close(orc.silu(g), g * expit(g))
+    # hand example (one feature, q = 1): G = ln 3, U = 2, H = ln3 * (3/4) * 2,
+    # Y = 4 H = 6 ln 3
+    ln3 = math.log(3.0)
+    H, Y = orc.swiglu_ffn([[1.0]], [[ln3]], [[2.0]], [[4.0]], "Qq", 1, [0])
+    _close(H, [[1.5 * ln3]])
+    _close(Y, [[6.0 * ln3]])
+    # q = 1 is the ordinary SwiGLU FFN
+    rng = _rng(11)
+    X = rng.standard_normal((6, 4))
+    Wg, Wu, Wd = rng.standard_normal((4, 5)), rng.standard_normal((4, 5)), rng.standard_normal((5, 4))
+    Gd = X @ Wg
+    H, Y = orc.swiglu_ffn(X, Wg, Wu, Wd, "Qq", 1, np.zeros(6, int))
+    _close(H, Gd * expit(Gd) * (X @ Wu))
+    _close(Y, (Gd * expit(Gd) * (X @ Wu)) @ Wd)
+
+
+def pin_executed_flops(orc):
+    for q in (2, 4, 32):
+        M, d_in, d_out = 4 * q, 2 * q, 3 * q
+        per = [M // q] * q
+        assert orc.executed_flops(per, d_in, d_out, "Qq", q) == Fraction(2 * M * d_in * d_out * (2 * q - 1), q * q)
+    assert orc.executed_flops([4] * 4, 8, 8, "Q2xQ2", 4) == Fraction(2 * 16 * 8 * 8 * 9, 16)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
