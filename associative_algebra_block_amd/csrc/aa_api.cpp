@@ -1,0 +1,152 @@
+// Entry points of libaa.so: host-side argument checks, then the launches in
+// aa_kernels.hip.  Every check happens before anything is enqueued, so a call
+// that fails leaves the stream untouched.
+#include <stdint.h>
+
+#include <string>
+
+#include "aa_internal.h"
+
+using aa::fail;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+aa_status_t check_ptr(const void* p, const char* what, const char* fn) {
+  if (!p) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": " + what + " is NULL");
+  if (!aligned16(p)) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": " + what + " is not 16-byte aligned");
+  return AA_OK;
+}
+
+size_t elem_size(aa_dtype_t t) { return t == AA_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Checks shared by the row-typed calls: M, the position offset and the type map.
+aa_status_t check_rows(const aa_plan_s& plan, int64_t M, int64_t pos_offset, const int32_t* row_types,
+                       const char* fn) {
+  if (M < 0) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": M is negative");
+  if (M >= (int64_t(1) << 31)) return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": M of 2^31 rows or more");
+  if (pos_offset < 0) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": pos_offset is negative");
+  if (plan.type_kind == AA_TYPES_EXPLICIT) {
+    if (!row_types && M > 0) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": explicit type map needs row_types");
+    if (row_types && (reinterpret_cast<uintptr_t>(row_types) & 3u))
+      return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": row_types is not 4-byte aligned");
+  } else if (row_types) {
+    return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": row_types given for a plan without an explicit type map");
+  }
+  if (plan.type_kind == AA_TYPES_BLOCK_ROWS && M % plan.q)
+    return fail(AA_ERR_SHAPE, std::string(fn) + ": block-row typing needs q to divide M");
+  return AA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aa_status_t aa_pack_weights(aa_plan_t plan, const void* W_rowmajor, void* W_packed, hipStream_t stream) {
+  aa::clear_error();
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_pack_weights: plan is NULL");
+  aa_status_t st;
+  if ((st = check_ptr(W_rowmajor, "W_rowmajor", "aa_pack_weights")) != AA_OK) return st;
+  if ((st = check_ptr(W_packed, "W_packed", "aa_pack_weights")) != AA_OK) return st;
+  const size_t bytes = size_t(plan->d_in * plan->d_out) * elem_size(plan->in_dtype);
+  if (overlaps(W_rowmajor, bytes, W_packed, bytes))
+    return fail(AA_ERR_INVALID_ARG, "aa_pack_weights: source and destination overlap");
+  return aa::launch_pack(*plan, W_rowmajor, W_packed, false, stream);
+}
+
+aa_status_t aa_unpack_weights(aa_plan_t plan, const void* W_packed, void* W_rowmajor, hipStream_t stream) {
+  aa::clear_error();
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_unpack_weights: plan is NULL");
+  aa_status_t st;
+  if ((st = check_ptr(W_packed, "W_packed", "aa_unpack_weights")) != AA_OK) return st;
+  if ((st = check_ptr(W_rowmajor, "W_rowmajor", "aa_unpack_weights")) != AA_OK) return st;
+  const size_t bytes = size_t(plan->d_in * plan->d_out) * elem_size(plan->in_dtype);
+  if (overlaps(W_rowmajor, bytes, W_packed, bytes))
+    return fail(AA_ERR_INVALID_ARG, "aa_unpack_weights: source and destination overlap");
+  return aa::launch_pack(*plan, W_packed, W_rowmajor, true, stream);
+}
+
+aa_status_t aa_project_fwd(aa_plan_t plan, const void* X, const void* W_packed, void* Y, int64_t M,
+                           int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  aa::clear_error();
+  static const char* fn = "aa_project_fwd";
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_fwd: plan is NULL");
+  aa_status_t st;
+  if ((st = check_rows(*plan, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if (M == 0) return AA_OK;
+  if ((st = check_ptr(X, "X", fn)) != AA_OK) return st;
+  if ((st = check_ptr(W_packed, "W_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Y, "Y", fn)) != AA_OK) return st;
+  const size_t xb = size_t(M * plan->d_in) * elem_size(plan->in_dtype);
+  const size_t wb = size_t(plan->d_in * plan->d_out) * elem_size(plan->in_dtype);
+  const size_t yb = size_t(M * plan->d_out) * elem_size(plan->out_dtype);
+  if (overlaps(Y, yb, X, xb) || overlaps(Y, yb, W_packed, wb))
+    return fail(AA_ERR_INVALID_ARG, "aa_project_fwd: Y overlaps X or W_packed");
+  aa::LeafCall call{X, W_packed, nullptr, Y, M, pos_offset, row_types, false};
+  return aa::launch_leaf_gemm(*plan, call, stream);
+}
+
+aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const void* Wg_packed,
+                              const void* Wu_packed, const void* Wd_packed, void* H, void* Y, int64_t M,
+                              int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  aa::clear_error();
+  static const char* fn = "aa_swiglu_ffn_fwd";
+  if (!up || !down) return fail(AA_ERR_INVALID_ARG, "aa_swiglu_ffn_fwd: plan is NULL");
+  if (up->law != down->law || up->q != down->q)
+    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: up and down plans use different laws or q");
+  if (up->type_kind != down->type_kind || up->period != down->period)
+    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: up and down plans use different type maps");
+  if (up->d_out != down->d_in || up->d_in != down->d_out)
+    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: up must map D -> F and down F -> D");
+  if (down->in_dtype != up->out_dtype)
+    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: down's input dtype must be up's output dtype (H)");
+  aa_status_t st;
+  if ((st = check_rows(*up, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if (M == 0) return AA_OK;
+  if ((st = check_ptr(X, "X", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Wg_packed, "Wg_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Wu_packed, "Wu_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Wd_packed, "Wd_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(H, "H", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Y, "Y", fn)) != AA_OK) return st;
+  const size_t hb = size_t(M * up->d_out) * elem_size(up->out_dtype);
+  const size_t yb = size_t(M * down->d_out) * elem_size(down->out_dtype);
+  const size_t xb = size_t(M * up->d_in) * elem_size(up->in_dtype);
+  if (overlaps(H, hb, Y, yb) || overlaps(H, hb, X, xb) || overlaps(Y, yb, X, xb))
+    return fail(AA_ERR_INVALID_ARG, "aa_swiglu_ffn_fwd: X, H and Y must not overlap");
+  aa::LeafCall gate_up{X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, true};
+  if ((st = aa::launch_leaf_gemm(*up, gate_up, stream)) != AA_OK) return st;
+  aa::LeafCall proj_down{H, Wd_packed, nullptr, Y, M, pos_offset, row_types, false};
+  return aa::launch_leaf_gemm(*down, proj_down, stream);
+}
+
+aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, void* y, int64_t n,
+                           int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  aa::clear_error();
+  static const char* fn = "aa_decode_gemv";
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: plan is NULL");
+  if (n < 0) return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: n is negative");
+  if (n >= (int64_t(1) << 20) * 16) return fail(AA_ERR_UNSUPPORTED, "aa_decode_gemv: too many tokens");
+  if (pos_offset < 0) return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: pos_offset is negative");
+  if (!row_types && plan->type_kind != AA_TYPES_POS_MOD)
+    return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: row_types is required unless the plan uses position typing");
+  if (row_types && (reinterpret_cast<uintptr_t>(row_types) & 3u))
+    return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: row_types is not 4-byte aligned");
+  if (n == 0) return AA_OK;
+  aa_status_t st;
+  if ((st = check_ptr(x, "x", fn)) != AA_OK) return st;
+  if ((st = check_ptr(W_packed, "W_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(y, "y", fn)) != AA_OK) return st;
+  const size_t xb = size_t(n * plan->d_in) * elem_size(plan->in_dtype);
+  const size_t yb = size_t(n * plan->d_out) * elem_size(plan->out_dtype);
+  if (overlaps(y, yb, x, xb)) return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: x and y overlap");
+  return aa::launch_decode(*plan, x, W_packed, y, n, pos_offset, row_types, stream);
+}
+
+}  // extern "C"

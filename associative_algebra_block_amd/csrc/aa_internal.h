@@ -1,0 +1,61 @@
+// Internal declarations shared by the host plan code, the entry points and the
+// kernel launchers of libaa.so.  Not installed; the public surface is aa.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+#include "aa.h"
+
+// Host-side plan: immutable after aa_plan_create.
+struct aa_plan_s {
+  aa_law_t law;
+  int32_t q;
+  int64_t d_in, d_out;
+  int64_t b_in, b_out;
+  aa_type_kind_t type_kind;
+  int64_t period;
+  aa_dtype_t in_dtype, out_dtype;
+  int64_t n_block_products;  // one full product
+  int64_t n_leaves;          // q * q
+  int32_t tile_override;     // -1: automatic; else a variant id (tuning only)
+};
+
+namespace aa {
+
+// Thread-local error text.
+void set_error(const std::string& msg);
+void clear_error();
+aa_status_t fail(aa_status_t st, const std::string& msg);
+
+// Number of block products in the table row of type i that ends in output
+// group k (1 for k == i under Q_q, 2 otherwise; 1, 2 or 4 under Q2 x Q2).
+int leaf_groups(aa_law_t law, int q, int i, int k, int* groups /* up to 4 */);
+
+// ---------------------------------------------------------------- launch ---
+
+// What a leaf-GEMM launch needs besides the plan.
+struct LeafCall {
+  const void* X;    // M x ldx, in_dtype
+  const void* W0;   // packed weight (projection, or SwiGLU gate)
+  const void* W1;   // packed SwiGLU up weight, or nullptr
+  void* Y;          // M x ldy, out_dtype
+  int64_t M;
+  int64_t pos_offset;
+  const int32_t* row_types;  // device, EXPLICIT only
+  bool swiglu;               // Y = silu(X*W0) * (X*W1)
+};
+
+aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream);
+
+aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool unpack,
+                        hipStream_t stream);
+
+aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, void* y, int64_t n,
+                          int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
+
+// Synchronise and check when AA_DEBUG=1; map launch errors to AA_ERR_HIP.
+aa_status_t after_launch(hipStream_t stream, const char* what);
+
+}  // namespace aa

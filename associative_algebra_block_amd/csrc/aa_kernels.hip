@@ -1,0 +1,625 @@
+// HIP kernels (gfx950) of libaa.so and their host launchers.
+//
+// What is computed (agihunt.info review of "Change the Product, Keep the
+// Parameters: Associative Algebra Layers for Transformers"; paragraphs on the
+// graph multiplication table, on row typing and on the pilot law): a row of
+// type i produces output group k as the sum over the table's input groups j of
+// x_j W_jk.  Under Q_q those groups are {i, k}; under the tensor square of Q2
+// (q = 4) they are the 1, 2 or 4 groups (a', b') with a' in {a, a''} and b' in
+// {b, b''}.  Each (type, output group) pair is one "leaf": a dense GEMM whose
+// K dimension is the concatenation of its input groups, [x_i | x_k] times
+// [W_ik ; W_kk], which is what the MFMA units are used for.
+//
+// Formulation.  The kernels compute the transposed leaf, Y^T = W^T X^T, with
+// the bf16 MFMA v_mfma_f32_16x16x32_bf16: the A operand is a 16 (n) x 32 (k)
+// fragment of W^T, the B operand a 32 (k) x 16 (m) fragment of X^T.  Both
+// operands then hold 8 consecutive k per lane, so
+//   - a weight fragment is one contiguous, fully coalesced 1 KiB read from the
+//     block-packed layout (aa_pack_weights writes W in exactly this order), and
+//   - an activation fragment is 16 B of one row of X,
+// and the 16 x 16 accumulator holds 4 consecutive output columns of one row
+// per lane, which are stored straight to row-major Y.  Weights stream from HBM
+// directly into registers (no LDS round trip); the X rows of the tile are
+// read per wave and shared through the L1/L2 caches.
+//
+// Work split.  One workgroup computes one tile of one leaf: TM rows of type i
+// (strided rows of X under position typing, contiguous under block-row typing,
+// a scanned list under explicit typing) by TN columns of output group k.
+// Tiles are numbered so that each XCD's share of the grid is one contiguous
+// run of output groups, which keeps the diagonal blocks W_kk that every row
+// type reads resident in that XCD's L2; within the run, consecutive tiles
+// share the row type, so the type's own activation block x_i stays hot too.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <string>
+
+#include "aa_internal.h"
+
+namespace aa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kNumXcd = 8;   // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ fragments ---
+
+// Eight consecutive k values of one lane, in the input element type.
+template <typename T> struct Run;
+template <> struct Run<__bf16> {
+  u32x4_t v;
+  __device__ static Run zero() { Run r; r.v = u32x4_t{0u, 0u, 0u, 0u}; return r; }
+  __device__ static Run load(const __bf16* p) {
+    Run r;
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return r;
+  }
+  __device__ static Run load_cached(const __bf16* p) {
+    Run r;
+    r.v = *reinterpret_cast<const u32x4_t*>(p);
+    return r;
+  }
+};
+template <> struct Run<float> {
+  u32x4_t lo, hi;
+  __device__ static Run zero() { Run r; r.lo = u32x4_t{0u, 0u, 0u, 0u}; r.hi = r.lo; return r; }
+  __device__ static Run load(const float* p) {
+    Run r;
+    r.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    r.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + 1);
+    return r;
+  }
+  __device__ static Run load_cached(const float* p) {
+    Run r;
+    r.lo = reinterpret_cast<const u32x4_t*>(p)[0];
+    r.hi = reinterpret_cast<const u32x4_t*>(p)[1];
+    return r;
+  }
+};
+
+// acc (16 n x 16 m) += A (16 n x 32 k) * B (32 k x 16 m).
+__device__ inline f32x4_t mma(const Run<__bf16>& a, const Run<__bf16>& b, f32x4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                 __builtin_bit_cast(bf16x8_t, b.v), acc, 0, 0, 0);
+}
+__device__ inline f32x4_t mma(const Run<float>& a, const Run<float>& b, f32x4_t acc) {
+  // Eight K=4 steps; step e pairs element e of every lane's run, so both
+  // operands see the same k for each hardware k slot.
+  const float* pa0 = reinterpret_cast<const float*>(&a.lo);
+  const float* pa1 = reinterpret_cast<const float*>(&a.hi);
+  const float* pb0 = reinterpret_cast<const float*>(&b.lo);
+  const float* pb1 = reinterpret_cast<const float*>(&b.hi);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa0[e], pb0[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa1[e], pb1[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// Four consecutive outputs of one row.
+__device__ inline void store4(__bf16* p, f32x4_t v) {
+  bf16x4_t o;
+  o[0] = (__bf16)v[0];
+  o[1] = (__bf16)v[1];
+  o[2] = (__bf16)v[2];
+  o[3] = (__bf16)v[3];
+  *reinterpret_cast<bf16x4_t*>(p) = o;
+}
+__device__ inline void store4(float* p, f32x4_t v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Input groups of leaf (type i, output group k); returns their count (<= 4).
+__device__ inline int device_leaf_groups(int law, int i, int k, int* g) {
+  if (law == AA_LAW_QQ) {
+    g[0] = i;
+    g[1] = k;
+    return i == k ? 1 : 2;
+  }
+  const int a = i >> 1, b = i & 1, a2 = k >> 1, b2 = k & 1;
+  int as1 = a2, bs1 = b2;
+  const int na = (a2 != a) ? 2 : 1, nb = (b2 != b) ? 2 : 1;
+  int n = 0;
+  for (int x = 0; x < na; ++x)
+    for (int y = 0; y < nb; ++y) g[n++] = 2 * (x ? as1 : a) + (y ? bs1 : b);
+  return n;
+}
+
+// ------------------------------------------------------------- leaf GEMM ---
+
+struct LeafParams {
+  const void* X;
+  const void* W0;
+  const void* W1;
+  void* Y;
+  int64_t M;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t q;
+  int32_t b_in;
+  int32_t b_out;
+  int32_t law;
+  int32_t kind;            // aa_type_kind_t
+  int32_t off_mod_q;       // pos_offset mod q (position typing)
+  int64_t rows_per_type;   // M / q (block-row typing)
+  const int32_t* row_types;
+  int32_t mt_count;        // m-tiles per leaf
+  int32_t nt_count;        // n-tiles per leaf
+  int32_t kc;              // output groups per tile-order chunk
+  uint32_t n_tiles;
+};
+
+// Rows of type i, in order; fills rows[0..TM) for m-tile mt and returns how
+// many are valid.  Position and block-row typing are closed-form.
+template <int TM>
+__device__ inline int tile_rows_closed_form(const LeafParams& p, int i, int mt, int32_t* rows) {
+  int64_t first, stride, count;
+  if (p.kind == AA_TYPES_BLOCK_ROWS) {
+    first = int64_t(i) * p.rows_per_type;
+    stride = 1;
+    count = p.rows_per_type;
+  } else {
+    int64_t r0 = int64_t(i) - p.off_mod_q;
+    if (r0 < 0) r0 += p.q;
+    first = r0;
+    stride = p.q;
+    count = r0 < p.M ? (p.M - r0 + p.q - 1) / p.q : 0;
+  }
+  const int64_t lo = int64_t(mt) * TM;
+  const int n = lo >= count ? 0 : int(count - lo < TM ? count - lo : TM);
+  for (int r = threadIdx.x; r < TM; r += blockDim.x)
+    rows[r] = r < n ? int32_t(first + (lo + r) * stride) : -1;
+  return n;
+}
+
+template <typename Tin, typename Tout, int WN, int WM, int NF, int MF, bool SWIGLU, int STAGES>
+__global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p) {
+  constexpr int TN = WN * NF * 16;
+  constexpr int TM = WM * MF * 16;
+  __shared__ int32_t rows_lds[TM];
+  __shared__ int32_t scan_state[2];
+
+  // XCD-aware tile numbering: XCD x (= blockIdx.x mod 8) receives a
+  // contiguous run of the tile order.
+  const uint32_t bid = blockIdx.x;
+  const uint32_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int nt = int(t % uint32_t(p.nt_count));
+  t /= uint32_t(p.nt_count);
+  const int mt = int(t % uint32_t(p.mt_count));
+  t /= uint32_t(p.mt_count);
+  const int kk = int(t % uint32_t(p.kc));
+  t /= uint32_t(p.kc);
+  const int i = int(t % uint32_t(p.q));
+  const int k = int(t / uint32_t(p.q)) * p.kc + kk;
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int wn = wave % WN, wm = wave / WN;
+  const int g = lane >> 4;       // which 8-run of the 32-wide k slab
+  const int l16 = lane & 15;
+
+  int segs[4];
+  const int nseg = device_leaf_groups(p.law, i, k, segs);
+  const int KF = (p.b_in + 31) / 32;
+  const int nsteps = nseg * KF;
+
+  const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
+  const Tin* __restrict__ W0 = static_cast<const Tin*>(p.W0);
+  const Tin* __restrict__ W1 = static_cast<const Tin*>(p.W1);
+  Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
+  const int64_t blk_elems = int64_t(p.b_in) * p.b_out;
+  const int nfrag0 = nt * (TN / 16) + wn * NF;   // first 16-column strip of this wave
+
+  // Explicit typing walks the type array; the others are one tile per group.
+  int64_t scan_pos = 0;
+  for (;;) {
+    int nrows;
+    if (p.kind != AA_TYPES_EXPLICIT) {
+      nrows = tile_rows_closed_form<TM>(p, i, mt, rows_lds);
+    } else {
+      // Wave 0 collects the next TM rows whose type is i.
+      if (wave == 0) {
+        int count = 0;
+        int64_t pos = scan_pos;
+        while (count < TM && pos < p.M) {
+          const int64_t r = pos + lane;
+          const bool hit = r < p.M && p.row_types[r] == i;
+          const uint64_t mask = __ballot(hit);
+          const int total = __popcll(mask);
+          const int take = total < TM - count ? total : TM - count;
+          const int before = __popcll(mask & ((uint64_t(1) << lane) - 1));
+          if (hit && before < take) rows_lds[count + before] = int32_t(r);
+          if (take < total) {
+            // stop after the take-th hit of this chunk
+            uint64_t m = mask;
+            for (int s = 0; s < take - 1; ++s) m &= m - 1;
+            pos += __builtin_ctzll(m) + 1;
+          } else {
+            pos += kWave;
+          }
+          count += take;
+        }
+        for (int r = count + lane; r < TM; r += kWave) rows_lds[r] = -1;
+        if (lane == 0) {
+          scan_state[0] = count;
+          scan_state[1] = int32_t(pos);  // M fits in int32 for explicit maps (checked on the host)
+        }
+      }
+      __syncthreads();
+      nrows = scan_state[0];
+      scan_pos = scan_state[1];
+    }
+    __syncthreads();
+    if (nrows == 0) return;
+
+    // This lane's activation rows (B operand: column m = l16 of each m-fragment).
+    const Tin* xrow[MF];
+    bool rvalid[MF];
+    int32_t rowid[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+      const int r = rows_lds[(wm * MF + f) * 16 + l16];
+      rvalid[f] = r >= 0;
+      rowid[f] = r;
+      xrow[f] = X + int64_t(r >= 0 ? r : 0) * p.ldx;
+    }
+    bool nvalid[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) nvalid[f] = (nfrag0 + f) * 16 < p.b_out;
+
+    f32x4_t acc0[NF][MF], acc1[NF][MF];
+#pragma unroll
+    for (int a = 0; a < NF; ++a)
+#pragma unroll
+      for (int b = 0; b < MF; ++b) {
+        acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+
+    Run<Tin> ra0[STAGES][NF], ra1[STAGES][NF], rb[STAGES][MF];
+
+    auto load_step = [&](int s, Run<Tin>* a0, Run<Tin>* a1, Run<Tin>* b) {
+      const int si = s / KF;
+      const int kf = s - si * KF;
+      const int seg = segs[si < nseg ? si : 0];
+      const bool kval = (s < nsteps) && (kf * 32 + g * 8 < p.b_in);
+      const int64_t wofs = int64_t(seg * p.q + k) * blk_elems + kf * 512 + lane * 8;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int64_t o = wofs + int64_t(nfrag0 + f) * 16 * p.b_in;
+        a0[f] = (kval && nvalid[f]) ? Run<Tin>::load(W0 + o) : Run<Tin>::zero();
+        if (SWIGLU) a1[f] = (kval && nvalid[f]) ? Run<Tin>::load(W1 + o) : Run<Tin>::zero();
+      }
+      const int xo = seg * p.b_in + kf * 32 + g * 8;
+#pragma unroll
+      for (int f = 0; f < MF; ++f)
+        b[f] = (kval && rvalid[f]) ? Run<Tin>::load_cached(xrow[f] + xo) : Run<Tin>::zero();
+    };
+
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) load_step(st, ra0[st], ra1[st], rb[st]);
+
+    for (int s0 = 0; s0 < nsteps; s0 += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) {
+        const int nx = (u + STAGES - 1) % STAGES;
+        load_step(s0 + u + STAGES - 1, ra0[nx], ra1[nx], rb[nx]);
+#pragma unroll
+        for (int a = 0; a < NF; ++a)
+#pragma unroll
+          for (int b = 0; b < MF; ++b) {
+            acc0[a][b] = mma(ra0[u][a], rb[u][b], acc0[a][b]);
+            if (SWIGLU) acc1[a][b] = mma(ra1[u][a], rb[u][b], acc1[a][b]);
+          }
+      }
+    }
+
+    // Epilogue: lane holds Y[row(m = l16)][col .. col + 3] of each fragment.
+    const int64_t col_base = int64_t(k) * p.b_out;
+#pragma unroll
+    for (int a = 0; a < NF; ++a) {
+      if (!nvalid[a]) continue;
+      const int col = (nfrag0 + a) * 16 + g * 4;
+#pragma unroll
+      for (int b = 0; b < MF; ++b) {
+        if (!rvalid[b]) continue;
+        f32x4_t v = acc0[a][b];
+        if (SWIGLU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+        }
+        store4(Y + int64_t(rowid[b]) * p.ldy + col_base + col, v);
+      }
+    }
+    if (p.kind != AA_TYPES_EXPLICIT) return;
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------- decode ---
+
+struct DecodeParams {
+  const void* x;
+  const void* W;
+  void* y;
+  int64_t n;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t q;
+  int32_t b_in;
+  int32_t b_out;
+  int32_t law;
+  int32_t off_mod_q;
+  const int32_t* row_types;
+  int32_t nfr;     // 16-column strips per output group
+  int32_t n_waves; // q * nfr
+};
+
+// One wave computes a 16-column strip of output group k for up to 16 tokens.
+// The diagonal block W_kk is shared by every token, so its strip is one MFMA
+// per k-slab for all 16 tokens.  Each token's other blocks (its own block-row
+// under Q_q) are multiplied with that token's activations placed in its own
+// column of the B operand and zeros elsewhere, accumulating into the same
+// 16 x 16 tile: the weight stream is read once per token, as a GEMV would,
+// while the MFMA does the multiply-adds.
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  const int lane = threadIdx.x % kWave;
+  const int wave_id = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (wave_id >= p.n_waves) return;
+  const int k = wave_id / p.nfr;
+  const int nf = wave_id % p.nfr;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t tok0 = int64_t(blockIdx.y) * 16;
+  const Tin* __restrict__ x = static_cast<const Tin*>(p.x);
+  const Tin* __restrict__ W = static_cast<const Tin*>(p.W);
+  Tout* __restrict__ y = static_cast<Tout*>(p.y);
+  const int KF = (p.b_in + 31) / 32;
+  const int64_t blk_elems = int64_t(p.b_in) * p.b_out;
+  const int64_t strip = int64_t(nf) * 16 * p.b_in + lane * 8;
+
+  // Type of this lane's token (column l16 of the tile).
+  const int64_t my_tok = tok0 + l16;
+  int my_type = -1;
+  if (my_tok < p.n) {
+    my_type = p.row_types ? p.row_types[my_tok] : int((p.off_mod_q + my_tok) % p.q);
+    if (my_type < 0 || my_type >= p.q) my_type = -1;
+  }
+  const bool my_ok = my_type >= 0;
+  const Tin* xr = x + (my_ok ? my_tok : 0) * p.ldx;
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // Shared diagonal block.
+  {
+    const Tin* wk = W + int64_t(k * p.q + k) * blk_elems + strip;
+    for (int kf = 0; kf < KF; ++kf) {
+      const bool kv = kf * 32 + g * 8 < p.b_in;
+      Run<Tin> a = kv ? Run<Tin>::load(wk + kf * 512) : Run<Tin>::zero();
+      Run<Tin> b = (kv && my_ok) ? Run<Tin>::load_cached(xr + k * p.b_in + kf * 32 + g * 8) : Run<Tin>::zero();
+      acc = mma(a, b, acc);
+    }
+  }
+  // Per-token blocks.
+  for (int t = 0; t < 16; ++t) {
+    const int ty = __shfl(my_type, t);   // uniform: token t's type
+    if (ty < 0) continue;
+    int segs[4];
+    const int ns = device_leaf_groups(p.law, ty, k, segs);
+    for (int s = 0; s < ns; ++s) {
+      const int seg = segs[s];
+      if (seg == k) continue;
+      const Tin* wb = W + int64_t(seg * p.q + k) * blk_elems + strip;
+      const bool mine = (l16 == t);
+#pragma unroll 4
+      for (int kf = 0; kf < KF; ++kf) {
+        const bool kv = kf * 32 + g * 8 < p.b_in;
+        Run<Tin> a = kv ? Run<Tin>::load(wb + kf * 512) : Run<Tin>::zero();
+        Run<Tin> b = (kv && mine) ? Run<Tin>::load_cached(xr + seg * p.b_in + kf * 32 + g * 8) : Run<Tin>::zero();
+        acc = mma(a, b, acc);
+      }
+    }
+  }
+  if (my_ok) store4(y + my_tok * p.ldy + int64_t(k) * p.b_out + nf * 16 + g * 4, acc);
+}
+
+// ----------------------------------------------------------------- pack ---
+
+// Thread c moves one run of 8 elements: packed elements [8c, 8c + 8) from/to
+// rows r .. r + 7 of one column of the row-major weight.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, T* __restrict__ dst, int32_t q,
+                                                   int32_t b_in, int32_t b_out, int64_t d_out,
+                                                   int64_t n_runs, bool unpack) {
+  const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= n_runs) return;
+  const int64_t runs_per_blk = int64_t(b_in) * b_out / 8;
+  const int64_t blk = c / runs_per_blk;
+  const int64_t w = c - blk * runs_per_blk;
+  const int64_t j = blk / q, kk = blk % q;
+  const int64_t nt = w / (2 * b_in);          // a 16-column strip holds 2 * b_in runs
+  const int64_t rr = w - nt * 2 * b_in;
+  const int64_t kf = rr / 64, ln = rr % 64;   // slab and lane
+  const int64_t row = j * b_in + kf * 32 + (ln >> 4) * 8;
+  const int64_t col = kk * b_out + nt * 16 + (ln & 15);
+  if (!unpack) {
+    T v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = src[(row + e) * d_out + col];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[c * 8 + e] = v[e];
+  } else {
+    T v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = src[c * 8 + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[(row + e) * d_out + col] = v[e];
+  }
+}
+
+// ------------------------------------------------------------- variants ---
+
+struct Variant {
+  int id;
+  int tn, tm, threads;
+  // launches for each dtype pair
+  void (*bb)(LeafParams, dim3, dim3, hipStream_t);   // bf16 -> bf16
+  void (*bf)(LeafParams, dim3, dim3, hipStream_t);   // bf16 -> f32
+  void (*ff)(LeafParams, dim3, dim3, hipStream_t);   // f32 -> f32
+  void (*fb)(LeafParams, dim3, dim3, hipStream_t);   // f32 -> bf16
+  void (*sbb)(LeafParams, dim3, dim3, hipStream_t);  // SwiGLU bf16 -> bf16
+  void (*sbf)(LeafParams, dim3, dim3, hipStream_t);
+  void (*sff)(LeafParams, dim3, dim3, hipStream_t);
+  void (*sfb)(LeafParams, dim3, dim3, hipStream_t);
+};
+
+template <typename Tin, typename Tout, int WN, int WM, int NF, int MF, bool SW, int ST>
+void launch_variant(LeafParams p, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((leaf_gemm_kernel<Tin, Tout, WN, WM, NF, MF, SW, ST>), grid, block, 0, s, p);
+}
+
+#define AA_VARIANT(ID, WN, WM, NF, MF, ST)                                                        \
+  Variant {                                                                                       \
+    ID, WN * NF * 16, WM * MF * 16, kWave * WN * WM,                                              \
+        launch_variant<__bf16, __bf16, WN, WM, NF, MF, false, ST>,                                \
+        launch_variant<__bf16, float, WN, WM, NF, MF, false, ST>,                                 \
+        launch_variant<float, float, WN, WM, NF, MF, false, ST>,                                  \
+        launch_variant<float, __bf16, WN, WM, NF, MF, false, ST>,                                 \
+        launch_variant<__bf16, __bf16, WN, WM, NF, MF, true, ST>,                                 \
+        launch_variant<__bf16, float, WN, WM, NF, MF, true, ST>,                                  \
+        launch_variant<float, float, WN, WM, NF, MF, true, ST>,                                   \
+        launch_variant<float, __bf16, WN, WM, NF, MF, true, ST>                                   \
+  }
+
+const Variant kVariants[] = {
+    AA_VARIANT(0, 4, 1, 2, 4, 2),   // TN 128, TM 64: few rows per type, wide blocks
+    AA_VARIANT(1, 2, 2, 4, 4, 2),   // TN 128, TM 128
+    AA_VARIANT(2, 1, 4, 3, 2, 2),   // TN 48,  TM 128: narrow output blocks
+    AA_VARIANT(3, 2, 2, 1, 1, 2),   // TN 32,  TM 32: small problems
+    AA_VARIANT(4, 4, 1, 1, 4, 2),   // TN 64,  TM 64
+    AA_VARIANT(5, 4, 1, 2, 4, 3),   // TN 128, TM 64, three stages
+    AA_VARIANT(6, 2, 2, 4, 4, 3),   // TN 128, TM 128, three stages
+};
+constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
+
+int64_t rows_per_type_max(const aa_plan_s& plan, int64_t M) {
+  if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
+  return (M + plan.q - 1) / plan.q;
+}
+
+int choose_variant(const aa_plan_s& plan, int64_t M) {
+  if (plan.tile_override >= 0 && plan.tile_override < kNumVariants) return plan.tile_override;
+  const int64_t mi = rows_per_type_max(plan, M);
+  if (plan.b_out <= 32 || mi <= 32) return 3;
+  if (plan.b_out <= 48) return 2;
+  if (mi <= 64) return 0;
+  return 1;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers ---
+
+aa_status_t after_launch(hipStream_t stream, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(AA_ERR_HIP, std::string(what) + ": launch failed: " + hipGetErrorString(e));
+  static const bool debug = [] {
+    const char* d = getenv("AA_DEBUG");
+    return d && d[0] == '1';
+  }();
+  if (debug) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(AA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  }
+  return AA_OK;
+}
+
+aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  const int vid = choose_variant(plan, call.M);
+  const Variant& v = kVariants[vid];
+  LeafParams p{};
+  p.X = call.X;
+  p.W0 = call.W0;
+  p.W1 = call.W1;
+  p.Y = call.Y;
+  p.M = call.M;
+  p.ldx = plan.d_in;
+  p.ldy = plan.d_out;
+  p.q = plan.q;
+  p.b_in = int32_t(plan.b_in);
+  p.b_out = int32_t(plan.b_out);
+  p.law = plan.law;
+  p.kind = plan.type_kind;
+  p.off_mod_q = int32_t(call.pos_offset % plan.q);
+  p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
+  p.row_types = call.row_types;
+  const int64_t mi = rows_per_type_max(plan, call.M);
+  p.mt_count = plan.type_kind == AA_TYPES_EXPLICIT ? 1 : int32_t((mi + v.tm - 1) / v.tm);
+  p.nt_count = int32_t((plan.b_out + v.tn - 1) / v.tn);
+  int kc = plan.q / kNumXcd;
+  if (kc < 1) kc = 1;
+  while (plan.q % kc) --kc;
+  p.kc = kc;
+  const int64_t n_tiles = int64_t(plan.q) * plan.q * p.mt_count * p.nt_count;
+  if (n_tiles > int64_t(0x7fffffff))
+    return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles for one launch");
+  if (p.mt_count < 1) return AA_OK;
+  p.n_tiles = uint32_t(n_tiles);
+  const dim3 grid{uint32_t(n_tiles), 1, 1}, block{uint32_t(v.threads), 1, 1};
+  const bool fin = plan.in_dtype == AA_F32, fout = plan.out_dtype == AA_F32;
+  void (*fn)(LeafParams, dim3, dim3, hipStream_t);
+  if (!call.swiglu) fn = fin ? (fout ? v.ff : v.fb) : (fout ? v.bf : v.bb);
+  else fn = fin ? (fout ? v.sff : v.sfb) : (fout ? v.sbf : v.sbb);
+  fn(p, grid, block, stream);
+  return after_launch(stream, call.swiglu ? "leaf_gemm(swiglu)" : "leaf_gemm");
+}
+
+aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool unpack, hipStream_t stream) {
+  const int64_t n_runs = plan.d_in * plan.d_out / 8;
+  if (n_runs == 0) return AA_OK;
+  const dim3 block{256, 1, 1}, grid{uint32_t((n_runs + 255) / 256), 1, 1};
+  if (plan.in_dtype == AA_BF16)
+    hipLaunchKernelGGL(pack_kernel<__bf16>, grid, block, 0, stream, static_cast<const __bf16*>(src),
+                       static_cast<__bf16*>(dst), plan.q, int32_t(plan.b_in), int32_t(plan.b_out), plan.d_out,
+                       n_runs, unpack);
+  else
+    hipLaunchKernelGGL(pack_kernel<float>, grid, block, 0, stream, static_cast<const float*>(src),
+                       static_cast<float*>(dst), plan.q, int32_t(plan.b_in), int32_t(plan.b_out), plan.d_out,
+                       n_runs, unpack);
+  return after_launch(stream, unpack ? "unpack" : "pack");
+}
+
+aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, void* y, int64_t n,
+                          int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  DecodeParams p{};
+  p.x = x;
+  p.W = W;
+  p.y = y;
+  p.n = n;
+  p.ldx = plan.d_in;
+  p.ldy = plan.d_out;
+  p.q = plan.q;
+  p.b_in = int32_t(plan.b_in);
+  p.b_out = int32_t(plan.b_out);
+  p.law = plan.law;
+  p.off_mod_q = int32_t(pos_offset % plan.q);
+  p.row_types = row_types;
+  p.nfr = int32_t(plan.b_out / 16);
+  p.n_waves = plan.q * p.nfr;
+  const dim3 block{256, 1, 1}, grid{uint32_t((p.n_waves + 3) / 4), uint32_t((n + 15) / 16), 1};
+  const bool fin = plan.in_dtype == AA_F32, fout = plan.out_dtype == AA_F32;
+  if (fin && fout) hipLaunchKernelGGL((decode_kernel<float, float>), grid, block, 0, stream, p);
+  else if (fin) hipLaunchKernelGGL((decode_kernel<float, __bf16>), grid, block, 0, stream, p);
+  else if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((decode_kernel<__bf16, __bf16>), grid, block, 0, stream, p);
+  return after_launch(stream, "decode_gemv");
+}
+
+}  // namespace aa

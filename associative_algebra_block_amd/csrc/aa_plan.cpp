@@ -1,0 +1,143 @@
+// Host-side plan construction and validation for libaa.so.  Nothing here
+// calls the HIP runtime, so plans can be created and checked on a machine
+// without a GPU.
+//
+// The interaction table (agihunt.info review of "Change the Product, Keep the
+// Parameters", paragraph on the graph multiplication table, and the pilot-law
+// paragraph) is kept in closed form: under Q_q output group k of a row of type
+// i takes input groups {i, k}; under the tensor square of Q2 (q = 4, group
+// g = 2a + b) it takes every (a', b') with a' in {a, a''} and b' in {b, b''}.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "aa_internal.h"
+
+namespace aa {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+void clear_error() { g_last_error.clear(); }
+aa_status_t fail(aa_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+int leaf_groups(aa_law_t law, int q, int i, int k, int* groups) {
+  if (law == AA_LAW_QQ) {
+    groups[0] = i;
+    if (k == i) return 1;
+    groups[1] = k;
+    return 2;
+  }
+  // Q2 x Q2: factors (a, b) of the type and (a2, b2) of the output group.
+  (void)q;
+  const int a = i >> 1, b = i & 1, a2 = k >> 1, b2 = k & 1;
+  int as[2], bs[2];
+  int na = 0, nb = 0;
+  as[na++] = a;
+  if (a2 != a) as[na++] = a2;
+  bs[nb++] = b;
+  if (b2 != b) bs[nb++] = b2;
+  int n = 0;
+  for (int x = 0; x < na; ++x)
+    for (int y = 0; y < nb; ++y) groups[n++] = 2 * as[x] + bs[y];
+  return n;
+}
+
+}  // namespace aa
+
+using aa::fail;
+
+extern "C" {
+
+const char* aa_status_string(aa_status_t s) {
+  switch (s) {
+    case AA_OK: return "AA_OK";
+    case AA_ERR_INVALID_ARG: return "AA_ERR_INVALID_ARG";
+    case AA_ERR_SHAPE: return "AA_ERR_SHAPE";
+    case AA_ERR_UNSUPPORTED: return "AA_ERR_UNSUPPORTED";
+    case AA_ERR_HIP: return "AA_ERR_HIP";
+  }
+  return "AA_ERR_UNKNOWN";
+}
+
+const char* aa_last_error(void) { return aa::g_last_error.c_str(); }
+
+aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in, int64_t d_out,
+                           aa_type_kind_t type_kind, int64_t period, aa_dtype_t in_dtype,
+                           aa_dtype_t out_dtype) {
+  aa::clear_error();
+  if (!out) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: out is NULL");
+  *out = nullptr;
+  if (law != AA_LAW_QQ && law != AA_LAW_Q2XQ2)
+    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown law");
+  if (type_kind != AA_TYPES_POS_MOD && type_kind != AA_TYPES_BLOCK_ROWS && type_kind != AA_TYPES_EXPLICIT)
+    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown type map");
+  if ((in_dtype != AA_BF16 && in_dtype != AA_F32) || (out_dtype != AA_BF16 && out_dtype != AA_F32))
+    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown dtype");
+  if (q < 1) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: q must be >= 1");
+  if (q > 65536) return fail(AA_ERR_UNSUPPORTED, "aa_plan_create: q above 65536");
+  if (law == AA_LAW_Q2XQ2 && q != 4)
+    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: the Q2xQ2 law has exactly q = 4 groups");
+  if (d_in < 1 || d_out < 1) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: widths must be positive");
+  if (d_in % q || d_out % q)
+    return fail(AA_ERR_SHAPE, "aa_plan_create: q must divide d_in and d_out");
+  if (period < 0) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: negative period");
+  if (type_kind == AA_TYPES_POS_MOD && period % q)
+    return fail(AA_ERR_UNSUPPORTED,
+                "aa_plan_create: a period that q does not divide needs AA_TYPES_EXPLICIT");
+  const int64_t b_in = d_in / q, b_out = d_out / q;
+  if (b_in % 16 || b_out % 16)
+    return fail(AA_ERR_UNSUPPORTED, "aa_plan_create: block sides d_in/q and d_out/q must be multiples of 16");
+  if (d_in > (int64_t(1) << 31) || d_out > (int64_t(1) << 31))
+    return fail(AA_ERR_UNSUPPORTED, "aa_plan_create: widths above 2^31");
+
+  aa_plan_s* p = new (std::nothrow) aa_plan_s;
+  if (!p) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: out of host memory");
+  p->law = law;
+  p->q = q;
+  p->d_in = d_in;
+  p->d_out = d_out;
+  p->b_in = b_in;
+  p->b_out = b_out;
+  p->type_kind = type_kind;
+  p->period = period;
+  p->in_dtype = in_dtype;
+  p->out_dtype = out_dtype;
+  int64_t n = 0;
+  int groups[4];
+  for (int i = 0; i < q; ++i)
+    for (int k = 0; k < q; ++k) n += aa::leaf_groups(law, q, i, k, groups);
+  p->n_block_products = n;
+  p->n_leaves = int64_t(q) * q;
+  p->tile_override = -1;
+  if (const char* t = getenv("AA_TILE")) {
+    char* end = nullptr;
+    long v = strtol(t, &end, 10);
+    if (end != t && *end == '\0' && v >= 0) p->tile_override = int32_t(v);
+  }
+  *out = p;
+  return AA_OK;
+}
+
+aa_status_t aa_plan_destroy(aa_plan_t plan) {
+  aa::clear_error();
+  delete plan;
+  return AA_OK;
+}
+
+aa_status_t aa_plan_info(aa_plan_t plan, int64_t* n_block_products, int64_t* n_leaves,
+                         int64_t* packed_elems) {
+  aa::clear_error();
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_plan_info: plan is NULL");
+  if (n_block_products) *n_block_products = plan->n_block_products;
+  if (n_leaves) *n_leaves = plan->n_leaves;
+  if (packed_elems) *packed_elems = plan->d_in * plan->d_out;
+  return AA_OK;
+}
+
+}  // extern "C"

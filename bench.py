@@ -1,0 +1,381 @@
+#!/usr/bin/env python3
+"""Benchmark of the row-typed associative-algebra projection on one MI355X.
+
+One step is one pass of the hot path over one batch of synthetic input at the
+Qwen3-8B-shaped workload (M = 2048 tokens, d_in = 4096, d_out = 12288, Q_32,
+bf16 in and out, fp32 accumulation):
+  1. aa_project_fwd      Y = X * W                      (one leaf-GEMM launch)
+  2. aa_swiglu_ffn_fwd   H = silu(X*Wg)(X*Wu), Y2 = H*Wd  (two leaf-GEMM launches)
+  3. aa_decode_gemv      32 new tokens, one per row type   (one decode launch)
+Inputs are resident in HBM before the timed region.  Two complete input sets
+(about 1.1 GB) alternate between steps so that the 256 MB Infinity Cache
+cannot hold a step's working set (a flushed-cache measurement).
+
+Printed (one JSON line): dense-equivalent TFLOP/s of the step (2 M d_in d_out
+per dense projection counted for every projection in the step), the roofline of
+the projection kernel (algorithmic HBM bytes / its event-timed duration), the
+same for every call, a dense bf16 torch.matmul comparator timed in the same
+run, and the fp64 oracle timed on the host on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload qwen3_8b_q32|square|pilot_ffn|expert_ffn]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_8b_q32",
+                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn"])
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    import aa_inputs as inp
+    import associative_algebra_block_amd as aa
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}), flush=True)
+        sys.exit(1)
+    aa.load()
+    dev = "cuda"
+    torch.manual_seed(0)
+
+    if args.workload == "qwen3_8b_q32":
+        res = bench_qwen3(args, torch, inp, aa, dev)
+    elif args.workload == "square":
+        res = bench_square(args, torch, inp, aa, dev)
+    else:
+        res = bench_ffn(args, torch, inp, aa, dev, args.workload)
+    print(json.dumps(res), flush=True)
+
+
+# ------------------------------------------------------------------ helpers ---
+
+def _ev(torch):
+    return torch.cuda.Event(enable_timing=True)
+
+
+def kernel_source_hash():
+    p = os.path.join(HERE, "associative_algebra_block_amd", "csrc", "aa_kernels.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters, if the committed
+    measurement was taken on the current kernel source; else None."""
+    p = os.path.join(HERE, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    v = rec.get("kernels", {}).get(kernel_key)
+    return None if v is None else v.get("hbm_bytes_per_launch")
+
+
+def roofline(bytes_alg, ms, traffic=None):
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def proj_bytes(M, d_in, d_out, eb_in=2, eb_out=2):
+    return eb_in * (M * d_in + d_in * d_out) + eb_out * M * d_out
+
+
+def exec_flops(M, d_in, d_out, law, q):
+    per = (2 * q - 1) / (q * q) if law == "Qq" else 9 / 16
+    return 2.0 * M * d_in * d_out * per
+
+
+def dense_timer(torch, fn, iters=20, warm=5):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        n = max((d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"), default=1)
+        return int(n)
+    except Exception:
+        return os.cpu_count() or 1
+
+
+# ---------------------------------------------------- Qwen3-8B-shaped step ---
+
+def bench_qwen3(args, torch, inp, aa, dev):
+    wl = inp.WORKLOADS[3]
+    M, D, F, q, law = wl.M, wl.d_in, wl.d_out, wl.q, wl.law
+    n_dec = wl.decode_tokens
+    plan = aa.aa_plan_create(law, q, D, F, "pos_mod", 0, "bf16", "bf16")    # projection and gate/up
+    down = aa.aa_plan_create(law, q, F, D, "pos_mod", 0, "bf16", "bf16")
+
+    set_bytes = 2 * (M * D + 3 * D * F + F * D + M * F * 2 + M * D + n_dec * (D + F))
+    n_sets = args.sets or max(2, math.ceil(1.0e9 / set_bytes))
+    sets = []
+    for s in range(n_sets):
+        seed_off = 100 * s
+        X = inp.gaussian((M, D), inp.seed_for(inp.ROLE_X, 3) + seed_off, 1.0, torch.bfloat16, dev)
+        W = inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, 3) + seed_off, D ** -0.5, torch.bfloat16, dev)
+        Wu = inp.gaussian((D, F), inp.seed_for(inp.ROLE_WU, 3) + seed_off, D ** -0.5, torch.bfloat16, dev)
+        Wd = inp.gaussian((F, D), inp.seed_for(inp.ROLE_WD, 3) + seed_off, F ** -0.5, torch.bfloat16, dev)
+        st = {
+            "X": X, "Wp": aa.pack(plan, W), "Wgp": aa.pack(plan, W), "Wup": aa.pack(plan, Wu),
+            "Wdp": aa.pack(down, Wd), "Y": torch.empty(M, F, dtype=torch.bfloat16, device=dev),
+            "H": torch.empty(M, F, dtype=torch.bfloat16, device=dev),
+            "Y2": torch.empty(M, D, dtype=torch.bfloat16, device=dev),
+            "x": X[:n_dec].clone(), "y": torch.empty(n_dec, F, dtype=torch.bfloat16, device=dev),
+        }
+        # the gate weight is its own tensor, not an alias of the projection weight
+        st["Wgp"] = aa.pack(plan, inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, 3) + seed_off + 50, D ** -0.5,
+                                               torch.bfloat16, dev))
+        del W, Wu, Wd
+        sets.append(st)
+    torch.cuda.synchronize()
+    pos_dec = 4096  # decode positions 4096 .. 4127: one token of every type
+
+    def step(st, evs=None):
+        if evs is not None:
+            evs[0].record()
+        aa.aa_project_fwd(plan, st["X"], st["Wp"], st["Y"])
+        if evs is not None:
+            evs[1].record()
+        aa.aa_swiglu_ffn_fwd(plan, down, st["X"], st["Wgp"], st["Wup"], st["Wdp"], st["H"], st["Y2"])
+        if evs is not None:
+            evs[2].record()
+        aa.aa_decode_gemv(plan, st["x"], st["Wp"], st["y"], None, pos_dec)
+        if evs is not None:
+            evs[3].record()
+
+    for w in range(args.warmup):
+        step(sets[w % n_sets])
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[_ev(torch) for _ in range(4)] for _ in range(K)]
+    t0e, t1e = _ev(torch), _ev(torch)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0e.record()
+    for s in range(K):
+        step(sets[s % n_sets], evs[s])
+    t1e.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_step = t0e.elapsed_time(t1e) / K
+    ms_proj = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    ms_swi = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    ms_dec = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+
+    dense_flops = {"project": 2.0 * M * D * F, "swiglu": 3 * 2.0 * M * D * F, "decode": 2.0 * n_dec * D * F}
+    total_dense = sum(dense_flops.values())
+    value = total_dense / (ms_step * 1e-3) / 1e12
+
+    b_proj = proj_bytes(M, D, F)
+    b_swi = 2 * (M * D + 2 * D * F + M * F) + 2 * (M * F + F * D + M * D)
+    b_dec = 2 * (n_dec * D + D * F + n_dec * F)
+    ex_proj = exec_flops(M, D, F, law, q)
+    parts = {
+        "project": {"ms": round(ms_proj, 5), "dense_equiv_tflops": round(dense_flops["project"] / ms_proj / 1e9, 2),
+                    "exec_tflops": round(ex_proj / ms_proj / 1e9, 2),
+                    "roofline": roofline(b_proj, ms_proj, traffic_for("project_qwen3_8b_q32"))},
+        "swiglu": {"ms": round(ms_swi, 5), "dense_equiv_tflops": round(dense_flops["swiglu"] / ms_swi / 1e9, 2),
+                   "exec_tflops": round(3 * ex_proj / ms_swi / 1e9, 2),
+                   "roofline": roofline(b_swi, ms_swi)},
+        "decode32": {"ms": round(ms_dec, 5), "dense_equiv_tflops": round(dense_flops["decode"] / ms_dec / 1e9, 3),
+                     "roofline": roofline(b_dec, ms_dec)},
+    }
+
+    dense = None
+    if not args.no_dense:
+        st = sets[0]
+        Xd = st["X"]
+        Wd1 = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
+        Wd2 = inp.gaussian((D, F), 998, D ** -0.5, torch.bfloat16, dev)
+        Wd3 = inp.gaussian((F, D), 997, F ** -0.5, torch.bfloat16, dev)
+        xd = st["x"]
+        t_p = dense_timer(torch, lambda: torch.matmul(Xd, Wd1))
+        t_s = dense_timer(torch, lambda: torch.matmul(
+            torch.nn.functional.silu(torch.matmul(Xd, Wd1)) * torch.matmul(Xd, Wd2), Wd3))
+        t_d = dense_timer(torch, lambda: torch.matmul(xd, Wd1))
+        dense = {"kind": "torch.matmul bf16 (hipBLASLt), hot cache, same run",
+                 "project_ms": round(t_p, 5), "swiglu_ms": round(t_s, 5), "decode32_ms": round(t_d, 5),
+                 "speedup_project": round(t_p / ms_proj, 3), "speedup_swiglu": round(t_s / ms_swi, 3),
+                 "speedup_decode32": round(t_d / ms_dec, 3),
+                 "speedup_step": round((t_p + t_s + t_d) / ms_step, 3)}
+        del Wd1, Wd2, Wd3
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_qwen3(args, torch, inp, sets[0], wl)
+
+    return {
+        "metric": "dense-equiv TFLOP/s + % roofline (HBM/MFMA), Qwen3-8B-shape q=32 M=2048 bf16",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3_8b_q32: project + SwiGLU FFN + 32-token decode", "M": M, "d_in": D,
+                   "d_out": F, "q": q, "law": law, "type_map": "pos mod q", "decode_tokens": n_dec,
+                   "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
+        "roofline": parts["project"]["roofline"],
+        "roofline_kernel": "leaf_gemm (aa_project_fwd) at the Qwen3-8B shape",
+        "parts": parts, "dense": dense, "cpu_baseline": cpu,
+        "wall_s_timed": round(wall1 - wall0, 4),
+        "kernel_source": kernel_source_hash(),
+    }
+
+
+def cpu_baseline_qwen3(args, torch, inp, st, wl):
+    """The fp64 oracle on the host, on a bounded sample of the same step: the
+    rows of the first s row types through the projection, the SwiGLU FFN and
+    the decode tokens of those types, scaled to dense-equivalent TFLOP/s."""
+    import numpy as np
+    import oracle
+    M, D, F, q = wl.M, wl.d_in, wl.d_out, wl.q
+    X = st["X"].float().cpu().numpy()
+    # unpacked weights are regenerated from their seeds (the packed copies are device-only)
+    W = inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, 3), D ** -0.5, torch.bfloat16, "cuda").float().cpu().numpy()
+    types = oracle.types_pos_mod(M, q)
+    s = 1
+    t_one = None
+    t_start = time.perf_counter()
+    rows = np.nonzero(types < s)[0]
+    oracle.project(X[rows], W, "Qq", q, types[rows])
+    t_one = time.perf_counter() - t_start
+    # grow the sample toward the time budget (a projection of s types, plus
+    # the two more SwiGLU projections at the same shape, is about 3x that)
+    s = int(max(1, min(q, args.cpu_seconds / max(t_one * 4, 1e-6))))
+    rows = np.nonzero(types < s)[0]
+    Wu = inp.gaussian((D, F), inp.seed_for(inp.ROLE_WU, 3), D ** -0.5, torch.bfloat16, "cuda").float().cpu().numpy()
+    Wdn = inp.gaussian((F, D), inp.seed_for(inp.ROLE_WD, 3), F ** -0.5, torch.bfloat16, "cuda").float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.project(X[rows], W, "Qq", q, types[rows])
+    oracle.swiglu_ffn(X[rows], W, Wu, Wdn, "Qq", q, types[rows])
+    oracle.decode(X[:s], W, "Qq", q, np.arange(s))
+    t = time.perf_counter() - t0
+    n = len(rows)
+    dense = 2.0 * n * D * F * 4 + 2.0 * s * D * F
+    return {"value": round(dense / t / 1e12, 5), "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"rows of row types 0..{s - 1} ({n} of {M} tokens) through the projection and the SwiGLU "
+                      f"FFN plus {s} decode tokens, fp64 numpy, {t:.2f} s",
+            "seconds": round(t, 3)}
+
+
+# ----------------------------------------------------- other workloads ------
+
+def bench_square(args, torch, inp, aa, dev):
+    """Fixed-block square product n = 32768, b = 128, q = 256 (block-row typing)."""
+    n, q = 32768, 256
+    plan = aa.aa_plan_create("Qq", q, n, n, "block_rows", 0, "bf16", "bf16")
+    X = inp.gaussian((n, n), inp.seed_for(inp.ROLE_X, 5), 1.0, torch.bfloat16, dev)
+    W = inp.gaussian((n, n), inp.seed_for(inp.ROLE_W, 5), n ** -0.5, torch.bfloat16, dev)
+    Wp = aa.pack(plan, W)
+    del W
+    Y = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        aa.aa_project_fwd(plan, X, Wp, Y)
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(K):
+        aa.aa_project_fwd(plan, X, Wp, Y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    dense = 2.0 * n ** 3
+    by = proj_bytes(n, n, n)
+    res = {"metric": "dense-equiv TFLOP/s + % roofline, square n=32768 b=128 q=256 bf16",
+           "value": round(dense / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "square_n32768_b128_q256", "n": n, "q": q, "law": "Qq", "type_map": "block rows"},
+           "roofline": roofline(by, ms, traffic_for("project_square_n32768")),
+           "exec_tflops": round(exec_flops(n, n, n, "Qq", q) / ms / 1e9, 2),
+           "kernel_source": kernel_source_hash()}
+    if not args.no_dense:
+        Wd = inp.gaussian((n, n), 999, n ** -0.5, torch.bfloat16, dev)
+        t = dense_timer(torch, lambda: torch.matmul(X, Wd), iters=3, warm=1)
+        res["dense"] = {"kind": "torch.matmul bf16", "ms": round(t, 4), "speedup": round(t / ms, 3)}
+    return res
+
+
+def bench_ffn(args, torch, inp, aa, dev, which):
+    wl = inp.WORKLOADS[2 if which == "pilot_ffn" else 4]
+    M, D, F, q, law = wl.M, wl.d_in, wl.d_out, wl.q, wl.law
+    period = wl.extra.get("period", 0)
+    up = aa.aa_plan_create(law, q, D, F, "pos_mod", period, "bf16", "bf16")
+    down = aa.aa_plan_create(law, q, F, D, "pos_mod", period, "bf16", "bf16")
+    X = inp.gaussian((M, D), inp.seed_for(inp.ROLE_X, wl.index), 1.0, torch.bfloat16, dev)
+    Wg = aa.pack(up, inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, wl.index), D ** -0.5, torch.bfloat16, dev))
+    Wu = aa.pack(up, inp.gaussian((D, F), inp.seed_for(inp.ROLE_WU, wl.index), D ** -0.5, torch.bfloat16, dev))
+    Wd = aa.pack(down, inp.gaussian((F, D), inp.seed_for(inp.ROLE_WD, wl.index), F ** -0.5, torch.bfloat16, dev))
+    H = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    Y = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    f = lambda: aa.aa_swiglu_ffn_fwd(up, down, X, Wg, Wu, Wd, H, Y)
+    ms = dense_timer(torch, f, iters=args.steps, warm=args.warmup)
+    dense = 3 * 2.0 * M * D * F
+    ex = 3 * exec_flops(M, D, F, law, q)
+    by = 2 * (M * D + 2 * D * F + M * F) + 2 * (M * F + F * D + M * D)
+    res = {"metric": f"dense-equiv TFLOP/s, {wl.name} SwiGLU forward bf16",
+           "value": round(dense / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.name, "M": M, "D": D, "F": F, "q": q, "law": law},
+           "exec_tflops": round(ex / ms / 1e9, 2),
+           "roofline_hbm": roofline(by, ms),
+           "roofline_mfma": {"bound": "mfma", "achieved": round(ex / ms / 1e9, 2), "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(ex / ms / 1e9 / BF16_PEAK_TFLOPS, 4)},
+           "kernel_source": kernel_source_hash()}
+    if not args.no_dense:
+        Wd1 = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
+        Wd2 = inp.gaussian((D, F), 998, D ** -0.5, torch.bfloat16, dev)
+        Wd3 = inp.gaussian((F, D), 997, F ** -0.5, torch.bfloat16, dev)
+        t = dense_timer(torch, lambda: torch.matmul(
+            torch.nn.functional.silu(torch.matmul(X, Wd1)) * torch.matmul(X, Wd2), Wd3))
+        res["dense"] = {"kind": "torch.matmul bf16 x3 + silu*mul", "ms": round(t, 5), "speedup": round(t / ms, 3)}
+    return res
+
+
+if __name__ == "__main__":
+    main()

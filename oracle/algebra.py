@@ -157,8 +157,10 @@ def project(X, W, law: str, q: int, types) -> np.ndarray:
     X[t, group j] @ W_jk.  X is M x d_in, W is d_in x d_out, q divides both.
     """
     _check_law(law, q)
-    X = np.asarray(X)
-    W = np.asarray(W)
+    # Anything with .shape and 2-D slicing will do for W (only the blocks the
+    # table names are read); lists are converted.
+    X = X if hasattr(X, "shape") else np.asarray(X)
+    W = W if hasattr(W, "shape") else np.asarray(W)
     types = np.asarray(types, dtype=np.int64)
     M, d_in = X.shape
     if W.shape[0] != d_in:
@@ -192,7 +194,7 @@ def project_block_row(X_rows, W, law: str, q: int, i: int) -> np.ndarray:
     (for example one block-row of a large full product).  Only the weight
     blocks the table row of type i names are read.
     """
-    X_rows = np.asarray(X_rows)
+    X_rows = X_rows if hasattr(X_rows, "shape") else np.asarray(X_rows)
     return project(X_rows, W, law, q, np.full(X_rows.shape[0], i, dtype=np.int64))
 
 

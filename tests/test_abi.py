@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: the library loads, exports every symbol aa.h declares,
+and rejects bad arguments on the host before any launch.  No compute call is
+made (this machine may have no GPU), so every call here must fail validation
+or be a plan call, which touches no HIP API."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import associative_algebra_block_amd as aa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(aa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(aa.lib_path()):
+        pytest.fail("libaa.so is not built (python -m associative_algebra_block_amd.build)")
+    return aa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(aa.EXPORTED) == declared
+
+
+def test_only_aa_symbols_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", aa.lib_path()], capture_output=True, text=True).stdout
+    funcs = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert funcs and all(f.startswith("aa_") for f in funcs), funcs
+
+
+@pytest.mark.parametrize("law,q,n", [("Qq", 1, 1), ("Qq", 2, 6), ("Qq", 3, 15), ("Qq", 16, 496),
+                                     ("Qq", 32, 2016), ("Qq", 256, 130816), ("Q2xQ2", 4, 36)])
+def test_plan_counts(lib, law, q, n):
+    p = aa.aa_plan_create(law, q, 16 * q, 32 * q)
+    nb, nl, pe = aa.aa_plan_info(p)
+    assert nb == n
+    assert nl == q * q
+    assert pe == 16 * q * 32 * q
+    aa.aa_plan_destroy(p)
+
+
+@pytest.mark.parametrize("args,status", [
+    (("Qq", 0, 64, 64), aa.AA_ERR_INVALID_ARG),
+    (("Q2xQ2", 2, 64, 64), aa.AA_ERR_INVALID_ARG),
+    (("Qq", 3, 64, 96), aa.AA_ERR_SHAPE),          # 3 does not divide 64
+    (("Qq", 2, 48, 64), aa.AA_ERR_UNSUPPORTED),    # b_in = 24 is not a multiple of 16
+    (("Qq", 4, 64, 64, "pos_mod", 6), aa.AA_ERR_UNSUPPORTED),  # period not a multiple of q
+    (("Qq", 4, 64, 64, "pos_mod", -4), aa.AA_ERR_INVALID_ARG),
+    (("Qq", 2, -64, 64), aa.AA_ERR_INVALID_ARG),
+])
+def test_plan_rejects(lib, args, status):
+    with pytest.raises(aa.AAError) as e:
+        aa.aa_plan_create(*args)
+    assert e.value.status == status
+    assert aa.aa_last_error()
+
+
+def test_plan_create_null_out(lib):
+    assert lib.aa_plan_create(None, 0, 2, 64, 64, 0, 0, 0, 0) == aa.AA_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    assert aa.aa_status_string(aa.AA_OK) == "AA_OK"
+    assert aa.aa_status_string(aa.AA_ERR_HIP) == "AA_ERR_HIP"
+    assert aa.aa_status_string(99) == "AA_ERR_UNKNOWN"
+
+
+def _raw(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def test_compute_calls_validate_before_launch(lib):
+    p = aa.aa_plan_create("Qq", 2, 64, 64)
+    h = p.handle
+    good = 0x10000
+    # NULL and misaligned pointers
+    assert _raw(lib, "aa_project_fwd", h, None, good, good * 4, 8, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_fwd", h, good + 2, good * 8, good * 16, 8, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    # negative M and offset
+    assert _raw(lib, "aa_project_fwd", h, good, good * 8, good * 16, -1, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_fwd", h, good, good * 8, good * 16, 8, -3, None, None) == aa.AA_ERR_INVALID_ARG
+    # row types given to a position-typed plan
+    assert _raw(lib, "aa_project_fwd", h, good, good * 8, good * 16, 8, 0, good * 32, None) == aa.AA_ERR_INVALID_ARG
+    # Y overlapping X
+    assert _raw(lib, "aa_project_fwd", h, good, good * 8, good + 64, 8, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    # M == 0 is a no-op that succeeds without touching the GPU
+    assert _raw(lib, "aa_project_fwd", h, None, None, None, 0, 0, None, None) == aa.AA_OK
+    # pack with overlapping buffers
+    assert _raw(lib, "aa_pack_weights", h, good, good + 16, None) == aa.AA_ERR_INVALID_ARG
+    # decode: NULL x
+    assert _raw(lib, "aa_decode_gemv", h, None, good, good * 8, 1, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_decode_gemv", h, good, good * 8, good * 16, -1, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    aa.aa_plan_destroy(p)
+
+
+def test_block_rows_needs_divisible_M(lib):
+    p = aa.aa_plan_create("Qq", 4, 64, 64, "block_rows")
+    good = 0x10000
+    assert _raw(lib, "aa_project_fwd", p.handle, good, good * 8, good * 16, 10, 0, None, None) == aa.AA_ERR_SHAPE
+    # decode on a block-row plan needs explicit types
+    assert _raw(lib, "aa_decode_gemv", p.handle, good, good * 8, good * 16, 1, 0, None, None) == aa.AA_ERR_INVALID_ARG
+
+
+def test_explicit_needs_types(lib):
+    p = aa.aa_plan_create("Qq", 4, 64, 64, "explicit")
+    good = 0x10000
+    assert _raw(lib, "aa_project_fwd", p.handle, good, good * 8, good * 16, 8, 0, None, None) == aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_fwd", p.handle, good, good * 8, good * 16, 8, 0, good * 32 + 2, None) == \
+        aa.AA_ERR_INVALID_ARG
+
+
+def test_swiglu_plan_mismatch(lib):
+    up = aa.aa_plan_create("Qq", 4, 64, 128)
+    down_q = aa.aa_plan_create("Qq", 2, 128, 64)
+    down_law = aa.aa_plan_create("Q2xQ2", 4, 128, 64)
+    down_shape = aa.aa_plan_create("Qq", 4, 128, 128)
+    down_dtype = aa.aa_plan_create("Qq", 4, 128, 64, "pos_mod", 0, "f32", "f32")
+    down_kind = aa.aa_plan_create("Qq", 4, 128, 64, "block_rows")
+    g = 0x100000
+    for d, st in [(down_q, aa.AA_ERR_SHAPE), (down_law, aa.AA_ERR_SHAPE), (down_shape, aa.AA_ERR_SHAPE),
+                  (down_dtype, aa.AA_ERR_SHAPE), (down_kind, aa.AA_ERR_SHAPE)]:
+        r = _raw(lib, "aa_swiglu_ffn_fwd", up.handle, d.handle, g, 2 * g, 3 * g, 4 * g, 5 * g, 6 * g, 8, 0, None, None)
+        assert r == st, aa.aa_last_error()
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    with pytest.raises(aa.AAError):
+        aa.aa_plan_create("Qq", 0, 64, 64)
+    mine = aa.aa_last_error()
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(aa.aa_last_error()))
+    t.start()
+    t.join()
+    assert mine and seen == [""]

@@ -1,0 +1,321 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every test here needs an MI355X.  Inputs are seeded (aa_inputs); the oracle
+gets exact host copies of the same bf16/fp32 values the GPU reads.  Each case
+prints its name and shape before its first GPU call.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import aa_inputs as inp
+import associative_algebra_block_amd as aa
+import oracle
+from tests._gpu_util import LazyRows, assert_parity, host, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    aa.load()   # fails loudly when libaa.so is missing
+    say("device", torch.cuda.get_device_name(0))
+
+
+def _types(kind, M, q, pos_offset=0, period=0):
+    if kind == "block_rows":
+        return oracle.types_block_rows(M, q)
+    return oracle.types_pos_mod(M, q, pos_offset, period)
+
+
+def _make(law, q, M, d_in, d_out, in_dt="bf16", out_dt="f32", kind="pos_mod", period=0, seed=0, int_exact=False):
+    plan = aa.aa_plan_create(law, q, d_in, d_out, kind, period, in_dt, out_dt)
+    if int_exact:
+        X = inp.small_integers((M, d_in), seed + 1, dtype=TD[in_dt], device=DEV)
+        W = inp.small_integers((d_in, d_out), seed + 2, dtype=TD[in_dt], device=DEV)
+        # a distinct power-of-two scale per weight block, so a block read from
+        # the wrong place changes the result
+        bi, bo = d_in // q, d_out // q
+        scale = torch.empty(q, q, device=DEV)
+        for j in range(q):
+            for k in range(q):
+                scale[j, k] = 2.0 ** ((5 * j + 3 * k) % 7)
+        W = (W.float().view(q, bi, q, bo) * scale.view(q, 1, q, 1)).view(d_in, d_out).to(TD[in_dt])
+    else:
+        X = inp.gaussian((M, d_in), seed + 1, 1.0, TD[in_dt], DEV)
+        W = inp.gaussian((d_in, d_out), seed + 2, d_in ** -0.5, TD[in_dt], DEV)
+    return plan, X, W
+
+
+def _run_project(plan, X, W, pos_offset=0, row_types=None):
+    Wp = aa.pack(plan, W)
+    Y = torch.empty(X.shape[0], plan.d_out, dtype=plan.out_torch_dtype, device=DEV)
+    aa.aa_project_fwd(plan, X, Wp, Y, None, pos_offset, row_types)
+    torch.cuda.synchronize()
+    return Y
+
+
+# ------------------------------------------------------------- packing ---
+
+@pytest.mark.parametrize("law,q,d_in,d_out,dt", [
+    ("Qq", 2, 64, 64, "f32"), ("Qq", 32, 4096, 12288, "bf16"), ("Qq", 16, 768, 2048, "bf16"),
+    ("Qq", 16, 2048, 768, "bf16"), ("Q2xQ2", 4, 768, 1536, "bf16"), ("Qq", 3, 96, 144, "f32")])
+def test_pack_roundtrip_and_layout(law, q, d_in, d_out, dt):
+    say("pack", law, q, d_in, d_out, dt)
+    plan = aa.aa_plan_create(law, q, d_in, d_out, "pos_mod", 0, dt, dt)
+    W = inp.gaussian((d_in, d_out), 77, 1.0, TD[dt], DEV)
+    P = aa.pack(plan, W)
+    back = torch.empty_like(W)
+    aa.aa_unpack_weights(plan, P, back)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16 if dt == "bf16" else torch.int32),
+                       W.view(torch.int16 if dt == "bf16" else torch.int32))
+    # the documented layout, element by element, on a sample of runs
+    bi, bo = d_in // q, d_out // q
+    Wh, Ph = W.float().cpu().numpy(), P.float().cpu().numpy()
+    rng = np.random.default_rng(0)
+    runs = rng.integers(0, d_in * d_out // 8, 4000)
+    for c in runs:
+        blk, w = divmod(int(c), bi * bo // 8)
+        j, k = divmod(blk, q)
+        nt, rr = divmod(w, 2 * bi)
+        kf, ln = divmod(rr, 64)
+        row = j * bi + kf * 32 + (ln // 16) * 8
+        col = k * bo + nt * 16 + ln % 16
+        assert np.array_equal(Ph[c * 8:(c + 1) * 8], Wh[row:row + 8, col]), (c, j, k, nt, kf, ln)
+
+
+# ------------------------------------------------- integer-exact routing ---
+
+@pytest.mark.parametrize("law,q,M,d_in,d_out,kind,in_dt", [
+    ("Qq", 32, 96, 4096, 12288, "pos_mod", "bf16"),     # q = 32 blocks 128 x 384, 3 rows per type
+    ("Qq", 16, 272, 2048, 768, "pos_mod", "bf16"),      # narrow 128 x 48 blocks, ragged
+    ("Qq", 16, 272, 768, 2048, "pos_mod", "bf16"),      # 48 x 128 blocks (odd multiple of 16)
+    ("Q2xQ2", 4, 520, 768, 1536, "pos_mod", "bf16"),
+    ("Qq", 8, 1024, 256, 256, "block_rows", "bf16"),
+    ("Qq", 2, 256, 64, 64, "pos_mod", "f32"),
+    ("Qq", 1, 40, 64, 48, "pos_mod", "bf16"),
+])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_integer_exact(law, q, M, d_in, d_out, kind, in_dt, out_dt):
+    say("int-exact", law, q, M, d_in, d_out, kind, in_dt, out_dt)
+    plan, X, W = _make(law, q, M, d_in, d_out, in_dt, out_dt, kind, seed=11, int_exact=True)
+    Y = _run_project(plan, X, W, pos_offset=3 if kind == "pos_mod" else 0)
+    ref = oracle.project(host(X), host(W), law, q, _types(kind, M, q, 3 if kind == "pos_mod" else 0))
+    assert np.abs(ref).max() < 2 ** 24
+    want = torch.from_numpy(ref).float()
+    if out_dt == "bf16":
+        want = want.to(torch.bfloat16)
+    got = Y.cpu()
+    assert torch.equal(got.view(torch.int16 if out_dt == "bf16" else torch.int32),
+                       want.view(torch.int16 if out_dt == "bf16" else torch.int32))
+
+
+# ---------------------------------------------- projection parity (float) ---
+
+@pytest.mark.parametrize("law,q,M,d_in,d_out,kind", [
+    ("Qq", 8, 1000, 512, 768, "pos_mod"),        # several tiles and a ragged tail
+    ("Qq", 4, 1, 256, 128, "pos_mod"),           # a single token
+    ("Qq", 32, 2048, 4096, 12288, "pos_mod"),    # the Qwen3-8B-shaped projection, full size
+    ("Q2xQ2", 4, 4100, 768, 1536, "pos_mod"),
+    ("Qq", 64, 8192, 8192, 8192, "block_rows"),  # full product, 128 x 128 blocks
+])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_project_parity(law, q, M, d_in, d_out, kind, out_dt):
+    say("project", law, q, M, d_in, d_out, kind, out_dt)
+    plan, X, W = _make(law, q, M, d_in, d_out, "bf16", out_dt, kind, seed=21)
+    Y = _run_project(plan, X, W, pos_offset=5 if kind == "pos_mod" else 0)
+    ref = oracle.project(host(X), host(W), law, q, _types(kind, M, q, 5 if kind == "pos_mod" else 0))
+    assert_parity(host(Y), ref, out_dt == "bf16", f"project {law} q={q} M={M}")
+
+
+def test_every_tile_variant_agrees():
+    """The tuning override picks each kernel variant in turn; all must match."""
+    law, q, M, d_in, d_out = "Qq", 8, 700, 512, 768
+    say("variants", law, q, M, d_in, d_out)
+    ref = None
+    for v in range(7):
+        os.environ["AA_TILE"] = str(v)
+        try:
+            plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=31)
+        finally:
+            del os.environ["AA_TILE"]
+        Y = _run_project(plan, X, W, pos_offset=2)
+        if ref is None:
+            ref = oracle.project(host(X), host(W), law, q, _types("pos_mod", M, q, 2))
+        assert_parity(host(Y), ref, False, f"variant {v}")
+
+
+def test_config1_q2_f32_full_product_and_associativity():
+    """Q_2 in fp32: row-typed projection, the full 64 x 64 product, and
+    (X * W1) * W2 == X * (W1 * W2) computed on the GPU."""
+    wl = inp.WORKLOADS[1]
+    say("config1", wl)
+    plan = aa.aa_plan_create("Qq", 2, 64, 64, "pos_mod", 0, "f32", "f32")
+    full = aa.aa_plan_create("Qq", 2, 64, 64, "block_rows", 0, "f32", "f32")
+    X = inp.gaussian((256, 64), inp.seed_for(inp.ROLE_X, 1), 1.0, torch.float32, DEV)
+    W1 = inp.gaussian((64, 64), inp.seed_for(inp.ROLE_W, 1), 64 ** -0.5, torch.float32, DEV)
+    W2 = inp.gaussian((64, 64), inp.seed_for(inp.ROLE_W2, 1), 64 ** -0.5, torch.float32, DEV)
+    Y = _run_project(plan, X, W1)
+    assert_parity(host(Y), oracle.project(host(X), host(W1), "Qq", 2, oracle.types_pos_mod(256, 2)), False,
+                  "config1 project")
+    Xs = X[:64].contiguous()
+    XW = _run_project(full, Xs, W1)
+    assert_parity(host(XW), oracle.star(host(Xs), host(W1), "Qq", 2), False, "config1 X*W")
+    lhs = _run_project(full, XW, W2)
+    W12 = _run_project(full, W1, W2)
+    rhs = _run_project(full, Xs, W12)
+    ref = oracle.star(oracle.star(host(Xs), host(W1), "Qq", 2), host(W2), "Qq", 2)
+    assert_parity(host(lhs), ref, False, "config1 (X*W1)*W2")
+    assert_parity(host(rhs), ref, False, "config1 X*(W1*W2)")
+    # the two GPU sides agree with each other to fp32 rounding
+    assert np.max(np.abs(host(lhs) - host(rhs))) <= 1e-4 * np.sqrt(np.mean(ref ** 2))
+
+
+# ------------------------------------------------------------ properties ---
+
+def test_deterministic_and_pos_shift():
+    law, q, M, d_in, d_out = "Qq", 16, 1024, 2048, 2048
+    say("determinism", law, q, M)
+    plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "bf16", seed=41)
+    Wp = aa.pack(plan, W)
+    outs = []
+    for off in (7, 7, 7 + q, 8):
+        Y = torch.empty(M, d_out, dtype=torch.bfloat16, device=DEV)
+        aa.aa_project_fwd(plan, X, Wp, Y, None, off)
+        outs.append(Y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])         # bitwise deterministic
+    assert torch.equal(outs[0], outs[2])         # a shift by q changes no type
+    assert not torch.equal(outs[0], outs[3])     # a shift by 1 changes every type
+    ref = oracle.project(host(X), host(W), law, q, oracle.types_pos_mod(M, q, 8))
+    assert_parity(host(outs[3]), ref, True, "shift by one")
+
+
+def test_period_and_empty():
+    law, q, M, d_in, d_out = "Q2xQ2", 4, 3 * 24, 256, 512
+    say("period", law, q, M)
+    plan = aa.aa_plan_create(law, q, d_in, d_out, "pos_mod", 24, "bf16", "f32")
+    _, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=51)
+    Y = _run_project(plan, X, W, pos_offset=4)
+    ref = oracle.project(host(X), host(W), law, q, oracle.types_pos_mod(M, q, 4, 24))
+    assert_parity(host(Y), ref, False, "period 24")
+    E = torch.empty(0, d_in, dtype=torch.bfloat16, device=DEV)
+    Yo = torch.empty(0, d_out, dtype=torch.float32, device=DEV)
+    aa.aa_project_fwd(plan, E, aa.pack(plan, W), Yo)
+    torch.cuda.synchronize()
+
+
+def test_explicit_types():
+    law, q, M, d_in, d_out = "Qq", 8, 333, 512, 256
+    say("explicit", law, q, M)
+    plan = aa.aa_plan_create(law, q, d_in, d_out, "explicit", 0, "bf16", "f32")
+    _, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=61)
+    types = inp.random_types(M, q, 62, DEV)
+    Y = _run_project(plan, X, W, row_types=types)
+    ref = oracle.project(host(X), host(W), law, q, types.cpu().numpy())
+    assert_parity(host(Y), ref, False, "explicit")
+
+
+def test_row_locality():
+    law, q, M, d_in, d_out = "Qq", 4, 64, 256, 256
+    say("row locality", law, q, M)
+    plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=71)
+    Y1 = _run_project(plan, X, W)
+    X2 = X.clone()
+    X2[::3] = inp.gaussian((X2[::3].shape[0], d_in), 72, 1.0, torch.bfloat16, DEV)
+    Y2 = _run_project(plan, X2, W)
+    keep = [t for t in range(M) if t % 3]
+    assert torch.equal(Y1[keep], Y2[keep])
+
+
+# ---------------------------------------------------------------- decode ---
+
+@pytest.mark.parametrize("law,q,d_in,d_out,n", [("Qq", 32, 4096, 12288, 32), ("Qq", 32, 4096, 12288, 1),
+                                                 ("Q2xQ2", 4, 768, 1536, 7), ("Qq", 16, 768, 2048, 20)])
+def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n):
+    say("decode", law, q, d_in, d_out, n)
+    plan, X, W = _make(law, q, 64, d_in, d_out, "bf16", "f32", seed=81)
+    Wp = aa.pack(plan, W)
+    pos0 = 1000 + 3
+    x = X[:n].contiguous()
+    y = torch.empty(n, d_out, dtype=torch.float32, device=DEV)
+    aa.aa_decode_gemv(plan, x, Wp, y, None, pos0)
+    # prefill of the same rows at the same positions through the leaf kernel
+    Yp = torch.empty(n, d_out, dtype=torch.float32, device=DEV)
+    aa.aa_project_fwd(plan, x, Wp, Yp, None, pos0)
+    torch.cuda.synchronize()
+    ref = oracle.decode(host(x), host(W), law, q, pos0 + np.arange(n))
+    assert_parity(host(y), ref, False, "decode")
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(host(y) - host(Yp))) <= 1e-4 * rms
+    # explicit per-token types (mixed positions)
+    types = inp.random_types(n, q, 82, DEV)
+    aa.aa_decode_gemv(plan, x, Wp, y, None, 0, types)
+    torch.cuda.synchronize()
+    assert_parity(host(y), oracle.project(host(x), host(W), law, q, types.cpu().numpy()), False, "decode explicit")
+
+
+# ---------------------------------------------------------------- SwiGLU ---
+
+def _swiglu_case(law, q, M, D, F, out_dt, seed, pos_offset=0, period=0):
+    up = aa.aa_plan_create(law, q, D, F, "pos_mod", period, "bf16", "bf16")
+    down = aa.aa_plan_create(law, q, F, D, "pos_mod", period, "bf16", out_dt)
+    X = inp.gaussian((M, D), seed + 1, 1.0, torch.bfloat16, DEV)
+    Wg = inp.gaussian((D, F), seed + 2, D ** -0.5, torch.bfloat16, DEV)
+    Wu = inp.gaussian((D, F), seed + 3, D ** -0.5, torch.bfloat16, DEV)
+    Wd = inp.gaussian((F, D), seed + 4, F ** -0.5, torch.bfloat16, DEV)
+    H = torch.empty(M, F, dtype=torch.bfloat16, device=DEV)
+    Y = torch.empty(M, D, dtype=TD[out_dt], device=DEV)
+    aa.aa_swiglu_ffn_fwd(up, down, X, aa.pack(up, Wg), aa.pack(up, Wu), aa.pack(down, Wd), H, Y, None, pos_offset)
+    torch.cuda.synchronize()
+    types = oracle.types_pos_mod(M, q, pos_offset, period)
+    Href, Yref = oracle.swiglu_ffn(host(X), host(Wg), host(Wu), host(Wd), law, q, types)
+    return H, Y, Href, Yref
+
+
+@pytest.mark.parametrize("name,law,q,M,D,F,period", [
+    ("small ragged", "Qq", 8, 999, 512, 1024, 0),
+    ("pilot Q2xQ2 FFN (full)", "Q2xQ2", 4, 8 * 1536, 768, 1536, 1536),
+    ("Qwen3-8B SwiGLU (full)", "Qq", 32, 2048, 4096, 12288, 0),
+    ("Qwen3-30B-A3B expert (full)", "Qq", 16, 2048, 2048, 768, 0),
+])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_swiglu_parity(name, law, q, M, D, F, period, out_dt):
+    say("swiglu", name, law, q, M, D, F, out_dt)
+    H, Y, Href, Yref = _swiglu_case(law, q, M, D, F, out_dt, 1000 * q + M % 97, 0, period)
+    assert_parity(host(H), Href, True, f"{name} H")
+    assert_parity(host(Y), Yref, out_dt == "bf16", f"{name} Y")
+
+
+# ------------------------------------------- full square product (sampled) ---
+
+def test_square_product_full_size_sampled():
+    """n = 32768, b = 128, q = 256, every block-row computed on the GPU in the
+    benchmark's launch configuration; the oracle checks sampled block-rows in
+    full and a sample of single rows elsewhere."""
+    n, q = 32768, 256
+    say("square", n, q)
+    plan = aa.aa_plan_create("Qq", q, n, n, "block_rows", 0, "bf16", "bf16")
+    X = inp.gaussian((n, n), inp.seed_for(inp.ROLE_X, 5), 1.0, torch.bfloat16, DEV)
+    W = inp.gaussian((n, n), inp.seed_for(inp.ROLE_W, 5), n ** -0.5, torch.bfloat16, DEV)
+    Wp = aa.pack(plan, W)
+    Y = torch.empty(n, n, dtype=torch.bfloat16, device=DEV)
+    aa.aa_project_fwd(plan, X, Wp, Y)
+    torch.cuda.synchronize()
+    Wl = LazyRows(W)
+    b = n // q
+    for i in (0, 137, 255):
+        rows = slice(i * b, (i + 1) * b)
+        ref = oracle.project_block_row(host(X[rows]), Wl, "Qq", q, i)
+        assert_parity(host(Y[rows]), ref, True, f"square block-row {i}")
+    rng = np.random.default_rng(5)
+    for r in rng.integers(0, n, 6):
+        i = int(r) // b
+        ref = oracle.project_block_row(host(X[int(r):int(r) + 1]), Wl, "Qq", q, i)
+        assert_parity(host(Y[int(r):int(r) + 1]), ref, True, f"square row {int(r)}")
