@@ -50,6 +50,14 @@ constexpr int kWave = 64;
 
 // ------------------------------------------------------------ fragments ---
 
+// Loads that fall outside the operands (rows past a type's last row, k past
+// the end of a block, pipeline steps past the last one) read from this
+// all-zero buffer instead of branching around the load: the kernels stay
+// branch-free between issuing a load and using it, so the compiler can keep
+// several steps of loads in flight (counted waits instead of full drains).
+// 64 lanes x 32 bytes covers an fp32 run of 8 values per lane.
+__device__ __attribute__((aligned(256))) uint32_t g_zero_runs[64 * 8];
+
 // Eight consecutive k values of one lane, in the input element type.
 template <typename T> struct Run;
 template <> struct Run<__bf16> {
@@ -112,6 +120,16 @@ __device__ inline void store4(__bf16* p, f32x4_t v) {
   *reinterpret_cast<bf16x4_t*>(p) = o;
 }
 __device__ inline void store4(float* p, f32x4_t v) { *reinterpret_cast<f32x4_t*>(p) = v; }
+// Streaming stores of outputs that are not read again by this kernel.
+__device__ inline void store4_nt(__bf16* p, f32x4_t v) {
+  bf16x4_t o;
+  o[0] = (__bf16)v[0];
+  o[1] = (__bf16)v[1];
+  o[2] = (__bf16)v[2];
+  o[3] = (__bf16)v[3];
+  __builtin_nontemporal_store(__builtin_bit_cast(unsigned long long, o), reinterpret_cast<unsigned long long*>(p));
+}
+__device__ inline void store4_nt(float* p, f32x4_t v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p)); }
 
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
@@ -153,6 +171,7 @@ struct LeafParams {
   int32_t nt_count;        // n-tiles per leaf
   int32_t kc;              // output groups per tile-order chunk
   uint32_t n_tiles;
+  int32_t cpr;             // streaming kernel: 16-byte LDS chunks per staged activation row
 };
 
 // Rows of type i, in order; fills rows[0..TM) for m-tile mt and returns how
@@ -178,6 +197,24 @@ __device__ inline int tile_rows_closed_form(const LeafParams& p, int i, int mt, 
   return n;
 }
 
+// XCD-aware tile numbering: XCD x (= blockIdx.x mod 8) receives a contiguous
+// run of the tile order (output-group chunk, row type, output group in the
+// chunk, m-tile, n-tile).
+__device__ inline void decode_tile(const LeafParams& p, int& i, int& k, int& mt, int& nt) {
+  const uint32_t bid = blockIdx.x;
+  const uint32_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  nt = int(t % uint32_t(p.nt_count));
+  t /= uint32_t(p.nt_count);
+  mt = int(t % uint32_t(p.mt_count));
+  t /= uint32_t(p.mt_count);
+  const int kk = int(t % uint32_t(p.kc));
+  t /= uint32_t(p.kc);
+  i = int(t % uint32_t(p.q));
+  k = int(t / uint32_t(p.q)) * p.kc + kk;
+}
+
 template <typename Tin, typename Tout, int WN, int WM, int NF, int MF, bool SWIGLU, int STAGES>
 __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p) {
   constexpr int TN = WN * NF * 16;
@@ -185,20 +222,8 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
   __shared__ int32_t rows_lds[TM];
   __shared__ int32_t scan_state[2];
 
-  // XCD-aware tile numbering: XCD x (= blockIdx.x mod 8) receives a
-  // contiguous run of the tile order.
-  const uint32_t bid = blockIdx.x;
-  const uint32_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
-  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
-  uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int nt = int(t % uint32_t(p.nt_count));
-  t /= uint32_t(p.nt_count);
-  const int mt = int(t % uint32_t(p.mt_count));
-  t /= uint32_t(p.mt_count);
-  const int kk = int(t % uint32_t(p.kc));
-  t /= uint32_t(p.kc);
-  const int i = int(t % uint32_t(p.q));
-  const int k = int(t / uint32_t(p.q)) * p.kc + kk;
+  int i, k, mt, nt;
+  decode_tile(p, i, k, mt, nt);
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -286,6 +311,7 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
 
     Run<Tin> ra0[STAGES][NF], ra1[STAGES][NF], rb[STAGES][MF];
 
+    const Tin* zrun = reinterpret_cast<const Tin*>(g_zero_runs) + lane * 8;
     auto load_step = [&](int s, Run<Tin>* a0, Run<Tin>* a1, Run<Tin>* b) {
       const int si = s / KF;
       const int kf = s - si * KF;
@@ -295,13 +321,13 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int64_t o = wofs + int64_t(nfrag0 + f) * 16 * p.b_in;
-        a0[f] = (kval && nvalid[f]) ? Run<Tin>::load(W0 + o) : Run<Tin>::zero();
-        if (SWIGLU) a1[f] = (kval && nvalid[f]) ? Run<Tin>::load(W1 + o) : Run<Tin>::zero();
+        const bool ok = kval && nvalid[f];
+        a0[f] = Run<Tin>::load(ok ? W0 + o : zrun);
+        if (SWIGLU) a1[f] = Run<Tin>::load(ok ? W1 + o : zrun);
       }
       const int xo = seg * p.b_in + kf * 32 + g * 8;
 #pragma unroll
-      for (int f = 0; f < MF; ++f)
-        b[f] = (kval && rvalid[f]) ? Run<Tin>::load_cached(xrow[f] + xo) : Run<Tin>::zero();
+      for (int f = 0; f < MF; ++f) b[f] = Run<Tin>::load_cached((kval && rvalid[f]) ? xrow[f] + xo : zrun);
     };
 
 #pragma unroll
@@ -341,6 +367,203 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
     }
     if (p.kind != AA_TYPES_EXPLICIT) return;
     __syncthreads();
+  }
+}
+
+
+// ------------------------------------------------------ streaming leaf GEMM ---
+//
+// For the memory-bound shapes (few rows per type, every weight read once) the
+// leaf's activation tile - TM rows by the whole concatenated K - is copied
+// into LDS once per workgroup with direct global-to-LDS loads, and each wave
+// streams its strips of the packed weight through two register buffers of CK
+// k-slabs each: while one chunk of slabs is multiplied the next is in flight.
+// A chunk never straddles two input groups, so all address arithmetic happens
+// once per chunk and the k-slabs inside it are immediate offsets; the scalar
+// unit, which the four SIMDs of a CU share, stays off the critical path.
+//
+// LDS layout of the activation tile: row r starts at byte r * (cpr + 1) * 16;
+// its cpr 16-byte chunks hold the concatenated K (zero-padded), followed by
+// one pad chunk.  With cpr a multiple of 16 the pad makes the 16 rows of a
+// B-operand read fall into 16 distinct groups of four banks.
+//
+// Only bf16 inputs with closed-form row maps and b_in a multiple of 32 * CK
+// take this path; the host falls back to the general kernel otherwise.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+template <int WN, int WM, int NF, int MF, int CK, bool SWIGLU, typename Tout>
+__global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams p) {
+  using Tin = __bf16;
+  constexpr int NWAVE = WN * WM;
+  constexpr int TN = WN * NF * 16;
+  constexpr int TM = WM * MF * 16;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __shared__ int32_t rows_lds[TM];
+
+  int i, k, mt, nt;
+  decode_tile(p, i, k, mt, nt);
+  const int nrows = tile_rows_closed_form<TM>(p, i, mt, rows_lds);
+  __syncthreads();
+  if (nrows == 0) return;
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int wn = wave % WN, wm = wave / WN;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+
+  int segs[4];
+  const int nseg = device_leaf_groups(p.law, i, k, segs);
+  const int cps = p.b_in / 8;                 // 16-byte chunks of one segment row
+  const int used = nseg * cps;
+  const int rstride = p.cpr + 1;              // chunks per LDS row, pad included
+  const int chunks_per_seg = p.b_in / (32 * CK);
+  const int nchunks = nseg * chunks_per_seg;
+
+  const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
+  Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
+  // 1. Activation tile -> LDS.  Wave-instruction j fills physical chunks
+  //    [64 j, 64 j + 64); each lane fetches the logical chunk stored there.
+  //    Lanes whose chunk is padding, lies past the leaf's K or belongs to a
+  //    row past the type's last row do not load: those LDS bytes are never
+  //    read into a kept output.
+  {
+    const int n_inst = (TM * rstride + 63) / 64;
+    for (int j = wave; j < n_inst; j += NWAVE) {
+      const int P = j * 64 + lane;
+      const int r = P / rstride;
+      const int c = P - r * rstride;
+      if (r < nrows && c < used) {
+        const int row = rows_lds[r];
+        const int sg = c / cps;
+        const Tin* src = X + int64_t(row) * p.ldx + segs[sg] * p.b_in + (c - sg * cps) * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)((lds_u8_t*)smem + j * 1024), 16, 0, 0);
+      }
+    }
+  }
+
+  // 2. Weight strips.  wl: this lane's byte offset inside a block (strip of
+  //    its first n-fragment, its run in the slab).  Chunk c covers k-slabs
+  //    [kf0, kf0 + CK) of segment c / chunks_per_seg.
+  const int nfrag0 = nt * (TN / 16) + wn * NF;
+  bool nvalid[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) nvalid[f] = (nfrag0 + f) * 16 < p.b_out;
+  const int64_t blk_bytes = int64_t(p.b_in) * p.b_out * 2;
+  const int64_t fstride = int64_t(16) * p.b_in * 2;        // bytes between 16-column strips
+  const int64_t wl = int64_t(nfrag0) * fstride + lane * 16;
+  const unsigned char* W0 = static_cast<const unsigned char*>(p.W0);
+  const unsigned char* W1 = static_cast<const unsigned char*>(p.W1);
+
+  auto chunk_ofs = [&](int c) -> int64_t {   // byte offset of chunk c's first slab, lane part excluded
+    const int si = c / chunks_per_seg;
+    const int kf0 = (c - si * chunks_per_seg) * CK;
+    return int64_t(segs[si] * p.q + k) * blk_bytes + kf0 * 1024;
+  };
+  // Strips past the block's last column read the block's first strip instead
+  // (their products are never stored), so every load hits real weight lines.
+  int64_t fofs[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) fofs[f] = (nvalid[f] ? int64_t(f) * fstride + wl : int64_t(lane) * 16);
+  auto load_chunk = [&](int c, Run<Tin> (&a0)[CK][NF], Run<Tin> (&a1)[CK][NF]) {
+    const int64_t base = chunk_ofs(c);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+      for (int kl = 0; kl < CK; ++kl) {
+        const int64_t o = base + fofs[f] + kl * 1024;
+        a0[kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
+        if (SWIGLU) a1[kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
+      }
+    }
+  };
+
+  Run<Tin> bufA0[CK][NF], bufA1[CK][NF], bufB0[CK][NF], bufB1[CK][NF];
+  load_chunk(0, bufA0, bufA1);
+
+  __syncthreads();   // activation tile resident (the wait covers every load above)
+
+  f32x4_t acc0[NF][MF], acc1[NF][MF];
+#pragma unroll
+  for (int a = 0; a < NF; ++a)
+#pragma unroll
+    for (int b = 0; b < MF; ++b) {
+      acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // Byte offset in LDS of this lane's B-operand run for m-fragment b at k-slab 0.
+  int xaddr[MF];
+#pragma unroll
+  for (int b = 0; b < MF; ++b) xaddr[b] = ((wm * MF + b) * 16 + l16) * rstride * 16 + g * 16;
+
+  auto compute_chunk = [&](int c, Run<Tin> (&a0)[CK][NF], Run<Tin> (&a1)[CK][NF]) {
+    const int si = c / chunks_per_seg;
+    const int cofs = (si * cps + (c - si * chunks_per_seg) * CK * 4) * 16;   // chunk's first LDS column, bytes
+#pragma unroll
+    for (int kl = 0; kl < CK; ++kl) {
+      Run<Tin> xb[MF];
+#pragma unroll
+      for (int b = 0; b < MF; ++b) xb[b].v = *reinterpret_cast<const u32x4_t*>(smem + xaddr[b] + cofs + kl * 64);
+#pragma unroll
+      for (int a = 0; a < NF; ++a)
+#pragma unroll
+        for (int b = 0; b < MF; ++b) {
+          acc0[a][b] = mma(a0[kl][a], xb[b], acc0[a][b]);
+          if (SWIGLU) acc1[a][b] = mma(a1[kl][a], xb[b], acc1[a][b]);
+        }
+    }
+  };
+
+  // Double-buffered chunk loop; the last one or two chunks are peeled so that
+  // no load is issued past the leaf's end.
+  int c = 0;
+  for (; c + 2 < nchunks; c += 2) {
+    load_chunk(c + 1, bufB0, bufB1);
+    compute_chunk(c, bufA0, bufA1);
+    load_chunk(c + 2, bufA0, bufA1);
+    compute_chunk(c + 1, bufB0, bufB1);
+  }
+  if (c + 1 < nchunks) {
+    load_chunk(c + 1, bufB0, bufB1);
+    compute_chunk(c, bufA0, bufA1);
+    compute_chunk(c + 1, bufB0, bufB1);
+  } else {
+    compute_chunk(c, bufA0, bufA1);
+  }
+
+  // 3. Epilogue.  Lane holds Y[m = l16][n .. n + 3] of each fragment; the
+  //    tile goes through LDS (row stride TN + 8 elements) so that the global
+  //    stores are whole 16-byte runs along rows.
+  __syncthreads();   // every wave is done reading the activation tile
+  constexpr int OSTR = TN + 8;   // elements per LDS output row
+  Tout* otile = reinterpret_cast<Tout*>(smem);
+#pragma unroll
+  for (int b = 0; b < MF; ++b) {
+    const int m = (wm * MF + b) * 16 + l16;
+#pragma unroll
+    for (int a = 0; a < NF; ++a) {
+      f32x4_t v = acc0[a][b];
+      if (SWIGLU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+      }
+      store4(otile + m * OSTR + (wn * NF + a) * 16 + g * 4, v);
+    }
+  }
+  __syncthreads();
+  constexpr int VPR = TN * int(sizeof(Tout)) / 16;   // 16-byte runs per tile row
+  const int64_t col0 = int64_t(k) * p.b_out + int64_t(nt) * TN;
+  const int ncols = p.b_out - nt * TN < TN ? p.b_out - nt * TN : TN;
+  for (int e = threadIdx.x; e < TM * VPR; e += kWave * NWAVE) {
+    const int r = e / VPR, v = e - r * VPR;
+    const int col = v * (16 / int(sizeof(Tout)));
+    if (r < nrows && col < ncols) {
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + r * OSTR + col);
+      *reinterpret_cast<u32x4_t*>(Y + int64_t(rows_lds[r]) * p.ldy + col0 + col) = val;
+    }
   }
 }
 
@@ -395,6 +618,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
   const bool my_ok = my_type >= 0;
   const Tin* xr = x + (my_ok ? my_tok : 0) * p.ldx;
+  const Tin* zrun = reinterpret_cast<const Tin*>(g_zero_runs) + lane * 8;
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   // Shared diagonal block.
@@ -402,8 +626,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const Tin* wk = W + int64_t(k * p.q + k) * blk_elems + strip;
     for (int kf = 0; kf < KF; ++kf) {
       const bool kv = kf * 32 + g * 8 < p.b_in;
-      Run<Tin> a = kv ? Run<Tin>::load(wk + kf * 512) : Run<Tin>::zero();
-      Run<Tin> b = (kv && my_ok) ? Run<Tin>::load_cached(xr + k * p.b_in + kf * 32 + g * 8) : Run<Tin>::zero();
+      Run<Tin> a = Run<Tin>::load(kv ? wk + kf * 512 : zrun);
+      Run<Tin> b = Run<Tin>::load_cached((kv && my_ok) ? xr + k * p.b_in + kf * 32 + g * 8 : zrun);
       acc = mma(a, b, acc);
     }
   }
@@ -421,8 +645,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll 4
       for (int kf = 0; kf < KF; ++kf) {
         const bool kv = kf * 32 + g * 8 < p.b_in;
-        Run<Tin> a = kv ? Run<Tin>::load(wb + kf * 512) : Run<Tin>::zero();
-        Run<Tin> b = (kv && mine) ? Run<Tin>::load_cached(xr + seg * p.b_in + kf * 32 + g * 8) : Run<Tin>::zero();
+        Run<Tin> a = Run<Tin>::load(kv ? wb + kf * 512 : zrun);
+        Run<Tin> b = Run<Tin>::load_cached((kv && mine) ? xr + seg * p.b_in + kf * 32 + g * 8 : zrun);
         acc = mma(a, b, acc);
       }
     }
@@ -499,19 +723,101 @@ void launch_variant(LeafParams p, dim3 grid, dim3 block, hipStream_t s) {
   }
 
 const Variant kVariants[] = {
-    AA_VARIANT(0, 4, 1, 2, 4, 2),   // TN 128, TM 64: few rows per type, wide blocks
-    AA_VARIANT(1, 2, 2, 4, 4, 2),   // TN 128, TM 128
-    AA_VARIANT(2, 1, 4, 3, 2, 2),   // TN 48,  TM 128: narrow output blocks
-    AA_VARIANT(3, 2, 2, 1, 1, 2),   // TN 32,  TM 32: small problems
-    AA_VARIANT(4, 4, 1, 1, 4, 2),   // TN 64,  TM 64
-    AA_VARIANT(5, 4, 1, 2, 4, 3),   // TN 128, TM 64, three stages
-    AA_VARIANT(6, 2, 2, 4, 4, 3),   // TN 128, TM 128, three stages
+    AA_VARIANT(0, 4, 1, 2, 4, 4),   // TN 128, TM 64: few rows per type, wide blocks
+    AA_VARIANT(1, 2, 2, 4, 4, 3),   // TN 128, TM 128
+    AA_VARIANT(2, 1, 4, 3, 2, 4),   // TN 48,  TM 128: narrow output blocks
+    AA_VARIANT(3, 2, 2, 1, 1, 4),   // TN 32,  TM 32: small problems
+    AA_VARIANT(4, 4, 1, 1, 4, 4),   // TN 64,  TM 64
+    AA_VARIANT(5, 4, 1, 2, 4, 2),   // TN 128, TM 64, two stages
+    AA_VARIANT(6, 2, 2, 4, 4, 2),   // TN 128, TM 128, two stages
+    AA_VARIANT(7, 4, 1, 6, 4, 2),   // TN 384, TM 64: one workgroup per Qwen3-8B leaf
+    AA_VARIANT(8, 4, 1, 3, 4, 4),   // TN 192, TM 64
 };
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
+
+// Streaming variants (bf16 inputs, closed-form row maps).
+struct StreamVariant {
+  int id;
+  int tn, tm, threads, ck;
+  void (*plain_b)(LeafParams, dim3, dim3, size_t, hipStream_t);   // bf16 out
+  void (*plain_f)(LeafParams, dim3, dim3, size_t, hipStream_t);   // f32 out
+  void (*swi_b)(LeafParams, dim3, dim3, size_t, hipStream_t);
+  void (*swi_f)(LeafParams, dim3, dim3, size_t, hipStream_t);
+};
+
+template <int WN, int WM, int NF, int MF, int CK, bool SW, typename Tout>
+void launch_stream(LeafParams p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((leaf_stream_kernel<WN, WM, NF, MF, CK, SW, Tout>), grid, block, lds, s, p);
+}
+
+#define AA_STREAM(ID, WN, WM, NF, MF, CK)                                                  \
+  StreamVariant {                                                                          \
+    ID, WN * NF * 16, WM * MF * 16, kWave * WN * WM, CK,                                   \
+        launch_stream<WN, WM, NF, MF, CK, false, __bf16>,                                  \
+        launch_stream<WN, WM, NF, MF, CK, false, float>,                                   \
+        launch_stream<WN, WM, NF, MF, CK, true, __bf16>,                                   \
+        launch_stream<WN, WM, NF, MF, CK, true, float>                                     \
+  }
+
+const StreamVariant kStream[] = {
+    AA_STREAM(0, 4, 1, 2, 4, 4),   // TN 128, TM 64
+    AA_STREAM(1, 2, 2, 4, 4, 2),   // TN 128, TM 128
+    AA_STREAM(2, 4, 1, 1, 4, 4),   // TN 64,  TM 64
+    AA_STREAM(3, 4, 1, 2, 2, 4),   // TN 128, TM 32
+    AA_STREAM(4, 3, 1, 1, 4, 4),   // TN 48,  TM 64: narrow output blocks
+    AA_STREAM(5, 4, 1, 3, 4, 2),   // TN 192, TM 64
+    AA_STREAM(6, 3, 1, 1, 8, 4),   // TN 48,  TM 128
+    AA_STREAM(7, 4, 1, 2, 4, 2),   // TN 128, TM 64, 2-slab chunks
+    AA_STREAM(8, 4, 2, 2, 4, 2),   // TN 128, TM 128, 8 waves
+};
+constexpr int kNumStream = int(sizeof(kStream) / sizeof(kStream[0]));
+constexpr size_t kStreamLdsMax = 64 * 1024;
 
 int64_t rows_per_type_max(const aa_plan_s& plan, int64_t M) {
   if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
   return (M + plan.q - 1) / plan.q;
+}
+
+// 16-byte LDS chunks per staged activation row: the widest leaf's K padded
+// to a multiple of 16 chunks.
+int stream_cpr(const aa_plan_s& plan) {
+  const int nseg_max = plan.law == AA_LAW_Q2XQ2 ? 4 : (plan.q > 1 ? 2 : 1);
+  const int chunks = nseg_max * int(plan.b_in / 8);
+  return (chunks + 15) / 16 * 16;
+}
+
+// LDS of a streaming launch: the activation tile, reused for the output tile.
+size_t stream_lds_bytes(const aa_plan_s& plan, int v) {
+  const size_t xt = size_t(kStream[v].tm) * (stream_cpr(plan) + 1) * 16;
+  const size_t ot = size_t(kStream[v].tm) * (kStream[v].tn + 8) * (plan.out_dtype == AA_F32 ? 4 : 2);
+  return xt > ot ? xt : ot;
+}
+
+// Streaming variant for this call, or -1 for the general kernel.
+int choose_stream(const aa_plan_s& plan, int64_t M, bool swiglu) {
+  if (plan.in_dtype != AA_BF16 || plan.type_kind == AA_TYPES_EXPLICIT) return -1;
+  auto fits = [&](int v) {
+    return stream_lds_bytes(plan, v) <= kStreamLdsMax && plan.b_in % (32 * kStream[v].ck) == 0;
+  };
+  if (plan.tile_override >= 100) {
+    const int v = plan.tile_override - 100;
+    return (v < kNumStream && fits(v)) ? v : -1;
+  }
+  if (plan.tile_override >= 0) return -1;
+  const int64_t mi = rows_per_type_max(plan, M);
+  // Many rows per type: the leaves are real GEMMs and the general kernel's
+  // register tiling is the better fit.
+  if (mi > 256) return -1;
+  (void)swiglu;
+  // Preference lists by output-block width; the first variant whose LDS tile
+  // fits and whose chunk divides the input block wins.
+  static const int wide[] = {0, 3, 7};
+  static const int mid[] = {2, 3, 7};
+  static const int narrow[] = {4, 2, 3};
+  const int* pref = plan.b_out % 128 == 0 ? wide : (plan.b_out % 48 == 0 && plan.b_out % 64 ? narrow : mid);
+  for (int j = 0; j < 3; ++j)
+    if (fits(pref[j])) return pref[j];
+  return -1;
 }
 
 int choose_variant(const aa_plan_s& plan, int64_t M) {
@@ -542,8 +848,12 @@ aa_status_t after_launch(hipStream_t stream, const char* what) {
 }
 
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
-  const int vid = choose_variant(plan, call.M);
+  const int sid = choose_stream(plan, call.M, call.swiglu);
+  const int vid = sid >= 0 ? 0 : choose_variant(plan, call.M);
   const Variant& v = kVariants[vid];
+  const int tn = sid >= 0 ? kStream[sid].tn : v.tn;
+  const int tm = sid >= 0 ? kStream[sid].tm : v.tm;
+  const int threads = sid >= 0 ? kStream[sid].threads : v.threads;
   LeafParams p{};
   p.X = call.X;
   p.W0 = call.W0;
@@ -561,8 +871,9 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
   p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
   p.row_types = call.row_types;
   const int64_t mi = rows_per_type_max(plan, call.M);
-  p.mt_count = plan.type_kind == AA_TYPES_EXPLICIT ? 1 : int32_t((mi + v.tm - 1) / v.tm);
-  p.nt_count = int32_t((plan.b_out + v.tn - 1) / v.tn);
+  p.mt_count = plan.type_kind == AA_TYPES_EXPLICIT ? 1 : int32_t((mi + tm - 1) / tm);
+  p.nt_count = int32_t((plan.b_out + tn - 1) / tn);
+  p.cpr = stream_cpr(plan);
   int kc = plan.q / kNumXcd;
   if (kc < 1) kc = 1;
   while (plan.q % kc) --kc;
@@ -572,8 +883,15 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
     return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles for one launch");
   if (p.mt_count < 1) return AA_OK;
   p.n_tiles = uint32_t(n_tiles);
-  const dim3 grid{uint32_t(n_tiles), 1, 1}, block{uint32_t(v.threads), 1, 1};
+  const dim3 grid{uint32_t(n_tiles), 1, 1}, block{uint32_t(threads), 1, 1};
   const bool fin = plan.in_dtype == AA_F32, fout = plan.out_dtype == AA_F32;
+  if (sid >= 0) {
+    const StreamVariant& sv = kStream[sid];
+    const size_t lds = stream_lds_bytes(plan, sid);
+    auto fn = call.swiglu ? (fout ? sv.swi_f : sv.swi_b) : (fout ? sv.plain_f : sv.plain_b);
+    fn(p, grid, block, lds, stream);
+    return after_launch(stream, call.swiglu ? "leaf_stream(swiglu)" : "leaf_stream");
+  }
   void (*fn)(LeafParams, dim3, dim3, hipStream_t);
   if (!call.swiglu) fn = fin ? (fout ? v.ff : v.fb) : (fout ? v.bf : v.bb);
   else fn = fin ? (fout ? v.sff : v.sfb) : (fout ? v.sbf : v.sbb);

@@ -136,10 +136,10 @@ def test_project_parity(law, q, M, d_in, d_out, kind, out_dt):
 
 def test_every_tile_variant_agrees():
     """The tuning override picks each kernel variant in turn; all must match."""
-    law, q, M, d_in, d_out = "Qq", 8, 700, 512, 768
+    law, q, M, d_in, d_out = "Qq", 8, 700, 1024, 1536
     say("variants", law, q, M, d_in, d_out)
     ref = None
-    for v in range(7):
+    for v in list(range(9)) + [100 + j for j in range(9)]:
         os.environ["AA_TILE"] = str(v)
         try:
             plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=31)
