@@ -20,6 +20,7 @@ struct aa_plan_s {
   int64_t n_block_products;  // one full product
   int64_t n_leaves;          // q * q
   int32_t tile_override;     // -1: automatic; else a variant id (tuning only)
+  int32_t wg_per_cu;         // persistent kernels: workgroups launched per CU (0: automatic)
 };
 
 namespace aa {

@@ -140,13 +140,17 @@ __device__ inline int device_leaf_groups(int law, int i, int k, int* g) {
     g[1] = k;
     return i == k ? 1 : 2;
   }
+  // Q2 x Q2: first factor from {a, a2}, second from {b, b2}; listed in the
+  // order (a,b), (a,b2), (a2,b), (a2,b2) with repeats dropped.
   const int a = i >> 1, b = i & 1, a2 = k >> 1, b2 = k & 1;
-  int as1 = a2, bs1 = b2;
-  const int na = (a2 != a) ? 2 : 1, nb = (b2 != b) ? 2 : 1;
-  int n = 0;
-  for (int x = 0; x < na; ++x)
-    for (int y = 0; y < nb; ++y) g[n++] = 2 * (x ? as1 : a) + (y ? bs1 : b);
-  return n;
+  const bool da = a2 != a, db = b2 != b;
+  g[0] = 2 * a + b;
+  g[1] = db ? 2 * a + b2 : 2 * a2 + b;
+  g[2] = 2 * a2 + b;
+  g[3] = 2 * a2 + b2;
+  if (db && !da) return 2;
+  if (da && db) return 4;
+  return da ? 2 : 1;
 }
 
 // ------------------------------------------------------------- leaf GEMM ---
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
-template <int WN, int WM, int NF, int MF, int CK, bool SWIGLU, typename Tout>
+template <int WN, int WM, int NF, int MF, int CK, int GC, bool DB, bool SWIGLU, typename Tout>
 __global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams p) {
   using Tin = __bf16;
   constexpr int NWAVE = WN * WM;
@@ -467,21 +471,46 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams
   int64_t fofs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) fofs[f] = (nvalid[f] ? int64_t(f) * fstride + wl : int64_t(lane) * 16);
-  auto load_chunk = [&](int c, Run<Tin> (&a0)[CK][NF], Run<Tin> (&a1)[CK][NF]) {
-    const int64_t base = chunk_ofs(c);
+  // A group is GC chunks; all of a group's weight loads are issued before
+  // any of them is waited on, so each wave keeps GC * CK * NF KiB in flight
+  // and a tile pays one memory latency per group, not one per chunk.  With
+  // DB the next group is issued while the current one is multiplied.
+  // The diagonal block W_kk is read by every row type, so it is loaded with
+  // the default cache policy; the other blocks are read by one type only and
+  // are streamed with the nontemporal hint so they do not evict it.
+  auto load_group = [&](int g0, Run<Tin> (&a0)[GC][CK][NF], Run<Tin> (&a1)[GC][CK][NF]) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    for (int gc = 0; gc < GC; ++gc) {
+      const int c = g0 * GC + gc;
+      if (c < nchunks) {
+        const int64_t base = chunk_ofs(c);
+        if (segs[c / chunks_per_seg] == k) {
 #pragma unroll
-      for (int kl = 0; kl < CK; ++kl) {
-        const int64_t o = base + fofs[f] + kl * 1024;
-        a0[kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
-        if (SWIGLU) a1[kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int kl = 0; kl < CK; ++kl) {
+              const int64_t o = base + fofs[f] + kl * 1024;
+              a0[gc][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + o));
+              if (SWIGLU) a1[gc][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + o));
+            }
+        } else {
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int kl = 0; kl < CK; ++kl) {
+              const int64_t o = base + fofs[f] + kl * 1024;
+              a0[gc][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
+              if (SWIGLU) a1[gc][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
+            }
+        }
       }
     }
   };
 
-  Run<Tin> bufA0[CK][NF], bufA1[CK][NF], bufB0[CK][NF], bufB1[CK][NF];
-  load_chunk(0, bufA0, bufA1);
+  constexpr int NB = DB ? 2 : 1;
+  Run<Tin> wb0[NB][GC][CK][NF], wb1[NB][GC][CK][NF];
+  const int ngroups = (nchunks + GC - 1) / GC;
+  load_group(0, wb0[0], wb1[0]);
 
   __syncthreads();   // activation tile resident (the wait covers every load above)
 
@@ -516,22 +545,35 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams
         }
     }
   };
+  auto compute_group = [&](int g0, Run<Tin> (&a0)[GC][CK][NF], Run<Tin> (&a1)[GC][CK][NF]) {
+#pragma unroll
+    for (int gc = 0; gc < GC; ++gc) {
+      const int c = g0 * GC + gc;
+      if (c < nchunks) compute_chunk(c, a0[gc], a1[gc]);
+    }
+  };
 
-  // Double-buffered chunk loop; the last one or two chunks are peeled so that
-  // no load is issued past the leaf's end.
-  int c = 0;
-  for (; c + 2 < nchunks; c += 2) {
-    load_chunk(c + 1, bufB0, bufB1);
-    compute_chunk(c, bufA0, bufA1);
-    load_chunk(c + 2, bufA0, bufA1);
-    compute_chunk(c + 1, bufB0, bufB1);
-  }
-  if (c + 1 < nchunks) {
-    load_chunk(c + 1, bufB0, bufB1);
-    compute_chunk(c, bufA0, bufA1);
-    compute_chunk(c + 1, bufB0, bufB1);
+  if (DB) {
+    int g0 = 0;
+    for (; g0 + 2 < ngroups; g0 += 2) {
+      load_group(g0 + 1, wb0[NB - 1], wb1[NB - 1]);
+      compute_group(g0, wb0[0], wb1[0]);
+      load_group(g0 + 2, wb0[0], wb1[0]);
+      compute_group(g0 + 1, wb0[NB - 1], wb1[NB - 1]);
+    }
+    if (g0 + 1 < ngroups) {
+      load_group(g0 + 1, wb0[NB - 1], wb1[NB - 1]);
+      compute_group(g0, wb0[0], wb1[0]);
+      compute_group(g0 + 1, wb0[NB - 1], wb1[NB - 1]);
+    } else {
+      compute_group(g0, wb0[0], wb1[0]);
+    }
   } else {
-    compute_chunk(c, bufA0, bufA1);
+    compute_group(0, wb0[0], wb1[0]);
+    for (int g0 = 1; g0 < ngroups; ++g0) {
+      load_group(g0, wb0[0], wb1[0]);
+      compute_group(g0, wb0[0], wb1[0]);
+    }
   }
 
   // 3. Epilogue.  Lane holds Y[m = l16][n .. n + 3] of each fragment; the
@@ -564,6 +606,272 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + r * OSTR + col);
       *reinterpret_cast<u32x4_t*>(Y + int64_t(rows_lds[r]) * p.ldy + col0 + col) = val;
     }
+  }
+}
+
+
+// ----------------------------------------------- persistent streaming leaf GEMM ---
+//
+// The same leaf tiles as the streaming kernel above, but each workgroup walks
+// a run of tiles and keeps the next tile's loads in flight while it
+// multiplies, transposes and stores the current one.  The next tile's
+// activation chunks and weight fragments are loaded into registers (the
+// weights into the other of two register sets) right after the current
+// tile's activations have been written to LDS; they are written to LDS only
+// when the next tile starts.  All loads are ordinary register loads, so the
+// compiler's wait counts stay exact, and barriers are plain s_barrier with
+// LDS-only waits.
+//
+// Rows of a type are found in closed form in every lane (position or
+// block-row typing).  One workgroup of four waves covers TN = 64 NF columns
+// and TM = 16 MF rows; the grid is two workgroups per CU.
+
+template <int NF, int MF, int CK, int NCH, bool SWIGLU, typename Tout>
+__global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
+  using Tin = __bf16;
+  constexpr int NWAVE = 4, NTHR = 256;
+  constexpr int TN = NWAVE * NF * 16;
+  constexpr int TM = MF * 16;
+  constexpr int CPR = NCH * CK * 4;                 // 16-byte chunks of a staged row
+  constexpr int RS = CPR + 1;                       // row stride in chunks (one pad chunk)
+  constexpr int NXC = (TM * CPR + NTHR - 1) / NTHR; // activation chunks per thread per tile
+  constexpr int OSTR = TN + 8;                      // staged output row stride (elements)
+  constexpr int XBYTES = (TM * RS * 16 > TM * OSTR * int(sizeof(Tout))) ? TM * RS * 16 : TM * OSTR * int(sizeof(Tout));
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[XBYTES];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int cps = p.b_in / 8;
+  const int chunks_per_seg = p.b_in / (32 * CK);
+  const int64_t blk_bytes = int64_t(p.b_in) * p.b_out * 2;
+  const int64_t fstride = int64_t(16) * p.b_in * 2;
+  const unsigned char* W0 = static_cast<const unsigned char*>(p.W0);
+  const unsigned char* W1 = static_cast<const unsigned char*>(p.W1);
+  const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
+  Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
+  const bool qq = p.law == AA_LAW_QQ;
+
+  // This workgroup's run of tiles: XCD x owns a contiguous run of the tile
+  // order; its G8 workgroups take every G8-th tile of it.
+  const uint32_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const uint32_t G8 = gridDim.x / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  const uint32_t run_begin = xcd * per + (xcd < rem ? xcd : rem);
+  const uint32_t run_end = run_begin + per + (xcd < rem ? 1 : 0);
+
+  struct Tile {
+    int i, k, nt, nseg, nchunks, nrows;
+    uint32_t gpack;          // Q2 x Q2: input group si in bits [2 si, 2 si + 2)
+    int64_t first, stride;   // row of local row r = first + r * stride
+  };
+  // Input group si of a leaf by arithmetic only (Q_q: i then k).
+  auto seg_of = [&](const Tile& T, int si) __attribute__((always_inline)) -> int {
+    return qq ? (si == 0 ? T.i : T.k) : int((T.gpack >> (2 * si)) & 3u);
+  };
+  auto setup = [&](uint32_t t, Tile& T) __attribute__((always_inline)) {
+    T.nt = int(t % uint32_t(p.nt_count));
+    t /= uint32_t(p.nt_count);
+    const int mt = int(t % uint32_t(p.mt_count));
+    t /= uint32_t(p.mt_count);
+    const int kk = int(t % uint32_t(p.kc));
+    t /= uint32_t(p.kc);
+    T.i = int(t % uint32_t(p.q));
+    T.k = int(t / uint32_t(p.q)) * p.kc + kk;
+    int sg[4] = {0, 0, 0, 0};
+    T.nseg = device_leaf_groups(p.law, T.i, T.k, sg);
+    T.gpack = uint32_t(sg[0] & 3) | (uint32_t(sg[1] & 3) << 2) | (uint32_t(sg[2] & 3) << 4) | (uint32_t(sg[3] & 3) << 6);
+    T.nchunks = T.nseg * chunks_per_seg;
+    int64_t count;
+    if (p.kind == AA_TYPES_BLOCK_ROWS) {
+      T.first = int64_t(T.i) * p.rows_per_type;
+      T.stride = 1;
+      count = p.rows_per_type;
+    } else {
+      int64_t r0 = int64_t(T.i) - p.off_mod_q;
+      if (r0 < 0) r0 += p.q;
+      T.first = r0;
+      T.stride = p.q;
+      count = r0 < p.M ? (p.M - r0 + p.q - 1) / p.q : 0;
+    }
+    const int64_t lo = int64_t(mt) * TM;
+    T.nrows = lo >= count ? 0 : int(count - lo < TM ? count - lo : TM);
+    T.first += lo * T.stride;
+  };
+
+  // Activation chunks: thread t holds logical chunks t, t + 256, ... of the
+  // TM x CPR tile (row-major).  Lanes past the tile's rows or K re-read a
+  // valid row (the tile's first, or row 0 of X for an empty tile); those
+  // values land in LDS cells that no kept output reads.
+  auto load_x = [&](const Tile& T, Run<Tin> (&xr)[NXC]) __attribute__((always_inline)) {
+    const int used = T.nseg * cps;
+    const int g0 = seg_of(T, 0) * p.b_in, g1 = seg_of(T, 1) * p.b_in, g2 = seg_of(T, 2) * p.b_in,
+              g3 = seg_of(T, 3) * p.b_in;
+#pragma unroll
+    for (int j = 0; j < NXC; ++j) {
+      const int e = j * NTHR + int(threadIdx.x);
+      const int r = e / CPR, c = e - r * CPR;
+      const bool real = e < TM * CPR && r < T.nrows && c < used;
+      const int sg = real ? c / cps : 0;
+      int gofs = g0;
+      gofs = sg == 1 ? g1 : gofs;
+      gofs = sg == 2 ? g2 : gofs;
+      gofs = sg == 3 ? g3 : gofs;
+      const int64_t row = T.nrows > 0 ? T.first + int64_t(real ? r : 0) * T.stride : 0;
+      xr[j] = Run<Tin>::load_cached(X + row * p.ldx + (real ? gofs + (c - sg * cps) * 8 : 0));
+    }
+  };
+  auto store_x = [&](const Run<Tin> (&xr)[NXC]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NXC; ++j) {
+      const int e = j * NTHR + int(threadIdx.x);
+      if (e < TM * CPR) {
+        const int r = e / CPR, c = e - r * CPR;
+        *reinterpret_cast<u32x4_t*>(lds + (r * RS + c) * 16) = xr[j].v;
+      }
+    }
+  };
+
+  // Weight fragments of tile T.  The cache policy is fixed per chunk slot so
+  // that no load sits in a branch: under Q_q chunk 0 is the row type's own
+  // block W_ik, read by this type only (nontemporal), and the last chunk is
+  // the diagonal block W_kk that every type reads (default policy, stays in
+  // L2).  A diagonal leaf has a single chunk; its second slot re-reads it.
+  auto load_w = [&](const Tile& T, Run<Tin> (&a0)[NCH][CK][NF], Run<Tin> (&a1)[NCH][CK][NF]) __attribute__((always_inline)) {
+    const int nfrag0 = T.nt * (TN / 16) + wave * NF;
+    const int64_t wl = int64_t(nfrag0) * fstride + lane * 16;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int c = ch < T.nchunks ? ch : 0;
+      const int si = c / chunks_per_seg;
+      const int64_t base = int64_t(seg_of(T, si) * p.q + T.k) * blk_bytes + (c - si * chunks_per_seg) * CK * 1024;
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int kl = 0; kl < CK; ++kl) {
+          const int64_t o = base + ((nfrag0 + f) * 16 < p.b_out ? wl + f * fstride : int64_t(lane) * 16) + kl * 1024;
+          if (ch == 0) {
+            a0[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
+            if (SWIGLU) a1[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
+          } else {
+            a0[ch][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + o));
+            if (SWIGLU) a1[ch][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + o));
+          }
+        }
+    }
+  };
+
+  auto compute_store = [&](const Tile& T, const Run<Tin> (&a0)[NCH][CK][NF], const Run<Tin> (&a1)[NCH][CK][NF]) __attribute__((always_inline)) {
+    f32x4_t acc0[NF][MF], acc1[NF][MF];
+#pragma unroll
+    for (int a = 0; a < NF; ++a)
+#pragma unroll
+      for (int b = 0; b < MF; ++b) {
+        acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      if (ch < T.nchunks) {
+        const int si = ch / chunks_per_seg;
+        const int cofs = (si * cps + (ch - si * chunks_per_seg) * CK * 4) * 16;
+#pragma unroll
+        for (int kl = 0; kl < CK; ++kl) {
+          Run<Tin> xv[MF];
+#pragma unroll
+          for (int b = 0; b < MF; ++b)
+            xv[b].v = *reinterpret_cast<const u32x4_t*>(lds + (b * 16 + l16) * RS * 16 + g * 16 + cofs + kl * 64);
+#pragma unroll
+          for (int a = 0; a < NF; ++a)
+#pragma unroll
+            for (int b = 0; b < MF; ++b) {
+              acc0[a][b] = mma(a0[ch][kl][a], xv[b], acc0[a][b]);
+              if (SWIGLU) acc1[a][b] = mma(a1[ch][kl][a], xv[b], acc1[a][b]);
+            }
+        }
+      }
+    }
+    // Every wave is done reading the activation tile: stage outputs in its place.
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    Tout* otile = reinterpret_cast<Tout*>(lds);
+#pragma unroll
+    for (int b = 0; b < MF; ++b)
+#pragma unroll
+      for (int a = 0; a < NF; ++a) {
+        f32x4_t v = acc0[a][b];
+        if (SWIGLU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+        }
+        store4(otile + (b * 16 + l16) * OSTR + (wave * NF + a) * 16 + g * 4, v);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    constexpr int VPR = TN * int(sizeof(Tout)) / 16;
+    const int64_t col0 = int64_t(T.k) * p.b_out + int64_t(T.nt) * TN;
+    const int ncols = p.b_out - T.nt * TN < TN ? p.b_out - T.nt * TN : TN;
+#pragma unroll
+    for (int e0 = 0; e0 < TM * VPR; e0 += NTHR) {
+      const int e = e0 + int(threadIdx.x);
+      const int r = e / VPR, v = e - r * VPR;
+      const int col = v * (16 / int(sizeof(Tout)));
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + (r < TM ? r : 0) * OSTR + col);
+      if (e < TM * VPR && r < T.nrows && col < ncols)
+        *reinterpret_cast<u32x4_t*>(Y + (T.first + int64_t(r) * T.stride) * p.ldy + col0 + col) = val;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // staged outputs read before the buffer is refilled
+    __builtin_amdgcn_s_barrier();
+  };
+
+  Run<Tin> xr[NXC];
+  Run<Tin> wa0[NCH][CK][NF], wa1[NCH][CK][NF], wb0[NCH][CK][NF], wb1[NCH][CK][NF];
+  Tile TA, TB;
+  uint32_t t = run_begin + slot;
+  if (t >= run_end) return;
+  setup(t, TA);
+  load_x(TA, xr);
+  load_w(TA, wa0, wa1);
+  for (;;) {
+    // TA: activations in xr, weights in wa
+    store_x(xr);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    const uint32_t tn = t + G8;
+    const bool more = tn < run_end;
+    if (more) {
+      setup(tn, TB);
+      load_x(TB, xr);
+      load_w(TB, wb0, wb1);
+    }
+    if (TA.nrows > 0) compute_store(TA, wa0, wa1);
+    else {
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+    }
+    if (!more) break;
+    t = tn;
+    // TB: activations in xr, weights in wb
+    store_x(xr);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    const uint32_t tn2 = t + G8;
+    const bool more2 = tn2 < run_end;
+    if (more2) {
+      setup(tn2, TA);
+      load_x(TA, xr);
+      load_w(TA, wa0, wa1);
+    }
+    if (TB.nrows > 0) compute_store(TB, wb0, wb1);
+    else {
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+    }
+    if (!more2) break;
+    t = tn2;
   }
 }
 
@@ -745,33 +1053,68 @@ struct StreamVariant {
   void (*swi_f)(LeafParams, dim3, dim3, size_t, hipStream_t);
 };
 
-template <int WN, int WM, int NF, int MF, int CK, bool SW, typename Tout>
+template <int WN, int WM, int NF, int MF, int CK, int GC, bool DB, bool SW, typename Tout>
 void launch_stream(LeafParams p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_stream_kernel<WN, WM, NF, MF, CK, SW, Tout>), grid, block, lds, s, p);
+  hipLaunchKernelGGL((leaf_stream_kernel<WN, WM, NF, MF, CK, GC, DB, SW, Tout>), grid, block, lds, s, p);
 }
 
-#define AA_STREAM(ID, WN, WM, NF, MF, CK)                                                  \
+// SwiGLU instances hold two weight streams, so they use half the group.
+#define AA_STREAM(ID, WN, WM, NF, MF, CK, GC, DB, GCS)                                     \
   StreamVariant {                                                                          \
     ID, WN * NF * 16, WM * MF * 16, kWave * WN * WM, CK,                                   \
-        launch_stream<WN, WM, NF, MF, CK, false, __bf16>,                                  \
-        launch_stream<WN, WM, NF, MF, CK, false, float>,                                   \
-        launch_stream<WN, WM, NF, MF, CK, true, __bf16>,                                   \
-        launch_stream<WN, WM, NF, MF, CK, true, float>                                     \
+        launch_stream<WN, WM, NF, MF, CK, GC, DB, false, __bf16>,                          \
+        launch_stream<WN, WM, NF, MF, CK, GC, DB, false, float>,                           \
+        launch_stream<WN, WM, NF, MF, CK, GCS, DB, true, __bf16>,                          \
+        launch_stream<WN, WM, NF, MF, CK, GCS, DB, true, float>                            \
   }
 
 const StreamVariant kStream[] = {
-    AA_STREAM(0, 4, 1, 2, 4, 4),   // TN 128, TM 64
-    AA_STREAM(1, 2, 2, 4, 4, 2),   // TN 128, TM 128
-    AA_STREAM(2, 4, 1, 1, 4, 4),   // TN 64,  TM 64
-    AA_STREAM(3, 4, 1, 2, 2, 4),   // TN 128, TM 32
-    AA_STREAM(4, 3, 1, 1, 4, 4),   // TN 48,  TM 64: narrow output blocks
-    AA_STREAM(5, 4, 1, 3, 4, 2),   // TN 192, TM 64
-    AA_STREAM(6, 3, 1, 1, 8, 4),   // TN 48,  TM 128
-    AA_STREAM(7, 4, 1, 2, 4, 2),   // TN 128, TM 64, 2-slab chunks
-    AA_STREAM(8, 4, 2, 2, 4, 2),   // TN 128, TM 128, 8 waves
+    AA_STREAM(0, 4, 1, 2, 4, 4, 2, false, 1),   // TN 128, TM 64, 16 KiB in flight per wave
+    AA_STREAM(1, 2, 2, 4, 4, 2, 2, false, 1),   // TN 128, TM 128
+    AA_STREAM(2, 4, 1, 1, 4, 4, 2, false, 2),   // TN 64,  TM 64
+    AA_STREAM(3, 4, 1, 2, 2, 4, 1, true, 1),    // TN 128, TM 32, double-buffered groups
+    AA_STREAM(4, 3, 1, 1, 4, 4, 2, false, 2),   // TN 48,  TM 64: narrow output blocks
+    AA_STREAM(5, 4, 1, 1, 4, 4, 1, true, 1),    // TN 64,  TM 64, double-buffered
+    AA_STREAM(6, 3, 1, 1, 8, 4, 2, false, 1),   // TN 48,  TM 128
+    AA_STREAM(7, 4, 1, 2, 4, 2, 2, true, 1),    // TN 128, TM 64, 2-slab chunks, double-buffered
+    AA_STREAM(8, 8, 1, 1, 4, 4, 2, false, 2),   // TN 128, TM 64, 8 waves
 };
 constexpr int kNumStream = int(sizeof(kStream) / sizeof(kStream[0]));
 constexpr size_t kStreamLdsMax = 64 * 1024;
+
+// Persistent streaming variants (bf16 inputs, closed-form row maps, b_in a
+// multiple of 32 * CK, at most NCH chunks per leaf).
+struct PersistVariant {
+  int id;
+  int tn, tm, ck, nch;
+  void (*plain_b)(LeafParams, dim3, dim3, size_t, hipStream_t);
+  void (*plain_f)(LeafParams, dim3, dim3, size_t, hipStream_t);
+  void (*swi_b)(LeafParams, dim3, dim3, size_t, hipStream_t);   // may be null
+  void (*swi_f)(LeafParams, dim3, dim3, size_t, hipStream_t);
+};
+
+template <int NF, int MF, int CK, int NCH, bool SW, typename Tout>
+void launch_persist(LeafParams p, dim3 grid, dim3 block, size_t, hipStream_t s) {
+  hipLaunchKernelGGL((leaf_persist_kernel<NF, MF, CK, NCH, SW, Tout>), grid, block, 0, s, p);
+}
+
+#define AA_PERSIST(ID, NF, MF, CK, NCH)                                                     \
+  PersistVariant {                                                                          \
+    ID, 4 * NF * 16, MF * 16, CK, NCH, launch_persist<NF, MF, CK, NCH, false, __bf16>,      \
+        launch_persist<NF, MF, CK, NCH, false, float>, nullptr, nullptr                     \
+  }
+#define AA_PERSIST_SW(ID, NF, MF, CK, NCH)                                                  \
+  PersistVariant {                                                                          \
+    ID, 4 * NF * 16, MF * 16, CK, NCH, launch_persist<NF, MF, CK, NCH, false, __bf16>,      \
+        launch_persist<NF, MF, CK, NCH, false, float>,                                      \
+        launch_persist<NF, MF, CK, NCH, true, __bf16>, launch_persist<NF, MF, CK, NCH, true, float> \
+  }
+
+const PersistVariant kPersist[] = {
+    AA_PERSIST(0, 2, 4, 4, 2),      // TN 128, TM 64: Q_q leaves with 128-wide input blocks
+    AA_PERSIST_SW(1, 1, 4, 4, 2),   // TN 64,  TM 64 (also the SwiGLU gate/up instance)
+};
+constexpr int kNumPersist = int(sizeof(kPersist) / sizeof(kPersist[0]));
 
 int64_t rows_per_type_max(const aa_plan_s& plan, int64_t M) {
   if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
@@ -820,6 +1163,41 @@ int choose_stream(const aa_plan_s& plan, int64_t M, bool swiglu) {
   return -1;
 }
 
+// Persistent variant for this call, or -1.
+int choose_persist(const aa_plan_s& plan, int64_t M, bool swiglu) {
+  if (plan.in_dtype != AA_BF16 || plan.type_kind == AA_TYPES_EXPLICIT) return -1;
+  const int nseg_max = plan.law == AA_LAW_Q2XQ2 ? 4 : (plan.q > 1 ? 2 : 1);
+  auto fits = [&](int v) {
+    const PersistVariant& pv = kPersist[v];
+    if (plan.b_in % (32 * pv.ck)) return false;
+    if (nseg_max * (plan.b_in / (32 * pv.ck)) > pv.nch) return false;
+    return !swiglu || pv.swi_b != nullptr;
+  };
+  if (plan.tile_override >= 200) {
+    const int v = plan.tile_override - 200;
+    return (v < kNumPersist && fits(v)) ? v : -1;
+  }
+  if (plan.tile_override >= 0) return -1;
+  if (rows_per_type_max(plan, M) > 256) return -1;
+  const int pref[] = {swiglu ? 1 : (plan.b_out % 128 == 0 ? 0 : 1), 1};
+  for (int v : pref)
+    if (fits(v)) return v;
+  return -1;
+}
+
+int device_cu_count() {
+  static int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached_cus = cus;
+    cached_dev = dev;
+  }
+  return cached_cus;
+}
+
 int choose_variant(const aa_plan_s& plan, int64_t M) {
   if (plan.tile_override >= 0 && plan.tile_override < kNumVariants) return plan.tile_override;
   const int64_t mi = rows_per_type_max(plan, M);
@@ -848,6 +1226,45 @@ aa_status_t after_launch(hipStream_t stream, const char* what) {
 }
 
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  const int pid = choose_persist(plan, call.M, call.swiglu);
+  if (pid >= 0) {
+    const PersistVariant& pv = kPersist[pid];
+    LeafParams p{};
+    p.X = call.X;
+    p.W0 = call.W0;
+    p.W1 = call.W1;
+    p.Y = call.Y;
+    p.M = call.M;
+    p.ldx = plan.d_in;
+    p.ldy = plan.d_out;
+    p.q = plan.q;
+    p.b_in = int32_t(plan.b_in);
+    p.b_out = int32_t(plan.b_out);
+    p.law = plan.law;
+    p.kind = plan.type_kind;
+    p.off_mod_q = int32_t(call.pos_offset % plan.q);
+    p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
+    const int64_t mi = rows_per_type_max(plan, call.M);
+    p.mt_count = int32_t((mi + pv.tm - 1) / pv.tm);
+    p.nt_count = int32_t((plan.b_out + pv.tn - 1) / pv.tn);
+    int kc = plan.q / kNumXcd;
+    if (kc < 1) kc = 1;
+    while (plan.q % kc) --kc;
+    p.kc = kc;
+    const int64_t n_tiles = int64_t(plan.q) * plan.q * p.mt_count * p.nt_count;
+    if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+    if (p.mt_count < 1) return AA_OK;
+    p.n_tiles = uint32_t(n_tiles);
+    int64_t wgs = int64_t(device_cu_count()) * (plan.wg_per_cu > 0 ? plan.wg_per_cu : 2);
+    const int64_t need = (n_tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (wgs > need) wgs = need;
+    wgs = (wgs + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const dim3 grid{uint32_t(wgs), 1, 1}, block{256, 1, 1};
+    const bool fout = plan.out_dtype == AA_F32;
+    auto fn = call.swiglu ? (fout ? pv.swi_f : pv.swi_b) : (fout ? pv.plain_f : pv.plain_b);
+    fn(p, grid, block, 0, stream);
+    return after_launch(stream, call.swiglu ? "leaf_persist(swiglu)" : "leaf_persist");
+  }
   const int sid = choose_stream(plan, call.M, call.swiglu);
   const int vid = sid >= 0 ? 0 : choose_variant(plan, call.M);
   const Variant& v = kVariants[vid];

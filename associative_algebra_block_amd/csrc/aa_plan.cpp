@@ -115,10 +115,17 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
   p->n_block_products = n;
   p->n_leaves = int64_t(q) * q;
   p->tile_override = -1;
+  p->wg_per_cu = 0;
+  // Tuning overrides, read once here so that a plan stays immutable.
   if (const char* t = getenv("AA_TILE")) {
     char* end = nullptr;
     long v = strtol(t, &end, 10);
     if (end != t && *end == '\0' && v >= 0) p->tile_override = int32_t(v);
+  }
+  if (const char* t = getenv("AA_WG_PER_CU")) {
+    char* end = nullptr;
+    long v = strtol(t, &end, 10);
+    if (end != t && *end == '\0' && v > 0 && v <= 64) p->wg_per_cu = int32_t(v);
   }
   *out = p;
   return AA_OK;

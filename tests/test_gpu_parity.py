@@ -139,7 +139,7 @@ def test_every_tile_variant_agrees():
     law, q, M, d_in, d_out = "Qq", 8, 700, 1024, 1536
     say("variants", law, q, M, d_in, d_out)
     ref = None
-    for v in list(range(9)) + [100 + j for j in range(9)]:
+    for v in list(range(9)) + [100 + j for j in range(9)] + [200, 201]:
         os.environ["AA_TILE"] = str(v)
         try:
             plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=31)
