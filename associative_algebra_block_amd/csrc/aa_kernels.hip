@@ -34,6 +34,7 @@
 #include <stdlib.h>
 
 #include <string>
+#include <type_traits>
 
 #include "aa_internal.h"
 
@@ -890,76 +891,141 @@ struct DecodeParams {
   int32_t law;
   int32_t off_mod_q;
   const int32_t* row_types;
-  int32_t nfr;     // 16-column strips per output group
-  int32_t n_waves; // q * nfr
+  int32_t nstrips;   // 16-column strips per output group
+  int32_t nchunks;   // 64-column chunks per output group
 };
 
-// One wave computes a 16-column strip of output group k for up to 16 tokens.
-// The diagonal block W_kk is shared by every token, so its strip is one MFMA
-// per k-slab for all 16 tokens.  Each token's other blocks (its own block-row
-// under Q_q) are multiplied with that token's activations placed in its own
-// column of the B operand and zeros elsewhere, accumulating into the same
-// 16 x 16 tile: the weight stream is read once per token, as a GEMV would,
-// while the MFMA does the multiply-adds.
-template <typename Tin, typename Tout>
+// Decode: a workgroup computes a 64-column chunk of output group k for a
+// group of TG tokens; wave w owns the chunk's w-th 16-column strip.  Every
+// weight strip the wave needs - the diagonal block W_kk's strip, shared by
+// the TG tokens, and for each token the strip of its own block W_ik - is
+// requested before any is used, so a wave keeps (TG + 1) * KF KiB in flight.
+// The tokens' activation segments are staged in LDS.  MFMA multiplies one
+// 16 x 32 weight fragment by a 32 x 16 activation tile in which column j is
+// token j's segment: all TG tokens at once for the diagonal block, and only
+// token j's column (the others zero) for token j's own block.
+template <typename Tin, typename Tout, int TG, int KF>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  static_assert(TG <= 16, "one MFMA column per token");
+  constexpr int NSEG = 3;                 // off-diagonal segments per token, at most (Q2 x Q2)
+  __shared__ __attribute__((aligned(16))) Tin xs[TG][1 + NSEG][KF * 32];
+  __shared__ int32_t tok_type[TG];
+
   const int lane = threadIdx.x % kWave;
-  const int wave_id = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (wave_id >= p.n_waves) return;
-  const int k = wave_id / p.nfr;
-  const int nf = wave_id % p.nfr;
+  const int wave = threadIdx.x / kWave;
   const int g = lane >> 4, l16 = lane & 15;
-  const int64_t tok0 = int64_t(blockIdx.y) * 16;
+  const int k = blockIdx.x / p.nchunks;
+  const int strip = (blockIdx.x % p.nchunks) * 4 + wave;
+  const int64_t tok0 = int64_t(blockIdx.y) * TG;
   const Tin* __restrict__ x = static_cast<const Tin*>(p.x);
   const Tin* __restrict__ W = static_cast<const Tin*>(p.W);
   Tout* __restrict__ y = static_cast<Tout*>(p.y);
-  const int KF = (p.b_in + 31) / 32;
-  const int64_t blk_elems = int64_t(p.b_in) * p.b_out;
-  const int64_t strip = int64_t(nf) * 16 * p.b_in + lane * 8;
+  const int64_t blk = int64_t(p.b_in) * p.b_out;
+  const bool strip_ok = strip < p.nstrips;
+  const int64_t sofs = int64_t(strip_ok ? strip : 0) * 16 * p.b_in + lane * 8;   // strip + run, elements
 
-  // Type of this lane's token (column l16 of the tile).
-  const int64_t my_tok = tok0 + l16;
-  int my_type = -1;
-  if (my_tok < p.n) {
-    my_type = p.row_types ? p.row_types[my_tok] : int((p.off_mod_q + my_tok) % p.q);
-    if (my_type < 0 || my_type >= p.q) my_type = -1;
+  if (threadIdx.x < TG) {
+    const int64_t r = tok0 + threadIdx.x;
+    int ty = -1;
+    if (r < p.n) {
+      ty = p.row_types ? p.row_types[r] : int((p.off_mod_q + r) % p.q);
+      if (ty < 0 || ty >= p.q) ty = -1;
+    }
+    tok_type[threadIdx.x] = ty;
   }
-  const bool my_ok = my_type >= 0;
-  const Tin* xr = x + (my_ok ? my_tok : 0) * p.ldx;
-  const Tin* zrun = reinterpret_cast<const Tin*>(g_zero_runs) + lane * 8;
+  __syncthreads();
+
+  // Input groups of token j's leaf other than k (at most NSEG), by arithmetic.
+  auto other_seg = [&](int ty, int s) -> int {
+    if (p.law == AA_LAW_QQ) return (s == 0 && ty != k) ? ty : -1;
+    int sg[4];
+    const int ns = device_leaf_groups(p.law, ty, k, sg);
+    int c = 0, out = -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < ns && sg[e] != k) {
+        if (c == s) out = sg[e];
+        ++c;
+      }
+    return out;
+  };
+
+  // Stage the activation segments: xs[j][0] = x_j[group k], xs[j][1 + s] = x_j[other segment s].
+  for (int e = threadIdx.x; e < TG * (1 + NSEG) * KF * 4; e += blockDim.x) {
+    const int run = e % (KF * 4), slotseg = (e / (KF * 4)) % (1 + NSEG), j = e / (KF * 4 * (1 + NSEG));
+    const int ty = tok_type[j];
+    const int sg = ty < 0 ? -1 : (slotseg == 0 ? k : other_seg(ty, slotseg - 1));
+    Run<Tin> v = Run<Tin>::zero();
+    if (sg >= 0 && run * 8 < p.b_in) v = Run<Tin>::load_cached(x + (tok0 + j) * p.ldx + int64_t(sg) * p.b_in + run * 8);
+    *reinterpret_cast<Run<Tin>*>(&xs[j][slotseg][run * 8]) = v;
+  }
+
+  // Weight strips: [0] the diagonal block's, [1 + j * NSEG + s] token j's segment s.
+  // Absent strips (a token of type k, a missing token, a segment the law does
+  // not use) re-read the diagonal strip, which is cached, and contribute
+  // nothing because their activation column is zero.
+  // In a half-width last slab (b_in an odd multiple of 16) the upper lane
+  // groups have no weights; they re-read their strip's first run, and their
+  // staged activations are zero.
+  constexpr int NW = 1 + TG;   // Q_q: one own block per token; Q2 x Q2 tokens loop below
+  Run<Tin> w[NW][KF];
+  int kofs[KF];
+#pragma unroll
+  for (int kf = 0; kf < KF; ++kf) kofs[kf] = (kf * 32 + g * 8 < p.b_in) ? kf * 512 : 0;
+  const Tin* wdiag = W + int64_t(k * p.q + k) * blk + sofs;
+#pragma unroll
+  for (int kf = 0; kf < KF; ++kf) w[0][kf] = Run<Tin>::load_cached(wdiag + kofs[kf]);
+#pragma unroll
+  for (int j = 0; j < TG; ++j) {
+    const int ty = tok_type[j];
+    const int sg = ty < 0 ? -1 : other_seg(ty, 0);
+    const Tin* wb = sg >= 0 ? W + int64_t(sg * p.q + k) * blk + sofs : wdiag;
+#pragma unroll
+    for (int kf = 0; kf < KF; ++kf) w[1 + j][kf] = Run<Tin>::load(wb + kofs[kf]);
+  }
+  __syncthreads();   // staged activations visible
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // Shared diagonal block.
-  {
-    const Tin* wk = W + int64_t(k * p.q + k) * blk_elems + strip;
+  const bool col_live = l16 < TG;
+  // Diagonal block: column j = token j's segment k.
+#pragma unroll
+  for (int kf = 0; kf < KF; ++kf) {
+    Run<Tin> b = Run<Tin>::zero();
+    if (col_live) b = *reinterpret_cast<const Run<Tin>*>(&xs[col_live ? l16 : 0][0][kf * 32 + g * 8]);
+    acc = mma(w[0][kf], b, acc);
+  }
+  // Own blocks: token j's column only.
+#pragma unroll
+  for (int j = 0; j < TG; ++j) {
+#pragma unroll
     for (int kf = 0; kf < KF; ++kf) {
-      const bool kv = kf * 32 + g * 8 < p.b_in;
-      Run<Tin> a = Run<Tin>::load(kv ? wk + kf * 512 : zrun);
-      Run<Tin> b = Run<Tin>::load_cached((kv && my_ok) ? xr + k * p.b_in + kf * 32 + g * 8 : zrun);
-      acc = mma(a, b, acc);
+      Run<Tin> b = Run<Tin>::zero();
+      if (l16 == j) b = *reinterpret_cast<const Run<Tin>*>(&xs[j][1][kf * 32 + g * 8]);
+      acc = mma(w[1 + j][kf], b, acc);
     }
   }
-  // Per-token blocks.
-  for (int t = 0; t < 16; ++t) {
-    const int ty = __shfl(my_type, t);   // uniform: token t's type
-    if (ty < 0) continue;
-    int segs[4];
-    const int ns = device_leaf_groups(p.law, ty, k, segs);
-    for (int s = 0; s < ns; ++s) {
-      const int seg = segs[s];
-      if (seg == k) continue;
-      const Tin* wb = W + int64_t(seg * p.q + k) * blk_elems + strip;
-      const bool mine = (l16 == t);
-#pragma unroll 4
-      for (int kf = 0; kf < KF; ++kf) {
-        const bool kv = kf * 32 + g * 8 < p.b_in;
-        Run<Tin> a = Run<Tin>::load(kv ? wb + kf * 512 : zrun);
-        Run<Tin> b = Run<Tin>::load_cached((kv && mine) ? xr + seg * p.b_in + kf * 32 + g * 8 : zrun);
-        acc = mma(a, b, acc);
+  // Q2 x Q2 tokens may have a second and third segment besides k.
+  if (p.law != AA_LAW_QQ) {
+    for (int j = 0; j < TG; ++j) {
+      const int ty = tok_type[j];
+      for (int s = 1; s < NSEG; ++s) {
+        const int sg = ty < 0 ? -1 : other_seg(ty, s);
+        if (sg < 0) continue;
+        const Tin* wb = W + int64_t(sg * p.q + k) * blk + sofs;
+        for (int kf = 0; kf < KF; ++kf) {
+          Run<Tin> a = Run<Tin>::load(wb + kofs[kf]);
+          Run<Tin> b = Run<Tin>::zero();
+          if (l16 == j) b = *reinterpret_cast<const Run<Tin>*>(&xs[j][1 + s][kf * 32 + g * 8]);
+          acc = mma(a, b, acc);
+        }
       }
     }
   }
-  if (my_ok) store4(y + my_tok * p.ldy + int64_t(k) * p.b_out + nf * 16 + g * 4, acc);
+  // Lane holds y[token l16][strip cols g*4 .. g*4+3].
+  if (col_live && strip_ok) {
+    const int64_t r = tok0 + l16;
+    if (r < p.n && tok_type[l16] >= 0) store4(y + r * p.ldy + int64_t(k) * p.b_out + strip * 16 + g * 4, acc);
+  }
 }
 
 // ----------------------------------------------------------------- pack ---
@@ -1346,14 +1412,48 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, v
   p.law = plan.law;
   p.off_mod_q = int32_t(pos_offset % plan.q);
   p.row_types = row_types;
-  p.nfr = int32_t(plan.b_out / 16);
-  p.n_waves = plan.q * p.nfr;
-  const dim3 block{256, 1, 1}, grid{uint32_t((p.n_waves + 3) / 4), uint32_t((n + 15) / 16), 1};
+  p.nstrips = int32_t(plan.b_out / 16);
+  p.nchunks = (p.nstrips + 3) / 4;
+  // KF k-slabs per input block; TG tokens per workgroup, fewer for wide
+  // blocks so that (TG + 1) * KF weight runs fit the registers.
+  const int kf = int((plan.b_in + 31) / 32);
   const bool fin = plan.in_dtype == AA_F32, fout = plan.out_dtype == AA_F32;
-  if (fin && fout) hipLaunchKernelGGL((decode_kernel<float, float>), grid, block, 0, stream, p);
-  else if (fin) hipLaunchKernelGGL((decode_kernel<float, __bf16>), grid, block, 0, stream, p);
-  else if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((decode_kernel<__bf16, __bf16>), grid, block, 0, stream, p);
+  auto go = [&](auto tg_c, auto kf_c) {
+    constexpr int TGc = decltype(tg_c)::value, KFc = decltype(kf_c)::value;
+    const int64_t groups = (n + TGc - 1) / TGc;
+    const dim3 block{256, 1, 1}, grid{uint32_t(plan.q * p.nchunks), uint32_t(groups), 1};
+    if (groups > 65535) return false;
+    if (fin && fout) hipLaunchKernelGGL((decode_kernel<float, float, TGc, KFc>), grid, block, 0, stream, p);
+    else if (fin) hipLaunchKernelGGL((decode_kernel<float, __bf16, TGc, KFc>), grid, block, 0, stream, p);
+    else if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float, TGc, KFc>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<__bf16, __bf16, TGc, KFc>), grid, block, 0, stream, p);
+    return true;
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  bool ok;
+  switch (kf) {
+    case 1: ok = go(I4{}, std::integral_constant<int, 1>{}); break;
+    case 2: ok = go(I4{}, std::integral_constant<int, 2>{}); break;
+    case 3: ok = go(I4{}, std::integral_constant<int, 3>{}); break;
+    case 4: ok = go(I4{}, std::integral_constant<int, 4>{}); break;
+    case 5: ok = go(I2{}, std::integral_constant<int, 5>{}); break;
+    case 6: ok = go(I2{}, std::integral_constant<int, 6>{}); break;
+    case 7: ok = go(I2{}, std::integral_constant<int, 7>{}); break;
+    case 8: ok = go(I2{}, std::integral_constant<int, 8>{}); break;
+    case 9: ok = go(I1{}, std::integral_constant<int, 9>{}); break;
+    case 10: ok = go(I1{}, std::integral_constant<int, 10>{}); break;
+    case 11: ok = go(I1{}, std::integral_constant<int, 11>{}); break;
+    case 12: ok = go(I1{}, std::integral_constant<int, 12>{}); break;
+    case 13: ok = go(I1{}, std::integral_constant<int, 13>{}); break;
+    case 14: ok = go(I1{}, std::integral_constant<int, 14>{}); break;
+    case 15: ok = go(I1{}, std::integral_constant<int, 15>{}); break;
+    case 16: ok = go(I1{}, std::integral_constant<int, 16>{}); break;
+    default:
+      return fail(AA_ERR_UNSUPPORTED, "aa_decode_gemv: input block width d_in/q above 512");
+  }
+  if (!ok) return fail(AA_ERR_UNSUPPORTED, "aa_decode_gemv: too many tokens for one launch");
   return after_launch(stream, "decode_gemv");
 }
 

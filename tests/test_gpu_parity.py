@@ -236,11 +236,13 @@ def test_row_locality():
 
 # ---------------------------------------------------------------- decode ---
 
-@pytest.mark.parametrize("law,q,d_in,d_out,n", [("Qq", 32, 4096, 12288, 32), ("Qq", 32, 4096, 12288, 1),
-                                                 ("Q2xQ2", 4, 768, 1536, 7), ("Qq", 16, 768, 2048, 20)])
-def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n):
-    say("decode", law, q, d_in, d_out, n)
-    plan, X, W = _make(law, q, 64, d_in, d_out, "bf16", "f32", seed=81)
+@pytest.mark.parametrize("law,q,d_in,d_out,n,dt", [
+    ("Qq", 32, 4096, 12288, 32, "bf16"), ("Qq", 32, 4096, 12288, 1, "bf16"),
+    ("Q2xQ2", 4, 768, 1536, 7, "bf16"), ("Qq", 16, 768, 2048, 20, "bf16"),
+    ("Qq", 32, 12288, 4096, 5, "bf16"), ("Qq", 2, 64, 64, 9, "f32"), ("Qq", 4, 320, 64, 6, "bf16")])
+def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n, dt):
+    say("decode", law, q, d_in, d_out, n, dt)
+    plan, X, W = _make(law, q, 64, d_in, d_out, dt, "f32", seed=81)
     Wp = aa.pack(plan, W)
     pos0 = 1000 + 3
     x = X[:n].contiguous()
