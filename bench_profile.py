@@ -1,0 +1,156 @@
+#!/usr/bin/env python3
+"""Summarise rocprofv3 results of bench.py into profiles/.
+
+    python bench_profile.py --name qwen3_8b_q32 --cmd-trace "..." --trace DIR \
+        [--fetch DIR --write DIR --cmd-pmc "..."]
+
+DIR is a rocprofv3 output directory (-d) holding a *_results.db written by
+--kernel-trace (and --pmc).  Writes:
+  profiles/<name>_kernel_trace.md   per-kernel calls and durations
+  profiles/<name>_hbm_traffic.md    FETCH_SIZE / WRITE_SIZE per launch, the
+                                    calibration against a 1 GiB device copy,
+                                    and calibrated HBM bytes per launch
+  profiles/traffic.json             the calibrated bytes per launch of the
+                                    projection kernel, tagged with the kernel
+                                    source hash (bench.py reports them only
+                                    while that hash matches)
+Runs on the host only; it reads the databases, it launches nothing.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(HERE, "profiles")
+COPY_BYTES = 1 << 30   # bench.py --calibration-copy copies 2^28 int32
+
+
+def kernel_source_hash():
+    with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", "aa_kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _db(d):
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no *_results.db under {d}")
+    return sqlite3.connect(dbs[-1])
+
+
+def short(name, n=96):
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def kernel_stats(d):
+    c = _db(d)
+    rows = c.execute("select name, grid_x, workgroup_x, count(*), avg(end - start), min(end - start), "
+                     "max(end - start), sum(end - start) from kernels group by name, grid_x "
+                     "order by sum(end - start) desc").fetchall()
+    total = sum(r[7] for r in rows) or 1
+    return [dict(name=r[0], grid=r[1], wg=r[2], calls=r[3], avg_us=r[4] / 1e3, min_us=r[5] / 1e3,
+                 max_us=r[6] / 1e3, total_us=r[7] / 1e3, pct=100.0 * r[7] / total) for r in rows]
+
+
+def pmc(d, counter):
+    """Mean counter value per kernel name, and the largest single dispatch."""
+    c = _db(d)
+    out = {}
+    for name, val in c.execute("select name, counter_value from pmc_events where counter_name = ?", (counter,)):
+        out.setdefault(name, []).append(val)
+    return {k: statistics.mean(v) for k, v in out.items()}, {k: max(v) for k, v in out.items()}
+
+
+def is_projection(name):
+    # the non-SwiGLU persistent streaming instance used by the Qwen3-8B-shaped projection
+    return "leaf_persist_kernel" in name and "Lb0E" in name and "ILi2ELi4E" in name
+
+
+def is_calibration_copy(name):
+    return "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--name", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--cmd-trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--cmd-pmc", default="")
+    ap.add_argument("--key", default=None, help="traffic.json key for the projection kernel")
+    ap.add_argument("--alg-bytes", type=float, default=None, help="algorithmic bytes per projection launch")
+    a = ap.parse_args()
+    os.makedirs(PROFILES, exist_ok=True)
+    src = kernel_source_hash()
+
+    ks = kernel_stats(a.trace)
+    lines = [f"# Kernel trace: {a.name}", "",
+             f"Command (run from /tmp with TMPDIR=/tmp): `{a.cmd_trace}`", "",
+             f"Kernel source (aa_kernels.hip) sha256[:16]: `{src}`", "",
+             "| kernel | grid (threads) | calls | avg us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    for k in ks:
+        lines.append(f"| `{short(k['name'])}` | {k['grid']} | {k['calls']} | {k['avg_us']:.2f} | "
+                     f"{k['min_us']:.2f} | {k['max_us']:.2f} | {k['pct']:.1f} |")
+    with open(os.path.join(PROFILES, f"{a.name}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[:14]))
+
+    if a.fetch and a.write:
+        (fe, fe_max), (wr, wr_max) = pmc(a.fetch, "FETCH_SIZE"), pmc(a.write, "WRITE_SIZE")
+        cal = [n for n in fe if is_calibration_copy(n)]
+        if not cal:
+            raise SystemExit("no calibration copy kernel in the FETCH_SIZE run (use bench.py --calibration-copy)")
+        # the 1 GiB copies are the largest dispatches of the copy kernel
+        # (smaller copies in the same run share its name)
+        cname = max(cal, key=lambda n: wr_max.get(n, 0))
+        f_fac = COPY_BYTES / (fe_max[cname] * 1024.0)
+        w_fac = COPY_BYTES / (wr_max[cname] * 1024.0)
+        fe[cname], wr[cname] = fe_max[cname], wr_max[cname]
+        lines = [f"# HBM traffic per launch: {a.name}", "",
+                 f"Commands (run from /tmp with TMPDIR=/tmp): `{a.cmd_pmc.replace('PMC', 'FETCH_SIZE')}` and "
+                 f"`{a.cmd_pmc.replace('PMC', 'WRITE_SIZE')}`", "",
+                 f"Kernel source (aa_kernels.hip) sha256[:16]: `{src}`", "",
+                 f"Calibration: a 1 GiB device copy (`{short(cname, 60)}`, its largest dispatches) reads FETCH_SIZE = {fe[cname]:.0f} KiB "
+                 f"and WRITE_SIZE = {wr[cname]:.0f} KiB per launch, so bytes = FETCH_SIZE x 1024 x {f_fac:.4f} "
+                 f"and WRITE_SIZE x 1024 x {w_fac:.4f}.", "",
+                 "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB | total MB |",
+                 "|---|---|---|---|---|---|"]
+        traffic = {}
+        for n in sorted(set(fe) | set(wr), key=lambda n: -(fe.get(n, 0) + wr.get(n, 0))):
+            r = fe.get(n, 0) * 1024 * f_fac
+            w = wr.get(n, 0) * 1024 * w_fac
+            lines.append(f"| `{short(n)}` | {fe.get(n, 0):.0f} | {wr.get(n, 0):.0f} | {r / 1e6:.2f} | "
+                         f"{w / 1e6:.2f} | {(r + w) / 1e6:.2f} |")
+            if is_projection(n):
+                traffic = {"read_bytes": r, "write_bytes": w, "hbm_bytes_per_launch": r + w, "kernel": n}
+        if traffic and a.alg_bytes:
+            lines += ["", f"Projection kernel: {traffic['hbm_bytes_per_launch'] / 1e6:.2f} MB measured per launch "
+                          f"against {a.alg_bytes / 1e6:.2f} MB algorithmic "
+                          f"({traffic['hbm_bytes_per_launch'] / a.alg_bytes:.3f}x)."]
+        with open(os.path.join(PROFILES, f"{a.name}_hbm_traffic.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        if traffic and a.key:
+            p = os.path.join(PROFILES, "traffic.json")
+            rec = {}
+            if os.path.exists(p):
+                with open(p) as f:
+                    rec = json.load(f)
+            if rec.get("kernel_source_sha256_16") != src:
+                rec = {"kernel_source_sha256_16": src, "kernels": {}}
+            rec["kernels"][a.key] = {k: (round(v) if isinstance(v, float) else v) for k, v in traffic.items()}
+            rec["calibration"] = {"fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+                                  "reference": "1 GiB device-to-device copy in the same run"}
+            with open(p, "w") as f:
+                json.dump(rec, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()
