@@ -21,6 +21,7 @@ struct aa_plan_s {
   int64_t n_leaves;          // q * q
   int32_t tile_override;     // -1: automatic; else a variant id (tuning only)
   int32_t wg_per_cu;         // persistent kernels: workgroups launched per CU (0: automatic)
+  int32_t persist_pol;       // persistent kernels: cache policy bits (-1: automatic; tuning only)
 };
 
 namespace aa {

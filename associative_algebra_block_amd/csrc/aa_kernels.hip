@@ -627,7 +627,15 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams
 // block-row typing).  One workgroup of four waves covers TN = 64 NF columns
 // and TM = 16 MF rows; the grid is two workgroups per CU.
 
-template <int NF, int MF, int CK, int NCH, bool SWIGLU, typename Tout>
+// Cache policy bits of the persistent kernel.  A block that only one tile
+// reads is streamed past L2 with nontemporal accesses, so that the blocks
+// several tiles share (the diagonal weight blocks W_kk, a type's own
+// activation block x_i) stay resident.
+constexpr int kPolWOwn = 1;   // own weight block W_ik: one m-tile per leaf
+constexpr int kPolXOwn = 2;   // own activation block x_k: one n-tile per leaf
+constexpr int kPolYNt = 4;    // outputs (written once)
+
+template <int NF, int MF, int CK, int NCH, bool SWIGLU, int POL, typename Tout>
 __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
   using Tin = __bf16;
   constexpr int NWAVE = 4, NTHR = 256;
@@ -644,8 +652,8 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
   const int wave = threadIdx.x / kWave;
   const int g = lane >> 4;
   const int l16 = lane & 15;
-  const int cps = p.b_in / 8;
-  const int chunks_per_seg = p.b_in / (32 * CK);
+  // One weight chunk (CK 32-row slabs) spans exactly one input group: the
+  // launcher only picks this kernel when b_in == 32 CK.
   const int64_t blk_bytes = int64_t(p.b_in) * p.b_out * 2;
   const int64_t fstride = int64_t(16) * p.b_in * 2;
   const unsigned char* W0 = static_cast<const unsigned char*>(p.W0);
@@ -683,7 +691,7 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
     int sg[4] = {0, 0, 0, 0};
     T.nseg = device_leaf_groups(p.law, T.i, T.k, sg);
     T.gpack = uint32_t(sg[0] & 3) | (uint32_t(sg[1] & 3) << 2) | (uint32_t(sg[2] & 3) << 4) | (uint32_t(sg[3] & 3) << 6);
-    T.nchunks = T.nseg * chunks_per_seg;
+    T.nchunks = T.nseg;
     int64_t count;
     if (p.kind == AA_TYPES_BLOCK_ROWS) {
       T.first = int64_t(T.i) * p.rows_per_type;
@@ -701,58 +709,66 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
     T.first += lo * T.stride;
   };
 
-  // Activation chunks: thread t holds logical chunks t, t + 256, ... of the
-  // TM x CPR tile (row-major).  Lanes past the tile's rows or K re-read a
-  // valid row (the tile's first, or row 0 of X for an empty tile); those
-  // values land in LDS cells that no kept output reads.
+  // Activation chunks, column-block major: the staged tile is NCH column
+  // blocks of XCB chunks (the K of one weight chunk); logical chunk e is
+  // block e / (TM XCB), row (e % (TM XCB)) / XCB, chunk e % XCB.  Thread t
+  // holds e = t, t + 256, ...; since TM XCB is a multiple of 256, each load
+  // instruction stays inside one column block and its cache policy is fixed
+  // (under Q_q the last block is the own activation block x_k).  Lanes past
+  // the tile's rows or K re-read a valid row (the tile's first, or row 0 of X
+  // for an empty tile); those values land in LDS cells no kept output reads.
+  constexpr int XCB = 4 * CK;                // = the chunks of one input group
+  constexpr int JPB = TM * XCB / NTHR;       // loads per column block
+  static_assert((TM * XCB) % NTHR == 0 && NXC == NCH * JPB, "staging layout");
+  const int x_cc = int(threadIdx.x) % XCB, x_r0 = int(threadIdx.x) / XCB;
   auto load_x = [&](const Tile& T, Run<Tin> (&xr)[NXC]) __attribute__((always_inline)) {
-    const int used = T.nseg * cps;
-    const int g0 = seg_of(T, 0) * p.b_in, g1 = seg_of(T, 1) * p.b_in, g2 = seg_of(T, 2) * p.b_in,
-              g3 = seg_of(T, 3) * p.b_in;
+    int64_t rowofs[JPB];
 #pragma unroll
-    for (int j = 0; j < NXC; ++j) {
-      const int e = j * NTHR + int(threadIdx.x);
-      const int r = e / CPR, c = e - r * CPR;
-      const bool real = e < TM * CPR && r < T.nrows && c < used;
-      const int sg = real ? c / cps : 0;
-      int gofs = g0;
-      gofs = sg == 1 ? g1 : gofs;
-      gofs = sg == 2 ? g2 : gofs;
-      gofs = sg == 3 ? g3 : gofs;
-      const int64_t row = T.nrows > 0 ? T.first + int64_t(real ? r : 0) * T.stride : 0;
-      xr[j] = Run<Tin>::load_cached(X + row * p.ldx + (real ? gofs + (c - sg * cps) * 8 : 0));
+    for (int jb = 0; jb < JPB; ++jb) {
+      const int r = jb * (NTHR / XCB) + x_r0;
+      rowofs[jb] = (T.nrows > 0 ? T.first + int64_t(r < T.nrows ? r : 0) * T.stride : 0) * p.ldx;
+    }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int colofs = ch < T.nchunks ? seg_of(T, ch) * p.b_in + x_cc * 8 : 0;
+#pragma unroll
+      for (int jb = 0; jb < JPB; ++jb) {
+        const Tin* src = X + rowofs[jb] + colofs;
+        if ((POL & kPolXOwn) && ch == NCH - 1) xr[ch * JPB + jb] = Run<Tin>::load(src);
+        else xr[ch * JPB + jb] = Run<Tin>::load_cached(src);
+      }
     }
   };
   auto store_x = [&](const Run<Tin> (&xr)[NXC]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NXC; ++j) {
-      const int e = j * NTHR + int(threadIdx.x);
-      if (e < TM * CPR) {
-        const int r = e / CPR, c = e - r * CPR;
-        *reinterpret_cast<u32x4_t*>(lds + (r * RS + c) * 16) = xr[j].v;
+    for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+      for (int jb = 0; jb < JPB; ++jb) {
+        const int r = jb * (NTHR / XCB) + x_r0;
+        *reinterpret_cast<u32x4_t*>(lds + (r * RS + ch * XCB + x_cc) * 16) = xr[ch * JPB + jb].v;
       }
-    }
   };
 
   // Weight fragments of tile T.  The cache policy is fixed per chunk slot so
   // that no load sits in a branch: under Q_q chunk 0 is the row type's own
-  // block W_ik, read by this type only (nontemporal), and the last chunk is
-  // the diagonal block W_kk that every type reads (default policy, stays in
-  // L2).  A diagonal leaf has a single chunk; its second slot re-reads it.
+  // block W_ik, read by this type only (nontemporal under kPolWOwn, i.e. when
+  // a leaf is a single m-tile; with several m-tiles the siblings reread it
+  // from L2), and the last chunk is the diagonal block W_kk that every type
+  // reads (default policy, stays in L2).  A diagonal leaf has a single chunk;
+  // its second slot re-reads it.
   auto load_w = [&](const Tile& T, Run<Tin> (&a0)[NCH][CK][NF], Run<Tin> (&a1)[NCH][CK][NF]) __attribute__((always_inline)) {
     const int nfrag0 = T.nt * (TN / 16) + wave * NF;
     const int64_t wl = int64_t(nfrag0) * fstride + lane * 16;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int c = ch < T.nchunks ? ch : 0;
-      const int si = c / chunks_per_seg;
-      const int64_t base = int64_t(seg_of(T, si) * p.q + T.k) * blk_bytes + (c - si * chunks_per_seg) * CK * 1024;
+      const int64_t base = int64_t(seg_of(T, c) * p.q + T.k) * blk_bytes;
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int kl = 0; kl < CK; ++kl) {
           const int64_t o = base + ((nfrag0 + f) * 16 < p.b_out ? wl + f * fstride : int64_t(lane) * 16) + kl * 1024;
-          if (ch == 0) {
+          if ((POL & kPolWOwn) && ch == 0) {
             a0[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
             if (SWIGLU) a1[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
           } else {
@@ -775,8 +791,7 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       if (ch < T.nchunks) {
-        const int si = ch / chunks_per_seg;
-        const int cofs = (si * cps + (ch - si * chunks_per_seg) * CK * 4) * 16;
+        const int cofs = ch * XCB * 16;
 #pragma unroll
         for (int kl = 0; kl < CK; ++kl) {
           Run<Tin> xv[MF];
@@ -819,8 +834,11 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
       const int r = e / VPR, v = e - r * VPR;
       const int col = v * (16 / int(sizeof(Tout)));
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + (r < TM ? r : 0) * OSTR + col);
-      if (e < TM * VPR && r < T.nrows && col < ncols)
-        *reinterpret_cast<u32x4_t*>(Y + (T.first + int64_t(r) * T.stride) * p.ldy + col0 + col) = val;
+      if (e < TM * VPR && r < T.nrows && col < ncols) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(Y + (T.first + int64_t(r) * T.stride) * p.ldy + col0 + col);
+        if (POL & kPolYNt) __builtin_nontemporal_store(val, dst);
+        else *dst = val;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);   // staged outputs read before the buffer is refilled
     __builtin_amdgcn_s_barrier();
@@ -1150,30 +1168,37 @@ constexpr size_t kStreamLdsMax = 64 * 1024;
 
 // Persistent streaming variants (bf16 inputs, closed-form row maps, b_in a
 // multiple of 32 * CK, at most NCH chunks per leaf).
+typedef void (*LeafLaunch)(LeafParams, dim3, dim3, size_t, hipStream_t);
 struct PersistVariant {
   int id;
   int tn, tm, ck, nch;
-  void (*plain_b)(LeafParams, dim3, dim3, size_t, hipStream_t);
-  void (*plain_f)(LeafParams, dim3, dim3, size_t, hipStream_t);
-  void (*swi_b)(LeafParams, dim3, dim3, size_t, hipStream_t);   // may be null
-  void (*swi_f)(LeafParams, dim3, dim3, size_t, hipStream_t);
+  // launchers indexed by the cache policy bits (kPol*)
+  LeafLaunch plain_b[8], plain_f[8];
+  LeafLaunch swi_b[8], swi_f[8];   // may be null
 };
 
-template <int NF, int MF, int CK, int NCH, bool SW, typename Tout>
+template <int NF, int MF, int CK, int NCH, bool SW, int POL, typename Tout>
 void launch_persist(LeafParams p, dim3 grid, dim3 block, size_t, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_persist_kernel<NF, MF, CK, NCH, SW, Tout>), grid, block, 0, s, p);
+  hipLaunchKernelGGL((leaf_persist_kernel<NF, MF, CK, NCH, SW, POL, Tout>), grid, block, 0, s, p);
 }
 
-#define AA_PERSIST(ID, NF, MF, CK, NCH)                                                     \
-  PersistVariant {                                                                          \
-    ID, 4 * NF * 16, MF * 16, CK, NCH, launch_persist<NF, MF, CK, NCH, false, __bf16>,      \
-        launch_persist<NF, MF, CK, NCH, false, float>, nullptr, nullptr                     \
+#define AA_PL(NF, MF, CK, NCH, SW, T)                                                            \
+  {                                                                                              \
+    launch_persist<NF, MF, CK, NCH, SW, 0, T>, launch_persist<NF, MF, CK, NCH, SW, 1, T>,       \
+        launch_persist<NF, MF, CK, NCH, SW, 2, T>, launch_persist<NF, MF, CK, NCH, SW, 3, T>,   \
+        launch_persist<NF, MF, CK, NCH, SW, 4, T>, launch_persist<NF, MF, CK, NCH, SW, 5, T>,   \
+        launch_persist<NF, MF, CK, NCH, SW, 6, T>, launch_persist<NF, MF, CK, NCH, SW, 7, T>    \
   }
-#define AA_PERSIST_SW(ID, NF, MF, CK, NCH)                                                  \
-  PersistVariant {                                                                          \
-    ID, 4 * NF * 16, MF * 16, CK, NCH, launch_persist<NF, MF, CK, NCH, false, __bf16>,      \
-        launch_persist<NF, MF, CK, NCH, false, float>,                                      \
-        launch_persist<NF, MF, CK, NCH, true, __bf16>, launch_persist<NF, MF, CK, NCH, true, float> \
+#define AA_PERSIST(ID, NF, MF, CK, NCH)                                                      \
+  PersistVariant {                                                                           \
+    ID, 4 * NF * 16, MF * 16, CK, NCH, AA_PL(NF, MF, CK, NCH, false, __bf16),                \
+        AA_PL(NF, MF, CK, NCH, false, float), {}, {}                                           \
+  }
+#define AA_PERSIST_SW(ID, NF, MF, CK, NCH)                                                   \
+  PersistVariant {                                                                           \
+    ID, 4 * NF * 16, MF * 16, CK, NCH, AA_PL(NF, MF, CK, NCH, false, __bf16),                \
+        AA_PL(NF, MF, CK, NCH, false, float), AA_PL(NF, MF, CK, NCH, true, __bf16),          \
+        AA_PL(NF, MF, CK, NCH, true, float)                                                  \
   }
 
 const PersistVariant kPersist[] = {
@@ -1235,9 +1260,9 @@ int choose_persist(const aa_plan_s& plan, int64_t M, bool swiglu) {
   const int nseg_max = plan.law == AA_LAW_Q2XQ2 ? 4 : (plan.q > 1 ? 2 : 1);
   auto fits = [&](int v) {
     const PersistVariant& pv = kPersist[v];
-    if (plan.b_in % (32 * pv.ck)) return false;
-    if (nseg_max * (plan.b_in / (32 * pv.ck)) > pv.nch) return false;
-    return !swiglu || pv.swi_b != nullptr;
+    if (plan.b_in != 32 * pv.ck) return false;
+    if (nseg_max > pv.nch) return false;
+    return !swiglu || pv.swi_b[0] != nullptr;
   };
   if (plan.tile_override >= 200) {
     const int v = plan.tile_override - 200;
@@ -1327,7 +1352,12 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
     wgs = (wgs + kNumXcd - 1) / kNumXcd * kNumXcd;
     const dim3 grid{uint32_t(wgs), 1, 1}, block{256, 1, 1};
     const bool fout = plan.out_dtype == AA_F32;
-    auto fn = call.swiglu ? (fout ? pv.swi_f : pv.swi_b) : (fout ? pv.plain_f : pv.plain_b);
+    int pol = (p.mt_count == 1 ? kPolWOwn : 0) | kPolYNt;
+    // the last staged column block is the own activation block x_k when the
+    // two input groups of a Q_q leaf fill the staged K exactly
+    if (p.nt_count == 1 && plan.law == AA_LAW_QQ && plan.q > 1 && pv.nch == 2) pol |= kPolXOwn;
+    if (plan.persist_pol >= 0) pol = plan.persist_pol;
+    auto fn = call.swiglu ? (fout ? pv.swi_f[pol] : pv.swi_b[pol]) : (fout ? pv.plain_f[pol] : pv.plain_b[pol]);
     fn(p, grid, block, 0, stream);
     return after_launch(stream, call.swiglu ? "leaf_persist(swiglu)" : "leaf_persist");
   }

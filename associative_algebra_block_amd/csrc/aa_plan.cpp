@@ -116,6 +116,7 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
   p->n_leaves = int64_t(q) * q;
   p->tile_override = -1;
   p->wg_per_cu = 0;
+  p->persist_pol = -1;
   // Tuning overrides, read once here so that a plan stays immutable.
   if (const char* t = getenv("AA_TILE")) {
     char* end = nullptr;
@@ -126,6 +127,11 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
     char* end = nullptr;
     long v = strtol(t, &end, 10);
     if (end != t && *end == '\0' && v > 0 && v <= 64) p->wg_per_cu = int32_t(v);
+  }
+  if (const char* t = getenv("AA_PERSIST_POL")) {
+    char* end = nullptr;
+    long v = strtol(t, &end, 10);
+    if (end != t && *end == '\0' && v >= 0 && v < 8) p->persist_pol = int32_t(v);
   }
   *out = p;
   return AA_OK;
