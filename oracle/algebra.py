@@ -22,7 +22,7 @@ block loops over the interaction table; the only library primitive is the
 matrix product of two blocks.  Nothing is blocked, fused or reordered beyond
 the definition.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * feature groups are contiguous and of equal width;
   * the row type of the token at absolute position p is p mod q;
   * a token's own (diagonal) group is the group whose index equals its type;

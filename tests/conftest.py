@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine only; on a machine with no GPU they are
-    # skipped rather than failed so that `-m gpu` is meaningful only there.
+    # GPU tests need a GPU; on a machine without one they are skipped rather
+    # than failed.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
