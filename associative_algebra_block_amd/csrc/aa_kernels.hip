@@ -672,6 +672,7 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 
   struct Tile {
     int i, k, nt, nseg, nchunks, nrows;
+    bool live;               // false: a step past the last tile (no stores)
     uint32_t gpack;          // Q2 x Q2: input group si in bits [2 si, 2 si + 2)
     int64_t first, stride;   // row of local row r = first + r * stride
   };
@@ -679,6 +680,10 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
   auto seg_of = [&](const Tile& T, int si) __attribute__((always_inline)) -> int {
     return qq ? (si == 0 ? T.i : T.k) : int((T.gpack >> (2 * si)) & 3u);
   };
+  // rows of type i under position typing: M / q, plus one for the first
+  // M mod q residues after the offset
+  const int64_t m_div_q = p.M / p.q;
+  const int m_mod_q = int(p.M - m_div_q * p.q);
   auto setup = [&](uint32_t t, Tile& T) __attribute__((always_inline)) {
     T.nt = int(t % uint32_t(p.nt_count));
     t /= uint32_t(p.nt_count);
@@ -698,11 +703,11 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
       T.stride = 1;
       count = p.rows_per_type;
     } else {
-      int64_t r0 = int64_t(T.i) - p.off_mod_q;
+      int r0 = T.i - p.off_mod_q;
       if (r0 < 0) r0 += p.q;
       T.first = r0;
       T.stride = p.q;
-      count = r0 < p.M ? (p.M - r0 + p.q - 1) / p.q : 0;
+      count = m_div_q + (r0 < m_mod_q ? 1 : 0);
     }
     const int64_t lo = int64_t(mt) * TM;
     T.nrows = lo >= count ? 0 : int(count - lo < TM ? count - lo : TM);
@@ -730,7 +735,8 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      const int colofs = ch < T.nchunks ? seg_of(T, ch) * p.b_in + x_cc * 8 : 0;
+      // a void step re-reads the type's own group, which stays in L2
+      const int colofs = ch < T.nchunks ? seg_of(T, T.live ? ch : 0) * p.b_in + x_cc * 8 : 0;
 #pragma unroll
       for (int jb = 0; jb < JPB; ++jb) {
         const Tin* src = X + rowofs[jb] + colofs;
@@ -762,7 +768,8 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int c = ch < T.nchunks ? ch : 0;
-      const int64_t base = int64_t(seg_of(T, c) * p.q + T.k) * blk_bytes;
+      // a void step re-reads the diagonal block W_kk, which stays in L2
+      const int64_t base = (int64_t(T.live ? seg_of(T, c) : T.k) * p.q + T.k) * blk_bytes;
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -834,7 +841,7 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
       const int r = e / VPR, v = e - r * VPR;
       const int col = v * (16 / int(sizeof(Tout)));
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + (r < TM ? r : 0) * OSTR + col);
-      if (e < TM * VPR && r < T.nrows && col < ncols) {
+      if (T.live && e < TM * VPR && r < T.nrows && col < ncols) {
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(Y + (T.first + int64_t(r) * T.stride) * p.ldy + col0 + col);
         if (POL & kPolYNt) __builtin_nontemporal_store(val, dst);
         else *dst = val;
@@ -847,50 +854,374 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
   Run<Tin> xr[NXC];
   Run<Tin> wa0[NCH][CK][NF], wa1[NCH][CK][NF], wb0[NCH][CK][NF], wb1[NCH][CK][NF];
   Tile TA, TB;
-  uint32_t t = run_begin + slot;
-  if (t >= run_end) return;
-  setup(t, TA);
+  const uint32_t t0 = run_begin + slot;
+  if (t0 >= run_end) return;
+  const int n_my = int((run_end - t0 + G8 - 1) / G8);
+  const uint32_t t_last = t0 + uint32_t(n_my - 1) * G8;
+  // Step u of this workgroup; steps past its last tile are void: they
+  // re-read data of the last tile that stays in L2 and store nothing.  No
+  // load is ever skipped by a branch, and the loop exits only after whole
+  // rounds of two steps, so every step sees the same queue of pending loads
+  // and the waits before the multiplies never drain the prefetch.
+  auto tile_at = [&](int u, Tile& T) __attribute__((always_inline)) {
+    const bool live = u < n_my;
+    setup(live ? t0 + uint32_t(u) * G8 : t_last, T);
+    T.live = live;
+  };
+  tile_at(0, TA);
   load_x(TA, xr);
   load_w(TA, wa0, wa1);
-  for (;;) {
+  const int rounds = (n_my + 1) / 2;
+  for (int rd = 0; rd < rounds; ++rd) {
     // TA: activations in xr, weights in wa
     store_x(xr);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
-    const uint32_t tn = t + G8;
-    const bool more = tn < run_end;
-    if (more) {
-      setup(tn, TB);
-      load_x(TB, xr);
-      load_w(TB, wb0, wb1);
-    }
-    if (TA.nrows > 0) compute_store(TA, wa0, wa1);
-    else {
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_s_barrier();
-    }
-    if (!more) break;
-    t = tn;
+    tile_at(2 * rd + 1, TB);
+    load_x(TB, xr);
+    load_w(TB, wb0, wb1);
+    compute_store(TA, wa0, wa1);
     // TB: activations in xr, weights in wb
     store_x(xr);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
-    const uint32_t tn2 = t + G8;
-    const bool more2 = tn2 < run_end;
-    if (more2) {
-      setup(tn2, TA);
-      load_x(TA, xr);
-      load_w(TA, wa0, wa1);
+    tile_at(2 * rd + 2, TA);
+    load_x(TA, xr);
+    load_w(TA, wa0, wa1);
+    compute_store(TB, wb0, wb1);
+  }
+}
+
+// ------------------------------------------------------------ job kernel ---
+//
+// Q_q leaves whose input groups are 32 CK wide, position or block-row typing.
+// The work is split into jobs: a job is one TN-column strip nt of one output
+// group k, over every row type i.  All leaves of a job share the diagonal
+// block strip W_kk, which the workgroup copies to LDS once; per tile only the
+// type's activation rows [x_i | x_k] and its own block strip W_ik stream in,
+// into NSET rotating register sets, so that NSET - 1 tiles of loads are in
+// flight while one tile is multiplied.  This raises the bytes in flight per
+// CU, which is what bounds a streaming kernel on HBM.
+//
+// Grid: XCD x (blockIdx % 8) owns output groups [x gpx, (x + 1) gpx).  Each
+// group gets wpg workgroups, dealt over its nt_count jobs; a job's workgroups
+// split its q * mt_count tiles (type-major, then m-tile) into contiguous,
+// balanced ranges.
+
+struct JobParams {
+  const void* X;
+  const void* W0;
+  const void* W1;
+  void* Y;
+  int64_t M;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t q;
+  int32_t b_out;
+  int32_t kind;            // aa_type_kind_t (position or block rows)
+  int32_t off_mod_q;
+  int64_t rows_per_type;   // block-row typing
+  int32_t mt_count;
+  int32_t nt_count;
+  int32_t gpx;             // output groups per XCD
+  int32_t wpg;             // workgroups per output group
+};
+
+template <int NF, int MF, int CK, int NSET, bool SWIGLU, int POL, typename Tout>
+__global__ __launch_bounds__(256, 2) void leaf_job_kernel(JobParams p) {
+  using Tin = __bf16;
+  constexpr int NTHR = 256;
+  constexpr int TN = 4 * NF * 16;
+  constexpr int TM = MF * 16;
+  constexpr int BIN = 32 * CK;             // input group width
+  constexpr int XCB = BIN / 8;             // 16-byte chunks of one group's row
+  constexpr int RS = 2 * XCB + 1;          // staged activation row stride (chunks, one pad)
+  constexpr int JPB = TM * XCB / NTHR;     // activation loads per thread per group
+  static_assert((TM * XCB) % NTHR == 0, "activation tile");
+  constexpr int NW = SWIGLU ? 2 : 1;
+  constexpr int STRIP = BIN * 32;          // bytes of one 16-column strip of a block
+  constexpr int WKK_BYTES = NW * (TN / 16) * STRIP;
+  constexpr int OSTR = TN + 8;             // staged output row stride (elements)
+  constexpr int XS_BYTES = TM * RS * 16 > TM * OSTR * int(sizeof(Tout)) ? TM * RS * 16 : TM * OSTR * int(sizeof(Tout));
+  __shared__ __attribute__((aligned(1024))) unsigned char wkk[WKK_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs[XS_BYTES];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int q = p.q;
+  const int nstrips = p.b_out / 16;
+  const int64_t blk_bytes = int64_t(BIN) * p.b_out * 2;
+  const unsigned char* W0 = static_cast<const unsigned char*>(p.W0);
+  const unsigned char* W1 = static_cast<const unsigned char*>(p.W1);
+  const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
+  Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
+
+  // ---- this workgroup's job and tile range
+  const int xcd = int(blockIdx.x % kNumXcd), slot = int(blockIdx.x / kNumXcd);
+  const int k = xcd * p.gpx + slot / p.wpg;
+  const int r = slot % p.wpg;
+  const int base = p.wpg / p.nt_count, extra = p.wpg % p.nt_count;
+  int nt, w, s_job;
+  if (r < extra * (base + 1)) {
+    nt = r / (base + 1);
+    w = r % (base + 1);
+    s_job = base + 1;
+  } else {
+    const int r2 = r - extra * (base + 1);
+    nt = extra + r2 / base;
+    w = r2 % base;
+    s_job = base;
+  }
+  const int tiles = q * p.mt_count;
+  const int u_begin = int(int64_t(tiles) * w / s_job);
+  const int u_end = int(int64_t(tiles) * (w + 1) / s_job);
+  const int n_my = u_end - u_begin;
+  if (n_my <= 0) return;
+
+  // ---- the diagonal block strip W_kk (and the up projection's): requested
+  // first, written to LDS after the first tiles have been requested
+  constexpr int NCP = WKK_BYTES / (NTHR * 16);
+  static_assert(WKK_BYTES % (NTHR * 16) == 0, "diagonal strip copy");
+  u32x4_t wkk_tmp[NCP];
+  {
+    u32x4_t (&tmp)[NCP] = wkk_tmp;
+#pragma unroll
+    for (int j = 0; j < NCP; ++j) {
+      const int e = (j * NTHR + int(threadIdx.x)) * 16;   // byte in wkk
+      const int wsel = e / ((TN / 16) * STRIP);
+      const int rem = e - wsel * (TN / 16) * STRIP;
+      int sl = nt * (TN / 16) + rem / STRIP;
+      sl = sl < nstrips ? sl : nstrips - 1;
+      const int64_t src = (int64_t(k) * q + k) * blk_bytes + int64_t(sl) * STRIP + (rem % STRIP);
+      tmp[j] = *reinterpret_cast<const u32x4_t*>((wsel ? W1 : W0) + src);
     }
-    if (TB.nrows > 0) compute_store(TB, wb0, wb1);
-    else {
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_s_barrier();
+  }
+  // (the loads of the first tiles follow in the same order as in the steady
+  // state, so the loop entry sees the same queue of pending loads)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- per-tile geometry (all wave-uniform)
+  // A step past the workgroup's last tile is a "void" tile: no rows (so no
+  // stores), type k (so only the first product runs), and its loads re-read
+  // the job's diagonal strip, which is in bounds and resident in L2.  Steps
+  // never branch around loads, so every step leaves the same queue of
+  // pending loads and the waits stay exact.
+  struct Tile {
+    int i, nrows;
+    bool valid;
+    int64_t first, stride;
+  };
+  // rows of type i under position typing: M / q, plus one for the first
+  // M mod q residues after the offset
+  const int64_t m_div_q = p.M / q;
+  const int m_mod_q = int(p.M - m_div_q * q);
+  auto setup = [&](int u, Tile& T) __attribute__((always_inline)) {
+    T.valid = u < n_my;
+    const int ug = u_begin + (T.valid ? u : 0);
+    T.i = p.mt_count == 1 ? ug : ug / p.mt_count;
+    const int mt = ug - T.i * p.mt_count;
+    int64_t count;
+    if (p.kind == AA_TYPES_BLOCK_ROWS) {
+      T.first = int64_t(T.i) * p.rows_per_type;
+      T.stride = 1;
+      count = p.rows_per_type;
+    } else {
+      int r0 = T.i - p.off_mod_q;
+      if (r0 < 0) r0 += q;
+      T.first = r0;
+      T.stride = q;
+      count = m_div_q + (r0 < m_mod_q ? 1 : 0);
     }
-    if (!more2) break;
-    t = tn2;
+    const int64_t lo = int64_t(mt) * TM;
+    T.nrows = lo >= count ? 0 : int(count - lo < TM ? count - lo : TM);
+    T.first += lo * T.stride;
+    if (!T.valid) {
+      T.i = k;
+      T.nrows = 0;
+    }
+  };
+
+  // ---- loads of one tile into a register set.  Activations: chunk x_cc of
+  // rows x_r0 + jb (NTHR / XCB), first of group i then of group k; rows past
+  // the tile re-read its first row (or row 0 of X).  Own weight block: this
+  // wave's NF strips of W_ik (strips past b_out re-read the last one).
+  const int x_cc = int(threadIdx.x) % XCB, x_r0 = int(threadIdx.x) / XCB;
+  // Addresses are a wave-uniform 64-bit base plus a 32-bit per-lane offset
+  // (a tile spans TM rows of stride q, well inside 4 GiB).
+  const int64_t wkk_base = (int64_t(k) * q + k) * blk_bytes;
+  auto load = [&](const Tile& T, Run<Tin> (&xr)[2 * JPB], Run<Tin> (&wr)[CK][NF],
+                  Run<Tin> (&wu)[CK][NF]) __attribute__((always_inline)) {
+    const Tin* xt = X + (T.nrows > 0 ? T.first : 0) * p.ldx;
+    const uint32_t rstep = uint32_t(T.stride * p.ldx);
+    uint32_t rowofs[JPB];
+#pragma unroll
+    for (int jb = 0; jb < JPB; ++jb) {
+      const int rr = jb * (NTHR / XCB) + x_r0;
+      rowofs[jb] = uint32_t(rr < T.nrows ? rr : 0) * rstep + uint32_t(x_cc * 8);
+    }
+    const Tin* xv = reinterpret_cast<const Tin*>(W0 + wkk_base);
+    const Tin* x0 = T.valid ? xt + T.i * BIN : xv;
+    const Tin* x1 = T.valid ? xt + k * BIN : xv;
+#pragma unroll
+    for (int jb = 0; jb < JPB; ++jb) xr[jb] = Run<Tin>::load_cached(x0 + rowofs[jb]);
+#pragma unroll
+    for (int jb = 0; jb < JPB; ++jb) {
+      if (POL & kPolXOwn) xr[JPB + jb] = Run<Tin>::load(x1 + rowofs[jb]);
+      else xr[JPB + jb] = Run<Tin>::load_cached(x1 + rowofs[jb]);
+    }
+    const int64_t wb = (T.valid ? (int64_t(T.i) * q + k) * blk_bytes : wkk_base) + lane * 16;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      int sl = nt * (TN / 16) + wave * NF + f;
+      sl = sl < nstrips ? sl : nstrips - 1;
+#pragma unroll
+      for (int kl = 0; kl < CK; ++kl) {
+        const int64_t o = wb + int64_t(sl) * STRIP + kl * 1024;
+        if (POL & kPolWOwn) {
+          wr[kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
+          if (SWIGLU) wu[kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
+        } else {
+          wr[kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + o));
+          if (SWIGLU) wu[kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + o));
+        }
+      }
+    }
+  };
+  auto store_x = [&](const Run<Tin> (&xr)[2 * JPB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int jb = 0; jb < JPB; ++jb) {
+        const int rr = jb * (NTHR / XCB) + x_r0;
+        *reinterpret_cast<u32x4_t*>(xs + (rr * RS + ch * XCB + x_cc) * 16) = xr[ch * JPB + jb].v;
+      }
+  };
+
+  // ---- multiply one tile and store it
+  constexpr int VPR = TN * int(sizeof(Tout)) / 16;   // 16-byte output vectors per row
+  constexpr int NYV = (TM * VPR + NTHR - 1) / NTHR;     // per thread
+  auto compute_store = [&](const Tile& T, const Run<Tin> (&wr)[CK][NF], const Run<Tin> (&wu)[CK][NF],
+                           u32x4_t (&yv)[NYV]) __attribute__((always_inline)) {
+    f32x4_t acc0[NF][MF], acc1[NF][MF];
+#pragma unroll
+    for (int a = 0; a < NF; ++a)
+#pragma unroll
+      for (int b = 0; b < MF; ++b) {
+        acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    // input group i times the own block W_ik (registers)
+#pragma unroll
+    for (int kl = 0; kl < CK; ++kl) {
+      Run<Tin> xv[MF];
+#pragma unroll
+      for (int b = 0; b < MF; ++b)
+        xv[b].v = *reinterpret_cast<const u32x4_t*>(xs + ((b * 16 + l16) * RS + kl * 4 + g) * 16);
+#pragma unroll
+      for (int a = 0; a < NF; ++a)
+#pragma unroll
+        for (int b = 0; b < MF; ++b) {
+          acc0[a][b] = mma(wr[kl][a], xv[b], acc0[a][b]);
+          if (SWIGLU) acc1[a][b] = mma(wu[kl][a], xv[b], acc1[a][b]);
+        }
+    }
+    // input group k times the diagonal block W_kk (LDS); a diagonal leaf
+    // (k == i) has only the first product
+    if (T.i != k) {
+#pragma unroll
+      for (int kl = 0; kl < CK; ++kl) {
+        Run<Tin> xv[MF], wk[NF], wk1[NF];
+#pragma unroll
+        for (int b = 0; b < MF; ++b)
+          xv[b].v = *reinterpret_cast<const u32x4_t*>(xs + ((b * 16 + l16) * RS + XCB + kl * 4 + g) * 16);
+#pragma unroll
+        for (int a = 0; a < NF; ++a) {
+          const int o = (wave * NF + a) * STRIP + kl * 1024 + lane * 16;
+          wk[a].v = *reinterpret_cast<const u32x4_t*>(wkk + o);
+          if (SWIGLU) wk1[a].v = *reinterpret_cast<const u32x4_t*>(wkk + (TN / 16) * STRIP + o);
+        }
+#pragma unroll
+        for (int a = 0; a < NF; ++a)
+#pragma unroll
+          for (int b = 0; b < MF; ++b) {
+            acc0[a][b] = mma(wk[a], xv[b], acc0[a][b]);
+            if (SWIGLU) acc1[a][b] = mma(wk1[a], xv[b], acc1[a][b]);
+          }
+      }
+    }
+    // every wave is done reading the activation tile: stage outputs in its place
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    Tout* otile = reinterpret_cast<Tout*>(xs);
+#pragma unroll
+    for (int b = 0; b < MF; ++b)
+#pragma unroll
+      for (int a = 0; a < NF; ++a) {
+        f32x4_t v = acc0[a][b];
+        if (SWIGLU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+        }
+        store4(otile + (b * 16 + l16) * OSTR + (wave * NF + a) * 16 + g * 4, v);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    const int64_t col0 = int64_t(k) * p.b_out + int64_t(nt) * TN;
+    const int ncols = p.b_out - nt * TN < TN ? p.b_out - nt * TN : TN;
+#pragma unroll
+    for (int j = 0; j < NYV; ++j) {
+      const int e = j * NTHR + int(threadIdx.x);
+      const int rr = e / VPR, v = e - rr * VPR;
+      const int col = v * (16 / int(sizeof(Tout)));
+      yv[j] = *reinterpret_cast<const u32x4_t*>(otile + (rr < TM ? rr : 0) * OSTR + col);
+      if (e < TM * VPR && rr < T.nrows && col < ncols) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(Y + (T.first + int64_t(rr) * T.stride) * p.ldy + col0 + col);
+        if (POL & kPolYNt) __builtin_nontemporal_store(yv[j], dst);
+        else *dst = yv[j];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // staged outputs read before the buffer is refilled
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // ---- software pipeline over NSET register sets
+  Run<Tin> xr[NSET][2 * JPB];
+  Run<Tin> wr[NSET][CK][NF], wu[NSET][CK][NF];
+  Tile T[NSET];
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) {
+    setup(s, T[s]);
+    load(T[s], xr[s], wr[s], wu[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < NCP; ++j)
+    *reinterpret_cast<u32x4_t*>(wkk + (j * NTHR + int(threadIdx.x)) * 16) = wkk_tmp[j];
+  // Per step: stage the activations of tile u, multiply, store its outputs,
+  // then request tile u + NSET - 1.  The stores go out before the new loads
+  // and their data registers stay live until those loads are issued: a
+  // register that a pending store still reads is only reused once newer
+  // loads exist, so waiting for the store never drains the loads in flight.
+  // The loop runs whole rounds of NSET steps and exits only after the last
+  // one, so the loop header is entered from one place with one queue.
+  const int rounds = (n_my + NSET - 1) / NSET;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      const int u = rd * NSET + s;
+      store_x(xr[s]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      u32x4_t yv[NYV];
+      compute_store(T[s], wr[s], wu[s], yv);
+      const int sn = (s + NSET - 1) % NSET;
+      setup(u + NSET - 1, T[sn]);
+      load(T[sn], xr[sn], wr[sn], wu[sn]);
+#pragma unroll
+      for (int j = 0; j < NYV; ++j) asm volatile("" ::"v"(yv[j]));
+    }
   }
 }
 
@@ -1207,6 +1538,50 @@ const PersistVariant kPersist[] = {
 };
 constexpr int kNumPersist = int(sizeof(kPersist) / sizeof(kPersist[0]));
 
+// Job-kernel variants (bf16 inputs, Q_q, closed-form row maps, b_in = 32 CK).
+// Launchers are indexed by the two own-block policy bits; outputs are always
+// stored nontemporally.
+typedef void (*JobLaunch)(JobParams, dim3, dim3, hipStream_t);
+struct JobVariant {
+  int id;
+  int tn, tm, ck;
+  JobLaunch plain_b[4], plain_f[4];
+  JobLaunch swi_b[4], swi_f[4];   // may be null
+};
+
+template <int NF, int MF, int CK, int NSET, bool SW, int POL, typename Tout>
+void launch_job(JobParams p, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((leaf_job_kernel<NF, MF, CK, NSET, SW, POL, Tout>), grid, block, 0, s, p);
+}
+
+#define AA_JL(NF, MF, CK, NSET, SW, T)                                                               \
+  {                                                                                                  \
+    launch_job<NF, MF, CK, NSET, SW, kPolYNt, T>, launch_job<NF, MF, CK, NSET, SW, kPolYNt | 1, T>, \
+        launch_job<NF, MF, CK, NSET, SW, kPolYNt | 2, T>, launch_job<NF, MF, CK, NSET, SW, kPolYNt | 3, T> \
+  }
+#define AA_JOB(ID, NF, MF, CK, NSET)                                                               \
+  JobVariant {                                                                                     \
+    ID, 4 * NF * 16, MF * 16, CK, AA_JL(NF, MF, CK, NSET, false, __bf16),                          \
+        AA_JL(NF, MF, CK, NSET, false, float), {}, {}                                              \
+  }
+#define AA_JOB_SW(ID, NF, MF, CK, NSET)                                                            \
+  JobVariant {                                                                                     \
+    ID, 4 * NF * 16, MF * 16, CK, AA_JL(NF, MF, CK, NSET, false, __bf16),                          \
+        AA_JL(NF, MF, CK, NSET, false, float), AA_JL(NF, MF, CK, NSET, true, __bf16),              \
+        AA_JL(NF, MF, CK, NSET, true, float)                                                       \
+  }
+
+const JobVariant kJob[] = {
+    AA_JOB(0, 2, 4, 4, 3),      // TN 128, TM 64, two tiles in flight
+    AA_JOB(1, 2, 2, 4, 4),      // TN 128, TM 32, three tiles in flight
+    AA_JOB(3, 2, 4, 4, 2),      // TN 128, TM 64, one tile in flight
+    AA_JOB_SW(2, 1, 4, 4, 3),   // TN 64,  TM 64 (also the SwiGLU gate/up instance)
+    AA_JOB(4, 2, 2, 4, 3),      // TN 128, TM 32, two tiles in flight
+    AA_JOB(5, 1, 4, 4, 4),      // TN 64,  TM 64, three tiles in flight
+    AA_JOB(6, 3, 2, 4, 3),      // TN 192, TM 32, two tiles in flight
+};
+constexpr int kNumJob = int(sizeof(kJob) / sizeof(kJob[0]));
+
 int64_t rows_per_type_max(const aa_plan_s& plan, int64_t M) {
   if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
   return (M + plan.q - 1) / plan.q;
@@ -1316,7 +1691,80 @@ aa_status_t after_launch(hipStream_t stream, const char* what) {
   return AA_OK;
 }
 
+// Workgroup slots per XCD for the two-per-CU persistent kernels.
+int slots_per_xcd() { return device_cu_count() * 2 / kNumXcd; }
+
+// Job variant for this call, or -1.
+int choose_job(const aa_plan_s& plan, int64_t M, bool swiglu) {
+  if (plan.in_dtype != AA_BF16 || plan.law != AA_LAW_QQ) return -1;
+  if (plan.type_kind != AA_TYPES_POS_MOD && plan.type_kind != AA_TYPES_BLOCK_ROWS) return -1;
+  if (plan.q % kNumXcd) return -1;
+  const int gpx = plan.q / kNumXcd;
+  // activation offsets inside a tile are 32-bit: TM rows of stride q (or 1)
+  const int64_t rstride = plan.type_kind == AA_TYPES_BLOCK_ROWS ? plan.d_in : int64_t(plan.q) * plan.d_in;
+  auto fits = [&](int v) {
+    const JobVariant& jv = kJob[v];
+    if (plan.b_in != 32 * jv.ck) return false;
+    if (rstride * jv.tm + plan.d_in >= (int64_t(1) << 32)) return false;
+    if (swiglu && jv.swi_b[0] == nullptr) return false;
+    const int64_t nt = (plan.b_out + jv.tn - 1) / jv.tn;
+    return slots_per_xcd() / gpx >= nt;
+  };
+  if (plan.tile_override >= 300) {
+    const int v = plan.tile_override - 300;
+    return (v < kNumJob && fits(v)) ? v : -1;
+  }
+  if (plan.tile_override >= 0) return -1;
+  if (rows_per_type_max(plan, M) > 256) return -1;
+  const int v = swiglu ? 2 : 0;
+  if (!fits(v)) return -1;
+  // The job kernel pays a prologue per workgroup (its diagonal strip) and
+  // balances a job's tiles over whole workgroups; it wins once every
+  // workgroup has many tiles.  Fewer go to the persistent kernel.
+  const JobVariant& jv = kJob[v];
+  const int64_t mt = (rows_per_type_max(plan, M) + jv.tm - 1) / jv.tm;
+  const int64_t nt = (plan.b_out + jv.tn - 1) / jv.tn;
+  const int64_t tiles_per_wg = int64_t(plan.q) * plan.q * mt * nt / (int64_t(kNumXcd) * slots_per_xcd());
+  return tiles_per_wg >= 16 ? v : -1;
+}
+
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  const int jid = choose_job(plan, call.M, call.swiglu);
+  if (jid >= 0) {
+    const JobVariant& jv = kJob[jid];
+    JobParams p{};
+    p.X = call.X;
+    p.W0 = call.W0;
+    p.W1 = call.W1;
+    p.Y = call.Y;
+    p.M = call.M;
+    p.ldx = plan.d_in;
+    p.ldy = plan.d_out;
+    p.q = plan.q;
+    p.b_out = int32_t(plan.b_out);
+    p.kind = plan.type_kind;
+    p.off_mod_q = int32_t(call.pos_offset % plan.q);
+    p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
+    const int64_t mi = rows_per_type_max(plan, call.M);
+    p.mt_count = int32_t((mi + jv.tm - 1) / jv.tm);
+    if (p.mt_count < 1) return AA_OK;
+    p.nt_count = int32_t((plan.b_out + jv.tn - 1) / jv.tn);
+    p.gpx = plan.q / kNumXcd;
+    p.wpg = slots_per_xcd() / p.gpx;
+    if (plan.wg_per_cu > 0) {
+      const int w = device_cu_count() * plan.wg_per_cu / kNumXcd / p.gpx;
+      if (w >= p.nt_count) p.wpg = w;
+    }
+    if (int64_t(plan.q) * p.mt_count > int64_t(0x7fffffff))
+      return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+    const dim3 grid{uint32_t(kNumXcd * p.gpx * p.wpg), 1, 1}, block{256, 1, 1};
+    int pol = (p.mt_count == 1 ? kPolWOwn : 0) | (p.nt_count == 1 ? kPolXOwn : 0);
+    if (plan.persist_pol >= 0) pol = plan.persist_pol & 3;
+    const bool fout = plan.out_dtype == AA_F32;
+    auto fn = call.swiglu ? (fout ? jv.swi_f[pol] : jv.swi_b[pol]) : (fout ? jv.plain_f[pol] : jv.plain_b[pol]);
+    fn(p, grid, block, stream);
+    return after_launch(stream, call.swiglu ? "leaf_job(swiglu)" : "leaf_job");
+  }
   const int pid = choose_persist(plan, call.M, call.swiglu);
   if (pid >= 0) {
     const PersistVariant& pv = kPersist[pid];

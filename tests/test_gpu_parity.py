@@ -139,7 +139,7 @@ def test_every_tile_variant_agrees():
     law, q, M, d_in, d_out = "Qq", 8, 700, 1024, 1536
     say("variants", law, q, M, d_in, d_out)
     ref = None
-    for v in list(range(9)) + [100 + j for j in range(9)] + [200, 201]:
+    for v in list(range(9)) + [100 + j for j in range(9)] + [200, 201] + [300 + j for j in range(7)]:
         os.environ["AA_TILE"] = str(v)
         try:
             plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=31)
@@ -149,6 +149,28 @@ def test_every_tile_variant_agrees():
         if ref is None:
             ref = oracle.project(host(X), host(W), law, q, _types("pos_mod", M, q, 2))
         assert_parity(host(Y), ref, False, f"variant {v}")
+
+
+@pytest.mark.parametrize("q,M,d_in,d_out,kind", [
+    (8, 20, 1024, 1536, "pos_mod"),        # fewer tiles than pipeline stages
+    (16, 2048, 2048, 768, "pos_mod"),      # 48-wide output blocks (ragged strips)
+    (64, 8192, 8192, 8192, "block_rows"),  # several m-tiles per leaf
+])
+def test_job_kernel_variants(q, M, d_in, d_out, kind):
+    """Each pipelined job-kernel variant, bf16 output, against the oracle."""
+    say("job variants", q, M, d_in, d_out, kind)
+    off = 3 if kind == "pos_mod" else 0
+    ref = None
+    for v in range(300, 307):
+        os.environ["AA_TILE"] = str(v)
+        try:
+            plan, X, W = _make("Qq", q, M, d_in, d_out, "bf16", "bf16", kind, seed=37)
+        finally:
+            del os.environ["AA_TILE"]
+        Y = _run_project(plan, X, W, pos_offset=off)
+        if ref is None:
+            ref = oracle.project(host(X), host(W), "Qq", q, _types(kind, M, q, off))
+        assert_parity(host(Y), ref, True, f"job variant {v}")
 
 
 def test_config1_q2_f32_full_product_and_associativity():
