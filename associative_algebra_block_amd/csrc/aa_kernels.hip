@@ -1225,6 +1225,264 @@ __global__ __launch_bounds__(256, 2) void leaf_job_kernel(JobParams p) {
   }
 }
 
+// ------------------------------------------------------- K-stream kernel ---
+//
+// Q_q leaves of any input-group width b_in = 32 CK cps, position or block-row
+// typing.  A tile (type i, output group k, m-tile, n-tile) is multiplied in
+// cps steps; step j covers K-chunk j of both input groups at once: slot 0 is
+// x_i chunk j times W_ik chunk j, slot 1 is x_k chunk j times W_kk chunk j,
+// so each slot's cache policy is fixed (own blocks streamed past L2, shared
+// ones kept).  Steps are pipelined over NSET rotating register sets with the
+// same discipline as the job kernel: loads of step e + NSET - 1 are issued
+// after step e's multiplies and stores, the stored values stay live past
+// them, void steps past the end re-read L2-resident data, and the loop exits
+// only after whole rounds.  Tiles are numbered and dealt as in the persistent
+// kernel (contiguous run of output groups per XCD, W_kk shared in its L2).
+
+template <int NF, int MF, int CK, int NSET, bool SWIGLU, int POL, typename Tout>
+__global__ __launch_bounds__(256, 2) void leaf_kstream_kernel(LeafParams p) {
+  using Tin = __bf16;
+  constexpr int NTHR = 256;
+  constexpr int TN = 4 * NF * 16;
+  constexpr int TM = MF * 16;
+  constexpr int XCB = 4 * CK;              // 16-byte chunks of one slot's row
+  constexpr int RS = 2 * XCB + 1;          // staged activation row stride (chunks, one pad)
+  constexpr int JPB = TM * XCB / NTHR;     // activation loads per thread per slot
+  static_assert((TM * XCB) % NTHR == 0, "activation tile");
+  constexpr int OSTR = TN + 8;
+  constexpr int XS_BYTES = TM * RS * 16 > TM * OSTR * int(sizeof(Tout)) ? TM * RS * 16 : TM * OSTR * int(sizeof(Tout));
+  __shared__ __attribute__((aligned(1024))) unsigned char xs[XS_BYTES];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int q = p.q;
+  const int cps = p.b_in / (32 * CK);      // steps per tile
+  const int nstrips = p.b_out / 16;
+  const int strip_bytes = p.b_in * 32;
+  const int64_t blk_bytes = int64_t(p.b_in) * p.b_out * 2;
+  const unsigned char* W0 = static_cast<const unsigned char*>(p.W0);
+  const unsigned char* W1 = static_cast<const unsigned char*>(p.W1);
+  const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
+  Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
+
+  // ---- this workgroup's tiles: every G8-th tile of its XCD's run
+  const uint32_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const uint32_t G8 = gridDim.x / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  const uint32_t run_begin = xcd * per + (xcd < rem ? xcd : rem);
+  const uint32_t run_end = run_begin + per + (xcd < rem ? 1 : 0);
+  const uint32_t t0 = run_begin + slot;
+  if (t0 >= run_end) return;
+  const int n_tiles_my = int((run_end - t0 + G8 - 1) / G8);
+  const int n_steps = n_tiles_my * cps;
+  const int64_t m_div_q = p.M / q;
+  const int m_mod_q = int(p.M - m_div_q * q);
+
+  struct Step {
+    int i, k, nt, nrows, j;
+    bool live, diag;
+    int64_t first, stride;
+  };
+  // Step (u, j): tile u of this workgroup, K-chunk j.  Past the last step the
+  // last tile is re-used with live = false.
+  auto setup = [&](int u, int j, Step& S) __attribute__((always_inline)) {
+    S.live = u < n_tiles_my;
+    uint32_t t = t0 + uint32_t(S.live ? u : n_tiles_my - 1) * G8;
+    S.j = S.live ? j : cps - 1;
+    S.nt = int(t % uint32_t(p.nt_count));
+    t /= uint32_t(p.nt_count);
+    const int mt = int(t % uint32_t(p.mt_count));
+    t /= uint32_t(p.mt_count);
+    const int kk = int(t % uint32_t(p.kc));
+    t /= uint32_t(p.kc);
+    S.i = int(t % uint32_t(q));
+    S.k = int(t / uint32_t(q)) * p.kc + kk;
+    S.diag = S.i == S.k;
+    int64_t count;
+    if (p.kind == AA_TYPES_BLOCK_ROWS) {
+      S.first = int64_t(S.i) * p.rows_per_type;
+      S.stride = 1;
+      count = p.rows_per_type;
+    } else {
+      int r0 = S.i - p.off_mod_q;
+      if (r0 < 0) r0 += q;
+      S.first = r0;
+      S.stride = q;
+      count = m_div_q + (r0 < m_mod_q ? 1 : 0);
+    }
+    const int64_t lo = int64_t(mt) * TM;
+    S.nrows = lo >= count ? 0 : int(count - lo < TM ? count - lo : TM);
+    S.first += lo * S.stride;
+  };
+
+  // ---- loads of one step.  Slot 0: x_i chunk j and W_ik chunk j; slot 1:
+  // x_k chunk j and W_kk chunk j (a diagonal leaf or a void step re-reads the
+  // cached data of slot 0 / of W_kk).  Activations: chunk x_cc of rows
+  // x_r0 + jb (NTHR / XCB); rows past the tile re-read its first row.
+  const int x_cc = int(threadIdx.x) % XCB, x_r0 = int(threadIdx.x) / XCB;
+  auto load = [&](const Step& S, Run<Tin> (&xr)[2 * JPB], Run<Tin> (&wr)[2][CK][NF],
+                  Run<Tin> (&wu)[2][CK][NF]) __attribute__((always_inline)) {
+    const Tin* xt = X + (S.nrows > 0 ? S.first : 0) * p.ldx;
+    const uint32_t rstep = uint32_t(S.stride * p.ldx);
+    uint32_t rowofs[JPB];
+#pragma unroll
+    for (int jb = 0; jb < JPB; ++jb) {
+      const int rr = jb * (NTHR / XCB) + x_r0;
+      rowofs[jb] = uint32_t(rr < S.nrows ? rr : 0) * rstep + uint32_t(S.j * 32 * CK + x_cc * 8);
+    }
+    const Tin* x0 = xt + S.i * p.b_in;
+    const Tin* x1 = (S.live && !S.diag) ? xt + S.k * p.b_in : x0;
+#pragma unroll
+    for (int jb = 0; jb < JPB; ++jb) xr[jb] = Run<Tin>::load_cached(x0 + rowofs[jb]);
+#pragma unroll
+    for (int jb = 0; jb < JPB; ++jb) {
+      if (POL & kPolXOwn) xr[JPB + jb] = Run<Tin>::load(x1 + rowofs[jb]);
+      else xr[JPB + jb] = Run<Tin>::load_cached(x1 + rowofs[jb]);
+    }
+    const int64_t kkb = (int64_t(S.k) * q + S.k) * blk_bytes;
+    const int64_t b0 = S.live ? (int64_t(S.i) * q + S.k) * blk_bytes : kkb;
+    const int64_t lo = int64_t(S.j) * CK * 1024 + lane * 16;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      int sl = S.nt * (TN / 16) + wave * NF + f;
+      sl = sl < nstrips ? sl : nstrips - 1;
+      const int64_t so = int64_t(sl) * strip_bytes + lo;
+#pragma unroll
+      for (int kl = 0; kl < CK; ++kl) {
+        const int64_t o0 = b0 + so + kl * 1024, o1 = kkb + so + kl * 1024;
+        if (POL & kPolWOwn) {
+          wr[0][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o0));
+          if (SWIGLU) wu[0][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o0));
+        } else {
+          wr[0][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + o0));
+          if (SWIGLU) wu[0][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + o0));
+        }
+        wr[1][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + o1));
+        if (SWIGLU) wu[1][kl][f] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + o1));
+      }
+    }
+  };
+  auto store_x = [&](const Run<Tin> (&xr)[2 * JPB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int jb = 0; jb < JPB; ++jb) {
+        const int rr = jb * (NTHR / XCB) + x_r0;
+        *reinterpret_cast<u32x4_t*>(xs + (rr * RS + ch * XCB + x_cc) * 16) = xr[ch * JPB + jb].v;
+      }
+  };
+
+  constexpr int VPR = TN * int(sizeof(Tout)) / 16;
+  constexpr int NYV = (TM * VPR + NTHR - 1) / NTHR;
+  f32x4_t acc0[NF][MF], acc1[NF][MF];
+  // ---- multiply one step; on a tile's last step stage and store its outputs
+  auto compute = [&](const Step& S, const Run<Tin> (&wr)[2][CK][NF], const Run<Tin> (&wu)[2][CK][NF],
+                     u32x4_t (&yv)[NYV]) __attribute__((always_inline)) {
+    if (S.j == 0) {
+#pragma unroll
+      for (int a = 0; a < NF; ++a)
+#pragma unroll
+        for (int b = 0; b < MF; ++b) {
+          acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (sl == 1 && S.diag) break;
+#pragma unroll
+      for (int kl = 0; kl < CK; ++kl) {
+        Run<Tin> xv[MF];
+#pragma unroll
+        for (int b = 0; b < MF; ++b)
+          xv[b].v = *reinterpret_cast<const u32x4_t*>(xs + ((b * 16 + l16) * RS + sl * XCB + kl * 4 + g) * 16);
+#pragma unroll
+        for (int a = 0; a < NF; ++a)
+#pragma unroll
+          for (int b = 0; b < MF; ++b) {
+            acc0[a][b] = mma(wr[sl][kl][a], xv[b], acc0[a][b]);
+            if (SWIGLU) acc1[a][b] = mma(wu[sl][kl][a], xv[b], acc1[a][b]);
+          }
+      }
+    }
+    // every wave is done reading the activation chunk before it is refilled
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (S.j == cps - 1) {
+      Tout* otile = reinterpret_cast<Tout*>(xs);
+#pragma unroll
+      for (int b = 0; b < MF; ++b)
+#pragma unroll
+        for (int a = 0; a < NF; ++a) {
+          f32x4_t v = acc0[a][b];
+          if (SWIGLU) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+          }
+          store4(otile + (b * 16 + l16) * OSTR + (wave * NF + a) * 16 + g * 4, v);
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      const int64_t col0 = int64_t(S.k) * p.b_out + int64_t(S.nt) * TN;
+      const int ncols = p.b_out - S.nt * TN < TN ? p.b_out - S.nt * TN : TN;
+#pragma unroll
+      for (int jj = 0; jj < NYV; ++jj) {
+        const int e = jj * NTHR + int(threadIdx.x);
+        const int rr = e / VPR, v = e - rr * VPR;
+        const int col = v * (16 / int(sizeof(Tout)));
+        yv[jj] = *reinterpret_cast<const u32x4_t*>(otile + (rr < TM ? rr : 0) * OSTR + col);
+        if (S.live && e < TM * VPR && rr < S.nrows && col < ncols) {
+          u32x4_t* dst = reinterpret_cast<u32x4_t*>(Y + (S.first + int64_t(rr) * S.stride) * p.ldy + col0 + col);
+          if (POL & kPolYNt) __builtin_nontemporal_store(yv[jj], dst);
+          else *dst = yv[jj];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // staged outputs read before the buffer is refilled
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+
+  // ---- software pipeline over NSET register sets
+  Run<Tin> xr[NSET][2 * JPB];
+  Run<Tin> wr[NSET][2][CK][NF], wu[NSET][2][CK][NF];
+  Step S[NSET];
+  int lu = 0, lj = 0;   // the next step to request
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++lj == cps) {
+      lj = 0;
+      ++lu;
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) {
+    setup(lu, lj, S[s]);
+    load(S[s], xr[s], wr[s], wu[s]);
+    advance();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int rounds = (n_steps + NSET - 1) / NSET;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      store_x(xr[s]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      u32x4_t yv[NYV];
+#pragma unroll
+      for (int jj = 0; jj < NYV; ++jj) yv[jj] = u32x4_t{0u, 0u, 0u, 0u};
+      compute(S[s], wr[s], wu[s], yv);
+      const int sn = (s + NSET - 1) % NSET;
+      setup(lu, lj, S[sn]);
+      load(S[sn], xr[sn], wr[sn], wu[sn]);
+      advance();
+#pragma unroll
+      for (int jj = 0; jj < NYV; ++jj) asm volatile("" ::"v"(yv[jj]));
+    }
+  }
+}
+
 // --------------------------------------------------------------- decode ---
 
 struct DecodeParams {
@@ -1582,6 +1840,49 @@ const JobVariant kJob[] = {
 };
 constexpr int kNumJob = int(sizeof(kJob) / sizeof(kJob[0]));
 
+// K-stream variants (bf16 inputs, Q_q, closed-form row maps, b_in a multiple
+// of 32 CK).  Launchers are indexed by the two own-block policy bits.
+typedef void (*LeafLaunch2)(LeafParams, dim3, dim3, hipStream_t);
+struct KStreamVariant {
+  int id;
+  int tn, tm, ck;
+  int wpc;   // workgroups per CU (the VGPR budget allows three for the narrow ones)
+  LeafLaunch2 plain_b[4], plain_f[4];
+  LeafLaunch2 swi_b[4], swi_f[4];   // may be null
+};
+
+template <int NF, int MF, int CK, int NSET, bool SW, int POL, typename Tout>
+void launch_kstream(LeafParams p, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((leaf_kstream_kernel<NF, MF, CK, NSET, SW, POL, Tout>), grid, block, 0, s, p);
+}
+
+#define AA_KL(NF, MF, CK, NSET, SW, T)                                                                       \
+  {                                                                                                          \
+    launch_kstream<NF, MF, CK, NSET, SW, kPolYNt, T>, launch_kstream<NF, MF, CK, NSET, SW, kPolYNt | 1, T>, \
+        launch_kstream<NF, MF, CK, NSET, SW, kPolYNt | 2, T>,                                                \
+        launch_kstream<NF, MF, CK, NSET, SW, kPolYNt | 3, T>                                                 \
+  }
+#define AA_KS(ID, NF, MF, CK, NSET)                                                                        \
+  KStreamVariant {                                                                                         \
+    ID, 4 * NF * 16, MF * 16, CK, NF == 1 ? 3 : 2, AA_KL(NF, MF, CK, NSET, false, __bf16),              \
+        AA_KL(NF, MF, CK, NSET, false, float), {}, {}                                                      \
+  }
+#define AA_KS_SW(ID, NF, MF, CK, NSET)                                                                     \
+  KStreamVariant {                                                                                         \
+    ID, 4 * NF * 16, MF * 16, CK, NF == 1 ? 3 : 2, AA_KL(NF, MF, CK, NSET, false, __bf16),              \
+        AA_KL(NF, MF, CK, NSET, false, float), AA_KL(NF, MF, CK, NSET, true, __bf16),                      \
+        AA_KL(NF, MF, CK, NSET, true, float)                                                               \
+  }
+
+const KStreamVariant kKStream[] = {
+    AA_KS(0, 2, 4, 2, 3),      // TN 128, TM 64, 64-wide K chunks, two steps in flight
+    AA_KS(1, 2, 4, 2, 4),      // TN 128, TM 64, three steps in flight
+    AA_KS_SW(2, 1, 4, 2, 3),   // TN 64,  TM 64 (also a SwiGLU gate/up instance)
+    AA_KS(3, 1, 4, 4, 3),      // TN 64,  TM 64, 128-wide K chunks (250 VGPRs: two per CU)
+    AA_KS_SW(4, 1, 4, 2, 4),   // TN 64,  TM 64, three steps in flight
+};
+constexpr int kNumKStream = int(sizeof(kKStream) / sizeof(kKStream[0]));
+
 int64_t rows_per_type_max(const aa_plan_s& plan, int64_t M) {
   if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
   return (M + plan.q - 1) / plan.q;
@@ -1728,7 +2029,72 @@ int choose_job(const aa_plan_s& plan, int64_t M, bool swiglu) {
   return tiles_per_wg >= 16 ? v : -1;
 }
 
+// K-stream variant for this call, or -1.
+int choose_kstream(const aa_plan_s& plan, int64_t M, bool swiglu) {
+  if (plan.in_dtype != AA_BF16 || plan.law != AA_LAW_QQ) return -1;
+  if (plan.type_kind != AA_TYPES_POS_MOD && plan.type_kind != AA_TYPES_BLOCK_ROWS) return -1;
+  const int64_t rstride = plan.type_kind == AA_TYPES_BLOCK_ROWS ? plan.d_in : int64_t(plan.q) * plan.d_in;
+  auto fits = [&](int v) {
+    const KStreamVariant& kv = kKStream[v];
+    if (plan.b_in % (32 * kv.ck)) return false;
+    if (swiglu && kv.swi_b[0] == nullptr) return false;
+    return rstride * kv.tm + plan.d_in < (int64_t(1) << 32);
+  };
+  if (plan.tile_override >= 400) {
+    const int v = plan.tile_override - 400;
+    return (v < kNumKStream && fits(v)) ? v : -1;
+  }
+  if (plan.tile_override >= 0) return -1;
+  if (rows_per_type_max(plan, M) > 256) return -1;
+  // 128-wide input groups go to the job and persistent kernels; wider ones
+  // (a SwiGLU down projection) are streamed in K chunks here.
+  if (plan.b_in == 128) return -1;
+  return fits(2) ? 2 : -1;
+}
+
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  const int kid = choose_kstream(plan, call.M, call.swiglu);
+  if (kid >= 0) {
+    const KStreamVariant& kv = kKStream[kid];
+    LeafParams p{};
+    p.X = call.X;
+    p.W0 = call.W0;
+    p.W1 = call.W1;
+    p.Y = call.Y;
+    p.M = call.M;
+    p.ldx = plan.d_in;
+    p.ldy = plan.d_out;
+    p.q = plan.q;
+    p.b_in = int32_t(plan.b_in);
+    p.b_out = int32_t(plan.b_out);
+    p.law = plan.law;
+    p.kind = plan.type_kind;
+    p.off_mod_q = int32_t(call.pos_offset % plan.q);
+    p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
+    const int64_t mi = rows_per_type_max(plan, call.M);
+    p.mt_count = int32_t((mi + kv.tm - 1) / kv.tm);
+    if (p.mt_count < 1) return AA_OK;
+    p.nt_count = int32_t((plan.b_out + kv.tn - 1) / kv.tn);
+    int kc = plan.q / kNumXcd;
+    if (kc < 1) kc = 1;
+    while (plan.q % kc) --kc;
+    p.kc = kc;
+    const int64_t n_tiles = int64_t(plan.q) * plan.q * p.mt_count * p.nt_count;
+    if (n_tiles * (plan.b_in / (32 * kv.ck)) > int64_t(0x7fffffff))
+      return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+    p.n_tiles = uint32_t(n_tiles);
+    int64_t wgs = int64_t(device_cu_count()) * (plan.wg_per_cu > 0 ? plan.wg_per_cu : kv.wpc);
+    const int64_t need = (n_tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (wgs > need) wgs = need;
+    wgs = (wgs + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const dim3 grid{uint32_t(wgs), 1, 1}, block{256, 1, 1};
+    int pol = (p.mt_count == 1 ? kPolWOwn : 0) | (p.nt_count == 1 ? kPolXOwn : 0);
+    if (plan.persist_pol >= 0) pol = plan.persist_pol & 3;
+    const bool fout = plan.out_dtype == AA_F32;
+    auto fn = call.swiglu ? (fout ? kv.swi_f[pol] : kv.swi_b[pol]) : (fout ? kv.plain_f[pol] : kv.plain_b[pol]);
+    fn(p, grid, block, stream);
+    return after_launch(stream, call.swiglu ? "leaf_kstream(swiglu)" : "leaf_kstream");
+  }
   const int jid = choose_job(plan, call.M, call.swiglu);
   if (jid >= 0) {
     const JobVariant& jv = kJob[jid];

@@ -66,9 +66,6 @@ def pmc(d, counter):
     return {k: statistics.mean(v) for k, v in out.items()}, {k: max(v) for k, v in out.items()}
 
 
-def is_projection(name):
-    # the non-SwiGLU persistent streaming instance used by the Qwen3-8B-shaped projection
-    return "leaf_persist_kernel" in name and "Lb0E" in name and "ILi2ELi4E" in name
 
 
 def is_calibration_copy(name):
@@ -85,6 +82,7 @@ def main():
     ap.add_argument("--cmd-pmc", default="")
     ap.add_argument("--key", default=None, help="traffic.json key for the projection kernel")
     ap.add_argument("--alg-bytes", type=float, default=None, help="algorithmic bytes per projection launch")
+    ap.add_argument("--match", default="leaf_", help="substring naming the projection kernel instance")
     a = ap.parse_args()
     os.makedirs(PROFILES, exist_ok=True)
     src = kernel_source_hash()
@@ -128,7 +126,7 @@ def main():
             w = wr.get(n, 0) * 1024 * w_fac
             lines.append(f"| `{short(n)}` | {fe.get(n, 0):.0f} | {wr.get(n, 0):.0f} | {r / 1e6:.2f} | "
                          f"{w / 1e6:.2f} | {(r + w) / 1e6:.2f} |")
-            if is_projection(n):
+            if a.match in n:
                 traffic = {"read_bytes": r, "write_bytes": w, "hbm_bytes_per_launch": r + w, "kernel": n}
         if traffic and a.alg_bytes:
             lines += ["", f"Projection kernel: {traffic['hbm_bytes_per_launch'] / 1e6:.2f} MB measured per launch "
