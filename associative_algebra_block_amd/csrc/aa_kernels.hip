@@ -1112,9 +1112,10 @@ __global__ __launch_bounds__(256, 2) void leaf_job_kernel(JobParams p) {
         acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
-    // input group i times the own block W_ik (registers)
+    // input group i times the own block W_ik (registers); a void step skips it
 #pragma unroll
     for (int kl = 0; kl < CK; ++kl) {
+      if (!T.valid) break;
       Run<Tin> xv[MF];
 #pragma unroll
       for (int b = 0; b < MF; ++b)
@@ -1479,6 +1480,223 @@ __global__ __launch_bounds__(256, 2) void leaf_kstream_kernel(LeafParams p) {
       advance();
 #pragma unroll
       for (int jj = 0; jj < NYV; ++jj) asm volatile("" ::"v"(yv[jj]));
+    }
+  }
+}
+
+// --------------------------------------------------------- tile kernel ---
+//
+// Leaves with many rows per type (the pilot FFN: 3072 rows per type, Q2 x Q2)
+// are real GEMMs and bound by the matrix cores, so this kernel uses large
+// tiles: one workgroup of four waves computes TM = 128 rows by TN = 128
+// columns of one leaf, each wave a 64 x 64 quarter (4 x 4 MFMA tiles).  K runs
+// over the leaf's input groups in stages of KC = 64 (two 32-row slabs):
+//   - the weight stage is 8 strips x 2 slabs of the packed layout, i.e.
+//     sixteen contiguous 1 KiB fragments, copied to LDS in the same order, so
+//     every MFMA A operand is one conflict-free ds_read_b128;
+//   - the activation stage is 128 rows x 128 bytes of X, stored in LDS with a
+//     16-byte pad per row.
+// Stages are double-buffered in LDS and staged through NSET register sets:
+// the global loads of stage s + NSET - 1 are issued before the multiplies of
+// stage s, and stage s + 1 is written to the other LDS buffer after them,
+// behind one barrier.  The multiplies of a stage take a fraction of the time
+// its loads need to arrive (even from L2), so several stages are in flight.
+// Loads are never skipped (past the last stage they re-read it), and the loop
+// runs whole rounds of NSET stages with the multiplies of void stages skipped,
+// which keeps the compiler's waits exact.  Workgroups are numbered so that the
+// leaves with the most input groups come first.  Outputs leave through LDS as
+// 16-byte row stores.
+
+template <bool SWIGLU, int NSET, typename Tout>
+__global__ __launch_bounds__(256, SWIGLU ? 1 : 2) void leaf_tile_kernel(LeafParams p) {
+  using Tin = __bf16;
+  constexpr int TM = 128, TN = 128, KC = 64;
+  constexpr int NW = SWIGLU ? 2 : 1;
+  constexpr int WST = (TN / 16) * (KC / 32) * 1024;   // one weight stage: 16 KiB
+  constexpr int XRS = KC * 2 + 16;                    // staged activation row (bytes)
+  constexpr int XST = TM * XRS;                       // 18 KiB
+  constexpr int STAGE = NW * WST + XST;
+  constexpr int OSTR = TN + 8;
+  static_assert(2 * STAGE >= TM * OSTR * int(sizeof(Tout)), "output staging fits");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+
+  const int tid = int(threadIdx.x);
+  const int lane = tid % kWave, wave = tid / kWave;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;    // this wave's quarter: rows wm*64, columns wn*64
+  const int q = p.q;
+  const int nstrips = p.b_out / 16;
+  const int strip_bytes = p.b_in * 32;
+  const int64_t blk_bytes = int64_t(p.b_in) * p.b_out * 2;
+  const unsigned char* W0 = static_cast<const unsigned char*>(p.W0);
+  const unsigned char* W1 = static_cast<const unsigned char*>(p.W1);
+  const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
+  Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
+
+  // ---- tile: leaf (in order of decreasing input-group count), m-tile, n-tile
+  const int per_leaf = p.mt_count * p.nt_count;
+  const int lo = int(blockIdx.x) / per_leaf;
+  const int rem = int(blockIdx.x) - lo * per_leaf;
+  const int mt = rem / p.nt_count, nt = rem - mt * p.nt_count;
+  int i, k;
+  if (p.law == AA_LAW_QQ) {
+    if (lo < q * (q - 1)) {   // off-diagonal leaves (two groups) first
+      i = lo / (q - 1);
+      const int j = lo - i * (q - 1);
+      k = j < i ? j : j + 1;
+    } else {
+      i = k = lo - q * (q - 1);
+    }
+  } else {   // Q2 x Q2: i ^ k = 3 (four groups), then 2 and 1 (two), then 0 (one)
+    i = lo & 3;
+    k = i ^ (3 - (lo >> 2));
+  }
+  int segs[4] = {0, 0, 0, 0};
+  const int nseg = device_leaf_groups(p.law, i, k, segs);
+  const uint32_t gpack = uint32_t(segs[0]) | (uint32_t(segs[1]) << 2) | (uint32_t(segs[2]) << 4) | (uint32_t(segs[3]) << 6);
+  const int cps = p.b_in / KC;                 // stages per input group
+  const int n_stages = nseg * cps;
+
+  // rows of this tile
+  int64_t first, stride, count;
+  if (p.kind == AA_TYPES_BLOCK_ROWS) {
+    first = int64_t(i) * p.rows_per_type;
+    stride = 1;
+    count = p.rows_per_type;
+  } else {
+    int r0 = i - p.off_mod_q;
+    if (r0 < 0) r0 += q;
+    first = r0;
+    stride = q;
+    count = r0 < p.M ? (p.M - r0 + q - 1) / q : 0;
+  }
+  const int64_t m0 = int64_t(mt) * TM;
+  const int nrows = m0 >= count ? 0 : int(count - m0 < TM ? count - m0 : TM);
+  if (nrows <= 0) return;
+  first += m0 * stride;
+
+  // ---- per-thread load geometry (fixed for the whole K loop)
+  // weights: fragment f = j * 4 + wave (j = 0..3): strip f / 2, slab f % 2
+  int64_t wofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = j * 4 + wave;
+    int sl = nt * (TN / 16) + f / 2;
+    sl = sl < nstrips ? sl : nstrips - 1;
+    wofs[j] = int64_t(sl) * strip_bytes + (f % 2) * 1024 + lane * 16;
+  }
+  // activations: row r = j * 32 + tid / 8 (j = 0..3), 16-byte chunk tid % 8
+  const Tin* xrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = j * 32 + tid / 8;
+    xrow[j] = X + (first + int64_t(r < nrows ? r : 0) * stride) * p.ldx + (tid % 8) * 8;
+  }
+
+  Run<Tin> sw[NSET][4], su[NSET][4], sx[NSET][4];
+  auto load_stage = [&](int st, Run<Tin> (&sw)[4], Run<Tin> (&su)[4], Run<Tin> (&sx)[4]) __attribute__((always_inline)) {
+    st = st < n_stages ? st : n_stages - 1;
+    const int s = st / cps, c = st - s * cps;
+    const int grp = int((gpack >> (2 * s)) & 3u);
+    const int gsel = p.law == AA_LAW_QQ ? (s == 0 ? i : k) : grp;
+    const int64_t wb = (int64_t(gsel) * q + k) * blk_bytes + int64_t(c) * (KC / 32) * 1024;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sw[j] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + wb + wofs[j]));
+      if (SWIGLU) su[j] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + wb + wofs[j]));
+    }
+    const int xc = gsel * p.b_in + c * KC;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sx[j] = Run<Tin>::load_cached(xrow[j] + xc);
+  };
+  auto store_stage = [&](int buf, const Run<Tin> (&sw)[4], const Run<Tin> (&su)[4], const Run<Tin> (&sx)[4])
+      __attribute__((always_inline)) {
+    unsigned char* base = lds + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4_t*>(base + (j * 4 + wave) * 1024 + lane * 16) = sw[j].v;
+      if (SWIGLU) *reinterpret_cast<u32x4_t*>(base + WST + (j * 4 + wave) * 1024 + lane * 16) = su[j].v;
+      *reinterpret_cast<u32x4_t*>(base + NW * WST + (j * 32 + tid / 8) * XRS + (tid % 8) * 16) = sx[j].v;
+    }
+  };
+
+  f32x4_t acc0[4][4], acc1[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  auto compute_stage = [&](int buf) __attribute__((always_inline)) {
+    const unsigned char* base = lds + buf * STAGE;
+#pragma unroll
+    for (int sl = 0; sl < KC / 32; ++sl) {
+      Run<Tin> av[4], uv[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int f = (wn * 4 + a) * 2 + sl;   // strip wn*4 + a, slab sl
+        av[a].v = *reinterpret_cast<const u32x4_t*>(base + f * 1024 + lane * 16);
+        if (SWIGLU) uv[a].v = *reinterpret_cast<const u32x4_t*>(base + WST + f * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        bv[b].v = *reinterpret_cast<const u32x4_t*>(base + NW * WST + (wm * 64 + b * 16 + l16) * XRS + (sl * 32 + g * 8) * 2);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc0[a][b] = mma(av[a], bv[b], acc0[a][b]);
+          if (SWIGLU) acc1[a][b] = mma(uv[a], bv[b], acc1[a][b]);
+        }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) load_stage(s, sw[s], su[s], sx[s]);
+  store_stage(0, sw[0], su[0], sx[0]);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  const int rounds = (n_stages + NSET - 1) / NSET;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      const int st = rd * NSET + s;
+      const int sl = (s + NSET - 1) % NSET, sn = (s + 1) % NSET;
+      load_stage(st + NSET - 1, sw[sl], su[sl], sx[sl]);
+      if (st < n_stages) compute_stage(st & 1);
+      store_stage((st + 1) & 1, sw[sn], su[sn], sx[sn]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+
+  // ---- epilogue through LDS (both stage buffers are free after the barrier)
+  Tout* otile = reinterpret_cast<Tout*>(lds);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4_t v = acc0[a][b];
+      if (SWIGLU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+      }
+      store4(otile + (wm * 64 + b * 16 + l16) * OSTR + (wn * 4 + a) * 16 + g * 4, v);
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  constexpr int VPR = TN * int(sizeof(Tout)) / 16;
+  const int64_t col0 = int64_t(k) * p.b_out + int64_t(nt) * TN;
+  const int ncols = p.b_out - nt * TN < TN ? p.b_out - nt * TN : TN;
+#pragma unroll
+  for (int e0 = 0; e0 < TM * VPR; e0 += 256) {
+    const int e = e0 + tid;
+    const int r = e / VPR, v = e - r * VPR;
+    const int col = v * (16 / int(sizeof(Tout)));
+    if (r < nrows && col < ncols) {
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(otile + r * OSTR + col);
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(Y + (first + int64_t(r) * stride) * p.ldy + col0 + col));
     }
   }
 }
@@ -2052,7 +2270,51 @@ int choose_kstream(const aa_plan_s& plan, int64_t M, bool swiglu) {
   return fits(2) ? 2 : -1;
 }
 
+// Large-tile kernel for leaves with many rows per type (override 500).
+bool choose_tile(const aa_plan_s& plan, int64_t M) {
+  if (plan.in_dtype != AA_BF16) return false;
+  if (plan.type_kind != AA_TYPES_POS_MOD && plan.type_kind != AA_TYPES_BLOCK_ROWS) return false;
+  if (plan.b_in % 64) return false;
+  if (plan.tile_override == 500) return true;
+  if (plan.tile_override >= 0) return false;
+  return rows_per_type_max(plan, M) > 256;
+}
+
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  if (choose_tile(plan, call.M)) {
+    LeafParams p{};
+    p.X = call.X;
+    p.W0 = call.W0;
+    p.W1 = call.W1;
+    p.Y = call.Y;
+    p.M = call.M;
+    p.ldx = plan.d_in;
+    p.ldy = plan.d_out;
+    p.q = plan.q;
+    p.b_in = int32_t(plan.b_in);
+    p.b_out = int32_t(plan.b_out);
+    p.law = plan.law;
+    p.kind = plan.type_kind;
+    p.off_mod_q = int32_t(call.pos_offset % plan.q);
+    p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
+    const int64_t mi = rows_per_type_max(plan, call.M);
+    p.mt_count = int32_t((mi + 127) / 128);
+    p.nt_count = int32_t((plan.b_out + 127) / 128);
+    if (p.mt_count < 1) return AA_OK;
+    const int64_t n_tiles = int64_t(plan.q) * plan.q * p.mt_count * p.nt_count;
+    if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+    const dim3 grid{uint32_t(n_tiles), 1, 1}, block{256, 1, 1};
+    const bool fout = plan.out_dtype == AA_F32;
+    if (call.swiglu) {
+      // two weight streams: two stage sets already fill the register file
+      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<true, 2, float>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((leaf_tile_kernel<true, 2, __bf16>), grid, block, 0, stream, p);
+    } else {
+      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<false, 4, float>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((leaf_tile_kernel<false, 4, __bf16>), grid, block, 0, stream, p);
+    }
+    return after_launch(stream, call.swiglu ? "leaf_tile(swiglu)" : "leaf_tile");
+  }
   const int kid = choose_kstream(plan, call.M, call.swiglu);
   if (kid >= 0) {
     const KStreamVariant& kv = kKStream[kid];

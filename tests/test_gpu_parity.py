@@ -97,6 +97,8 @@ def test_pack_roundtrip_and_layout(law, q, d_in, d_out, dt):
     ("Qq", 16, 272, 2048, 768, "pos_mod", "bf16"),      # narrow 128 x 48 blocks, ragged
     ("Qq", 16, 272, 768, 2048, "pos_mod", "bf16"),      # 48 x 128 blocks (odd multiple of 16)
     ("Q2xQ2", 4, 520, 768, 1536, "pos_mod", "bf16"),
+    ("Q2xQ2", 4, 2100, 768, 1536, "pos_mod", "bf16"),  # 525 rows per type: large tiles, ragged
+    ("Qq", 4, 2048, 512, 448, "block_rows", "bf16"),   # 512 rows per type, ragged output strips
     ("Qq", 8, 1024, 256, 256, "block_rows", "bf16"),
     ("Qq", 2, 256, 64, 64, "pos_mod", "f32"),
     ("Qq", 1, 40, 64, 48, "pos_mod", "bf16"),
@@ -139,7 +141,7 @@ def test_every_tile_variant_agrees():
     law, q, M, d_in, d_out = "Qq", 8, 700, 1024, 1536
     say("variants", law, q, M, d_in, d_out)
     ref = None
-    for v in list(range(9)) + [100 + j for j in range(9)] + [200, 201] + [300 + j for j in range(7)] + [400 + j for j in range(5)]:
+    for v in list(range(9)) + [100 + j for j in range(9)] + [200, 201] + [300 + j for j in range(7)] + [400 + j for j in range(5)] + [500]:
         os.environ["AA_TILE"] = str(v)
         try:
             plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "f32", seed=31)
