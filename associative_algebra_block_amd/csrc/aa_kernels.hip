@@ -975,6 +975,9 @@ __global__ __launch_bounds__(256, 2) void leaf_job_kernel(JobParams p) {
     s_job = base;
   }
   const int tiles = q * p.mt_count;
+  // (Contiguous ranges measure better than dealing the tiles in turn: with
+  // every workgroup on the same row type at once, the traffic concentrates
+  // on one row block of X, W and Y at a time.)
   const int u_begin = int(int64_t(tiles) * w / s_job);
   const int u_end = int(int64_t(tiles) * (w + 1) / s_job);
   const int n_my = u_end - u_begin;

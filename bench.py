@@ -256,6 +256,9 @@ def bench_qwen3(args, torch, inp, aa, dev):
                  "speedup_step": round((t_p + t_s + t_d) / ms_step, 3)}
         del Wd1, Wd2, Wd3
 
+    dec1 = decode_single_token(torch, aa, plan, sets, pos_dec, n_dec, D, F, q,
+                               None if dense is None else sets[0])
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_qwen3(args, torch, inp, sets[0], wl)
@@ -269,11 +272,63 @@ def bench_qwen3(args, torch, inp, aa, dev):
                    "d_out": F, "q": q, "law": law, "type_map": "pos mod q", "decode_tokens": n_dec,
                    "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
         "roofline": parts["project"]["roofline"],
-        "roofline_kernel": "leaf_gemm (aa_project_fwd) at the Qwen3-8B shape",
-        "parts": parts, "dense": dense, "cpu_baseline": cpu,
+        "roofline_kernel": "aa_project_fwd at the Qwen3-8B shape (leaf_persist_kernel)",
+        "parts": parts, "decode_single_token": dec1, "dense": dense, "cpu_baseline": cpu,
         "wall_s_timed": round(wall1 - wall0, 4),
         "kernel_source": kernel_source_hash(),
     }
+
+
+def decode_single_token(torch, aa, plan, sets, pos0, n_tok, D, F, q, dense_set=None, reps=20):
+    """Generation decode: one new token per call (M = 1), n_tok calls at
+    positions pos0, pos0 + 1, ... (one per row type).  Timed eagerly (each
+    call launched from the host) and with the n_tok calls of an input set
+    captured in one HIP graph and replayed, sets alternating.  Each token
+    reads its 2q - 1 weight blocks: 2((2q-1) b_in b_out + d_in + d_out) bytes."""
+    xs = [[st["x"][j:j + 1] for j in range(n_tok)] for st in sets]
+    ys = [[st["y"][j:j + 1] for j in range(n_tok)] for st in sets]
+
+    def calls(si):
+        for j in range(n_tok):
+            aa.aa_decode_gemv(plan, xs[si][j], sets[si]["Wp"], ys[si][j], None, pos0 + j)
+
+    for si in range(len(sets)):
+        calls(si)
+    torch.cuda.synchronize()
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for r in range(reps):
+        calls(r % len(sets))
+    b.record()
+    torch.cuda.synchronize()
+    eager_us = a.elapsed_time(b) * 1e3 / (reps * n_tok)
+    graphs = []
+    for si in range(len(sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls(si)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for r in range(reps):
+        graphs[r % len(graphs)].replay()
+    b.record()
+    torch.cuda.synchronize()
+    graph_us = a.elapsed_time(b) * 1e3 / (reps * n_tok)
+    per_tok = 2 * ((2 * q - 1) * (D // q) * (F // q) + D + F)
+    out = {"tokens": n_tok, "eager_us_per_token": round(eager_us, 3), "graph_us_per_token": round(graph_us, 3),
+           "bytes_per_token": per_tok, "graph_GBs": round(per_tok / graph_us / 1e3, 1)}
+    if dense_set is not None:
+        Wdn = torch.empty(D, F, dtype=torch.bfloat16, device=dense_set["X"].device).normal_(0.0, D ** -0.5)
+        x1 = dense_set["x"][:1]
+        t = dense_timer(torch, lambda: torch.matmul(x1, Wdn), iters=50)
+        out["dense_us_per_token"] = round(t * 1e3, 3)
+        out["speedup_graph_vs_dense"] = round(t * 1e3 / graph_us, 3)
+        del Wdn
+    return out
 
 
 def cpu_baseline_qwen3(args, torch, inp, st, wl):

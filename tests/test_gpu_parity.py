@@ -223,6 +223,39 @@ def test_kstream_swiglu_matches_oracle():
     assert_parity(host(Y), oracle.project(host(H), host(Wd), "Qq", q, types), False, "kstream swiglu Y")
 
 
+def test_decode_single_tokens_in_a_graph_replay():
+    """Single-token decode calls captured in one HIP graph: every replay,
+    with eager work and synchronisations between replays, equals the eager
+    calls bit for bit, and the eager calls match the oracle."""
+    q, D, F, n = 8, 1024, 1536, 8
+    say("decode graph", q, D, F, n)
+    plan = aa.aa_plan_create("Qq", q, D, F, "pos_mod", 0, "bf16", "f32")
+    x = inp.gaussian((n, D), 61, 1.0, torch.bfloat16, DEV)
+    W = inp.gaussian((D, F), 62, D ** -0.5, torch.bfloat16, DEV)
+    Wp = aa.pack(plan, W)
+    y_eager = torch.empty(n, F, dtype=torch.float32, device=DEV)
+    y_graph = torch.empty(n, F, dtype=torch.float32, device=DEV)
+    pos0 = 1000
+    for j in range(n):
+        aa.aa_decode_gemv(plan, x[j:j + 1], Wp, y_eager[j:j + 1], None, pos0 + j)
+    torch.cuda.synchronize()
+    ref = oracle.decode(host(x), host(W), "Qq", q, np.arange(pos0, pos0 + n))
+    assert_parity(host(y_eager), ref, False, "decode eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(n):
+            aa.aa_decode_gemv(plan, x[j:j + 1], Wp, y_graph[j:j + 1], None, pos0 + j)
+    other = aa.aa_plan_create("Qq", q, D, F, "pos_mod", 0, "bf16", "bf16")
+    Y_other = torch.empty(300, F, dtype=torch.bfloat16, device=DEV)
+    for r in range(4):
+        y_graph.fill_(float("nan"))
+        g.replay()
+        # eager work between replays
+        aa.aa_project_fwd(other, inp.gaussian((300, D), 70 + r, 1.0, torch.bfloat16, DEV), Wp, Y_other)
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph, y_eager), f"replay {r}"
+
+
 def test_config1_q2_f32_full_product_and_associativity():
     """Q_2 in fp32: row-typed projection, the full 64 x 64 product, and
     (X * W1) * W2 == X * (W1 * W2) computed on the GPU."""
