@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
       const int kf = s - si * KF;
       const int seg = segs[si < nseg ? si : 0];
       const bool kval = (s < nsteps) && (kf * 32 + g * 8 < p.b_in);
-      const int64_t wofs = int64_t(seg * p.q + k) * blk_elems + kf * 512 + lane * 8;
+      const int64_t wofs = (int64_t(seg) * p.q + k) * blk_elems + kf * 512 + lane * 8;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int64_t o = wofs + int64_t(nfrag0 + f) * 16 * p.b_in;
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_stream_kernel(LeafParams
   auto chunk_ofs = [&](int c) -> int64_t {   // byte offset of chunk c's first slab, lane part excluded
     const int si = c / chunks_per_seg;
     const int kf0 = (c - si * chunks_per_seg) * CK;
-    return int64_t(segs[si] * p.q + k) * blk_bytes + kf0 * 1024;
+    return (int64_t(segs[si]) * p.q + k) * blk_bytes + kf0 * 1024;
   };
   // Strips past the block's last column read the block's first strip instead
   // (their products are never stored), so every load hits real weight lines.
@@ -1491,42 +1491,45 @@ __global__ __launch_bounds__(256, 2) void leaf_kstream_kernel(LeafParams p) {
 //
 // Leaves with many rows per type (the pilot FFN: 3072 rows per type, Q2 x Q2)
 // are real GEMMs and bound by the matrix cores, so this kernel uses large
-// tiles: one workgroup of four waves computes TM = 128 rows by TN = 128
-// columns of one leaf, each wave a 64 x 64 quarter (4 x 4 MFMA tiles).  K runs
-// over the leaf's input groups in stages of KC = 64 (two 32-row slabs):
-//   - the weight stage is 8 strips x 2 slabs of the packed layout, i.e.
-//     sixteen contiguous 1 KiB fragments, copied to LDS in the same order, so
-//     every MFMA A operand is one conflict-free ds_read_b128;
-//   - the activation stage is 128 rows x 128 bytes of X, stored in LDS with a
-//     16-byte pad per row.
-// Stages are double-buffered in LDS and staged through NSET register sets:
-// the global loads of stage s + NSET - 1 are issued before the multiplies of
-// stage s, and stage s + 1 is written to the other LDS buffer after them,
-// behind one barrier.  The multiplies of a stage take a fraction of the time
-// its loads need to arrive (even from L2), so several stages are in flight.
-// Loads are never skipped (past the last stage they re-read it), and the loop
-// runs whole rounds of NSET stages with the multiplies of void stages skipped,
-// which keeps the compiler's waits exact.  Workgroups are numbered so that the
-// leaves with the most input groups come first.  Outputs leave through LDS as
-// 16-byte row stores.
+// tiles: one workgroup of four waves computes TM = 128 rows of one leaf, each
+// wave a 64-row half by four 16-column strips (4 x 4 MFMA tiles).  K runs over
+// the leaf's input groups in stages of KC = 64 (two 32-row slabs).
+//   - Weights go straight to registers: the packed layout stores every MFMA
+//     A operand as one contiguous 1 KiB fragment, so each wave reads its own
+//     eight fragments per stage with fully coalesced loads (the two waves of
+//     a column half read the same fragments; the second read hits L2).
+//   - Activations are shared by the waves of a row half: the stage (128 rows
+//     x 128 bytes) is staged through LDS with a 16-byte pad per row.
+// Keeping the weights out of LDS halves its traffic, which bounded the
+// previous version.  The fused SwiGLU gate/up interleaves strips: each wave
+// takes two gate strips and the same two up strips, so its accumulators hold
+// g and u of the same outputs and the epilogue forms silu(g) u in registers;
+// a workgroup then covers 64 output columns instead of 128, with the same
+// register budget as the plain projection (two workgroups per CU).
+// Stages are staged through NSET register sets: the loads of stage s + NSET -
+// 1 are issued before the multiplies of stage s, the activations of stage s +
+// 1 are written to the other LDS buffer after them, behind one barrier.
+// Loads are never skipped (past the last stage they re-read it) and the loop
+// runs whole rounds of NSET stages with the multiplies of void stages
+// skipped, which keeps the compiler's waits exact.  Workgroups are numbered
+// so that the leaves with the most input groups come first.  Outputs leave
+// through LDS as 16-byte row stores.
 
 template <bool SWIGLU, int NSET, typename Tout>
-__global__ __launch_bounds__(256, SWIGLU ? 1 : 2) void leaf_tile_kernel(LeafParams p) {
+__global__ __launch_bounds__(256, 2) void leaf_tile_kernel(LeafParams p) {
   using Tin = __bf16;
-  constexpr int TM = 128, TN = 128, KC = 64;
-  constexpr int NW = SWIGLU ? 2 : 1;
-  constexpr int WST = (TN / 16) * (KC / 32) * 1024;   // one weight stage: 16 KiB
+  constexpr int TM = 128, KC = 64;
+  constexpr int TN = SWIGLU ? 64 : 128;               // output columns per workgroup
   constexpr int XRS = KC * 2 + 16;                    // staged activation row (bytes)
-  constexpr int XST = TM * XRS;                       // 18 KiB
-  constexpr int STAGE = NW * WST + XST;
+  constexpr int XST = TM * XRS;                       // 18 KiB per stage
   constexpr int OSTR = TN + 8;
-  static_assert(2 * STAGE >= TM * OSTR * int(sizeof(Tout)), "output staging fits");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * STAGE];
+  constexpr int LDS_BYTES = 2 * XST > TM * OSTR * int(sizeof(Tout)) ? 2 * XST : TM * OSTR * int(sizeof(Tout));
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
   const int tid = int(threadIdx.x);
   const int lane = tid % kWave, wave = tid / kWave;
   const int g = lane >> 4, l16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;    // this wave's quarter: rows wm*64, columns wn*64
+  const int wm = wave >> 1, wn = wave & 1;    // this wave's rows wm*64.., column half wn
   const int q = p.q;
   const int nstrips = p.b_out / 16;
   const int strip_bytes = p.b_in * 32;
@@ -1579,14 +1582,15 @@ __global__ __launch_bounds__(256, SWIGLU ? 1 : 2) void leaf_tile_kernel(LeafPara
   first += m0 * stride;
 
   // ---- per-thread load geometry (fixed for the whole K loop)
-  // weights: fragment f = j * 4 + wave (j = 0..3): strip f / 2, slab f % 2
+  // weights: this wave's strip a (0..3) of the tile; plain: strips
+  // nt*8 + wn*4 + a of W0; SwiGLU: strips nt*4 + wn*2 + (a & 1) of W0 (a < 2,
+  // gate) or W1 (a >= 2, up)
   int64_t wofs[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = j * 4 + wave;
-    int sl = nt * (TN / 16) + f / 2;
+  for (int a = 0; a < 4; ++a) {
+    int sl = SWIGLU ? nt * 4 + wn * 2 + (a & 1) : nt * 8 + wn * 4 + a;
     sl = sl < nstrips ? sl : nstrips - 1;
-    wofs[j] = int64_t(sl) * strip_bytes + (f % 2) * 1024 + lane * 16;
+    wofs[a] = int64_t(sl) * strip_bytes + lane * 16;
   }
   // activations: row r = j * 32 + tid / 8 (j = 0..3), 16-byte chunk tid % 8
   const Tin* xrow[4];
@@ -1596,68 +1600,54 @@ __global__ __launch_bounds__(256, SWIGLU ? 1 : 2) void leaf_tile_kernel(LeafPara
     xrow[j] = X + (first + int64_t(r < nrows ? r : 0) * stride) * p.ldx + (tid % 8) * 8;
   }
 
-  Run<Tin> sw[NSET][4], su[NSET][4], sx[NSET][4];
-  auto load_stage = [&](int st, Run<Tin> (&sw)[4], Run<Tin> (&su)[4], Run<Tin> (&sx)[4]) __attribute__((always_inline)) {
+  Run<Tin> sw[NSET][KC / 32][4], sx[NSET][4];
+  auto load_stage = [&](int st, Run<Tin> (&w)[KC / 32][4], Run<Tin> (&x)[4]) __attribute__((always_inline)) {
     st = st < n_stages ? st : n_stages - 1;
     const int s = st / cps, c = st - s * cps;
     const int grp = int((gpack >> (2 * s)) & 3u);
     const int gsel = p.law == AA_LAW_QQ ? (s == 0 ? i : k) : grp;
     const int64_t wb = (int64_t(gsel) * q + k) * blk_bytes + int64_t(c) * (KC / 32) * 1024;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sw[j] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W0 + wb + wofs[j]));
-      if (SWIGLU) su[j] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(W1 + wb + wofs[j]));
-    }
+    for (int sl = 0; sl < KC / 32; ++sl)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const unsigned char* wp = (SWIGLU && a >= 2) ? W1 : W0;
+        w[sl][a] = Run<Tin>::load_cached(reinterpret_cast<const Tin*>(wp + wb + wofs[a] + sl * 1024));
+      }
     const int xc = gsel * p.b_in + c * KC;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sx[j] = Run<Tin>::load_cached(xrow[j] + xc);
+    for (int j = 0; j < 4; ++j) x[j] = Run<Tin>::load_cached(xrow[j] + xc);
   };
-  auto store_stage = [&](int buf, const Run<Tin> (&sw)[4], const Run<Tin> (&su)[4], const Run<Tin> (&sx)[4])
-      __attribute__((always_inline)) {
-    unsigned char* base = lds + buf * STAGE;
+  auto store_stage = [&](int buf, const Run<Tin> (&x)[4]) __attribute__((always_inline)) {
+    unsigned char* base = lds + buf * XST;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4_t*>(base + (j * 4 + wave) * 1024 + lane * 16) = sw[j].v;
-      if (SWIGLU) *reinterpret_cast<u32x4_t*>(base + WST + (j * 4 + wave) * 1024 + lane * 16) = su[j].v;
-      *reinterpret_cast<u32x4_t*>(base + NW * WST + (j * 32 + tid / 8) * XRS + (tid % 8) * 16) = sx[j].v;
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4_t*>(base + (j * 32 + tid / 8) * XRS + (tid % 8) * 16) = x[j].v;
   };
 
-  f32x4_t acc0[4][4], acc1[4][4];
+  f32x4_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc0[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc1[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  auto compute_stage = [&](int buf) __attribute__((always_inline)) {
-    const unsigned char* base = lds + buf * STAGE;
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute_stage = [&](int buf, const Run<Tin> (&w)[KC / 32][4]) __attribute__((always_inline)) {
+    const unsigned char* base = lds + buf * XST;
 #pragma unroll
     for (int sl = 0; sl < KC / 32; ++sl) {
-      Run<Tin> av[4], uv[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int f = (wn * 4 + a) * 2 + sl;   // strip wn*4 + a, slab sl
-        av[a].v = *reinterpret_cast<const u32x4_t*>(base + f * 1024 + lane * 16);
-        if (SWIGLU) uv[a].v = *reinterpret_cast<const u32x4_t*>(base + WST + f * 1024 + lane * 16);
-      }
+      Run<Tin> bv[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        bv[b].v = *reinterpret_cast<const u32x4_t*>(base + NW * WST + (wm * 64 + b * 16 + l16) * XRS + (sl * 32 + g * 8) * 2);
+        bv[b].v = *reinterpret_cast<const u32x4_t*>(base + (wm * 64 + b * 16 + l16) * XRS + (sl * 32 + g * 8) * 2);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          acc0[a][b] = mma(av[a], bv[b], acc0[a][b]);
-          if (SWIGLU) acc1[a][b] = mma(uv[a], bv[b], acc1[a][b]);
-        }
+        for (int b = 0; b < 4; ++b) acc[a][b] = mma(w[sl][a], bv[b], acc[a][b]);
     }
   };
 
 #pragma unroll
-  for (int s = 0; s < NSET - 1; ++s) load_stage(s, sw[s], su[s], sx[s]);
-  store_stage(0, sw[0], su[0], sx[0]);
+  for (int s = 0; s < NSET - 1; ++s) load_stage(s, sw[s], sx[s]);
+  store_stage(0, sx[0]);
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
   const int rounds = (n_stages + NSET - 1) / NSET;
@@ -1666,9 +1656,9 @@ __global__ __launch_bounds__(256, SWIGLU ? 1 : 2) void leaf_tile_kernel(LeafPara
     for (int s = 0; s < NSET; ++s) {
       const int st = rd * NSET + s;
       const int sl = (s + NSET - 1) % NSET, sn = (s + 1) % NSET;
-      load_stage(st + NSET - 1, sw[sl], su[sl], sx[sl]);
-      if (st < n_stages) compute_stage(st & 1);
-      store_stage((st + 1) & 1, sw[sn], su[sn], sx[sn]);
+      load_stage(st + NSET - 1, sw[sl], sx[sl]);
+      if (st < n_stages) compute_stage(st & 1, sw[s]);
+      store_stage((st + 1) & 1, sx[sn]);
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_s_barrier();
     }
@@ -1677,16 +1667,21 @@ __global__ __launch_bounds__(256, SWIGLU ? 1 : 2) void leaf_tile_kernel(LeafPara
   // ---- epilogue through LDS (both stage buffers are free after the barrier)
   Tout* otile = reinterpret_cast<Tout*>(lds);
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < 4; ++b) {
+    if (SWIGLU) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      f32x4_t v = acc0[a][b];
-      if (SWIGLU) {
+      for (int a = 0; a < 2; ++a) {
+        f32x4_t v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[a][b][e], acc1[a][b][e]);
+        for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc[a][b][e], acc[a + 2][b][e]);
+        store4(otile + (wm * 64 + b * 16 + l16) * OSTR + (wn * 2 + a) * 16 + g * 4, v);
       }
-      store4(otile + (wm * 64 + b * 16 + l16) * OSTR + (wn * 4 + a) * 16 + g * 4, v);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        store4(otile + (wm * 64 + b * 16 + l16) * OSTR + (wn * 4 + a) * 16 + g * 4, acc[a][b]);
     }
+  }
   __builtin_amdgcn_s_waitcnt(0xc07f);
   __builtin_amdgcn_s_barrier();
   constexpr int VPR = TN * int(sizeof(Tout)) / 16;
@@ -1800,14 +1795,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   int kofs[KF];
 #pragma unroll
   for (int kf = 0; kf < KF; ++kf) kofs[kf] = (kf * 32 + g * 8 < p.b_in) ? kf * 512 : 0;
-  const Tin* wdiag = W + int64_t(k * p.q + k) * blk + sofs;
+  const Tin* wdiag = W + (int64_t(k) * p.q + k) * blk + sofs;
 #pragma unroll
   for (int kf = 0; kf < KF; ++kf) w[0][kf] = Run<Tin>::load_cached(wdiag + kofs[kf]);
 #pragma unroll
   for (int j = 0; j < TG; ++j) {
     const int ty = tok_type[j];
     const int sg = ty < 0 ? -1 : other_seg(ty, 0);
-    const Tin* wb = sg >= 0 ? W + int64_t(sg * p.q + k) * blk + sofs : wdiag;
+    const Tin* wb = sg >= 0 ? W + (int64_t(sg) * p.q + k) * blk + sofs : wdiag;
 #pragma unroll
     for (int kf = 0; kf < KF; ++kf) w[1 + j][kf] = Run<Tin>::load(wb + kofs[kf]);
   }
@@ -1839,7 +1834,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       for (int s = 1; s < NSEG; ++s) {
         const int sg = ty < 0 ? -1 : other_seg(ty, s);
         if (sg < 0) continue;
-        const Tin* wb = W + int64_t(sg * p.q + k) * blk + sofs;
+        const Tin* wb = W + (int64_t(sg) * p.q + k) * blk + sofs;
         for (int kf = 0; kf < KF; ++kf) {
           Run<Tin> a = Run<Tin>::load(wb + kofs[kf]);
           Run<Tin> b = Run<Tin>::zero();
@@ -2173,8 +2168,10 @@ int choose_persist(const aa_plan_s& plan, int64_t M, bool swiglu) {
   return -1;
 }
 
+// Compute units of the current device (cached per calling thread, so calls
+// from several host threads do not race on the cache).
 int device_cu_count() {
-  static int cached_dev = -1, cached_cus = 0;
+  static thread_local int cached_dev = -1, cached_cus = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (dev != cached_dev) {
@@ -2302,19 +2299,19 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
     p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
     const int64_t mi = rows_per_type_max(plan, call.M);
     p.mt_count = int32_t((mi + 127) / 128);
-    p.nt_count = int32_t((plan.b_out + 127) / 128);
+    const int tn = call.swiglu ? 64 : 128;   // output columns per workgroup
+    p.nt_count = int32_t((plan.b_out + tn - 1) / tn);
     if (p.mt_count < 1) return AA_OK;
     const int64_t n_tiles = int64_t(plan.q) * plan.q * p.mt_count * p.nt_count;
     if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
     const dim3 grid{uint32_t(n_tiles), 1, 1}, block{256, 1, 1};
     const bool fout = plan.out_dtype == AA_F32;
     if (call.swiglu) {
-      // two weight streams: two stage sets already fill the register file
-      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<true, 2, float>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((leaf_tile_kernel<true, 2, __bf16>), grid, block, 0, stream, p);
+      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<true, 3, float>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((leaf_tile_kernel<true, 3, __bf16>), grid, block, 0, stream, p);
     } else {
-      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<false, 4, float>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((leaf_tile_kernel<false, 4, __bf16>), grid, block, 0, stream, p);
+      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<false, 3, float>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((leaf_tile_kernel<false, 3, __bf16>), grid, block, 0, stream, p);
     }
     return after_launch(stream, call.swiglu ? "leaf_tile(swiglu)" : "leaf_tile");
   }
