@@ -90,4 +90,8 @@ WORKLOADS = {
                 ffn=True, notes="narrow expert FFN D=2048, F=768, q=16"),
     5: Workload(5, "square_n32768_b128", "Qq", 256, 32768, 32768, 32768, "square", "bf16", "block_rows",
                 notes="fixed-block square product, b=128, q=256"),
+    # a further row of the pages' projection table; widths from the model's
+    # public configuration (hidden 2048, intermediate 6144)
+    6: Workload(6, "qwen3_1p7b_q32", "Qq", 32, 2048, 2048, 6144, "project", "bf16", "pos_mod",
+                notes="Qwen3-1.7B FFN shape, M=2048, q=32 (blocks 64 x 192)"),
 }

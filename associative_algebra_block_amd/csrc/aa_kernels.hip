@@ -2538,16 +2538,25 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, v
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
+  // A decode of one or two tokens (generation: one new position per call)
+  // takes a group that size instead of leaving group slots empty.
+  auto go_tg = [&](auto tg_max, auto kf_c) {
+    constexpr int TGm = decltype(tg_max)::value;
+    if (n == 1) return go(I1{}, kf_c);
+    if (n == 2 && TGm >= 2) return go(I2{}, kf_c);
+    if (TGm >= 4) return go(I4{}, kf_c);
+    return go(std::integral_constant<int, TGm>{}, kf_c);
+  };
   bool ok;
   switch (kf) {
-    case 1: ok = go(I4{}, std::integral_constant<int, 1>{}); break;
-    case 2: ok = go(I4{}, std::integral_constant<int, 2>{}); break;
-    case 3: ok = go(I4{}, std::integral_constant<int, 3>{}); break;
-    case 4: ok = go(I4{}, std::integral_constant<int, 4>{}); break;
-    case 5: ok = go(I2{}, std::integral_constant<int, 5>{}); break;
-    case 6: ok = go(I2{}, std::integral_constant<int, 6>{}); break;
-    case 7: ok = go(I2{}, std::integral_constant<int, 7>{}); break;
-    case 8: ok = go(I2{}, std::integral_constant<int, 8>{}); break;
+    case 1: ok = go_tg(I4{}, std::integral_constant<int, 1>{}); break;
+    case 2: ok = go_tg(I4{}, std::integral_constant<int, 2>{}); break;
+    case 3: ok = go_tg(I4{}, std::integral_constant<int, 3>{}); break;
+    case 4: ok = go_tg(I4{}, std::integral_constant<int, 4>{}); break;
+    case 5: ok = go_tg(I2{}, std::integral_constant<int, 5>{}); break;
+    case 6: ok = go_tg(I2{}, std::integral_constant<int, 6>{}); break;
+    case 7: ok = go_tg(I2{}, std::integral_constant<int, 7>{}); break;
+    case 8: ok = go_tg(I2{}, std::integral_constant<int, 8>{}); break;
     case 9: ok = go(I1{}, std::integral_constant<int, 9>{}); break;
     case 10: ok = go(I1{}, std::integral_constant<int, 10>{}); break;
     case 11: ok = go(I1{}, std::integral_constant<int, 11>{}); break;

@@ -17,7 +17,8 @@ the projection kernel (algorithmic HBM bytes / its event-timed duration), the
 same for every call, a dense bf16 torch.matmul comparator timed in the same
 run, and the fp64 oracle timed on the host on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload qwen3_8b_q32|square|pilot_ffn|expert_ffn]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+                    [--workload qwen3_8b_q32|square|pilot_ffn|expert_ffn|qwen3_1p7b]
 """
 from __future__ import annotations
 
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
-                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn"])
+                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -81,6 +82,8 @@ def main():
 
     if args.workload == "qwen3_8b_q32":
         res = bench_qwen3(args, torch, inp, aa, dev)
+    elif args.workload == "qwen3_1p7b":
+        res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[6])
     elif args.workload == "square":
         res = bench_square(args, torch, inp, aa, dev)
     else:
@@ -258,6 +261,7 @@ def bench_qwen3(args, torch, inp, aa, dev):
 
     dec1 = decode_single_token(torch, aa, plan, sets, pos_dec, n_dec, D, F, q,
                                None if dense is None else sets[0])
+    alone = projection_alone(torch, aa, plan, [(st["X"], st["Wp"], st["Y"]) for st in sets], b_proj)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -273,10 +277,82 @@ def bench_qwen3(args, torch, inp, aa, dev):
                    "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
         "roofline": parts["project"]["roofline"],
         "roofline_kernel": "aa_project_fwd at the Qwen3-8B shape (leaf_persist_kernel)",
-        "parts": parts, "decode_single_token": dec1, "dense": dense, "cpu_baseline": cpu,
+        "parts": parts, "projection_alone": alone, "decode_single_token": dec1, "dense": dense,
+        "cpu_baseline": cpu,
         "wall_s_timed": round(wall1 - wall0, 4),
         "kernel_source": kernel_source_hash(),
     }
+
+
+def projection_alone(torch, aa, plan, sets, bytes_alg, reps=50):
+    """The projection launched back to back (no other kernels or events in
+    between): rotating the input sets (flushed cache: the sets together exceed
+    the 256 MB Infinity Cache) and repeating one set (hot cache, as the pages
+    also report)."""
+    out = {}
+    for name, order in (("flushed", list(range(len(sets)))), ("hot", [0])):
+        for r in range(5):
+            X, W, Y = sets[order[r % len(order)]]
+            aa.aa_project_fwd(plan, X, W, Y)
+        torch.cuda.synchronize()
+        a, b = _ev(torch), _ev(torch)
+        a.record()
+        for r in range(reps):
+            X, W, Y = sets[order[r % len(order)]]
+            aa.aa_project_fwd(plan, X, W, Y)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[name] = {"ms": round(ms, 5), "GBs": round(bytes_alg / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_8TBs": round(bytes_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def bench_projection(args, torch, inp, aa, dev, wl):
+    """A single row-typed projection shape (position typing), flushed cache
+    (rotating input sets of >= 1 GB in total) and hot cache, with a dense bf16
+    comparator of the same shape."""
+    M, D, F, q = wl.M, wl.d_in, wl.d_out, wl.q
+    plan = aa.aa_plan_create(wl.law, q, D, F, "pos_mod", 0, "bf16", "bf16")
+    per_set = 2 * (M * D + D * F + M * F)
+    n_sets = args.sets or max(2, math.ceil(1.0e9 / per_set))
+    sets = []
+    for s in range(n_sets):
+        X = inp.gaussian((M, D), inp.seed_for(inp.ROLE_X, wl.index) + 100 * s, 1.0, torch.bfloat16, dev)
+        W = inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, wl.index) + 100 * s, D ** -0.5, torch.bfloat16, dev)
+        sets.append((X, aa.pack(plan, W), torch.empty(M, F, dtype=torch.bfloat16, device=dev)))
+        del W
+    torch.cuda.synchronize()
+    for w in range(args.warmup):
+        X, Wp, Y = sets[w % n_sets]
+        aa.aa_project_fwd(plan, X, Wp, Y)
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for s in range(K):
+        X, Wp, Y = sets[s % n_sets]
+        aa.aa_project_fwd(plan, X, Wp, Y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    alone = projection_alone(torch, aa, plan, sets, per_set)
+    dense = None
+    if not args.no_dense:
+        Wd = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
+        X0 = sets[0][0]
+        t = dense_timer(torch, lambda: torch.matmul(X0, Wd))
+        dense = {"kind": "torch.matmul bf16 (hipBLASLt), hot cache", "ms": round(t, 5),
+                 "speedup_flushed": round(t / ms, 3), "speedup_hot": round(t / alone["hot"]["ms"], 3)}
+    return {"metric": f"dense-equiv TFLOP/s + % roofline, {wl.name} projection bf16",
+            "value": round(2.0 * M * D * F / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": wl.name, "M": M, "d_in": D, "d_out": F, "q": q, "law": wl.law,
+                       "type_map": "pos mod q", "input_sets": n_sets},
+            "roofline": roofline(per_set, ms), "projection_alone": alone, "dense": dense,
+            "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / (ms * 1e-3) / 1e12, 2),
+            "kernel_source": kernel_source_hash()}
 
 
 def decode_single_token(torch, aa, plan, sets, pos0, n_tok, D, F, q, dense_set=None, reps=20):

@@ -124,6 +124,7 @@ def test_integer_exact(law, q, M, d_in, d_out, kind, in_dt, out_dt):
     ("Qq", 8, 1000, 512, 768, "pos_mod"),        # several tiles and a ragged tail
     ("Qq", 4, 1, 256, 128, "pos_mod"),           # a single token
     ("Qq", 32, 2048, 4096, 12288, "pos_mod"),    # the Qwen3-8B-shaped projection, full size
+    ("Qq", 32, 2048, 2048, 6144, "pos_mod"),     # the Qwen3-1.7B-shaped projection (64 x 192 blocks)
     ("Q2xQ2", 4, 4100, 768, 1536, "pos_mod"),
     ("Qq", 64, 8192, 8192, 8192, "block_rows"),  # full product, 128 x 128 blocks
 ])
@@ -344,7 +345,8 @@ def test_row_locality():
 @pytest.mark.parametrize("law,q,d_in,d_out,n,dt", [
     ("Qq", 32, 4096, 12288, 32, "bf16"), ("Qq", 32, 4096, 12288, 1, "bf16"),
     ("Q2xQ2", 4, 768, 1536, 7, "bf16"), ("Qq", 16, 768, 2048, 20, "bf16"),
-    ("Qq", 32, 12288, 4096, 5, "bf16"), ("Qq", 2, 64, 64, 9, "f32"), ("Qq", 4, 320, 64, 6, "bf16")])
+    ("Qq", 32, 12288, 4096, 5, "bf16"), ("Qq", 2, 64, 64, 9, "f32"), ("Qq", 4, 320, 64, 6, "bf16"),
+    ("Qq", 8, 1024, 1536, 2, "bf16"), ("Q2xQ2", 4, 768, 1536, 1, "bf16"), ("Qq", 16, 6144, 2048, 2, "bf16")])
 def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n, dt):
     say("decode", law, q, d_in, d_out, n, dt)
     plan, X, W = _make(law, q, 64, d_in, d_out, dt, "f32", seed=81)
