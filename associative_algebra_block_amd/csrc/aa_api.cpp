@@ -120,6 +120,14 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
   const size_t xb = size_t(M * up->d_in) * elem_size(up->in_dtype);
   if (overlaps(H, hb, Y, yb) || overlaps(H, hb, X, xb) || overlaps(Y, yb, X, xb))
     return fail(AA_ERR_INVALID_ARG, "aa_swiglu_ffn_fwd: X, H and Y must not overlap");
+  // A few tokens (at most one per row type on average: generation decodes one
+  // new position per call) take the matrix-vector kernels, which read each
+  // token's 2q - 1 blocks once; the leaf GEMMs would pad them to full tiles.
+  if (M <= up->q && up->type_kind != AA_TYPES_BLOCK_ROWS && aa::decode_swiglu_ok(*up)) {
+    if ((st = aa::launch_decode(*up, X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, stream)) != AA_OK)
+      return st;
+    return aa::launch_decode(*down, H, Wd_packed, nullptr, Y, M, pos_offset, row_types, stream);
+  }
   aa::LeafCall gate_up{X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, true};
   if ((st = aa::launch_leaf_gemm(*up, gate_up, stream)) != AA_OK) return st;
   aa::LeafCall proj_down{H, Wd_packed, nullptr, Y, M, pos_offset, row_types, false};
@@ -146,7 +154,7 @@ aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, 
   const size_t xb = size_t(n * plan->d_in) * elem_size(plan->in_dtype);
   const size_t yb = size_t(n * plan->d_out) * elem_size(plan->out_dtype);
   if (overlaps(y, yb, x, xb)) return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: x and y overlap");
-  return aa::launch_decode(*plan, x, W_packed, y, n, pos_offset, row_types, stream);
+  return aa::launch_decode(*plan, x, W_packed, nullptr, y, n, pos_offset, row_types, stream);
 }
 
 }  // extern "C"

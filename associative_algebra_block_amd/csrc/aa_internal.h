@@ -54,8 +54,11 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
 aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool unpack,
                         hipStream_t stream);
 
-aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, void* y, int64_t n,
-                          int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
+// W1 non-null: SwiGLU gate/up (W gate, W1 up, y = silu(x W) * (x W1)); bf16
+// input and input blocks of at most 256 rows (decode_swiglu_ok).
+aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,
+                          int64_t n, int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
+bool decode_swiglu_ok(const aa_plan_s& plan);
 
 // Synchronise and check when AA_DEBUG=1; map launch errors to AA_ERR_HIP.
 aa_status_t after_launch(hipStream_t stream, const char* what);

@@ -1704,6 +1704,7 @@ __global__ __launch_bounds__(256, 2) void leaf_tile_kernel(LeafParams p) {
 struct DecodeParams {
   const void* x;
   const void* W;
+  const void* W1;   // SwiGLU: the up weight (W is the gate); else unused
   void* y;
   int64_t n;
   int64_t ldx;
@@ -1727,7 +1728,7 @@ struct DecodeParams {
 // 16 x 32 weight fragment by a 32 x 16 activation tile in which column j is
 // token j's segment: all TG tokens at once for the diagonal block, and only
 // token j's column (the others zero) for token j's own block.
-template <typename Tin, typename Tout, int TG, int KF>
+template <typename Tin, typename Tout, int TG, int KF, bool SWIGLU = false>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   static_assert(TG <= 16, "one MFMA column per token");
   constexpr int NSEG = 3;                 // off-diagonal segments per token, at most (Q2 x Q2)
@@ -1742,6 +1743,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int64_t tok0 = int64_t(blockIdx.y) * TG;
   const Tin* __restrict__ x = static_cast<const Tin*>(p.x);
   const Tin* __restrict__ W = static_cast<const Tin*>(p.W);
+  const Tin* __restrict__ Wu = static_cast<const Tin*>(p.W1);
   Tout* __restrict__ y = static_cast<Tout*>(p.y);
   const int64_t blk = int64_t(p.b_in) * p.b_out;
   const bool strip_ok = strip < p.nstrips;
@@ -1790,25 +1792,33 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   // In a half-width last slab (b_in an odd multiple of 16) the upper lane
   // groups have no weights; they re-read their strip's first run, and their
   // staged activations are zero.
+  // With SWIGLU the same strips of the up weight are read too (u) and the
+  // output is silu(gate) * up.
   constexpr int NW = 1 + TG;   // Q_q: one own block per token; Q2 x Q2 tokens loop below
-  Run<Tin> w[NW][KF];
+  Run<Tin> w[NW][KF], u[SWIGLU ? NW : 1][KF];
   int kofs[KF];
 #pragma unroll
   for (int kf = 0; kf < KF; ++kf) kofs[kf] = (kf * 32 + g * 8 < p.b_in) ? kf * 512 : 0;
-  const Tin* wdiag = W + (int64_t(k) * p.q + k) * blk + sofs;
+  const int64_t odiag = (int64_t(k) * p.q + k) * blk + sofs;
 #pragma unroll
-  for (int kf = 0; kf < KF; ++kf) w[0][kf] = Run<Tin>::load_cached(wdiag + kofs[kf]);
+  for (int kf = 0; kf < KF; ++kf) {
+    w[0][kf] = Run<Tin>::load_cached(W + odiag + kofs[kf]);
+    if (SWIGLU) u[0][kf] = Run<Tin>::load_cached(Wu + odiag + kofs[kf]);
+  }
 #pragma unroll
   for (int j = 0; j < TG; ++j) {
     const int ty = tok_type[j];
     const int sg = ty < 0 ? -1 : other_seg(ty, 0);
-    const Tin* wb = sg >= 0 ? W + (int64_t(sg) * p.q + k) * blk + sofs : wdiag;
+    const int64_t ob = sg >= 0 ? (int64_t(sg) * p.q + k) * blk + sofs : odiag;
 #pragma unroll
-    for (int kf = 0; kf < KF; ++kf) w[1 + j][kf] = Run<Tin>::load(wb + kofs[kf]);
+    for (int kf = 0; kf < KF; ++kf) {
+      w[1 + j][kf] = Run<Tin>::load(W + ob + kofs[kf]);
+      if (SWIGLU) u[SWIGLU ? 1 + j : 0][kf] = Run<Tin>::load(Wu + ob + kofs[kf]);
+    }
   }
   __syncthreads();   // staged activations visible
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const bool col_live = l16 < TG;
   // Diagonal block: column j = token j's segment k.
 #pragma unroll
@@ -1816,6 +1826,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     Run<Tin> b = Run<Tin>::zero();
     if (col_live) b = *reinterpret_cast<const Run<Tin>*>(&xs[col_live ? l16 : 0][0][kf * 32 + g * 8]);
     acc = mma(w[0][kf], b, acc);
+    if (SWIGLU) acc1 = mma(u[0][kf], b, acc1);
   }
   // Own blocks: token j's column only.
 #pragma unroll
@@ -1825,6 +1836,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       Run<Tin> b = Run<Tin>::zero();
       if (l16 == j) b = *reinterpret_cast<const Run<Tin>*>(&xs[j][1][kf * 32 + g * 8]);
       acc = mma(w[1 + j][kf], b, acc);
+      if (SWIGLU) acc1 = mma(u[SWIGLU ? 1 + j : 0][kf], b, acc1);
     }
   }
   // Q2 x Q2 tokens may have a second and third segment besides k.
@@ -1834,15 +1846,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       for (int s = 1; s < NSEG; ++s) {
         const int sg = ty < 0 ? -1 : other_seg(ty, s);
         if (sg < 0) continue;
-        const Tin* wb = W + (int64_t(sg) * p.q + k) * blk + sofs;
+        const int64_t ob = (int64_t(sg) * p.q + k) * blk + sofs;
         for (int kf = 0; kf < KF; ++kf) {
-          Run<Tin> a = Run<Tin>::load(wb + kofs[kf]);
+          Run<Tin> a = Run<Tin>::load(W + ob + kofs[kf]);
+          Run<Tin> au = a;
+          if (SWIGLU) au = Run<Tin>::load(Wu + ob + kofs[kf]);
           Run<Tin> b = Run<Tin>::zero();
           if (l16 == j) b = *reinterpret_cast<const Run<Tin>*>(&xs[j][1 + s][kf * 32 + g * 8]);
           acc = mma(a, b, acc);
+          if (SWIGLU) acc1 = mma(au, b, acc1);
         }
       }
     }
+  }
+  if (SWIGLU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = silu_mul(acc[e], acc1[e]);
   }
   // Lane holds y[token l16][strip cols g*4 .. g*4+3].
   if (col_live && strip_ok) {
@@ -2503,11 +2522,14 @@ aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool 
   return after_launch(stream, unpack ? "unpack" : "pack");
 }
 
-aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, void* y, int64_t n,
-                          int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+bool decode_swiglu_ok(const aa_plan_s& plan) { return plan.in_dtype == AA_BF16 && plan.b_in <= 256; }
+
+aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,
+                          int64_t n, int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
   DecodeParams p{};
   p.x = x;
   p.W = W;
+  p.W1 = W1;
   p.y = y;
   p.n = n;
   p.ldx = plan.d_in;
@@ -2529,6 +2551,16 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, v
     const int64_t groups = (n + TGc - 1) / TGc;
     const dim3 block{256, 1, 1}, grid{uint32_t(plan.q * p.nchunks), uint32_t(groups), 1};
     if (groups > 65535) return false;
+    if (W1 != nullptr) {   // SwiGLU gate/up (bf16 input; the caller checked KF <= 8)
+      if constexpr (KFc <= 8) {
+        if (fin) return false;
+        if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float, TGc, KFc, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((decode_kernel<__bf16, __bf16, TGc, KFc, true>), grid, block, 0, stream, p);
+        return true;
+      } else {
+        return false;
+      }
+    }
     if (fin && fout) hipLaunchKernelGGL((decode_kernel<float, float, TGc, KFc>), grid, block, 0, stream, p);
     else if (fin) hipLaunchKernelGGL((decode_kernel<float, __bf16, TGc, KFc>), grid, block, 0, stream, p);
     else if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float, TGc, KFc>), grid, block, 0, stream, p);
@@ -2569,7 +2601,7 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, v
       return fail(AA_ERR_UNSUPPORTED, "aa_decode_gemv: input block width d_in/q above 512");
   }
   if (!ok) return fail(AA_ERR_UNSUPPORTED, "aa_decode_gemv: too many tokens for one launch");
-  return after_launch(stream, "decode_gemv");
+  return after_launch(stream, W1 ? "decode_gemv(swiglu)" : "decode_gemv");
 }
 
 }  // namespace aa

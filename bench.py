@@ -261,6 +261,7 @@ def bench_qwen3(args, torch, inp, aa, dev):
 
     dec1 = decode_single_token(torch, aa, plan, sets, pos_dec, n_dec, D, F, q,
                                None if dense is None else sets[0])
+    ffn1 = ffn_single_token(torch, aa, plan, down, sets, pos_dec, n_dec, D, F, q, dense is not None)
     alone = projection_alone(torch, aa, plan, [(st["X"], st["Wp"], st["Y"]) for st in sets], b_proj)
 
     cpu = None
@@ -277,7 +278,8 @@ def bench_qwen3(args, torch, inp, aa, dev):
                    "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
         "roofline": parts["project"]["roofline"],
         "roofline_kernel": "aa_project_fwd at the Qwen3-8B shape (leaf_persist_kernel)",
-        "parts": parts, "projection_alone": alone, "decode_single_token": dec1, "dense": dense,
+        "parts": parts, "projection_alone": alone, "decode_single_token": dec1, "ffn_single_token": ffn1,
+        "dense": dense,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall1 - wall0, 4),
         "kernel_source": kernel_source_hash(),
@@ -404,6 +406,69 @@ def decode_single_token(torch, aa, plan, sets, pos0, n_tok, D, F, q, dense_set=N
         out["dense_us_per_token"] = round(t * 1e3, 3)
         out["speedup_graph_vs_dense"] = round(t * 1e3 / graph_us, 3)
         del Wdn
+    return out
+
+
+def ffn_single_token(torch, aa, up, down, sets, pos0, n_tok, D, F, q, dense=True, reps=20):
+    """Generation-time SwiGLU FFN: one new token per call (M = 1), n_tok calls
+    at positions pos0, pos0 + 1, ..., eager and replayed from one HIP graph
+    per input set.  A token reads its 2q - 1 blocks of each of the three
+    weights: 2(3 (2q-1) b_in b_out + 2 D + 2 F) bytes.  The dense comparator
+    is the same FFN with torch.matmul (three GEMVs), also graph-replayed."""
+    def calls(si):
+        st = sets[si]
+        for j in range(n_tok):
+            aa.aa_swiglu_ffn_fwd(up, down, st["x"][j:j + 1], st["Wgp"], st["Wup"], st["Wdp"], st["H"][j:j + 1],
+                                 st["Y2"][j:j + 1], None, pos0 + j)
+
+    def timed(fn):
+        a, b = _ev(torch), _ev(torch)
+        a.record()
+        for r in range(reps):
+            fn(r)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * n_tok)
+
+    for si in range(len(sets)):
+        calls(si)
+    torch.cuda.synchronize()
+    eager_us = timed(lambda r: calls(r % len(sets)))
+    graphs = []
+    for si in range(len(sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls(si)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = timed(lambda r: graphs[r % len(graphs)].replay())
+    per_tok = 2 * (3 * (2 * q - 1) * (D // q) * (F // q) + 2 * D + 2 * F)
+    out = {"tokens": n_tok, "eager_us_per_token": round(eager_us, 3), "graph_us_per_token": round(graph_us, 3),
+           "bytes_per_token": per_tok, "graph_GBs": round(per_tok / graph_us / 1e3, 1)}
+    if dense:
+        dev = sets[0]["x"].device
+        # two weight sets (about 600 MB) so that replays alternate and the cache is cold
+        ws = [[torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(0.0, shape[0] ** -0.5)
+               for shape in ((D, F), (D, F), (F, D))] for _ in range(2)]
+        x1 = sets[0]["x"][:1].clone()
+        dgs = []
+        for Wg, Wu, Wd in ws:
+            for _ in range(2):
+                torch.matmul(torch.nn.functional.silu(torch.matmul(x1, Wg)) * torch.matmul(x1, Wu), Wd)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                torch.matmul(torch.nn.functional.silu(torch.matmul(x1, Wg)) * torch.matmul(x1, Wu), Wd)
+            dgs.append(g)
+        for g in dgs:
+            g.replay()
+        torch.cuda.synchronize()
+        t = timed(lambda r: dgs[r % 2].replay()) * n_tok
+        out["dense_graph_us_per_token"] = round(t, 3)
+        out["speedup_graph_vs_dense"] = round(t / graph_us, 3)
+        del ws, dgs
     return out
 
 

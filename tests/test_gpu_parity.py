@@ -402,6 +402,76 @@ def test_swiglu_parity(name, law, q, M, D, F, period, out_dt):
     assert_parity(host(Y), Yref, out_dt == "bf16", f"{name} Y")
 
 
+@pytest.mark.parametrize("name,law,q,M,D,F,period,pos_offset,out_dt", [
+    ("Qwen3-8B one token", "Qq", 32, 1, 4096, 12288, 0, 4101, "bf16"),
+    ("Qwen3-8B two tokens across the wrap", "Qq", 32, 2, 4096, 12288, 0, 31, "f32"),
+    ("Qwen3-8B one token per type", "Qq", 32, 32, 4096, 12288, 0, 7, "bf16"),
+    ("pilot Q2xQ2 one token", "Q2xQ2", 4, 1, 768, 1536, 1536, 1535, "f32"),
+    ("pilot Q2xQ2 three tokens", "Q2xQ2", 4, 3, 768, 1536, 1536, 2, "bf16"),
+    ("Qwen3-30B-A3B expert, five tokens", "Qq", 16, 5, 2048, 768, 0, 13, "bf16"),
+])
+def test_swiglu_few_tokens_matches_oracle(name, law, q, M, D, F, period, pos_offset, out_dt):
+    """At most q tokens: the FFN runs as a fused gate/up matrix-vector kernel
+    (silu(x Wg) * (x Wu) per token) followed by the down matrix-vector kernel."""
+    say("swiglu decode", name, law, q, M, D, F, pos_offset, out_dt)
+    H, Y, Href, Yref = _swiglu_case(law, q, M, D, F, out_dt, 2000 + 7 * M + q, pos_offset, period)
+    assert_parity(host(H), Href, True, f"{name} H")
+    assert_parity(host(Y), Yref, out_dt == "bf16", f"{name} Y")
+
+
+def test_swiglu_few_tokens_explicit_types():
+    """Explicit per-token types, some outside [0, q): those rows of H and Y
+    are left as they were; the others match the oracle."""
+    q, M, D, F = 8, 7, 1024, 1536
+    say("swiglu decode explicit", q, M, D, F)
+    up = aa.aa_plan_create("Qq", q, D, F, "explicit", 0, "bf16", "bf16")
+    down = aa.aa_plan_create("Qq", q, F, D, "explicit", 0, "bf16", "f32")
+    X = inp.gaussian((M, D), 91, 1.0, torch.bfloat16, DEV)
+    Wg = inp.gaussian((D, F), 92, D ** -0.5, torch.bfloat16, DEV)
+    Wu = inp.gaussian((D, F), 93, D ** -0.5, torch.bfloat16, DEV)
+    Wd = inp.gaussian((F, D), 94, F ** -0.5, torch.bfloat16, DEV)
+    types = torch.tensor([5, -1, 0, 7, q, 3, 5], dtype=torch.int32, device=DEV)
+    H = torch.full((M, F), 3.0, dtype=torch.bfloat16, device=DEV)
+    Y = torch.full((M, D), 3.0, dtype=torch.float32, device=DEV)
+    aa.aa_swiglu_ffn_fwd(up, down, X, aa.pack(up, Wg), aa.pack(up, Wu), aa.pack(down, Wd), H, Y, None, 0, types)
+    torch.cuda.synchronize()
+    t = types.cpu().numpy()
+    live = (t >= 0) & (t < q)
+    Href, Yref = oracle.swiglu_ffn(host(X)[live], host(Wg), host(Wu), host(Wd), "Qq", q, t[live])
+    assert_parity(host(H)[live], Href, True, "explicit H")
+    assert_parity(host(Y)[live], Yref, False, "explicit Y")
+    assert np.all(host(H)[~live] == 3.0) and np.all(host(Y)[~live] == 3.0)
+
+
+def test_swiglu_single_token_in_a_graph_replay():
+    """One-token FFN calls captured in a HIP graph replay bit for bit like the
+    eager calls, with eager work between replays."""
+    q, D, F, n = 32, 4096, 12288, 4
+    say("swiglu decode graph", q, D, F, n)
+    up = aa.aa_plan_create("Qq", q, D, F, "pos_mod", 0, "bf16", "bf16")
+    down = aa.aa_plan_create("Qq", q, F, D, "pos_mod", 0, "bf16", "bf16")
+    X = inp.gaussian((n, D), 95, 1.0, torch.bfloat16, DEV)
+    Wg, Wu = (aa.pack(up, inp.gaussian((D, F), s, D ** -0.5, torch.bfloat16, DEV)) for s in (96, 97))
+    Wd = aa.pack(down, inp.gaussian((F, D), 98, F ** -0.5, torch.bfloat16, DEV))
+    He, Ye = torch.empty(n, F, dtype=torch.bfloat16, device=DEV), torch.empty(n, D, dtype=torch.bfloat16, device=DEV)
+    Hg, Yg = torch.empty_like(He), torch.empty_like(Ye)
+    pos0 = 77
+    for j in range(n):
+        aa.aa_swiglu_ffn_fwd(up, down, X[j:j + 1], Wg, Wu, Wd, He[j:j + 1], Ye[j:j + 1], None, pos0 + j)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(n):
+            aa.aa_swiglu_ffn_fwd(up, down, X[j:j + 1], Wg, Wu, Wd, Hg[j:j + 1], Yg[j:j + 1], None, pos0 + j)
+    for r in range(3):
+        Yg.fill_(float("nan"))
+        Hg.fill_(float("nan"))
+        g.replay()
+        aa.aa_swiglu_ffn_fwd(up, down, X, Wg, Wu, Wd, He.clone(), Ye.clone(), None, 5)   # eager work
+        torch.cuda.synchronize()
+        assert torch.equal(Hg, He) and torch.equal(Yg, Ye), f"replay {r}"
+
+
 # ------------------------------------------- full square product (sampled) ---
 
 def test_square_product_full_size_sampled():
