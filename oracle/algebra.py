@@ -230,6 +230,93 @@ def decode(x, W, law: str, q: int, positions) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Gradients of the row-typed projection
+# --------------------------------------------------------------------------
+#
+# The pages report a backward pass for the projection (authors' measurements
+# of forward plus gradient on the Qwen3-30B-A3B expert shape, [review] kernel
+# paragraph) without writing it out.  Reading: the backward is the exact
+# gradient of the bilinear map Y = X * W defined by `project`.  With
+# T the interaction table and tau(t) the type of row t,
+#     Y[t, k] = sum over j with (tau(t), j, k) in T of X[t, j] W_jk,
+# so for an upstream gradient dY
+#     dX[t, j] = sum over k with (tau(t), j, k) in T of dY[t, k] W_jk^T,
+#     dW_jk    = sum over rows t with (tau(t), j, k) in T of X[t, j]^T dY[t, k].
+# Both are written out below as block loops over the same table.
+
+def project_grad_input(dY, W, law: str, q: int, types) -> np.ndarray:
+    """dX of the row-typed projection for upstream gradient dY (M x d_out).
+
+    Row t of type i receives, in input group j, dY[t, k] W_jk^T summed over
+    the output groups k whose table entry (i, j, k) is kept.  Under Q_q that
+    is every k for j == i and only k == j otherwise.
+    """
+    _check_law(law, q)
+    dY = _f64(dY)
+    W = _f64(W)
+    types = np.asarray(types, dtype=np.int64)
+    M, d_out = dY.shape
+    d_in = W.shape[0]
+    if W.shape[1] != d_out:
+        raise ValueError("dY and W disagree on d_out")
+    if d_in % q or d_out % q:
+        raise ValueError("q must divide d_in and d_out")
+    if types.shape != (M,):
+        raise ValueError("one type per row")
+    if M and (types.min() < 0 or types.max() >= q):
+        raise ValueError("row type out of range")
+    bi, bo = d_in // q, d_out // q
+    dX = np.zeros((M, d_in), dtype=np.float64)
+    for i in range(q):
+        rows = np.nonzero(types == i)[0]
+        if rows.size == 0:
+            continue
+        dYi = dY[rows]
+        for j in range(q):
+            acc = np.zeros((rows.size, bi), dtype=np.float64)
+            for k in range(q):
+                if in_table(law, q, i, j, k):
+                    acc += dYi[:, k * bo:(k + 1) * bo] @ W[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo].T
+            dX[rows, j * bi:(j + 1) * bi] = acc
+    return dX
+
+
+def project_grad_weight(X, dY, law: str, q: int, types) -> np.ndarray:
+    """dW (d_in x d_out, row-major) of the row-typed projection.
+
+    Block W_jk collects X[t, j]^T dY[t, k] over the rows t whose type i keeps
+    the entry (i, j, k).  Under Q_q an off-diagonal block W_jk (j != k) is
+    reached only by rows of type j; a diagonal block W_kk by rows of every
+    type.  Blocks no row reaches get zero.
+    """
+    _check_law(law, q)
+    X = _f64(X)
+    dY = _f64(dY)
+    types = np.asarray(types, dtype=np.int64)
+    M, d_in = X.shape
+    if dY.shape[0] != M:
+        raise ValueError("X and dY disagree on M")
+    d_out = dY.shape[1]
+    if d_in % q or d_out % q:
+        raise ValueError("q must divide d_in and d_out")
+    if types.shape != (M,):
+        raise ValueError("one type per row")
+    if M and (types.min() < 0 or types.max() >= q):
+        raise ValueError("row type out of range")
+    bi, bo = d_in // q, d_out // q
+    dW = np.zeros((d_in, d_out), dtype=np.float64)
+    for i in range(q):
+        rows = np.nonzero(types == i)[0]
+        if rows.size == 0:
+            continue
+        Xi, dYi = X[rows], dY[rows]
+        for k in range(q):
+            for j in leaf_groups(law, q, i, k):
+                dW[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo] += Xi[:, j * bi:(j + 1) * bi].T @ dYi[:, k * bo:(k + 1) * bo]
+    return dW
+
+
+# --------------------------------------------------------------------------
 # Arithmetic counts
 # --------------------------------------------------------------------------
 

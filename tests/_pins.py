@@ -292,6 +292,104 @@ def pin_swiglu(orc):
     _close(Y, (Gd * expit(Gd) * (X @ Wu)) @ Wd)
 
 
+# ------------------------------------------------------------- gradients ---
+
+def pin_grad_golden_q2(orc):
+    g = _load("q2_grad_hand_example.json")
+    _close(orc.project(g["X"], g["W"], g["law"], g["q"], g["types"]), g["Y"], 0)
+    _close(orc.project_grad_input(g["dY"], g["W"], g["law"], g["q"], g["types"]), g["dX"], 0)
+    _close(orc.project_grad_weight(g["X"], g["dY"], g["law"], g["q"], g["types"]), g["dW"], 0)
+    _close(orc.project_grad_weight(g["X"][:1], g["dY"][:1], g["law"], g["q"], g["types"][:1]), g["dW_type0"], 0)
+
+
+def _torch_grads(fwd, X, W, dY):
+    """dX, dW of sum(fwd(X, W) * dY) by torch autograd on the CPU in float64."""
+    import torch
+    Xt = torch.tensor(X, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    (fwd(torch, Xt, Wt) * torch.tensor(dY, dtype=torch.float64)).sum().backward()
+    return Xt.grad.numpy(), Wt.grad.numpy()
+
+
+def pin_grad_q1_is_dense(orc):
+    # q = 1: the gradients of an ordinary matrix product
+    rng = _rng(21)
+    X, W, dY = rng.standard_normal((6, 5)), rng.standard_normal((5, 3)), rng.standard_normal((6, 3))
+    gX, gW = _torch_grads(lambda torch, x, w: x @ w, X, W, dY)
+    z = np.zeros(6, int)
+    _close(orc.project_grad_input(dY, W, "Qq", 1, z), gX)
+    _close(orc.project_grad_weight(X, dY, "Qq", 1, z), gW)
+    _close(gX, dY @ W.T)
+    _close(gW, X.T @ dY)
+
+
+def _group_mask(q, width, keep):
+    """0/1 vector over q groups of `width` features: 1 where keep(group)."""
+    return np.repeat(np.array([1.0 if keep(g) else 0.0 for g in range(q)]), width)
+
+
+def pin_grad_closed_form_qq(orc):
+    # Autograd through the closed form y_t = x_t W - off_tau(x_t) off(W)
+    # (library products only), rectangular blocks, every type present.
+    rng = _rng(22)
+    for q, bi, bo, M in [(2, 3, 2, 7), (3, 2, 3, 9), (5, 1, 2, 13)]:
+        X = rng.standard_normal((M, q * bi))
+        W = rng.standard_normal((q * bi, q * bo))
+        dY = rng.standard_normal((M, q * bo))
+        types = np.concatenate([np.arange(q), rng.integers(0, q, M - q)])
+        keep_off = np.stack([_group_mask(q, bi, lambda g, t=t: g != t) for t in types])
+        mask_off = _off_qq(np.ones_like(W), q)
+
+        def fwd(torch, x, w):
+            return x @ w - (x * torch.tensor(keep_off)) @ (w * torch.tensor(mask_off))
+
+        gX, gW = _torch_grads(fwd, X, W, dY)
+        _close(orc.project_grad_input(dY, W, "Qq", q, types), gX)
+        _close(orc.project_grad_weight(X, dY, "Qq", q, types), gW)
+
+
+def pin_grad_closed_form_q2xq2(orc):
+    # Autograd through the row-typed inclusion-exclusion form of the tensor
+    # square: y_t = x_t W - Pa_t(x_t) Pa(W) - Pb_t(x_t) Pb(W) + Pab_t(x_t) Pab(W),
+    # where Pa(W) keeps blocks (g, g'') whose first factors differ and Pa_t
+    # keeps the groups of x_t whose first factor differs from the type's.
+    rng = _rng(23)
+    for bi, bo, M in [(1, 1, 6), (2, 3, 9), (3, 1, 8)]:
+        X = rng.standard_normal((M, 4 * bi))
+        W = rng.standard_normal((4 * bi, 4 * bo))
+        dY = rng.standard_normal((M, 4 * bo))
+        types = np.concatenate([np.arange(4), rng.integers(0, 4, M - 4)])
+        ones = np.ones_like(W)
+        mPa = _proj_q2xq2(ones, lambda a, b, a1, b1: a != a1)
+        mPb = _proj_q2xq2(ones, lambda a, b, a1, b1: b != b1)
+        mPab = _proj_q2xq2(ones, lambda a, b, a1, b1: a != a1 and b != b1)
+        ka = np.stack([_group_mask(4, bi, lambda g, t=t: g // 2 != t // 2) for t in types])
+        kb = np.stack([_group_mask(4, bi, lambda g, t=t: g % 2 != t % 2) for t in types])
+        kab = ka * kb
+
+        def fwd(torch, x, w):
+            T = lambda a: torch.tensor(a, dtype=torch.float64)
+            return (x @ w - (x * T(ka)) @ (w * T(mPa)) - (x * T(kb)) @ (w * T(mPb))
+                    + (x * T(kab)) @ (w * T(mPab)))
+
+        gX, gW = _torch_grads(fwd, X, W, dY)
+        _close(orc.project_grad_input(dY, W, "Q2xQ2", 4, types), gX)
+        _close(orc.project_grad_weight(X, dY, "Q2xQ2", 4, types), gW)
+
+
+def pin_grad_adjoint(orc):
+    # Y is linear in X and in W, so <X * W, dY> = <X, dX> = <W, dW>.
+    rng = _rng(24)
+    for law, q, bi, bo, M in [("Qq", 4, 3, 2, 17), ("Qq", 7, 1, 3, 30), ("Q2xQ2", 4, 2, 5, 19)]:
+        X = rng.standard_normal((M, q * bi))
+        W = rng.standard_normal((q * bi, q * bo))
+        dY = rng.standard_normal((M, q * bo))
+        types = rng.integers(0, q, M)
+        v = float(np.sum(orc.project(X, W, law, q, types) * dY))
+        _close(np.sum(X * orc.project_grad_input(dY, W, law, q, types)), v)
+        _close(np.sum(W * orc.project_grad_weight(X, dY, law, q, types)), v)
+
+
 def pin_executed_flops(orc):
     for q in (2, 4, 32):
         M, d_in, d_out = 4 * q, 2 * q, 3 * q

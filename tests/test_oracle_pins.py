@@ -51,6 +51,14 @@ MUTANTS = [
     ("decode_type_from_row_index", "return project(x, W, law, q, positions % q)",
      "return project(x, W, law, q, np.arange(len(positions)) % q)"),
     ("flops_missing_factor_two", "sum(2 * int(m) * bi * bo", "sum(int(m) * bi * bo"),
+    ("grad_input_untransposed_table", "if in_table(law, q, i, j, k):", "if in_table(law, q, i, k, j):"),
+    ("grad_input_wrong_dy_group", "acc += dYi[:, k * bo:(k + 1) * bo] @ W", "acc += dYi[:, j * bo:(j + 1) * bo] @ W"),
+    ("grad_input_transposed_block", "@ W[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo].T",
+     "@ W[k * bi:(k + 1) * bi, j * bo:(j + 1) * bo].T"),
+    ("grad_input_only_own_group", "if in_table(law, q, i, j, k):", "if j == i:"),
+    ("grad_weight_wrong_x_group", "+= Xi[:, j * bi:(j + 1) * bi].T @ dYi", "+= Xi[:, k * bi:(k + 1) * bi].T @ dYi"),
+    ("grad_weight_overwrites", "dW[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo] += Xi", "dW[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo] = Xi"),
+    ("grad_weight_dense", "for j in leaf_groups(law, q, i, k):\n                dW", "for j in range(q):\n                dW"),
 ]
 
 
