@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libaa.so")
 
-SOURCES = ["aa_plan.cpp", "aa_api.cpp", "aa_kernels.hip"]
+SOURCES = ["aa_plan.cpp", "aa_api.cpp", "aa_kernels.hip", "aa_backward.hip"]
 ARCH = "gfx950"
 
 # Device-code flags.  Packed fp32 arithmetic is switched off for every HIP

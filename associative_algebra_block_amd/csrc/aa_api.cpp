@@ -44,6 +44,16 @@ aa_status_t check_rows(const aa_plan_s& plan, int64_t M, int64_t pos_offset, con
   return AA_OK;
 }
 
+aa_status_t check_bwd(const aa_plan_s& plan, int64_t M, int64_t pos_offset, const int32_t* row_types,
+                      const char* fn) {
+  aa_status_t st;
+  if ((st = check_rows(plan, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if (plan.type_kind == AA_TYPES_EXPLICIT)
+    return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": explicit type lists are not supported by the gradients");
+  if (plan.in_dtype != AA_BF16) return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": gradients need bf16 operands");
+  return AA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +142,64 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
   if ((st = aa::launch_leaf_gemm(*up, gate_up, stream)) != AA_OK) return st;
   aa::LeafCall proj_down{H, Wd_packed, nullptr, Y, M, pos_offset, row_types, false};
   return aa::launch_leaf_gemm(*down, proj_down, stream);
+}
+
+aa_status_t aa_project_bwd_data_workspace(aa_plan_t plan, int64_t M, size_t* bytes) {
+  aa::clear_error();
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data_workspace: plan is NULL");
+  if (!bytes) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data_workspace: bytes is NULL");
+  if (M < 0) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data_workspace: M is negative");
+  *bytes = aa::bwd_data_workspace_bytes(*plan, M);
+  return AA_OK;
+}
+
+aa_status_t aa_project_bwd_data(aa_plan_t plan, const void* dY, const void* W_packed, void* dX, int64_t M,
+                                int64_t pos_offset, const int32_t* row_types, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  aa::clear_error();
+  static const char* fn = "aa_project_bwd_data";
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data: plan is NULL");
+  aa_status_t st;
+  if ((st = check_bwd(*plan, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if (plan->b_in > 512) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_data: input blocks wider than 512 features");
+  if (M == 0) return AA_OK;
+  if ((st = check_ptr(dY, "dY", fn)) != AA_OK) return st;
+  if ((st = check_ptr(W_packed, "W_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(dX, "dX", fn)) != AA_OK) return st;
+  const size_t need = aa::bwd_data_workspace_bytes(*plan, M);
+  if (workspace_bytes < need)
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data: workspace smaller than aa_project_bwd_data_workspace reports");
+  if (need > 0 && (st = check_ptr(workspace, "workspace", fn)) != AA_OK) return st;
+  const size_t yb = size_t(M * plan->d_out) * elem_size(plan->in_dtype);
+  const size_t wb = size_t(plan->d_in * plan->d_out) * elem_size(plan->in_dtype);
+  const size_t xb = size_t(M * plan->d_in) * elem_size(plan->out_dtype);
+  if (overlaps(dX, xb, dY, yb) || overlaps(dX, xb, W_packed, wb))
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data: dX overlaps dY or W_packed");
+  if (need > 0 && (overlaps(workspace, need, dX, xb) || overlaps(workspace, need, dY, yb) ||
+                   overlaps(workspace, need, W_packed, wb)))
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data: workspace overlaps an operand");
+  return aa::launch_bwd_data(*plan, dY, W_packed, dX, M, pos_offset, need > 0 ? workspace : nullptr, stream);
+}
+
+aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY, void* dW_packed, int64_t M,
+                                  int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  aa::clear_error();
+  static const char* fn = "aa_project_bwd_weight";
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: plan is NULL");
+  aa_status_t st;
+  if ((st = check_bwd(*plan, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if (plan->b_in > 384)
+    return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_weight: input blocks wider than 384 features");
+  if (M == 0) return AA_OK;
+  if ((st = check_ptr(X, "X", fn)) != AA_OK) return st;
+  if ((st = check_ptr(dY, "dY", fn)) != AA_OK) return st;
+  if ((st = check_ptr(dW_packed, "dW_packed", fn)) != AA_OK) return st;
+  const size_t xb = size_t(M * plan->d_in) * elem_size(plan->in_dtype);
+  const size_t yb = size_t(M * plan->d_out) * elem_size(plan->in_dtype);
+  const size_t wb = size_t(plan->d_in * plan->d_out) * elem_size(plan->out_dtype);
+  if (overlaps(dW_packed, wb, X, xb) || overlaps(dW_packed, wb, dY, yb))
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: dW_packed overlaps X or dY");
+  return aa::launch_bwd_weight(*plan, X, dY, dW_packed, M, pos_offset, stream);
 }
 
 aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, void* y, int64_t n,

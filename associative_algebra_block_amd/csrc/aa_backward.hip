@@ -1,0 +1,701 @@
+// Gradients of the row-typed projection (HIP, gfx950).
+//
+// The authors report a backward pass for the projection beside the forward
+// one (agihunt.info review of "Change the Product, Keep the Parameters:
+// Associative Algebra Layers for Transformers", paragraph on the kernel
+// measurements: forward plus gradient on the Qwen3-30B-A3B expert shape).  It
+// is the exact gradient of the bilinear map.  With T the interaction table
+// (multiplication-table and pilot-law paragraphs) and tau(t) the type of row t
+// (row-typing paragraph):
+//   forward   Y[t, k]  = sum_j  X[t, j] W_jk        over (tau(t), j, k) in T
+//   data      dX[t, j] = sum_k  dY[t, k] W_jk^T     over (tau(t), j, k) in T
+//   weight    dW_jk    = sum_t  X[t, j]^T dY[t, k]  over (tau(t), j, k) in T
+//
+// Both gradients contract over an index the packed layout does not keep
+// contiguous for the MFMA operands (the data gradient over the weight's
+// columns, the weight gradient over tokens), so the operand that needs it is
+// staged in LDS and read back with ds_read_b64_tr_b16, which transposes 16-bit
+// elements across each group of 16 lanes: lane 4a + b receives element b of
+// the 8-byte chunks addressed by lanes a, a + 4, a + 8 and a + 12 of its group.
+// With a matrix stored k-major in LDS (its m index contiguous), lane r of group
+// g addressing (k = 8g + r/4, m = m0 + 4 (r mod 4)) leaves lane (g, m0 + j)
+// holding k = 8g .. 8g + 3 of row m0 + j; a second read at k + 4 completes the
+// 8-element MFMA operand run.
+//
+// Data gradient.  Per row type i and input group j the sum runs over the
+// output groups K(i, j) = {k : (i, j, k) in T}: under Q_q every k when j = i,
+// only k = j otherwise (2q - 1 block products per type, as in the forward);
+// under Q2 x Q2 one, two or four.  A work item is (type i, token tile, j, part
+// of K(i, j)); long lists (Q_q's own group) are cut into parts of R blocks
+// whose fp32 partial sums go to a workspace and are added by a second kernel.
+// Per item the kernel computes dX^T = W_jk dY^T: the A operand (16 input
+// features x 32 output features of W_jk) is a two-strip piece of the packed
+// block copied to LDS as it is (the packed octets of 8 rows already hold the
+// m index contiguous) and read transposed; the B operand is 16 bytes of a dY
+// row, loaded straight from HBM.
+//
+// Weight gradient.  One workgroup owns a column chunk of one output group k
+// and walks every row type i: each 32-token chunk of type i adds
+// X[rows, j]^T dY[rows, k] to the accumulator of block (j, k) for every j with
+// (i, j, k) in T.  Under Q_q those are j = i (block (i, k), complete after
+// type i) and j = k (the diagonal block, complete after the last type); under
+// Q2 x Q2 the four blocks of column k stay in registers to the end.  Both MFMA
+// operands (X^T and dY, contracted over tokens) come from LDS tiles read
+// transposed; the result lands in the packed layout directly (a lane holds
+// four consecutive rows of one column, half of a packed run).
+//
+// Both kernels keep the forward kernels' pipeline discipline: NSET rotating
+// register sets, loads of step e + NSET - 1 issued after step e's multiplies,
+// void steps past the end re-reading valid addresses, whole rounds only.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "aa_device.h"
+#include "aa_internal.h"
+
+namespace aa {
+namespace {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// One MFMA operand run from two transposing LDS reads (k and k + 4).
+__device__ inline Run<__bf16> lds_run_tr(__bf16* p0, __bf16* p1) {
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p1));
+  const u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+  Run<__bf16> r;
+  r.v = u32x4_t{a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// Rows of type i: first + s * stride for s < count (closed-form typings).
+struct TypeRows {
+  int64_t first, stride, count;
+};
+__device__ inline TypeRows type_rows(int kind, int q, int off_mod_q, int64_t M, int64_t rows_per_type, int i) {
+  TypeRows t;
+  if (kind == AA_TYPES_BLOCK_ROWS) {
+    t.first = int64_t(i) * rows_per_type;
+    t.stride = 1;
+    t.count = rows_per_type;
+  } else {
+    int r0 = i - off_mod_q;
+    if (r0 < 0) r0 += q;
+    t.first = r0;
+    t.stride = q;
+    t.count = r0 < M ? (M - r0 + q - 1) / q : 0;
+  }
+  return t;
+}
+
+// K(i, j): output groups k whose entry (i, j, k) is kept, ascending.
+__device__ inline int klist_len(int law, int q, int i, int j) {
+  if (law == AA_LAW_QQ) return j == i ? q : 1;
+  const int a = i >> 1, b = i & 1, a1 = j >> 1, b1 = j & 1;
+  return (a1 == a ? 2 : 1) * (b1 == b ? 2 : 1);
+}
+__device__ inline int klist_at(int law, int i, int j, int m) {
+  if (law == AA_LAW_QQ) return j == i ? m : j;
+  // Q2 x Q2: j = (a1, b1) is kept for k = (a2, b2) when a1 is a or a2 and b1
+  // is b or b2, so a2 is free when a1 = a and must equal a1 otherwise.
+  const int a = i >> 1, b = i & 1, a1 = j >> 1, b1 = j & 1;
+  const int nb = b1 == b ? 2 : 1;
+  const int a2 = a1 == a ? m / nb : a1;
+  const int b2 = b1 == b ? m % nb : b1;
+  return 2 * a2 + b2;
+}
+
+// ------------------------------------------------------- data gradient ---
+
+struct BwdDataParams {
+  const __bf16* dY;   // M x ldy
+  const __bf16* W;    // packed
+  void* dX;           // M x ldx (Tout)
+  float* ws;          // split leaves: [part][M][b_in] fp32 partial sums
+  int64_t M, ldy, ldx;
+  int32_t q, b_in, b_out, law, kind, off_mod_q;
+  int64_t rows_per_type;
+  int32_t mt_count;   // token tiles per type
+  int32_t R;          // blocks per part of a split leaf
+  int32_t nb;         // block products per type: 2q - 1 (Q_q) or 9
+  int32_t ksb;        // k-steps (32 output features) per block
+  int64_t units;      // q * mt_count * nb
+};
+
+// A work item: blocks kofs .. kofs + nblk - 1 of K(i, j) for token tile mt.
+struct DItem {
+  int64_t gu;   // global index of its first unit
+  int i, mt, j, p, kofs, nblk;
+  bool split;   // K(i, j) has more than one part
+};
+
+// The item that contains global unit g.  Units are numbered type by type
+// (then token tile), and inside a type by input group j, then K(i, j).
+__device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
+  DItem it;
+  const int64_t tmi = g / P.nb;
+  const int u = int(g - tmi * P.nb);
+  it.i = int(tmi / P.mt_count);
+  it.mt = int(tmi - int64_t(it.i) * P.mt_count);
+  int j, start;
+  if (P.law == AA_LAW_QQ) {
+    j = u < it.i ? u : (u < it.i + P.q ? it.i : u - (P.q - 1));
+    start = j + (j > it.i ? P.q - 1 : 0);
+  } else {
+    j = 0;
+    start = 0;
+    while (j < P.q - 1 && u >= start + klist_len(P.law, P.q, it.i, j)) {
+      start += klist_len(P.law, P.q, it.i, j);
+      ++j;
+    }
+  }
+  const int len = klist_len(P.law, P.q, it.i, j);
+  it.j = j;
+  it.p = (u - start) / P.R;
+  it.kofs = it.p * P.R;
+  it.nblk = len - it.kofs < P.R ? len - it.kofs : P.R;
+  it.split = len > P.R;
+  it.gu = tmi * P.nb + start + it.kofs;
+  return it;
+}
+
+template <typename Tout, int NFI, int MF, int NSET>
+__global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
+  constexpr int NTHR = 256;
+  constexpr int TM = 64 * MF;
+  constexpr int NWL = (NFI * 16 + 63) / 64;   // 16-byte loads per thread of a step's weight tile
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __bf16* lds = reinterpret_cast<__bf16*>(smem);
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int g = lane >> 4, r = lane & 15;
+  const int b_in = P.b_in, q = P.q;
+  const int nfi = b_in / 16;
+  const int nstrips = P.b_out / 16;
+  const int tile_elems = 32 * b_in;         // two strips of b_in x 16
+  const int tile_chunks = 4 * b_in;         // 16-byte chunks of a tile
+  const int64_t blk = int64_t(b_in) * P.b_out;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+  Tout* __restrict__ dX = static_cast<Tout*>(P.dX);
+
+  // ---- this workgroup's units: a contiguous share of its XCD's run
+  const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int64_t S8 = gridDim.x / kNumXcd;
+  const int64_t xlo = P.units * xcd / kNumXcd, xhi = P.units * (xcd + 1) / kNumXcd;
+  const int64_t lo = xlo + (xhi - xlo) * slot / S8, hi = xlo + (xhi - xlo) * (slot + 1) / S8;
+  if (lo >= hi) return;
+  DItem first = ditem_at(P, lo);
+  if (first.gu < lo) first = ditem_at(P, first.gu + first.nblk);
+  if (first.gu >= hi) return;
+  int n_steps = 0;
+  for (DItem it = first;;) {
+    n_steps += it.nblk * P.ksb;
+    const int64_t nx = it.gu + it.nblk;
+    if (nx >= hi || nx >= P.units) break;
+    it = ditem_at(P, nx);
+  }
+
+  struct Step {
+    DItem it;
+    int m, s;          // block of the item, k-step of the block
+    bool live, last;   // last: the item's final step
+    TypeRows tr;
+  };
+  // Cursor of the next step to request.
+  DItem cur_it = first;
+  int cur_m = 0, cur_s = 0, issued = 0;
+  auto setup = [&](Step& S) __attribute__((always_inline)) {
+    S.live = issued < n_steps;
+    S.it = cur_it;
+    S.m = cur_m;
+    S.s = cur_s;
+    S.last = S.live && cur_m == cur_it.nblk - 1 && cur_s == P.ksb - 1;
+    S.tr = type_rows(P.kind, q, P.off_mod_q, P.M, P.rows_per_type, cur_it.i);
+    if (S.live) {
+      ++issued;
+      if (++cur_s == P.ksb) {
+        cur_s = 0;
+        if (++cur_m == cur_it.nblk) {
+          cur_m = 0;
+          const int64_t nx = cur_it.gu + cur_it.nblk;
+          if (issued < n_steps) cur_it = ditem_at(P, nx);
+        }
+      }
+    }
+  };
+
+  // ---- loads of one step: the weight tile (two strips of block (j, k), or
+  // one strip and zeros at an odd tail) and each lane's dY run(s).
+  auto load = [&](const Step& S, u32x4_t (&wr)[NWL], Run<__bf16> (&br)[MF]) __attribute__((always_inline)) {
+    const int k = klist_at(P.law, S.it.i, S.it.j, S.it.kofs + S.m);
+    const int ns = nstrips - 2 * S.s < 2 ? 1 : 2;
+    const __bf16* wt = P.W + (int64_t(S.it.j) * q + k) * blk + int64_t(2 * S.s) * (b_in * 16);
+    const int nvalid = ns * 2 * b_in;   // valid 16-byte chunks
+#pragma unroll
+    for (int c = 0; c < NWL; ++c) {
+      const int ch = c * NTHR + int(threadIdx.x);
+      const __bf16* src = ch < nvalid ? wt + ch * 8 : zero;
+      wr[c] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+    const bool kok = g < 2 || ns == 2;
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      const int64_t tt = int64_t(S.it.mt) * TM + (wave * MF + mf) * 16 + r;
+      const bool ok = kok && tt < S.tr.count;
+      const __bf16* src = ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + S.s * 32 + g * 8
+                             : zero;
+      br[mf] = Run<__bf16>::load_cached(src);
+    }
+  };
+  auto store_w = [&](const u32x4_t (&wr)[NWL], int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < NWL; ++c) {
+      const int ch = c * NTHR + int(threadIdx.x);
+      if (ch < tile_chunks) *reinterpret_cast<u32x4_t*>(lds + buf * tile_elems + ch * 8) = wr[c];
+    }
+  };
+
+  // Per-lane offset of its transposing read inside a tile (see the header).
+  const int lane_off = (g >> 1) * (b_in * 16) + (8 * (g & 1) + (r >> 2)) * 8 + ((r & 3) >> 1) * 128 + (r & 1) * 4;
+  f32x4_t acc[MF][NFI];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int f = 0; f < NFI; ++f) acc[mf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Step& S, const Run<__bf16> (&br)[MF], int buf) __attribute__((always_inline)) {
+    if (!S.live) return;
+    __bf16* t = lds + buf * tile_elems + lane_off;
+#pragma unroll
+    for (int f = 0; f < NFI; ++f) {
+      if (f < nfi) {
+        const Run<__bf16> a = lds_run_tr(t + f * 256, t + f * 256 + 32);
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) acc[mf][f] = mma(a, br[mf], acc[mf][f]);
+      }
+    }
+    if (!S.last) return;
+    // lane (token r, g) holds input features f * 16 + 4g .. + 3 of its token
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) {
+      const int64_t tt = int64_t(S.it.mt) * TM + (wave * MF + mf) * 16 + r;
+      if (tt < S.tr.count) {
+        const int64_t row = S.tr.first + tt * S.tr.stride;
+#pragma unroll
+        for (int f = 0; f < NFI; ++f) {
+          if (f < nfi) {
+            if (S.it.split) store4(P.ws + (int64_t(S.it.p) * P.M + row) * b_in + f * 16 + 4 * g, acc[mf][f]);
+            else store4(dX + row * P.ldx + int64_t(S.it.j) * b_in + f * 16 + 4 * g, acc[mf][f]);
+          }
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < NFI; ++f) acc[mf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  // ---- software pipeline over NSET register sets
+  u32x4_t wr[NSET][NWL];
+  Run<__bf16> br[NSET][MF];
+  Step S[NSET];
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) {
+    setup(S[s]);
+    load(S[s], wr[s], br[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int rounds = (n_steps + NSET - 1) / NSET;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      const int buf = s & 1 ? 1 : 0;   // NSET is even, so set parity = step parity
+      store_w(wr[s], buf);
+      __syncthreads();
+      compute(S[s], br[s], buf);
+      const int sn = (s + NSET - 1) % NSET;
+      setup(S[sn]);
+      load(S[sn], wr[sn], br[sn]);
+    }
+  }
+}
+
+// Sum the partial sums of the split leaves into dX: Q_q's own group, row by
+// row (row t of type i gets input group i).
+template <typename Tout>
+__global__ __launch_bounds__(256) void bwd_data_reduce_kernel(BwdDataParams P, int nparts) {
+  const int cpr = P.b_in / 4;
+  const int64_t n = P.M * cpr;
+  Tout* __restrict__ dX = static_cast<Tout*>(P.dX);
+  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = e / cpr;
+    const int c = int(e - t * cpr) * 4;
+    const int i = P.kind == AA_TYPES_BLOCK_ROWS ? int(t / P.rows_per_type) : int((P.off_mod_q + t) % P.q);
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < nparts; ++p) s += *reinterpret_cast<const f32x4_t*>(P.ws + (int64_t(p) * P.M + t) * P.b_in + c);
+    store4(dX + t * P.ldx + int64_t(i) * P.b_in + c, s);
+  }
+}
+
+// ----------------------------------------------------- weight gradient ---
+
+struct BwdWeightParams {
+  const __bf16* X;    // M x ldx
+  const __bf16* dY;   // M x ldy
+  void* dW;           // packed (Tout)
+  int64_t M, ldx, ldy;
+  int32_t q, b_in, b_out, law, kind, off_mod_q;
+  int64_t rows_per_type;
+  int32_t nchunks;    // column chunks of NC strips per output group
+  int32_t ldsx, ldsy; // LDS row pitch (elements) of the X and dY tiles
+};
+
+// Accumulator slots: Q_q uses slot 0 for block (i, k) of the current type and
+// slot 1 for the diagonal block (k, k); Q2 x Q2 uses slot j for block (j, k).
+template <typename Tout, bool QQ, int NFW, int NC, int NSET>
+__global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
+  constexpr int NTHR = 256;
+  constexpr int NSLOT = QQ ? 2 : 4;
+  constexpr int NXL = NFW;   // 16-byte loads per thread of the 32 x b_in X tile (b_in <= 64 NFW)
+  constexpr int NYL = (64 * NC + NTHR - 1) / NTHR;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __bf16* lds = reinterpret_cast<__bf16*>(smem);
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int g = lane >> 4, r = lane & 15;
+  const int b_in = P.b_in, q = P.q;
+  const int nfi = b_in / 16;
+  const int nstrips = P.b_out / 16;
+  const int xcpr = b_in / 8;                      // 16-byte chunks of a tile row
+  const int x_chunks = 32 * xcpr;
+  const int x_elems = 32 * P.ldsx, y_elems = 32 * P.ldsy;
+  const int buf_elems = x_elems + y_elems;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+  Tout* __restrict__ dW = static_cast<Tout*>(P.dW);
+  const int64_t blk = int64_t(b_in) * P.b_out;
+
+  // ---- (output group k, column chunk c): each XCD takes a contiguous run
+  const int64_t n_items = int64_t(q) * P.nchunks;
+  const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int64_t xlo = n_items * xcd / kNumXcd, xhi = n_items * (xcd + 1) / kNumXcd;
+  const int64_t item = xlo + slot;
+  if (item >= xhi) return;
+  const int k = int(item / P.nchunks), c = int(item - int64_t(k) * P.nchunks);
+  const int col0 = c * NC * 16;   // first column of the chunk inside group k
+
+  // steps: every type i, every 32-token chunk of it (at least one, so that a
+  // type without rows still writes its zero block), every j with (i, j, k) in T
+  auto chunks_of = [&](int i) __attribute__((always_inline)) {
+    const TypeRows t = type_rows(P.kind, q, P.off_mod_q, P.M, P.rows_per_type, i);
+    return t.count > 0 ? int((t.count + 31) / 32) : 1;
+  };
+  int n_steps = 0;
+  for (int i = 0; i < q; ++i) {
+    int gl[4];
+    n_steps += chunks_of(i) * device_leaf_groups(P.law, i, k, gl);
+  }
+
+  struct Step {
+    int i, tc, j, slot;
+    bool live, flush0;   // flush0 (Q_q): the type's last step, block (i, k) done
+    TypeRows tr;
+  };
+  int cur_i = 0, cur_tc = 0, cur_jx = 0, issued = 0;
+  auto setup = [&](Step& S) __attribute__((always_inline)) {
+    S.live = issued < n_steps;
+    int gl[4];
+    const int ng = device_leaf_groups(P.law, cur_i, k, gl);
+    const int nch = chunks_of(cur_i);
+    S.i = cur_i;
+    S.tc = cur_tc;
+    S.j = gl[cur_jx];
+    S.slot = QQ ? (S.j == k ? 1 : 0) : S.j;
+    S.flush0 = QQ && S.live && cur_i != k && cur_tc == nch - 1 && cur_jx == ng - 1;
+    S.tr = type_rows(P.kind, q, P.off_mod_q, P.M, P.rows_per_type, cur_i);
+    if (S.live) {
+      ++issued;
+      if (++cur_jx == ng) {
+        cur_jx = 0;
+        if (++cur_tc == nch) {
+          cur_tc = 0;
+          if (issued < n_steps) ++cur_i;
+        }
+      }
+    }
+  };
+
+  auto load = [&](const Step& S, u32x4_t (&xr)[NXL], u32x4_t (&yr)[NYL]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int l = 0; l < NXL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / xcpr, cc = ch - tk * xcpr;
+      const int64_t tt = int64_t(S.tc) * 32 + tk;
+      const bool ok = ch < x_chunks && tt < S.tr.count;
+      const __bf16* src = ok ? P.X + (S.tr.first + tt * S.tr.stride) * P.ldx + int64_t(S.j) * b_in + cc * 8 : zero;
+      xr[l] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+#pragma unroll
+    for (int l = 0; l < NYL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
+      const int64_t tt = int64_t(S.tc) * 32 + tk;
+      const bool ok = ch < 64 * NC && tt < S.tr.count && col0 + cc * 8 < P.b_out;
+      const __bf16* src =
+          ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + col0 + cc * 8 : zero;
+      yr[l] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+  };
+  auto store_tiles = [&](const u32x4_t (&xr)[NXL], const u32x4_t (&yr)[NYL], int buf) __attribute__((always_inline)) {
+    __bf16* base = lds + buf * buf_elems;
+#pragma unroll
+    for (int l = 0; l < NXL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / xcpr, cc = ch - tk * xcpr;
+      if (ch < x_chunks) *reinterpret_cast<u32x4_t*>(base + tk * P.ldsx + cc * 8) = xr[l];
+    }
+#pragma unroll
+    for (int l = 0; l < NYL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
+      if (ch < 64 * NC) *reinterpret_cast<u32x4_t*>(base + x_elems + tk * P.ldsy + cc * 8) = yr[l];
+    }
+  };
+
+  f32x4_t acc[NSLOT][NFW][NC];
+#pragma unroll
+  for (int s = 0; s < NSLOT; ++s)
+#pragma unroll
+    for (int a = 0; a < NFW; ++a)
+#pragma unroll
+      for (int b = 0; b < NC; ++b) acc[s][a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Transposing-read offsets: token 8g + r/4, features / columns 4 (r mod 4).
+  const int xoff = (8 * g + (r >> 2)) * P.ldsx + 4 * (r & 3);
+  const int yoff = (8 * g + (r >> 2)) * P.ldsy + 4 * (r & 3);
+
+  auto flush = [&](int sl, int j) __attribute__((always_inline)) {
+    Tout* blkp = dW + (int64_t(j) * q + k) * blk;
+#pragma unroll
+    for (int a = 0; a < NFW; ++a) {
+      const int f = wave + 4 * a;
+      if (f < nfi) {
+        const int row = f * 16 + 4 * g;
+#pragma unroll
+        for (int b = 0; b < NC; ++b) {
+          const int st = c * NC + b;
+          if (st < nstrips) store4(blkp + int64_t(st) * (b_in * 16) + (row >> 3) * 128 + r * 8 + (row & 7), acc[sl][a][b]);
+        }
+      }
+    }
+  };
+
+  auto compute = [&](const Step& S, int buf) __attribute__((always_inline)) {
+    if (!S.live) return;
+    __bf16* base = lds + buf * buf_elems;
+    Run<__bf16> bv[NC];
+#pragma unroll
+    for (int b = 0; b < NC; ++b) {
+      __bf16* p = base + x_elems + yoff + b * 16;
+      bv[b] = lds_run_tr(p, p + 4 * P.ldsy);
+    }
+#pragma unroll
+    for (int a = 0; a < NFW; ++a) {
+      const int f = wave + 4 * a;
+      if (f < nfi) {
+        __bf16* p = base + xoff + f * 16;
+        const Run<__bf16> av = lds_run_tr(p, p + 4 * P.ldsx);
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) {
+          if (S.slot == sl) {
+#pragma unroll
+            for (int b = 0; b < NC; ++b) acc[sl][a][b] = mma(av, bv[b], acc[sl][a][b]);
+          }
+        }
+      }
+    }
+    if (QQ && S.flush0) {
+      flush(0, S.i);
+#pragma unroll
+      for (int a = 0; a < NFW; ++a)
+#pragma unroll
+        for (int b = 0; b < NC; ++b) acc[0][a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  u32x4_t xr[NSET][NXL], yr[NSET][NYL];
+  Step S[NSET];
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) {
+    setup(S[s]);
+    load(S[s], xr[s], yr[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int rounds = (n_steps + NSET - 1) / NSET;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      const int buf = s & 1;
+      store_tiles(xr[s], yr[s], buf);
+      __syncthreads();
+      compute(S[s], buf);
+      const int sn = (s + NSET - 1) % NSET;
+      setup(S[sn]);
+      load(S[sn], xr[sn], yr[sn]);
+    }
+  }
+  if (QQ) {
+    flush(1, k);
+  } else {
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) flush(sl, sl);
+  }
+}
+
+int lds_pitch(int cols) {
+  // A pitch of 16 mod 64 elements (32 mod 128 bytes) puts the four tokens of
+  // a transposing read's 16-lane group on disjoint banks.
+  const int pad = ((16 - cols) % 64 + 64) % 64;
+  return cols + pad;
+}
+
+// Blocks per part of a split data-gradient leaf.  Q_q's own-group leaf has q
+// blocks and every other leaf one; parts of four keep the work items within a
+// factor of four of each other (Q2 x Q2 leaves, at most four blocks, never split).
+constexpr int kDataSplit = 4;
+
+int64_t max_rows_per_type(const aa_plan_s& plan, int64_t M) {
+  if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
+  return (M + plan.q - 1) / plan.q;
+}
+
+}  // namespace
+
+size_t bwd_data_workspace_bytes(const aa_plan_s& plan, int64_t M) {
+  const int R = kDataSplit;
+  const int len = plan.law == AA_LAW_QQ ? plan.q : 4;
+  if (len <= R) return 0;
+  const int nparts = (len + R - 1) / R;
+  return size_t(nparts) * size_t(M) * size_t(plan.b_in) * sizeof(float);
+}
+
+aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W, void* dX, int64_t M,
+                            int64_t pos_offset, void* ws, hipStream_t stream) {
+  BwdDataParams P{};
+  P.dY = static_cast<const __bf16*>(dY);
+  P.W = static_cast<const __bf16*>(W);
+  P.dX = dX;
+  P.ws = static_cast<float*>(ws);
+  P.M = M;
+  P.ldy = plan.d_out;
+  P.ldx = plan.d_in;
+  P.q = plan.q;
+  P.b_in = int32_t(plan.b_in);
+  P.b_out = int32_t(plan.b_out);
+  P.law = plan.law;
+  P.kind = plan.type_kind;
+  P.off_mod_q = int32_t(pos_offset % plan.q);
+  P.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
+  P.R = kDataSplit;
+  P.nb = plan.law == AA_LAW_QQ ? 2 * plan.q - 1 : 9;
+  P.ksb = int32_t((plan.b_out + 31) / 32);
+  const int nfi = int(plan.b_in / 16);
+  const int64_t rpt = max_rows_per_type(plan, M);
+  const int MF = (rpt > 64 && nfi <= 8) ? 2 : 1;
+  P.mt_count = int32_t((rpt + 64 * MF - 1) / (64 * MF));
+  P.units = int64_t(plan.q) * P.mt_count * P.nb;
+  const size_t lds = size_t(2) * 64 * plan.b_in;
+  int grid = device_cu_count() * 2;
+  grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
+  const bool f32 = plan.out_dtype == AA_F32;
+  auto go = [&](auto nfi_c, auto mf_c, auto nset_c) {
+    constexpr int NFIc = decltype(nfi_c)::value, MFc = decltype(mf_c)::value, NS = decltype(nset_c)::value;
+    if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, NS>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, NS>), dim3(grid), dim3(256), lds, stream, P);
+  };
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C4 = std::integral_constant<int, 4>;
+  if (nfi <= 4) {
+    if (MF == 2) go(C4{}, C2{}, C4{});
+    else go(C4{}, C1{}, C4{});
+  } else if (nfi <= 8) {
+    if (MF == 2) go(std::integral_constant<int, 8>{}, C2{}, C4{});
+    else go(std::integral_constant<int, 8>{}, C1{}, C4{});
+  } else if (nfi <= 16) {
+    go(std::integral_constant<int, 16>{}, C1{}, C2{});
+  } else if (nfi <= 32) {
+    go(std::integral_constant<int, 32>{}, C1{}, C2{});
+  } else {
+    return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_data: input blocks wider than 512 features");
+  }
+  aa_status_t st = after_launch(stream, "bwd_data");
+  if (st != AA_OK) return st;
+  const int len = plan.law == AA_LAW_QQ ? plan.q : 4;
+  if (len > P.R) {
+    const int nparts = (len + P.R - 1) / P.R;
+    const int64_t n = M * (plan.b_in / 4);
+    const int blocks = int(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+    if (f32) hipLaunchKernelGGL((bwd_data_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, P, nparts);
+    else hipLaunchKernelGGL((bwd_data_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, P, nparts);
+    st = after_launch(stream, "bwd_data_reduce");
+  }
+  return st;
+}
+
+aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
+                              int64_t pos_offset, hipStream_t stream) {
+  BwdWeightParams P{};
+  P.X = static_cast<const __bf16*>(X);
+  P.dY = static_cast<const __bf16*>(dY);
+  P.dW = dW;
+  P.M = M;
+  P.ldx = plan.d_in;
+  P.ldy = plan.d_out;
+  P.q = plan.q;
+  P.b_in = int32_t(plan.b_in);
+  P.b_out = int32_t(plan.b_out);
+  P.law = plan.law;
+  P.kind = plan.type_kind;
+  P.off_mod_q = int32_t(pos_offset % plan.q);
+  P.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
+  const int nfw = int((plan.b_in / 16 + 3) / 4);
+  const bool qq = plan.law == AA_LAW_QQ;
+  const int NC = (qq ? nfw <= 4 : nfw <= 2) ? 2 : 1;
+  P.nchunks = int32_t((plan.b_out / 16 + NC - 1) / NC);
+  P.ldsx = lds_pitch(int(plan.b_in));
+  P.ldsy = lds_pitch(16 * NC);
+  const size_t lds = size_t(2) * 32 * (P.ldsx + P.ldsy) * 2;
+  const int64_t n_items = int64_t(plan.q) * P.nchunks;
+  const int grid = int((n_items + kNumXcd - 1) / kNumXcd * kNumXcd);
+  const bool f32 = plan.out_dtype == AA_F32;
+  auto go = [&](auto qq_c, auto nfw_c, auto nc_c) {
+    constexpr bool QQc = decltype(qq_c)::value;
+    constexpr int NFWc = decltype(nfw_c)::value, NCc = decltype(nc_c)::value;
+    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, QQc, NFWc, NCc, 2>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, QQc, NFWc, NCc, 2>), dim3(grid), dim3(256), lds, stream, P);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C4 = std::integral_constant<int, 4>;
+  using C8 = std::integral_constant<int, 8>;
+  if (plan.b_in > 384) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_weight: input blocks wider than 384 features");
+  if (qq) {
+    if (nfw <= 1) go(T{}, C1{}, C2{});
+    else if (nfw <= 2) go(T{}, C2{}, C2{});
+    else if (nfw <= 4) go(T{}, C4{}, C2{});
+    else go(T{}, C8{}, C1{});
+  } else {
+    if (nfw <= 1) go(F{}, C1{}, C2{});
+    else if (nfw <= 2) go(F{}, C2{}, C2{});
+    else if (nfw <= 4) go(F{}, C4{}, C1{});
+    else go(F{}, C8{}, C1{});
+  }
+  return after_launch(stream, "bwd_weight");
+}
+
+}  // namespace aa

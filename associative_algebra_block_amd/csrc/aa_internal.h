@@ -60,6 +60,18 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, c
                           int64_t n, int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
 bool decode_swiglu_ok(const aa_plan_s& plan);
 
+// Gradients (bf16 operands, position or block-row typing).  The data
+// gradient needs bwd_data_workspace_bytes(plan, M) bytes of device workspace
+// (0: none).
+size_t bwd_data_workspace_bytes(const aa_plan_s& plan, int64_t M);
+aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W, void* dX, int64_t M,
+                            int64_t pos_offset, void* ws, hipStream_t stream);
+aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
+                              int64_t pos_offset, hipStream_t stream);
+
+// Compute units of the current device.
+int device_cu_count();
+
 // Synchronise and check when AA_DEBUG=1; map launch errors to AA_ERR_HIP.
 aa_status_t after_launch(hipStream_t stream, const char* what);
 

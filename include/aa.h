@@ -44,6 +44,7 @@
 #ifndef AA_H_
 #define AA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -150,6 +151,34 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
  * 2q - 1 weight blocks: its own block-row and the other diagonal blocks. */
 aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, void* y, int64_t n,
                            int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
+
+/* Gradients of the row-typed projection for an upstream gradient dY (the
+ * pages report a backward pass of the projection beside the forward one:
+ * agihunt.info review, paragraph on the kernel measurements; it is the exact
+ * gradient of the bilinear map of aa_project_fwd).  With T the plan's table
+ * and tau(t) the type of row t:
+ *   dX[t, j] = sum over k with (tau(t), j, k) in T of dY[t, k] W_jk^T
+ *   dW_jk    = sum over rows t with (tau(t), j, k) in T of X[t, j]^T dY[t, k]
+ * dY is M x d_out and X M x d_in, both of the plan's in_dtype; W_packed is the
+ * packed weight; dX (M x d_in) and dW_packed (packed layout, d_in * d_out
+ * elements, the same order as W_packed) are written in the plan's out_dtype.
+ * dW_packed is overwritten, not accumulated; every block is written (blocks
+ * no row reaches are zero).  Outputs must not overlap inputs.  M, pos_offset
+ * and the type map mean what they mean for aa_project_fwd, M == 0 is a no-op
+ * (dW is then not written).
+ * Limits of this implementation: in_dtype AA_BF16; AA_TYPES_POS_MOD or
+ * AA_TYPES_BLOCK_ROWS (row_types must be NULL; explicit type lists return
+ * AA_ERR_UNSUPPORTED); b_in <= 512 for dX and b_in <= 384 for dW.
+ * aa_project_bwd_data needs device workspace of at least the size that
+ * aa_project_bwd_data_workspace reports for the same plan and M (it may be 0,
+ * and workspace may then be NULL); the workspace is caller-owned scratch whose
+ * contents are overwritten.  Calls that share a workspace must not overlap. */
+aa_status_t aa_project_bwd_data_workspace(aa_plan_t plan, int64_t M, size_t* bytes);
+aa_status_t aa_project_bwd_data(aa_plan_t plan, const void* dY, const void* W_packed, void* dX, int64_t M,
+                                int64_t pos_offset, const int32_t* row_types, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY, void* dW_packed, int64_t M,
+                                  int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
 
 /* A static English name of a status code. */
 const char* aa_status_string(aa_status_t status);
