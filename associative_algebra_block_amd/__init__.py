@@ -20,7 +20,7 @@ __all__ = [
     "AA_BF16", "AA_F32", "AA_OK", "AA_ERR_INVALID_ARG", "AA_ERR_SHAPE", "AA_ERR_UNSUPPORTED",
     "AA_ERR_HIP", "AAError", "Plan", "lib_path", "load",
     "aa_plan_create", "aa_plan_destroy", "aa_plan_info", "aa_pack_weights", "aa_unpack_weights",
-    "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_decode_gemv", "aa_project_bwd_data_workspace",
+    "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_decode_gemv", "aa_project_bwd_workspace",
     "aa_project_bwd_data", "aa_project_bwd_weight", "aa_status_string", "aa_last_error",
 ]
 
@@ -52,10 +52,12 @@ _SIGNATURES = {
     "aa_swiglu_ffn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p,
                                          _c_p]),
     "aa_decode_gemv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
-    "aa_project_bwd_data_workspace": (ctypes.c_int, [_c_p, _c_i64, ctypes.POINTER(ctypes.c_size_t)]),
+    "aa_project_bwd_workspace": (ctypes.c_int, [_c_p, _c_i64, ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
     "aa_project_bwd_data": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.c_size_t,
                                            _c_p]),
-    "aa_project_bwd_weight": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
+    "aa_project_bwd_weight": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.c_size_t,
+                                             _c_p]),
     "aa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "aa_last_error": (ctypes.c_char_p, []),
 }
@@ -230,10 +232,12 @@ def aa_decode_gemv(plan: Plan, x, W_packed, y, n=None, pos_offset=0, row_types=N
         _ptr(row_types, "row_types", torch.int32, n), _stream(stream)), "aa_decode_gemv")
 
 
-def aa_project_bwd_data_workspace(plan: Plan, M: int) -> int:
-    n = ctypes.c_size_t(0)
-    _check(load().aa_project_bwd_data_workspace(plan.handle, int(M), ctypes.byref(n)), "aa_project_bwd_data_workspace")
-    return int(n.value)
+def aa_project_bwd_workspace(plan: Plan, M: int) -> tuple[int, int]:
+    """(bytes for aa_project_bwd_data, bytes for aa_project_bwd_weight)."""
+    nd, nw = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load().aa_project_bwd_workspace(plan.handle, int(M), ctypes.byref(nd), ctypes.byref(nw)),
+           "aa_project_bwd_workspace")
+    return int(nd.value), int(nw.value)
 
 
 def aa_project_bwd_data(plan: Plan, dY, W_packed, dX, M=None, pos_offset=0, row_types=None, workspace=None,
@@ -249,13 +253,17 @@ def aa_project_bwd_data(plan: Plan, dY, W_packed, dX, M=None, pos_offset=0, row_
         _stream(stream)), "aa_project_bwd_data")
 
 
-def aa_project_bwd_weight(plan: Plan, X, dY, dW_packed, M=None, pos_offset=0, row_types=None, stream=None):
+def aa_project_bwd_weight(plan: Plan, X, dY, dW_packed, M=None, pos_offset=0, row_types=None, workspace=None,
+                          workspace_bytes=None, stream=None):
     M = _rows_of(X, M)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().aa_project_bwd_weight(
         plan.handle, _ptr(X, "X", plan.in_torch_dtype, M * plan.d_in),
         _ptr(dY, "dY", plan.in_torch_dtype, M * plan.d_out),
         _ptr(dW_packed, "dW_packed", plan.out_torch_dtype, plan.d_in * plan.d_out), M, int(pos_offset),
-        _ptr(row_types, "row_types", torch.int32, M), _stream(stream)), "aa_project_bwd_weight")
+        _ptr(row_types, "row_types", torch.int32, M), _ptr(workspace, "workspace"), int(workspace_bytes),
+        _stream(stream)), "aa_project_bwd_weight")
 
 
 # ----------------------------------------------------------- conveniences ---

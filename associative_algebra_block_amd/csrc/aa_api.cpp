@@ -144,12 +144,12 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
   return aa::launch_leaf_gemm(*down, proj_down, stream);
 }
 
-aa_status_t aa_project_bwd_data_workspace(aa_plan_t plan, int64_t M, size_t* bytes) {
+aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_bytes, size_t* weight_bytes) {
   aa::clear_error();
-  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data_workspace: plan is NULL");
-  if (!bytes) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data_workspace: bytes is NULL");
-  if (M < 0) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data_workspace: M is negative");
-  *bytes = aa::bwd_data_workspace_bytes(*plan, M);
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: plan is NULL");
+  if (M < 0) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: M is negative");
+  if (data_bytes) *data_bytes = aa::bwd_data_workspace_bytes(*plan, M);
+  if (weight_bytes) *weight_bytes = aa::bwd_weight_workspace_bytes(*plan);
   return AA_OK;
 }
 
@@ -168,7 +168,7 @@ aa_status_t aa_project_bwd_data(aa_plan_t plan, const void* dY, const void* W_pa
   if ((st = check_ptr(dX, "dX", fn)) != AA_OK) return st;
   const size_t need = aa::bwd_data_workspace_bytes(*plan, M);
   if (workspace_bytes < need)
-    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data: workspace smaller than aa_project_bwd_data_workspace reports");
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_data: workspace smaller than aa_project_bwd_workspace reports");
   if (need > 0 && (st = check_ptr(workspace, "workspace", fn)) != AA_OK) return st;
   const size_t yb = size_t(M * plan->d_out) * elem_size(plan->in_dtype);
   const size_t wb = size_t(plan->d_in * plan->d_out) * elem_size(plan->in_dtype);
@@ -182,7 +182,8 @@ aa_status_t aa_project_bwd_data(aa_plan_t plan, const void* dY, const void* W_pa
 }
 
 aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY, void* dW_packed, int64_t M,
-                                  int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+                                  int64_t pos_offset, const int32_t* row_types, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
   aa::clear_error();
   static const char* fn = "aa_project_bwd_weight";
   if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: plan is NULL");
@@ -199,7 +200,14 @@ aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY,
   const size_t wb = size_t(plan->d_in * plan->d_out) * elem_size(plan->out_dtype);
   if (overlaps(dW_packed, wb, X, xb) || overlaps(dW_packed, wb, dY, yb))
     return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: dW_packed overlaps X or dY");
-  return aa::launch_bwd_weight(*plan, X, dY, dW_packed, M, pos_offset, stream);
+  const size_t need = aa::bwd_weight_workspace_bytes(*plan);
+  if (workspace_bytes < need)
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: workspace smaller than aa_project_bwd_workspace reports");
+  if (need > 0 && (st = check_ptr(workspace, "workspace", fn)) != AA_OK) return st;
+  if (need > 0 && (overlaps(workspace, need, dW_packed, wb) || overlaps(workspace, need, X, xb) ||
+                   overlaps(workspace, need, dY, yb)))
+    return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: workspace overlaps an operand");
+  return aa::launch_bwd_weight(*plan, X, dY, dW_packed, M, pos_offset, need > 0 ? workspace : nullptr, stream);
 }
 
 aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, void* y, int64_t n,

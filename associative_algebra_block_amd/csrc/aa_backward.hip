@@ -73,24 +73,31 @@ __device__ inline Run<__bf16> lds_run_tr(__bf16* p0, __bf16* p1) {
 }
 
 // Rows of type i: first + s * stride for s < count (closed-form typings).
+// The divisions are done once per kernel (TypeMap), not per pipeline step.
 struct TypeRows {
   int64_t first, stride, count;
 };
-__device__ inline TypeRows type_rows(int kind, int q, int off_mod_q, int64_t M, int64_t rows_per_type, int i) {
-  TypeRows t;
-  if (kind == AA_TYPES_BLOCK_ROWS) {
-    t.first = int64_t(i) * rows_per_type;
-    t.stride = 1;
-    t.count = rows_per_type;
-  } else {
-    int r0 = i - off_mod_q;
-    if (r0 < 0) r0 += q;
-    t.first = r0;
-    t.stride = q;
-    t.count = r0 < M ? (M - r0 + q - 1) / q : 0;
+struct TypeMap {
+  int kind, q, off_mod_q, m_mod_q;
+  int64_t m_div_q, rows_per_type;
+  __device__ TypeMap(int kind_, int q_, int off, int64_t M, int64_t rpt)
+      : kind(kind_), q(q_), off_mod_q(off), m_mod_q(int(M % q_)), m_div_q(M / q_), rows_per_type(rpt) {}
+  __device__ TypeRows rows(int i) const {
+    TypeRows t;
+    if (kind == AA_TYPES_BLOCK_ROWS) {
+      t.first = int64_t(i) * rows_per_type;
+      t.stride = 1;
+      t.count = rows_per_type;
+    } else {
+      int r0 = i - off_mod_q;
+      if (r0 < 0) r0 += q;
+      t.first = r0;
+      t.stride = q;
+      t.count = m_div_q + (r0 < m_mod_q ? 1 : 0);   // rows r0 + s q below M
+    }
+    return t;
   }
-  return t;
-}
+};
 
 // K(i, j): output groups k whose entry (i, j, k) is kept, ascending.
 __device__ inline int klist_len(int law, int q, int i, int j) {
@@ -122,7 +129,7 @@ struct BwdDataParams {
   int32_t mt_count;   // token tiles per type
   int32_t R;          // blocks per part of a split leaf
   int32_t nb;         // block products per type: 2q - 1 (Q_q) or 9
-  int32_t ksb;        // k-steps (32 output features) per block
+  int32_t ksb;        // steps (KS strips) per block
   int64_t units;      // q * mt_count * nb
 };
 
@@ -137,10 +144,11 @@ struct DItem {
 // (then token tile), and inside a type by input group j, then K(i, j).
 __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   DItem it;
-  const int64_t tmi = g / P.nb;
-  const int u = int(g - tmi * P.nb);
-  it.i = int(tmi / P.mt_count);
-  it.mt = int(tmi - int64_t(it.i) * P.mt_count);
+  // units < 2^31 (checked on the host), so 32-bit divisions
+  const uint32_t tmi = uint32_t(g) / uint32_t(P.nb);
+  const int u = int(uint32_t(g) - tmi * uint32_t(P.nb));
+  it.i = int(tmi / uint32_t(P.mt_count));
+  it.mt = int(tmi - uint32_t(it.i) * uint32_t(P.mt_count));
   int j, start;
   if (P.law == AA_LAW_QQ) {
     j = u < it.i ? u : (u < it.i + P.q ? it.i : u - (P.q - 1));
@@ -159,15 +167,18 @@ __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   it.kofs = it.p * P.R;
   it.nblk = len - it.kofs < P.R ? len - it.kofs : P.R;
   it.split = len > P.R;
-  it.gu = tmi * P.nb + start + it.kofs;
+  it.gu = int64_t(tmi) * P.nb + start + it.kofs;
   return it;
 }
 
-template <typename Tout, int NFI, int MF, int NSET>
+// A step covers KS strips (16 KS output features, KS / 2 MFMA k-steps) of one
+// block: its weight tile is KS strips of the packed block, contiguous in HBM.
+template <typename Tout, int NFI, int MF, int KS, int NSET>
 __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   constexpr int NTHR = 256;
   constexpr int TM = 64 * MF;
-  constexpr int NWL = (NFI * 16 + 63) / 64;   // 16-byte loads per thread of a step's weight tile
+  constexpr int KH = KS / 2;                        // MFMA k-steps per step
+  constexpr int NWL = (32 * KS * NFI + NTHR - 1) / NTHR;   // 16-byte weight loads per thread
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem);
 
@@ -176,12 +187,14 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   const int b_in = P.b_in, q = P.q;
   const int nfi = b_in / 16;
   const int nstrips = P.b_out / 16;
-  const int tile_elems = 32 * b_in;         // two strips of b_in x 16
-  const int tile_chunks = 4 * b_in;         // 16-byte chunks of a tile
+  const int strip_elems = 16 * b_in;
+  const int tile_elems = KS * strip_elems;  // KS strips of b_in x 16
+  const int tile_chunks = 2 * KS * b_in;    // 16-byte chunks of a tile
   const int64_t blk = int64_t(b_in) * P.b_out;
   const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
   Tout* __restrict__ dX = static_cast<Tout*>(P.dX);
 
+  const TypeMap tmap(P.kind, q, P.off_mod_q, P.M, P.rows_per_type);
   // ---- this workgroup's units: a contiguous share of its XCD's run
   const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
   const int64_t S8 = gridDim.x / kNumXcd;
@@ -214,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
     S.m = cur_m;
     S.s = cur_s;
     S.last = S.live && cur_m == cur_it.nblk - 1 && cur_s == P.ksb - 1;
-    S.tr = type_rows(P.kind, q, P.off_mod_q, P.M, P.rows_per_type, cur_it.i);
+    S.tr = tmap.rows(cur_it.i);
     if (S.live) {
       ++issued;
       if (++cur_s == P.ksb) {
@@ -228,12 +241,13 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
     }
   };
 
-  // ---- loads of one step: the weight tile (two strips of block (j, k), or
-  // one strip and zeros at an odd tail) and each lane's dY run(s).
-  auto load = [&](const Step& S, u32x4_t (&wr)[NWL], Run<__bf16> (&br)[MF]) __attribute__((always_inline)) {
+  // ---- loads of one step: the weight tile (KS strips of block (j, k); past
+  // the block's last strip, zeros) and each lane's dY runs.
+  auto load = [&](const Step& S, u32x4_t (&wr)[NWL], Run<__bf16> (&br)[KH][MF]) __attribute__((always_inline)) {
     const int k = klist_at(P.law, S.it.i, S.it.j, S.it.kofs + S.m);
-    const int ns = nstrips - 2 * S.s < 2 ? 1 : 2;
-    const __bf16* wt = P.W + (int64_t(S.it.j) * q + k) * blk + int64_t(2 * S.s) * (b_in * 16);
+    const int st0 = KS * S.s;
+    const __bf16* wt = P.W + (int64_t(S.it.j) * q + k) * blk + int64_t(st0) * strip_elems;
+    const int ns = nstrips - st0 < KS ? nstrips - st0 : KS;
     const int nvalid = ns * 2 * b_in;   // valid 16-byte chunks
 #pragma unroll
     for (int c = 0; c < NWL; ++c) {
@@ -241,14 +255,18 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
       const __bf16* src = ch < nvalid ? wt + ch * 8 : zero;
       wr[c] = *reinterpret_cast<const u32x4_t*>(src);
     }
-    const bool kok = g < 2 || ns == 2;
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      const int64_t tt = int64_t(S.it.mt) * TM + (wave * MF + mf) * 16 + r;
-      const bool ok = kok && tt < S.tr.count;
-      const __bf16* src = ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + S.s * 32 + g * 8
-                             : zero;
-      br[mf] = Run<__bf16>::load_cached(src);
+    for (int h = 0; h < KH; ++h) {
+      const bool kok = st0 + 2 * h + (g >> 1) < nstrips;
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        const int64_t tt = int64_t(S.it.mt) * TM + (wave * MF + mf) * 16 + r;
+        const bool ok = kok && tt < S.tr.count;
+        const __bf16* src =
+            ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + st0 * 16 + h * 32 + g * 8
+               : zero;
+        br[h][mf] = Run<__bf16>::load_cached(src);
+      }
     }
   };
   auto store_w = [&](const u32x4_t (&wr)[NWL], int buf) __attribute__((always_inline)) {
@@ -260,22 +278,27 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   };
 
   // Per-lane offset of its transposing read inside a tile (see the header).
-  const int lane_off = (g >> 1) * (b_in * 16) + (8 * (g & 1) + (r >> 2)) * 8 + ((r & 3) >> 1) * 128 + (r & 1) * 4;
+  const int lane_off = (g >> 1) * strip_elems + (8 * (g & 1) + (r >> 2)) * 8 + ((r & 3) >> 1) * 128 + (r & 1) * 4;
   f32x4_t acc[MF][NFI];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
     for (int f = 0; f < NFI; ++f) acc[mf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Step& S, const Run<__bf16> (&br)[MF], int buf) __attribute__((always_inline)) {
+  auto compute = [&](const Step& S, const Run<__bf16> (&br)[KH][MF], int buf) __attribute__((always_inline)) {
     if (!S.live) return;
-    __bf16* t = lds + buf * tile_elems + lane_off;
+    // No branch between the reads and the multiplies, so the reads of later
+    // fragments overlap the multiplies of earlier ones.  Fragments past nfi
+    // (NFI rounded up) re-read the last one and are never stored.
 #pragma unroll
-    for (int f = 0; f < NFI; ++f) {
-      if (f < nfi) {
-        const Run<__bf16> a = lds_run_tr(t + f * 256, t + f * 256 + 32);
+    for (int h = 0; h < KH; ++h) {
+      __bf16* t = lds + buf * tile_elems + 2 * h * strip_elems + lane_off;
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf) acc[mf][f] = mma(a, br[mf], acc[mf][f]);
+      for (int f = 0; f < NFI; ++f) {
+        const int fc = f < nfi ? f : nfi - 1;
+        const Run<__bf16> a = lds_run_tr(t + fc * 256, t + fc * 256 + 32);
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) acc[mf][f] = mma(a, br[h][mf], acc[mf][f]);
       }
     }
     if (!S.last) return;
@@ -300,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
 
   // ---- software pipeline over NSET register sets
   u32x4_t wr[NSET][NWL];
-  Run<__bf16> br[NSET][MF];
+  Run<__bf16> br[NSET][KH][MF];
   Step S[NSET];
 #pragma unroll
   for (int s = 0; s < NSET - 1; ++s) {
@@ -346,54 +369,69 @@ struct BwdWeightParams {
   const __bf16* X;    // M x ldx
   const __bf16* dY;   // M x ldy
   void* dW;           // packed (Tout)
+  float* ws;          // ntg > 1: [type group][k][packed block] fp32 partial diagonal blocks
   int64_t M, ldx, ldy;
   int32_t q, b_in, b_out, law, kind, off_mod_q;
   int64_t rows_per_type;
   int32_t nchunks;    // column chunks of NC strips per output group
+  int32_t ndin;       // row chunks of 64 NFW input features per block
+  int32_t ntg;        // type groups (Q_q only): partial diagonal blocks, added by a second kernel
   int32_t ldsx, ldsy; // LDS row pitch (elements) of the X and dY tiles
 };
 
 // Accumulator slots: Q_q uses slot 0 for block (i, k) of the current type and
 // slot 1 for the diagonal block (k, k); Q2 x Q2 uses slot j for block (j, k).
+// A step is 64 tokens of one type i and one input group j (two MFMA k-steps).
 template <typename Tout, bool QQ, int NFW, int NC, int NSET>
 __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   constexpr int NTHR = 256;
+  constexpr int TK = 64;                         // tokens per step
+  constexpr int DIN = 64 * NFW;                  // input features per workgroup
   constexpr int NSLOT = QQ ? 2 : 4;
-  constexpr int NXL = NFW;   // 16-byte loads per thread of the 32 x b_in X tile (b_in <= 64 NFW)
-  constexpr int NYL = (64 * NC + NTHR - 1) / NTHR;
+  constexpr int XCPR = DIN / 8;                  // 16-byte chunks of an X tile row
+  constexpr int NXL = TK * XCPR / NTHR;          // X loads per thread
+  constexpr int NYL = (TK * 2 * NC + NTHR - 1) / NTHR;
+  static_assert((TK * XCPR) % NTHR == 0, "X tile");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem);
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int g = lane >> 4, r = lane & 15;
   const int b_in = P.b_in, q = P.q;
-  const int nfi = b_in / 16;
   const int nstrips = P.b_out / 16;
-  const int xcpr = b_in / 8;                      // 16-byte chunks of a tile row
-  const int x_chunks = 32 * xcpr;
-  const int x_elems = 32 * P.ldsx, y_elems = 32 * P.ldsy;
+  const int x_elems = TK * P.ldsx, y_elems = TK * P.ldsy;
   const int buf_elems = x_elems + y_elems;
   const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
   Tout* __restrict__ dW = static_cast<Tout*>(P.dW);
   const int64_t blk = int64_t(b_in) * P.b_out;
 
-  // ---- (output group k, column chunk c): each XCD takes a contiguous run
-  const int64_t n_items = int64_t(q) * P.nchunks;
+  // ---- item (output group k, type group tg, column chunk c, row chunk dc);
+  // each XCD takes a contiguous run, so one group's items share its L2
+  const int64_t n_items = int64_t(q) * P.ntg * P.nchunks * P.ndin;
   const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
   const int64_t xlo = n_items * xcd / kNumXcd, xhi = n_items * (xcd + 1) / kNumXcd;
-  const int64_t item = xlo + slot;
+  int64_t item = xlo + slot;
   if (item >= xhi) return;
-  const int k = int(item / P.nchunks), c = int(item - int64_t(k) * P.nchunks);
+  const int dc = int(item % P.ndin);
+  item /= P.ndin;
+  const int c = int(item % P.nchunks);
+  item /= P.nchunks;
+  const int tg = int(item % P.ntg);
+  const int k = int(item / P.ntg);
   const int col0 = c * NC * 16;   // first column of the chunk inside group k
+  const int row0 = dc * DIN;      // first input feature of the chunk inside a block
+  const int t_begin = tg * q / P.ntg, t_end = (tg + 1) * q / P.ntg;
+  const TypeMap tmap(P.kind, q, P.off_mod_q, P.M, P.rows_per_type);
 
-  // steps: every type i, every 32-token chunk of it (at least one, so that a
-  // type without rows still writes its zero block), every j with (i, j, k) in T
+  // steps: every type of the group, every 64-token chunk of it (at least one,
+  // so that a type without rows still writes its zero block), every j with
+  // (i, j, k) in T
   auto chunks_of = [&](int i) __attribute__((always_inline)) {
-    const TypeRows t = type_rows(P.kind, q, P.off_mod_q, P.M, P.rows_per_type, i);
-    return t.count > 0 ? int((t.count + 31) / 32) : 1;
+    const int64_t n = tmap.rows(i).count;
+    return n > 0 ? int((n + TK - 1) / TK) : 1;
   };
   int n_steps = 0;
-  for (int i = 0; i < q; ++i) {
+  for (int i = t_begin; i < t_end; ++i) {
     int gl[4];
     n_steps += chunks_of(i) * device_leaf_groups(P.law, i, k, gl);
   }
@@ -403,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     bool live, flush0;   // flush0 (Q_q): the type's last step, block (i, k) done
     TypeRows tr;
   };
-  int cur_i = 0, cur_tc = 0, cur_jx = 0, issued = 0;
+  int cur_i = t_begin, cur_tc = 0, cur_jx = 0, issued = 0;
   auto setup = [&](Step& S) __attribute__((always_inline)) {
     S.live = issued < n_steps;
     int gl[4];
@@ -414,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     S.j = gl[cur_jx];
     S.slot = QQ ? (S.j == k ? 1 : 0) : S.j;
     S.flush0 = QQ && S.live && cur_i != k && cur_tc == nch - 1 && cur_jx == ng - 1;
-    S.tr = type_rows(P.kind, q, P.off_mod_q, P.M, P.rows_per_type, cur_i);
+    S.tr = tmap.rows(cur_i);
     if (S.live) {
       ++issued;
       if (++cur_jx == ng) {
@@ -431,18 +469,19 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
 #pragma unroll
     for (int l = 0; l < NXL; ++l) {
       const int ch = l * NTHR + int(threadIdx.x);
-      const int tk = ch / xcpr, cc = ch - tk * xcpr;
-      const int64_t tt = int64_t(S.tc) * 32 + tk;
-      const bool ok = ch < x_chunks && tt < S.tr.count;
-      const __bf16* src = ok ? P.X + (S.tr.first + tt * S.tr.stride) * P.ldx + int64_t(S.j) * b_in + cc * 8 : zero;
+      const int tk = ch / XCPR, cc = ch - tk * XCPR;
+      const int64_t tt = int64_t(S.tc) * TK + tk;
+      const bool ok = tt < S.tr.count && row0 + cc * 8 < b_in;
+      const __bf16* src =
+          ok ? P.X + (S.tr.first + tt * S.tr.stride) * P.ldx + int64_t(S.j) * b_in + row0 + cc * 8 : zero;
       xr[l] = *reinterpret_cast<const u32x4_t*>(src);
     }
 #pragma unroll
     for (int l = 0; l < NYL; ++l) {
       const int ch = l * NTHR + int(threadIdx.x);
       const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
-      const int64_t tt = int64_t(S.tc) * 32 + tk;
-      const bool ok = ch < 64 * NC && tt < S.tr.count && col0 + cc * 8 < P.b_out;
+      const int64_t tt = int64_t(S.tc) * TK + tk;
+      const bool ok = ch < TK * 2 * NC && tt < S.tr.count && col0 + cc * 8 < P.b_out;
       const __bf16* src =
           ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + col0 + cc * 8 : zero;
       yr[l] = *reinterpret_cast<const u32x4_t*>(src);
@@ -453,14 +492,14 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
 #pragma unroll
     for (int l = 0; l < NXL; ++l) {
       const int ch = l * NTHR + int(threadIdx.x);
-      const int tk = ch / xcpr, cc = ch - tk * xcpr;
-      if (ch < x_chunks) *reinterpret_cast<u32x4_t*>(base + tk * P.ldsx + cc * 8) = xr[l];
+      const int tk = ch / XCPR, cc = ch - tk * XCPR;
+      *reinterpret_cast<u32x4_t*>(base + tk * P.ldsx + cc * 8) = xr[l];
     }
 #pragma unroll
     for (int l = 0; l < NYL; ++l) {
       const int ch = l * NTHR + int(threadIdx.x);
       const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
-      if (ch < 64 * NC) *reinterpret_cast<u32x4_t*>(base + x_elems + tk * P.ldsy + cc * 8) = yr[l];
+      if (ch < TK * 2 * NC) *reinterpret_cast<u32x4_t*>(base + x_elems + tk * P.ldsy + cc * 8) = yr[l];
     }
   };
 
@@ -472,21 +511,35 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
 #pragma unroll
       for (int b = 0; b < NC; ++b) acc[s][a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Transposing-read offsets: token 8g + r/4, features / columns 4 (r mod 4).
+  // Transposing-read offsets: token 8g + r/4, features / columns 4 (r mod 4);
+  // a wave's row fragments past the block re-read fragment 0 (never stored).
   const int xoff = (8 * g + (r >> 2)) * P.ldsx + 4 * (r & 3);
   const int yoff = (8 * g + (r >> 2)) * P.ldsy + 4 * (r & 3);
+  int fofs[NFW];
+  bool fok[NFW];
+#pragma unroll
+  for (int a = 0; a < NFW; ++a) {
+    const int f = wave + 4 * a;
+    fok[a] = row0 + f * 16 < b_in;
+    fofs[a] = fok[a] ? f * 16 : 0;
+  }
 
-  auto flush = [&](int sl, int j) __attribute__((always_inline)) {
-    Tout* blkp = dW + (int64_t(j) * q + k) * blk;
+  // Store slot sl as block (j, k): lane (column r, g) holds rows 4g .. 4g+3 of
+  // each of its fragments, half of a packed run.  To the workspace when the
+  // block is a partial sum over this workgroup's types.
+  auto flush = [&](int sl, int j, bool partial) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < NFW; ++a) {
-      const int f = wave + 4 * a;
-      if (f < nfi) {
-        const int row = f * 16 + 4 * g;
+      if (fok[a]) {
+        const int row = row0 + fofs[a] + 4 * g;
 #pragma unroll
         for (int b = 0; b < NC; ++b) {
           const int st = c * NC + b;
-          if (st < nstrips) store4(blkp + int64_t(st) * (b_in * 16) + (row >> 3) * 128 + r * 8 + (row & 7), acc[sl][a][b]);
+          if (st < nstrips) {
+            const int64_t o = int64_t(st) * (b_in * 16) + (row >> 3) * 128 + r * 8 + (row & 7);
+            if (partial) store4(P.ws + (int64_t(tg) * q + k) * blk + o, acc[sl][a][b]);
+            else store4(dW + (int64_t(j) * q + k) * blk + o, acc[sl][a][b]);
+          }
         }
       }
     }
@@ -495,29 +548,33 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   auto compute = [&](const Step& S, int buf) __attribute__((always_inline)) {
     if (!S.live) return;
     __bf16* base = lds + buf * buf_elems;
-    Run<__bf16> bv[NC];
+    Run<__bf16> bv[2][NC], av[2][NFW];
 #pragma unroll
-    for (int b = 0; b < NC; ++b) {
-      __bf16* p = base + x_elems + yoff + b * 16;
-      bv[b] = lds_run_tr(p, p + 4 * P.ldsy);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < NC; ++b) {
+        __bf16* p = base + x_elems + yoff + 32 * h * P.ldsy + b * 16;
+        bv[h][b] = lds_run_tr(p, p + 4 * P.ldsy);
+      }
+#pragma unroll
+      for (int a = 0; a < NFW; ++a) {
+        __bf16* p = base + xoff + 32 * h * P.ldsx + fofs[a];
+        av[h][a] = lds_run_tr(p, p + 4 * P.ldsx);
+      }
     }
 #pragma unroll
-    for (int a = 0; a < NFW; ++a) {
-      const int f = wave + 4 * a;
-      if (f < nfi) {
-        __bf16* p = base + xoff + f * 16;
-        const Run<__bf16> av = lds_run_tr(p, p + 4 * P.ldsx);
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      if (S.slot == sl) {
 #pragma unroll
-        for (int sl = 0; sl < NSLOT; ++sl) {
-          if (S.slot == sl) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int b = 0; b < NC; ++b) acc[sl][a][b] = mma(av, bv[b], acc[sl][a][b]);
-          }
-        }
+          for (int a = 0; a < NFW; ++a)
+#pragma unroll
+            for (int b = 0; b < NC; ++b) acc[sl][a][b] = mma(av[h][a], bv[h][b], acc[sl][a][b]);
       }
     }
     if (QQ && S.flush0) {
-      flush(0, S.i);
+      flush(0, S.i, false);
 #pragma unroll
       for (int a = 0; a < NFW; ++a)
 #pragma unroll
@@ -537,7 +594,7 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
     for (int s = 0; s < NSET; ++s) {
-      const int buf = s & 1;
+      const int buf = s & 1;   // NSET is even, so set parity = step parity
       store_tiles(xr[s], yr[s], buf);
       __syncthreads();
       compute(S[s], buf);
@@ -547,10 +604,26 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     }
   }
   if (QQ) {
-    flush(1, k);
+    // the diagonal block: a type group's partial sum, or the whole of it
+    flush(1, k, P.ntg > 1);
   } else {
 #pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl) flush(sl, sl);
+    for (int sl = 0; sl < NSLOT; ++sl) flush(sl, sl, false);
+  }
+}
+
+// Add the type groups' partial diagonal blocks (Q_q) into dW.
+template <typename Tout>
+__global__ __launch_bounds__(256) void bwd_weight_reduce_kernel(BwdWeightParams P) {
+  const int64_t blk = int64_t(P.b_in) * P.b_out;
+  const int64_t n4 = int64_t(P.q) * blk / 4;
+  Tout* __restrict__ dW = static_cast<Tout*>(P.dW);
+  for (int64_t e4 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e4 < n4; e4 += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t e = e4 * 4;
+    const int64_t k = e / blk, o = e - k * blk;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    for (int tg = 0; tg < P.ntg; ++tg) s += *reinterpret_cast<const f32x4_t*>(P.ws + int64_t(tg) * P.q * blk + e);
+    store4(dW + (k * P.q + k) * blk + o, s);
   }
 }
 
@@ -561,24 +634,78 @@ int lds_pitch(int cols) {
   return cols + pad;
 }
 
-// Blocks per part of a split data-gradient leaf.  Q_q's own-group leaf has q
-// blocks and every other leaf one; parts of four keep the work items within a
-// factor of four of each other (Q2 x Q2 leaves, at most four blocks, never split).
-constexpr int kDataSplit = 4;
-
 int64_t max_rows_per_type(const aa_plan_s& plan, int64_t M) {
   if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
   return (M + plan.q - 1) / plan.q;
 }
 
+// Blocks per part of a split data-gradient leaf.  Q_q's own-group leaf has q
+// blocks and every other leaf one.  Parts of R blocks keep work items within a
+// factor R of each other; R follows the average work per workgroup (units /
+// 512, between 2 and 4), so that small problems are not held up by a few long
+// items.  Q2 x Q2 leaves (at most four blocks) are never split.
+struct DataSplit {
+  int mf, mt_count, R, nparts;
+  int64_t units;
+};
+DataSplit data_split(const aa_plan_s& plan, int64_t M) {
+  DataSplit d;
+  const int nfi = int(plan.b_in / 16);
+  const int64_t rpt = max_rows_per_type(plan, M);
+  d.mf = (rpt > 64 && nfi <= 4) ? 2 : 1;
+  d.mt_count = int((rpt + 64 * d.mf - 1) / (64 * d.mf));
+  if (d.mt_count < 1) d.mt_count = 1;
+  const int nb = plan.law == AA_LAW_QQ ? 2 * plan.q - 1 : 9;
+  d.units = int64_t(plan.q) * d.mt_count * nb;
+  const int64_t per = (d.units + 256) / 512;
+  d.R = plan.law == AA_LAW_QQ ? int(per < 2 ? 2 : (per > 4 ? 4 : per)) : 4;
+  const int len = plan.law == AA_LAW_QQ ? plan.q : 4;
+  d.nparts = len > d.R ? (len + d.R - 1) / d.R : 1;
+  return d;
+}
+
+// Work split of the weight gradient: NFW row fragments per wave (64 NFW input
+// features per workgroup), NC strips per column chunk, and for Q_q type groups
+// whose partial diagonal blocks a second kernel adds (only while the other
+// splits leave fewer than 384 workgroups, and at most q / 2 groups, which keeps
+// the partial sums within the size of dW).
+struct WeightShape {
+  bool qq;
+  int nfw, nc, nchunks, ndin, ntg;
+};
+WeightShape weight_shape(const aa_plan_s& plan) {
+  WeightShape s;
+  s.qq = plan.law == AA_LAW_QQ;
+  const int nstrips = int(plan.b_out / 16);
+  // Q_q: 128 features by 2 strips, or 64 by 4 (the register budget of two
+  // workgroups per CU); Q2 x Q2 keeps four accumulator slots, so 2 strips.
+  auto nc_of = [&](int nfw) { return s.qq && nfw == 1 ? 4 : 2; };
+  auto items = [&](int nfw) {
+    const int nc = nc_of(nfw);
+    return int64_t(plan.q) * ((nstrips + nc - 1) / nc) * ((plan.b_in + 64 * nfw - 1) / (64 * nfw));
+  };
+  s.nfw = plan.b_in >= 128 && items(2) >= 128 ? 2 : 1;
+  s.nc = nc_of(s.nfw);
+  s.nchunks = (nstrips + s.nc - 1) / s.nc;
+  s.ndin = int((plan.b_in + 64 * s.nfw - 1) / (64 * s.nfw));
+  s.ntg = 1;
+  while (s.qq && items(s.nfw) * s.ntg < 384 && s.ntg * 2 <= plan.q / 2) s.ntg *= 2;
+  return s;
+}
+
+
 }  // namespace
 
 size_t bwd_data_workspace_bytes(const aa_plan_s& plan, int64_t M) {
-  const int R = kDataSplit;
-  const int len = plan.law == AA_LAW_QQ ? plan.q : 4;
-  if (len <= R) return 0;
-  const int nparts = (len + R - 1) / R;
-  return size_t(nparts) * size_t(M) * size_t(plan.b_in) * sizeof(float);
+  const DataSplit d = data_split(plan, M);
+  if (d.nparts == 1) return 0;
+  return size_t(d.nparts) * size_t(M) * size_t(plan.b_in) * sizeof(float);
+}
+
+size_t bwd_weight_workspace_bytes(const aa_plan_s& plan) {
+  const WeightShape sh = weight_shape(plan);
+  if (sh.ntg == 1) return 0;
+  return size_t(sh.ntg) * size_t(plan.q) * size_t(plan.b_in) * size_t(plan.b_out) * sizeof(float);
 }
 
 aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W, void* dX, int64_t M,
@@ -598,22 +725,25 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
   P.kind = plan.type_kind;
   P.off_mod_q = int32_t(pos_offset % plan.q);
   P.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
-  P.R = kDataSplit;
+  const DataSplit dsp = data_split(plan, M);
+  P.R = dsp.R;
   P.nb = plan.law == AA_LAW_QQ ? 2 * plan.q - 1 : 9;
-  P.ksb = int32_t((plan.b_out + 31) / 32);
   const int nfi = int(plan.b_in / 16);
-  const int64_t rpt = max_rows_per_type(plan, M);
-  const int MF = (rpt > 64 && nfi <= 8) ? 2 : 1;
-  P.mt_count = int32_t((rpt + 64 * MF - 1) / (64 * MF));
-  P.units = int64_t(plan.q) * P.mt_count * P.nb;
-  const size_t lds = size_t(2) * 64 * plan.b_in;
+  const int KS = nfi <= 8 ? 4 : 2;   // strips per step
+  P.ksb = int32_t((plan.b_out / 16 + KS - 1) / KS);
+  const int MF = dsp.mf;
+  P.mt_count = dsp.mt_count;
+  P.units = dsp.units;
+  if (P.units >= (int64_t(1) << 31)) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_data: too many rows per type");
+  const size_t lds = size_t(2) * KS * 32 * plan.b_in;
   int grid = device_cu_count() * 2;
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
   const bool f32 = plan.out_dtype == AA_F32;
   auto go = [&](auto nfi_c, auto mf_c, auto nset_c) {
     constexpr int NFIc = decltype(nfi_c)::value, MFc = decltype(mf_c)::value, NS = decltype(nset_c)::value;
-    if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, NS>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, NS>), dim3(grid), dim3(256), lds, stream, P);
+    constexpr int KSc = NFIc <= 8 ? 4 : 2;
+    if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, KSc, NS>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, KSc, NS>), dim3(grid), dim3(256), lds, stream, P);
   };
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
@@ -622,10 +752,11 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
     if (MF == 2) go(C4{}, C2{}, C4{});
     else go(C4{}, C1{}, C4{});
   } else if (nfi <= 8) {
-    if (MF == 2) go(std::integral_constant<int, 8>{}, C2{}, C4{});
-    else go(std::integral_constant<int, 8>{}, C1{}, C4{});
+    go(std::integral_constant<int, 8>{}, C1{}, C4{});
   } else if (nfi <= 16) {
     go(std::integral_constant<int, 16>{}, C1{}, C2{});
+  } else if (nfi <= 24) {
+    go(std::integral_constant<int, 24>{}, C1{}, C2{});
   } else if (nfi <= 32) {
     go(std::integral_constant<int, 32>{}, C1{}, C2{});
   } else {
@@ -633,9 +764,8 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
   }
   aa_status_t st = after_launch(stream, "bwd_data");
   if (st != AA_OK) return st;
-  const int len = plan.law == AA_LAW_QQ ? plan.q : 4;
-  if (len > P.R) {
-    const int nparts = (len + P.R - 1) / P.R;
+  if (dsp.nparts > 1) {
+    const int nparts = dsp.nparts;
     const int64_t n = M * (plan.b_in / 4);
     const int blocks = int(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
     if (f32) hipLaunchKernelGGL((bwd_data_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, P, nparts);
@@ -646,11 +776,13 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
 }
 
 aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
-                              int64_t pos_offset, hipStream_t stream) {
+                              int64_t pos_offset, void* ws, hipStream_t stream) {
+  const WeightShape sh = weight_shape(plan);
   BwdWeightParams P{};
   P.X = static_cast<const __bf16*>(X);
   P.dY = static_cast<const __bf16*>(dY);
   P.dW = dW;
+  P.ws = static_cast<float*>(ws);
   P.M = M;
   P.ldx = plan.d_in;
   P.ldy = plan.d_out;
@@ -661,41 +793,39 @@ aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* 
   P.kind = plan.type_kind;
   P.off_mod_q = int32_t(pos_offset % plan.q);
   P.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
-  const int nfw = int((plan.b_in / 16 + 3) / 4);
-  const bool qq = plan.law == AA_LAW_QQ;
-  const int NC = (qq ? nfw <= 4 : nfw <= 2) ? 2 : 1;
-  P.nchunks = int32_t((plan.b_out / 16 + NC - 1) / NC);
-  P.ldsx = lds_pitch(int(plan.b_in));
-  P.ldsy = lds_pitch(16 * NC);
-  const size_t lds = size_t(2) * 32 * (P.ldsx + P.ldsy) * 2;
-  const int64_t n_items = int64_t(plan.q) * P.nchunks;
+  P.nchunks = sh.nchunks;
+  P.ndin = sh.ndin;
+  P.ntg = sh.ntg;
+  P.ldsx = lds_pitch(64 * sh.nfw);
+  P.ldsy = lds_pitch(16 * sh.nc);
+  const size_t lds = size_t(2) * 64 * (P.ldsx + P.ldsy) * 2;
+  const int64_t n_items = int64_t(plan.q) * sh.ntg * sh.nchunks * sh.ndin;
   const int grid = int((n_items + kNumXcd - 1) / kNumXcd * kNumXcd);
   const bool f32 = plan.out_dtype == AA_F32;
   auto go = [&](auto qq_c, auto nfw_c, auto nc_c) {
     constexpr bool QQc = decltype(qq_c)::value;
     constexpr int NFWc = decltype(nfw_c)::value, NCc = decltype(nc_c)::value;
-    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, QQc, NFWc, NCc, 2>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, QQc, NFWc, NCc, 2>), dim3(grid), dim3(256), lds, stream, P);
+    constexpr int NS = 4;   // six sets measured slower: the weight gradient is bound by L2 reads, not latency
+    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, QQc, NFWc, NCc, NS>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, QQc, NFWc, NCc, NS>), dim3(grid), dim3(256), lds, stream, P);
   };
-  using T = std::true_type;
-  using F = std::false_type;
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
   using C4 = std::integral_constant<int, 4>;
-  using C8 = std::integral_constant<int, 8>;
-  if (plan.b_in > 384) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_weight: input blocks wider than 384 features");
-  if (qq) {
-    if (nfw <= 1) go(T{}, C1{}, C2{});
-    else if (nfw <= 2) go(T{}, C2{}, C2{});
-    else if (nfw <= 4) go(T{}, C4{}, C2{});
-    else go(T{}, C8{}, C1{});
+  if (sh.qq) {
+    if (sh.nfw == 2) go(std::true_type{}, C2{}, C2{});
+    else go(std::true_type{}, C1{}, C4{});
   } else {
-    if (nfw <= 1) go(F{}, C1{}, C2{});
-    else if (nfw <= 2) go(F{}, C2{}, C2{});
-    else if (nfw <= 4) go(F{}, C4{}, C1{});
-    else go(F{}, C8{}, C1{});
+    if (sh.nfw == 2) go(std::false_type{}, C2{}, C2{});
+    else go(std::false_type{}, C1{}, C2{});
   }
-  return after_launch(stream, "bwd_weight");
+  aa_status_t st = after_launch(stream, "bwd_weight");
+  if (st != AA_OK || sh.ntg == 1) return st;
+  const int64_t n4 = int64_t(plan.q) * plan.b_in * plan.b_out / 4;
+  const int blocks = int(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
+  if (f32) hipLaunchKernelGGL((bwd_weight_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, P);
+  else hipLaunchKernelGGL((bwd_weight_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, P);
+  return after_launch(stream, "bwd_weight_reduce");
 }
 
 }  // namespace aa

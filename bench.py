@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
-                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b"])
+                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "backward_qwen3_8b",
+                             "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -84,6 +85,8 @@ def main():
         res = bench_qwen3(args, torch, inp, aa, dev)
     elif args.workload == "qwen3_1p7b":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[6])
+    elif args.workload.startswith("backward_"):
+        res = bench_backward(args, torch, inp, aa, dev, args.workload)
     elif args.workload == "square":
         res = bench_square(args, torch, inp, aa, dev)
     else:
@@ -354,6 +357,101 @@ def bench_projection(args, torch, inp, aa, dev, wl):
                        "type_map": "pos mod q", "input_sets": n_sets},
             "roofline": roofline(per_set, ms), "projection_alone": alone, "dense": dense,
             "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / (ms * 1e-3) / 1e12, 2),
+            "kernel_source": kernel_source_hash()}
+
+
+def bench_backward(args, torch, inp, aa, dev, which):
+    """Gradients of the projection(s): aa_project_bwd_data (dX) and
+    aa_project_bwd_weight (dW) for an upstream gradient dY, bf16 in and out.
+    backward_qwen3_8b: the Qwen3-8B projection (M = 2048, 4096 -> 12288, Q_32).
+    backward_expert: the three projections of the Qwen3-30B-A3B expert FFN
+    (M = 2048, 2048 -> 768 gate and up, 768 -> 2048 down, Q_16), the shape
+    whose forward-plus-gradient the pages report.  A step is dX and dW of
+    every projection; input sets rotate (flushed cache).  Each call's bytes
+    are those of the forward: 2 (M d_in + d_in d_out + M d_out)."""
+    M = 2048
+    if which == "backward_qwen3_8b":
+        q, shapes = 32, [("proj", 4096, 12288)]
+    else:
+        q, shapes = 16, [("gate", 2048, 768), ("up", 2048, 768), ("down", 768, 2048)]
+    plans = {n: aa.aa_plan_create("Qq", q, di, do, "pos_mod", 0, "bf16", "bf16") for n, di, do in shapes}
+    per_set = sum(2 * (2 * M * di + 2 * di * do + 2 * M * do) for _, di, do in shapes)
+    n_sets = args.sets or max(2, math.ceil(1.0e9 / per_set))
+    sets = []
+    for s_ in range(n_sets):
+        st = {}
+        for j, (n, di, do) in enumerate(shapes):
+            base = 1000 * (s_ + 1) + 10 * j
+            W = inp.gaussian((di, do), base + 1, di ** -0.5, torch.bfloat16, dev)
+            nd, nw = aa.aa_project_bwd_workspace(plans[n], M)
+            st[n] = {"X": inp.gaussian((M, di), base + 2, 1.0, torch.bfloat16, dev),
+                     "dY": inp.gaussian((M, do), base + 3, 1.0, torch.bfloat16, dev),
+                     "Wp": aa.pack(plans[n], W),
+                     "dX": torch.empty(M, di, dtype=torch.bfloat16, device=dev),
+                     "dWp": torch.empty(di * do, dtype=torch.bfloat16, device=dev),
+                     "wsd": torch.empty(max(nd, 1), dtype=torch.uint8, device=dev), "nd": nd,
+                     "wsw": torch.empty(max(nw, 1), dtype=torch.uint8, device=dev), "nw": nw}
+            del W
+        sets.append(st)
+    torch.cuda.synchronize()
+    calls = [(n, kind) for n, _, _ in shapes for kind in ("dX", "dW")]
+
+    def step(st, evs=None):
+        for c, (n, kind) in enumerate(calls):
+            if evs is not None:
+                evs[c].record()
+            b = st[n]
+            if kind == "dX":
+                aa.aa_project_bwd_data(plans[n], b["dY"], b["Wp"], b["dX"], None, 0, None, b["wsd"], b["nd"])
+            else:
+                aa.aa_project_bwd_weight(plans[n], b["X"], b["dY"], b["dWp"], None, 0, None, b["wsw"], b["nw"])
+        if evs is not None:
+            evs[len(calls)].record()
+
+    for w in range(args.warmup):
+        step(sets[w % n_sets])
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[_ev(torch) for _ in range(len(calls) + 1)] for _ in range(K)]
+    a, b = _ev(torch), _ev(torch)
+    torch.cuda.synchronize()
+    a.record()
+    for s_ in range(K):
+        step(sets[s_ % n_sets], evs[s_])
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / K
+    dims = {n: (di, do) for n, di, do in shapes}
+    parts = {}
+    for c, (n, kind) in enumerate(calls):
+        ms = sum(e[c].elapsed_time(e[c + 1]) for e in evs) / K
+        di, do = dims[n]
+        parts[f"{n}_{kind}"] = {"ms": round(ms, 5), "roofline": roofline(2 * (M * di + di * do + M * do), ms),
+                                "exec_tflops": round(exec_flops(M, di, do, "Qq", q) / (ms * 1e-3) / 1e12, 2)}
+    dense_flops = sum(2 * 2.0 * M * di * do for _, di, do in shapes)
+    dense = None
+    if not args.no_dense:
+        t_total = 0.0
+        dense = {"kind": "torch.mm bf16 (hipBLASLt), dY W^T and X^T dY, hot cache, same run"}
+        for n, di, do in shapes:
+            b0 = sets[0][n]
+            Wd = inp.gaussian((di, do), 997, di ** -0.5, torch.bfloat16, dev)
+            t_dx = dense_timer(torch, lambda: torch.mm(b0["dY"], Wd.t()))
+            t_dw = dense_timer(torch, lambda: torch.mm(b0["X"].t(), b0["dY"]))
+            dense[f"{n}_dX_ms"], dense[f"{n}_dW_ms"] = round(t_dx, 5), round(t_dw, 5)
+            t_total += t_dx + t_dw
+            del Wd
+        dense["step_ms"] = round(t_total, 5)
+        dense["speedup_step"] = round(t_total / ms_step, 3)
+    big = max(parts.items(), key=lambda kv: kv[1]["ms"])
+    return {"metric": f"dense-equiv TFLOP/s + % roofline, {which} (dX and dW of each projection) bf16",
+            "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": which, "M": M, "q": q, "law": "Qq", "type_map": "pos mod q",
+                       "projections": [{"name": n, "d_in": di, "d_out": do} for n, di, do in shapes],
+                       "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
+            "roofline": big[1]["roofline"], "roofline_kernel": big[0], "parts": parts, "dense": dense,
             "kernel_source": kernel_source_hash()}
 
 

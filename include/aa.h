@@ -164,21 +164,24 @@ aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, 
  * elements, the same order as W_packed) are written in the plan's out_dtype.
  * dW_packed is overwritten, not accumulated; every block is written (blocks
  * no row reaches are zero).  Outputs must not overlap inputs.  M, pos_offset
- * and the type map mean what they mean for aa_project_fwd, M == 0 is a no-op
+ * and the type map mean what they mean for aa_project_fwd; M == 0 is a no-op
  * (dW is then not written).
  * Limits of this implementation: in_dtype AA_BF16; AA_TYPES_POS_MOD or
  * AA_TYPES_BLOCK_ROWS (row_types must be NULL; explicit type lists return
  * AA_ERR_UNSUPPORTED); b_in <= 512 for dX and b_in <= 384 for dW.
- * aa_project_bwd_data needs device workspace of at least the size that
- * aa_project_bwd_data_workspace reports for the same plan and M (it may be 0,
- * and workspace may then be NULL); the workspace is caller-owned scratch whose
- * contents are overwritten.  Calls that share a workspace must not overlap. */
-aa_status_t aa_project_bwd_data_workspace(aa_plan_t plan, int64_t M, size_t* bytes);
+ * Workspace: each call needs caller-owned device scratch of at least the size
+ * aa_project_bwd_workspace reports for the same plan and M (data_bytes for
+ * aa_project_bwd_data, weight_bytes for aa_project_bwd_weight; either may be
+ * 0, and the workspace pointer may then be NULL).  Its contents are
+ * overwritten; calls that share a workspace must not overlap in time.  Either
+ * output pointer of aa_project_bwd_workspace may be NULL. */
+aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_bytes, size_t* weight_bytes);
 aa_status_t aa_project_bwd_data(aa_plan_t plan, const void* dY, const void* W_packed, void* dX, int64_t M,
                                 int64_t pos_offset, const int32_t* row_types, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY, void* dW_packed, int64_t M,
-                                  int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
+                                  int64_t pos_offset, const int32_t* row_types, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* A static English name of a status code. */
 const char* aa_status_string(aa_status_t status);

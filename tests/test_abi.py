@@ -142,14 +142,16 @@ def test_gradients_validate_before_launch(lib):
     g = 0x1000000
     p = aa.aa_plan_create("Qq", 8, 1024, 1536)          # b_in 128, b_out 192
     h = p.handle
-    n = ctypes.c_size_t(7)
-    assert lib.aa_project_bwd_data_workspace(h, 100, ctypes.byref(n)) == aa.AA_OK
-    assert n.value == 2 * 100 * 128 * 4                  # q = 8: own-group leaf in two parts of four
-    assert aa.aa_project_bwd_data_workspace(aa.aa_plan_create("Qq", 4, 256, 256), 100) == 0
-    assert aa.aa_project_bwd_data_workspace(aa.aa_plan_create("Q2xQ2", 4, 256, 256), 100) == 0
-    assert lib.aa_project_bwd_data_workspace(None, 100, ctypes.byref(n)) == aa.AA_ERR_INVALID_ARG
-    assert lib.aa_project_bwd_data_workspace(h, -1, ctypes.byref(n)) == aa.AA_ERR_INVALID_ARG
-    ws = 2 * 100 * 128 * 4
+    nd, nw = ctypes.c_size_t(7), ctypes.c_size_t(7)
+    assert lib.aa_project_bwd_workspace(h, 100, ctypes.byref(nd), ctypes.byref(nw)) == aa.AA_OK
+    assert nd.value > 0 and nd.value % (100 * 128 * 4) == 0   # q = 8: the own-group leaf is split
+    assert nw.value % (8 * 128 * 192 * 4) == 0           # whole partial diagonal blocks, if any
+    assert lib.aa_project_bwd_workspace(h, 100, None, None) == aa.AA_OK
+    assert aa.aa_project_bwd_workspace(aa.aa_plan_create("Qq", 2, 256, 256), 100)[0] == 0
+    assert aa.aa_project_bwd_workspace(aa.aa_plan_create("Q2xQ2", 4, 256, 256), 100) == (0, 0)
+    assert lib.aa_project_bwd_workspace(None, 100, None, None) == aa.AA_ERR_INVALID_ARG
+    assert lib.aa_project_bwd_workspace(h, -1, None, None) == aa.AA_ERR_INVALID_ARG
+    ws = nd.value
     # NULL operands, negative M or offset, a short or missing workspace, overlaps
     assert _raw(lib, "aa_project_bwd_data", h, None, 2 * g, 3 * g, 100, 0, None, 4 * g, ws, None) == \
         aa.AA_ERR_INVALID_ARG
@@ -165,22 +167,38 @@ def test_gradients_validate_before_launch(lib):
     assert _raw(lib, "aa_project_bwd_data", h, g, 2 * g, 3 * g, 100, 0, None, 3 * g + 64, ws, None) == \
         aa.AA_ERR_INVALID_ARG
     assert _raw(lib, "aa_project_bwd_data", h, None, None, None, 0, 0, None, None, 0, None) == aa.AA_OK
-    assert _raw(lib, "aa_project_bwd_weight", h, None, 2 * g, 3 * g, 100, 0, None, None) == aa.AA_ERR_INVALID_ARG
-    assert _raw(lib, "aa_project_bwd_weight", h, g, 2 * g, g + 64, 100, 0, None, None) == aa.AA_ERR_INVALID_ARG
-    assert _raw(lib, "aa_project_bwd_weight", h, g, 2 * g, 3 * g, 100, 0, 4 * g, None) == aa.AA_ERR_INVALID_ARG
-    assert _raw(lib, "aa_project_bwd_weight", h, None, None, None, 0, 0, None, None) == aa.AA_OK
+    wsw = max(nw.value, 16)
+    assert _raw(lib, "aa_project_bwd_weight", h, None, 2 * g, 3 * g, 100, 0, None, 4 * g, wsw, None) == \
+        aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_bwd_weight", h, g, 2 * g, g + 64, 100, 0, None, 4 * g, wsw, None) == \
+        aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_bwd_weight", h, g, 2 * g, 3 * g, 100, 0, 4 * g, 5 * g, wsw, None) == \
+        aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_bwd_weight", h, None, None, None, 0, 0, None, None, 0, None) == aa.AA_OK
+    # a plan whose weight gradient splits the types needs its workspace
+    sp = aa.aa_plan_create("Qq", 16, 2048, 768)
+    nws = aa.aa_project_bwd_workspace(sp, 2048)[1]
+    assert nws > 0
+    assert _raw(lib, "aa_project_bwd_weight", sp.handle, g, 2 * g, 3 * g, 64, 0, None, 4 * g, nws - 16, None) == \
+        aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, "aa_project_bwd_weight", sp.handle, g, 2 * g, 3 * g, 64, 0, None, None, nws, None) == \
+        aa.AA_ERR_INVALID_ARG
     # unsupported: fp32 operands, explicit type lists, blocks too wide
     f32 = aa.aa_plan_create("Qq", 4, 256, 256, "pos_mod", 0, "f32", "f32")
-    assert _raw(lib, "aa_project_bwd_weight", f32.handle, g, 2 * g, 3 * g, 8, 0, None, None) == aa.AA_ERR_UNSUPPORTED
+    assert _raw(lib, "aa_project_bwd_weight", f32.handle, g, 2 * g, 3 * g, 8, 0, None, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
     ex = aa.aa_plan_create("Qq", 4, 256, 256, "explicit")
-    assert _raw(lib, "aa_project_bwd_weight", ex.handle, g, 2 * g, 3 * g, 8, 0, 4 * g, None) == aa.AA_ERR_UNSUPPORTED
+    assert _raw(lib, "aa_project_bwd_weight", ex.handle, g, 2 * g, 3 * g, 8, 0, 4 * g, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
     assert _raw(lib, "aa_project_bwd_data", ex.handle, g, 2 * g, 3 * g, 8, 0, 4 * g, None, 0, None) == \
         aa.AA_ERR_UNSUPPORTED
     wide = aa.aa_plan_create("Qq", 2, 1024, 64)          # b_in 512
-    assert _raw(lib, "aa_project_bwd_weight", wide.handle, g, 2 * g, 3 * g, 8, 0, None, None) == aa.AA_ERR_UNSUPPORTED
+    assert _raw(lib, "aa_project_bwd_weight", wide.handle, g, 2 * g, 3 * g, 8, 0, None, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
     # block-row typing still needs q | M
     br = aa.aa_plan_create("Qq", 4, 256, 256, "block_rows")
-    assert _raw(lib, "aa_project_bwd_weight", br.handle, g, 2 * g, 3 * g, 10, 0, None, None) == aa.AA_ERR_SHAPE
+    assert _raw(lib, "aa_project_bwd_weight", br.handle, g, 2 * g, 3 * g, 10, 0, None, None, 0, None) == \
+        aa.AA_ERR_SHAPE
 
 
 def test_last_error_is_thread_local(lib):

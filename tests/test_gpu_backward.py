@@ -52,10 +52,11 @@ def _run(law, q, M, d_in, d_out, out_dt="f32", kind="pos_mod", pos_offset=0, per
     Wp = aa.pack(plan, W)
     dX = torch.full((M, d_in), float("nan"), dtype=TD[out_dt], device=DEV)
     dWp = torch.full((d_in * d_out,), float("nan"), dtype=TD[out_dt], device=DEV)
-    nws = aa.aa_project_bwd_data_workspace(plan, M)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
-    aa.aa_project_bwd_data(plan, dY, Wp, dX, None, pos_offset, None, ws if nws else None, nws)
-    aa.aa_project_bwd_weight(plan, X, dY, dWp, None, pos_offset)
+    nd, nw = aa.aa_project_bwd_workspace(plan, M)
+    wsd = torch.empty(max(nd, 1), dtype=torch.uint8, device=DEV)
+    wsw = torch.empty(max(nw, 1), dtype=torch.uint8, device=DEV)
+    aa.aa_project_bwd_data(plan, dY, Wp, dX, None, pos_offset, None, wsd if nd else None, nd)
+    aa.aa_project_bwd_weight(plan, X, dY, dWp, None, pos_offset, None, wsw if nw else None, nw)
     torch.cuda.synchronize()
     dW = _unpack(plan, dWp)
     torch.cuda.synchronize()
@@ -119,11 +120,12 @@ def test_gradient_adjoint_identity_on_gpu():
     Y = torch.empty(M, d_out, dtype=torch.float32, device=DEV)
     aa.aa_project_fwd(plan, X, Wp, Y)
     dX = torch.empty(M, d_in, dtype=torch.float32, device=DEV)
-    nws = aa.aa_project_bwd_data_workspace(plan, M)
-    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
-    aa.aa_project_bwd_data(plan, dY, Wp, dX, None, 0, None, ws, nws)
+    nd, nw = aa.aa_project_bwd_workspace(plan, M)
+    wsd = torch.empty(max(nd, 1), dtype=torch.uint8, device=DEV)
+    wsw = torch.empty(max(nw, 1), dtype=torch.uint8, device=DEV)
+    aa.aa_project_bwd_data(plan, dY, Wp, dX, None, 0, None, wsd, nd)
     dWp = torch.empty(d_in * d_out, dtype=torch.float32, device=DEV)
-    aa.aa_project_bwd_weight(plan, X, dY, dWp)
+    aa.aa_project_bwd_weight(plan, X, dY, dWp, None, 0, None, wsw, nw)
     dW = _unpack(plan, dWp)
     torch.cuda.synchronize()
     v = float((Y.double() * dY.double()).sum())
