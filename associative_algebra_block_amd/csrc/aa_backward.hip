@@ -140,8 +140,13 @@ struct DItem {
   bool split;   // K(i, j) has more than one part
 };
 
-// The item that contains global unit g.  Units are numbered type by type
-// (then token tile), and inside a type by input group j, then K(i, j).
+// The item that contains global unit g.  Units are numbered type by type,
+// then token tile.  Under Q_q the units of a type come in groups p = 0, 1, ...:
+// part p of the own-group leaf (blocks k in [pR, pR + R)) followed by the
+// one-block leaves (i, j) for j in the same range other than i.  A part and
+// the leaves after it read the same dY blocks dY[rows_i, k], so the second
+// read finds them in L2.  Under Q2 x Q2 the units follow input group j, then
+// K(i, j).
 __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   DItem it;
   // units < 2^31 (checked on the host), so 32-bit divisions
@@ -149,17 +154,40 @@ __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   const int u = int(uint32_t(g) - tmi * uint32_t(P.nb));
   it.i = int(tmi / uint32_t(P.mt_count));
   it.mt = int(tmi - uint32_t(it.i) * uint32_t(P.mt_count));
-  int j, start;
+  const int64_t base = int64_t(tmi) * P.nb;
   if (P.law == AA_LAW_QQ) {
-    j = u < it.i ? u : (u < it.i + P.q ? it.i : u - (P.q - 1));
-    start = j + (j > it.i ? P.q - 1 : 0);
-  } else {
-    j = 0;
-    start = 0;
-    while (j < P.q - 1 && u >= start + klist_len(P.law, P.q, it.i, j)) {
-      start += klist_len(P.law, P.q, it.i, j);
-      ++j;
+    const int q = P.q, R = P.R, i = it.i;
+    const int np = (q + R - 1) / R;
+    auto start = [&](int p) { return 2 * p * R - (i < p * R ? 1 : 0); };
+    int p = u / (2 * R);
+    if (p > np - 1) p = np - 1;
+    if (u < start(p)) --p;
+    else if (p + 1 < np && u >= start(p + 1)) ++p;
+    const int sp = q - p * R < R ? q - p * R : R;
+    const int o = u - start(p);
+    if (o < sp) {   // part p of the own-group leaf
+      it.j = i;
+      it.p = p;
+      it.kofs = p * R;
+      it.nblk = sp;
+      it.split = q > R;
+      it.gu = base + start(p);
+    } else {        // a one-block leaf of the range
+      int j = p * R + (o - sp);
+      if (i >= p * R && i < p * R + sp && j >= i) ++j;
+      it.j = j;
+      it.p = 0;
+      it.kofs = 0;
+      it.nblk = 1;
+      it.split = false;
+      it.gu = base + u;
     }
+    return it;
+  }
+  int j = 0, start = 0;
+  while (j < P.q - 1 && u >= start + klist_len(P.law, P.q, it.i, j)) {
+    start += klist_len(P.law, P.q, it.i, j);
+    ++j;
   }
   const int len = klist_len(P.law, P.q, it.i, j);
   it.j = j;
@@ -167,12 +195,10 @@ __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   it.kofs = it.p * P.R;
   it.nblk = len - it.kofs < P.R ? len - it.kofs : P.R;
   it.split = len > P.R;
-  it.gu = int64_t(tmi) * P.nb + start + it.kofs;
+  it.gu = base + start + it.kofs;
   return it;
 }
 
-// A step covers KS strips (16 KS output features, KS / 2 MFMA k-steps) of one
-// block: its weight tile is KS strips of the packed block, contiguous in HBM.
 template <typename Tout, int NFI, int MF, int KS, int NSET>
 __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   constexpr int NTHR = 256;
@@ -187,9 +213,21 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   const int b_in = P.b_in, q = P.q;
   const int nfi = b_in / 16;
   const int nstrips = P.b_out / 16;
-  const int strip_elems = 16 * b_in;
-  const int tile_elems = KS * strip_elems;  // KS strips of b_in x 16
+  // LDS copy of a tile: the packed octets (8 rows x 16 columns, 256 bytes)
+  // with 64 bytes of padding after each, so that the transposing reads of a
+  // fragment's two octets fall on different banks.
+  constexpr int OP = 160;                   // octet pitch in LDS (elements)
+  const int strip_elems = 16 * b_in;        // in HBM
+  const int lstrip = (b_in / 8) * OP;       // in LDS
+  const int tile_elems = KS * lstrip;       // KS strips of b_in x 16
   const int tile_chunks = 2 * KS * b_in;    // 16-byte chunks of a tile
+  int wofs[NWL];                            // LDS offset of this thread's chunks
+#pragma unroll
+  for (int c = 0; c < NWL; ++c) {
+    const int ch = c * NTHR + int(threadIdx.x);
+    const int st = ch / (2 * b_in), rr = ch - st * (2 * b_in);
+    wofs[c] = st * lstrip + (rr >> 4) * OP + (rr & 15) * 8;
+  }
   const int64_t blk = int64_t(b_in) * P.b_out;
   const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
   Tout* __restrict__ dX = static_cast<Tout*>(P.dX);
@@ -273,12 +311,12 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
 #pragma unroll
     for (int c = 0; c < NWL; ++c) {
       const int ch = c * NTHR + int(threadIdx.x);
-      if (ch < tile_chunks) *reinterpret_cast<u32x4_t*>(lds + buf * tile_elems + ch * 8) = wr[c];
+      if (ch < tile_chunks) *reinterpret_cast<u32x4_t*>(lds + buf * tile_elems + wofs[c]) = wr[c];
     }
   };
 
   // Per-lane offset of its transposing read inside a tile (see the header).
-  const int lane_off = (g >> 1) * strip_elems + (8 * (g & 1) + (r >> 2)) * 8 + ((r & 3) >> 1) * 128 + (r & 1) * 4;
+  const int lane_off = (g >> 1) * lstrip + (8 * (g & 1) + (r >> 2)) * 8 + ((r & 3) >> 1) * OP + (r & 1) * 4;
   f32x4_t acc[MF][NFI];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
@@ -292,11 +330,11 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
     // (NFI rounded up) re-read the last one and are never stored.
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
-      __bf16* t = lds + buf * tile_elems + 2 * h * strip_elems + lane_off;
+      __bf16* t = lds + buf * tile_elems + 2 * h * lstrip + lane_off;
 #pragma unroll
       for (int f = 0; f < NFI; ++f) {
         const int fc = f < nfi ? f : nfi - 1;
-        const Run<__bf16> a = lds_run_tr(t + fc * 256, t + fc * 256 + 32);
+        const Run<__bf16> a = lds_run_tr(t + fc * 2 * OP, t + fc * 2 * OP + 32);
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) acc[mf][f] = mma(a, br[h][mf], acc[mf][f]);
       }
@@ -378,6 +416,12 @@ struct BwdWeightParams {
   int32_t ntg;        // type groups (Q_q only): partial diagonal blocks, added by a second kernel
   int32_t ldsx, ldsy; // LDS row pitch (elements) of the X and dY tiles
 };
+
+// LDS row of token t in a 64-token tile: bits 2 and 3 swapped.  A transposing
+// read takes tokens 8g + 0..3 for lane groups g = 0, 1 together; with a row
+// pitch of an odd multiple of 32 bytes the swap puts those eight tokens on
+// eight different 32-byte bank windows.
+__device__ inline int tile_row(int t) { return t ^ ((((t >> 2) ^ (t >> 3)) & 1) * 12); }
 
 // Accumulator slots: Q_q uses slot 0 for block (i, k) of the current type and
 // slot 1 for the diagonal block (k, k); Q2 x Q2 uses slot j for block (j, k).
@@ -493,13 +537,13 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     for (int l = 0; l < NXL; ++l) {
       const int ch = l * NTHR + int(threadIdx.x);
       const int tk = ch / XCPR, cc = ch - tk * XCPR;
-      *reinterpret_cast<u32x4_t*>(base + tk * P.ldsx + cc * 8) = xr[l];
+      *reinterpret_cast<u32x4_t*>(base + tile_row(tk) * P.ldsx + cc * 8) = xr[l];
     }
 #pragma unroll
     for (int l = 0; l < NYL; ++l) {
       const int ch = l * NTHR + int(threadIdx.x);
       const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
-      if (ch < TK * 2 * NC) *reinterpret_cast<u32x4_t*>(base + x_elems + tk * P.ldsy + cc * 8) = yr[l];
+      if (ch < TK * 2 * NC) *reinterpret_cast<u32x4_t*>(base + x_elems + tile_row(tk) * P.ldsy + cc * 8) = yr[l];
     }
   };
 
@@ -511,10 +555,12 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
 #pragma unroll
       for (int b = 0; b < NC; ++b) acc[s][a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Transposing-read offsets: token 8g + r/4, features / columns 4 (r mod 4);
-  // a wave's row fragments past the block re-read fragment 0 (never stored).
-  const int xoff = (8 * g + (r >> 2)) * P.ldsx + 4 * (r & 3);
-  const int yoff = (8 * g + (r >> 2)) * P.ldsy + 4 * (r & 3);
+  // Transposing-read offsets: token 8g + r/4 (and + 4), features / columns
+  // 4 (r mod 4), at the token's permuted row; a wave's row fragments past the
+  // block re-read fragment 0 (never stored).
+  const int trow = tile_row(8 * g + (r >> 2));   // = 16 (g / 2) + 4 (g mod 2) + r / 4; token + 4 is 8 rows on
+  const int xoff = trow * P.ldsx + 4 * (r & 3);
+  const int yoff = trow * P.ldsy + 4 * (r & 3);
   int fofs[NFW];
   bool fok[NFW];
 #pragma unroll
@@ -554,12 +600,12 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
 #pragma unroll
       for (int b = 0; b < NC; ++b) {
         __bf16* p = base + x_elems + yoff + 32 * h * P.ldsy + b * 16;
-        bv[h][b] = lds_run_tr(p, p + 4 * P.ldsy);
+        bv[h][b] = lds_run_tr(p, p + 8 * P.ldsy);
       }
 #pragma unroll
       for (int a = 0; a < NFW; ++a) {
         __bf16* p = base + xoff + 32 * h * P.ldsx + fofs[a];
-        av[h][a] = lds_run_tr(p, p + 4 * P.ldsx);
+        av[h][a] = lds_run_tr(p, p + 8 * P.ldsx);
       }
     }
 #pragma unroll
@@ -735,7 +781,7 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
   P.mt_count = dsp.mt_count;
   P.units = dsp.units;
   if (P.units >= (int64_t(1) << 31)) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_data: too many rows per type");
-  const size_t lds = size_t(2) * KS * 32 * plan.b_in;
+  const size_t lds = size_t(2) * KS * (plan.b_in / 8) * 160 * 2;
   int grid = device_cu_count() * 2;
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
   const bool f32 = plan.out_dtype == AA_F32;
