@@ -101,9 +101,13 @@ def _ev(torch):
 
 
 def kernel_source_hash():
-    p = os.path.join(HERE, "associative_algebra_block_amd", "csrc", "aa_kernels.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources (aa_kernels.hip and the device
+    header it includes): stored traffic figures are used only while it matches."""
+    h = hashlib.sha256()
+    for name in ("aa_kernels.hip", "aa_device.h"):
+        with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel_key):

@@ -32,8 +32,13 @@ COPY_BYTES = 1 << 30   # bench.py --calibration-copy copies 2^28 int32
 
 
 def kernel_source_hash():
-    with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", "aa_kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernels' sources (aa_kernels.hip and the device
+    header it includes): stored traffic figures are used only while it matches."""
+    h = hashlib.sha256()
+    for name in ("aa_kernels.hip", "aa_device.h"):
+        with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _db(d):
@@ -90,7 +95,7 @@ def main():
     ks = kernel_stats(a.trace)
     lines = [f"# Kernel trace: {a.name}", "",
              f"Command (run from /tmp with TMPDIR=/tmp): `{a.cmd_trace}`", "",
-             f"Kernel source (aa_kernels.hip) sha256[:16]: `{src}`", "",
+             f"Forward kernel sources (aa_kernels.hip, aa_device.h) sha256[:16]: `{src}`", "",
              "| kernel | grid (threads) | calls | avg us | min us | max us | % of GPU time |",
              "|---|---|---|---|---|---|---|"]
     for k in ks:
@@ -114,7 +119,7 @@ def main():
         lines = [f"# HBM traffic per launch: {a.name}", "",
                  f"Commands (run from /tmp with TMPDIR=/tmp): `{a.cmd_pmc.replace('PMC', 'FETCH_SIZE')}` and "
                  f"`{a.cmd_pmc.replace('PMC', 'WRITE_SIZE')}`", "",
-                 f"Kernel source (aa_kernels.hip) sha256[:16]: `{src}`", "",
+                 f"Forward kernel sources (aa_kernels.hip, aa_device.h) sha256[:16]: `{src}`", "",
                  f"Calibration: a 1 GiB device copy (`{short(cname, 60)}`, its largest dispatches) reads FETCH_SIZE = {fe[cname]:.0f} KiB "
                  f"and WRITE_SIZE = {wr[cname]:.0f} KiB per launch, so bytes = FETCH_SIZE x 1024 x {f_fac:.4f} "
                  f"and WRITE_SIZE x 1024 x {w_fac:.4f}.", "",
