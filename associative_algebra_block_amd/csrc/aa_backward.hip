@@ -130,23 +130,29 @@ struct BwdDataParams {
   int32_t R;          // blocks per part of a split leaf
   int32_t nb;         // block products per type: 2q - 1 (Q_q) or 9
   int32_t ksb;        // steps (KS strips) per block
+  int32_t pair;       // Q_q items carry their one-block leaves (see DItem)
   int64_t units;      // q * mt_count * nb
 };
 
 // A work item: blocks kofs .. kofs + nblk - 1 of K(i, j) for token tile mt.
+// Under Q_q an item also carries the one-block leaves (i, k) for the blocks k
+// of its range other than i ("pairs"): dY[rows_i, k] feeds both W_ik (the
+// own-group sum) and W_kk (input group k of the same rows), so it is read once.
 struct DItem {
   int64_t gu;   // global index of its first unit
+  int nu;       // units (block products) it covers
   int i, mt, j, p, kofs, nblk;
   bool split;   // K(i, j) has more than one part
 };
 
 // The item that contains global unit g.  Units are numbered type by type,
-// then token tile.  Under Q_q the units of a type come in groups p = 0, 1, ...:
-// part p of the own-group leaf (blocks k in [pR, pR + R)) followed by the
-// one-block leaves (i, j) for j in the same range other than i.  A part and
-// the leaves after it read the same dY blocks dY[rows_i, k], so the second
-// read finds them in L2.  Under Q2 x Q2 the units follow input group j, then
-// K(i, j).
+// then token tile.  Under Q_q a type's units come in groups p = 0, 1, ...:
+// the blocks k in [pR, pR + R) of the own-group leaf and the one-block leaves
+// of the same range, 2R units (one fewer when the range holds i).  With pairs
+// one group is one item; without (wide blocks, whose two accumulator sets
+// would not fit the registers) the part and each one-block leaf are items of
+// their own, numbered side by side.  Under Q2 x Q2 the units follow input
+// group j, then K(i, j).
 __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   DItem it;
   // units < 2^31 (checked on the host), so 32-bit divisions
@@ -165,14 +171,15 @@ __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
     else if (p + 1 < np && u >= start(p + 1)) ++p;
     const int sp = q - p * R < R ? q - p * R : R;
     const int o = u - start(p);
-    if (o < sp) {   // part p of the own-group leaf
+    if (P.pair || o < sp) {   // the group (pairs), or part p of the own-group leaf
       it.j = i;
       it.p = p;
       it.kofs = p * R;
       it.nblk = sp;
       it.split = q > R;
       it.gu = base + start(p);
-    } else {        // a one-block leaf of the range
+      it.nu = P.pair ? 2 * sp - (i >= p * R && i < p * R + sp ? 1 : 0) : sp;
+    } else {                  // without pairs: a one-block leaf of the range
       int j = p * R + (o - sp);
       if (i >= p * R && i < p * R + sp && j >= i) ++j;
       it.j = j;
@@ -181,6 +188,7 @@ __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
       it.nblk = 1;
       it.split = false;
       it.gu = base + u;
+      it.nu = 1;
     }
     return it;
   }
@@ -196,14 +204,16 @@ __device__ inline DItem ditem_at(const BwdDataParams& P, int64_t g) {
   it.nblk = len - it.kofs < P.R ? len - it.kofs : P.R;
   it.split = len > P.R;
   it.gu = base + start + it.kofs;
+  it.nu = it.nblk;
   return it;
 }
 
-template <typename Tout, int NFI, int MF, int KS, int NSET>
+template <typename Tout, int NFI, int MF, int KS, int NSET, bool PAIR>
 __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   constexpr int NTHR = 256;
   constexpr int TM = 64 * MF;
   constexpr int KH = KS / 2;                        // MFMA k-steps per step
+  constexpr int NT = PAIR ? 2 : 1;                  // weight tiles per step
   constexpr int NWL = (32 * KS * NFI + NTHR - 1) / NTHR;   // 16-byte weight loads per thread
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem);
@@ -240,12 +250,12 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   const int64_t lo = xlo + (xhi - xlo) * slot / S8, hi = xlo + (xhi - xlo) * (slot + 1) / S8;
   if (lo >= hi) return;
   DItem first = ditem_at(P, lo);
-  if (first.gu < lo) first = ditem_at(P, first.gu + first.nblk);
+  if (first.gu < lo) first = ditem_at(P, first.gu + first.nu);
   if (first.gu >= hi) return;
   int n_steps = 0;
   for (DItem it = first;;) {
     n_steps += it.nblk * P.ksb;
-    const int64_t nx = it.gu + it.nblk;
+    const int64_t nx = it.gu + it.nu;
     if (nx >= hi || nx >= P.units) break;
     it = ditem_at(P, nx);
   }
@@ -254,6 +264,8 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
     DItem it;
     int m, s;          // block of the item, k-step of the block
     bool live, last;   // last: the item's final step
+    bool pair;         // PAIR: block k != i, whose W_kk product goes to dX[rows, k]
+    bool blk_last;     // the block's final step
     TypeRows tr;
   };
   // Cursor of the next step to request.
@@ -265,6 +277,8 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
     S.m = cur_m;
     S.s = cur_s;
     S.last = S.live && cur_m == cur_it.nblk - 1 && cur_s == P.ksb - 1;
+    S.blk_last = S.live && cur_s == P.ksb - 1;
+    S.pair = PAIR && cur_it.kofs + cur_m != cur_it.i;
     S.tr = tmap.rows(cur_it.i);
     if (S.live) {
       ++issued;
@@ -272,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
         cur_s = 0;
         if (++cur_m == cur_it.nblk) {
           cur_m = 0;
-          const int64_t nx = cur_it.gu + cur_it.nblk;
+          const int64_t nx = cur_it.gu + cur_it.nu;
           if (issued < n_steps) cur_it = ditem_at(P, nx);
         }
       }
@@ -281,17 +295,22 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
 
   // ---- loads of one step: the weight tile (KS strips of block (j, k); past
   // the block's last strip, zeros) and each lane's dY runs.
-  auto load = [&](const Step& S, u32x4_t (&wr)[NWL], Run<__bf16> (&br)[KH][MF]) __attribute__((always_inline)) {
+  auto load = [&](const Step& S, u32x4_t (&wr)[NT][NWL], Run<__bf16> (&br)[KH][MF]) __attribute__((always_inline)) {
     const int k = klist_at(P.law, S.it.i, S.it.j, S.it.kofs + S.m);
     const int st0 = KS * S.s;
-    const __bf16* wt = P.W + (int64_t(S.it.j) * q + k) * blk + int64_t(st0) * strip_elems;
     const int ns = nstrips - st0 < KS ? nstrips - st0 : KS;
     const int nvalid = ns * 2 * b_in;   // valid 16-byte chunks
 #pragma unroll
-    for (int c = 0; c < NWL; ++c) {
-      const int ch = c * NTHR + int(threadIdx.x);
-      const __bf16* src = ch < nvalid ? wt + ch * 8 : zero;
-      wr[c] = *reinterpret_cast<const u32x4_t*>(src);
+    for (int t = 0; t < NT; ++t) {
+      // tile 1 (PAIR): W_kk, or W_ik again (from L2) when k = i
+      const int jj = t == 1 && S.pair ? k : S.it.j;
+      const __bf16* wt = P.W + (int64_t(jj) * q + k) * blk + int64_t(st0) * strip_elems;
+#pragma unroll
+      for (int c = 0; c < NWL; ++c) {
+        const int ch = c * NTHR + int(threadIdx.x);
+        const __bf16* src = ch < nvalid ? wt + ch * 8 : zero;
+        wr[t][c] = *reinterpret_cast<const u32x4_t*>(src);
+      }
     }
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
@@ -307,21 +326,27 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
       }
     }
   };
-  auto store_w = [&](const u32x4_t (&wr)[NWL], int buf) __attribute__((always_inline)) {
+  auto store_w = [&](const u32x4_t (&wr)[NT][NWL], int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < NWL; ++c) {
-      const int ch = c * NTHR + int(threadIdx.x);
-      if (ch < tile_chunks) *reinterpret_cast<u32x4_t*>(lds + buf * tile_elems + wofs[c]) = wr[c];
-    }
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < NWL; ++c) {
+        const int ch = c * NTHR + int(threadIdx.x);
+        if (ch < tile_chunks) *reinterpret_cast<u32x4_t*>(lds + (buf * NT + t) * tile_elems + wofs[c]) = wr[t][c];
+      }
   };
 
   // Per-lane offset of its transposing read inside a tile (see the header).
   const int lane_off = (g >> 1) * lstrip + (8 * (g & 1) + (r >> 2)) * 8 + ((r & 3) >> 1) * OP + (r & 1) * 4;
-  f32x4_t acc[MF][NFI];
+  f32x4_t acc[MF][NFI], acc2[PAIR ? MF : 1][PAIR ? NFI : 1];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
     for (int f = 0; f < NFI; ++f) acc[mf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mf = 0; mf < (PAIR ? MF : 1); ++mf)
+#pragma unroll
+    for (int f = 0; f < (PAIR ? NFI : 1); ++f) acc2[mf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const Step& S, const Run<__bf16> (&br)[KH][MF], int buf) __attribute__((always_inline)) {
     if (!S.live) return;
@@ -330,13 +355,43 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
     // (NFI rounded up) re-read the last one and are never stored.
 #pragma unroll
     for (int h = 0; h < KH; ++h) {
-      __bf16* t = lds + buf * tile_elems + 2 * h * lstrip + lane_off;
+      __bf16* t = lds + buf * NT * tile_elems + 2 * h * lstrip + lane_off;
 #pragma unroll
       for (int f = 0; f < NFI; ++f) {
         const int fc = f < nfi ? f : nfi - 1;
         const Run<__bf16> a = lds_run_tr(t + fc * 2 * OP, t + fc * 2 * OP + 32);
 #pragma unroll
         for (int mf = 0; mf < MF; ++mf) acc[mf][f] = mma(a, br[h][mf], acc[mf][f]);
+      }
+    }
+    if (PAIR && S.pair) {
+#pragma unroll
+      for (int h = 0; h < KH; ++h) {
+        __bf16* t = lds + (buf * NT + 1) * tile_elems + 2 * h * lstrip + lane_off;
+#pragma unroll
+        for (int f = 0; f < NFI; ++f) {
+          const int fc = f < nfi ? f : nfi - 1;
+          const Run<__bf16> a = lds_run_tr(t + fc * 2 * OP, t + fc * 2 * OP + 32);
+#pragma unroll
+          for (int mf = 0; mf < (PAIR ? MF : 1); ++mf)
+            acc2[mf][f < (PAIR ? NFI : 1) ? f : 0] = mma(a, br[h][mf], acc2[mf][f < (PAIR ? NFI : 1) ? f : 0]);
+        }
+      }
+      if (S.blk_last) {
+        // block k complete: input group k of these rows
+        const int k = S.it.kofs + S.m;
+#pragma unroll
+        for (int mf = 0; mf < (PAIR ? MF : 1); ++mf) {
+          const int64_t tt = int64_t(S.it.mt) * TM + (wave * MF + mf) * 16 + r;
+          if (tt < S.tr.count) {
+            const int64_t row = S.tr.first + tt * S.tr.stride;
+#pragma unroll
+            for (int f = 0; f < (PAIR ? NFI : 1); ++f)
+              if (f < nfi) store4(dX + row * P.ldx + int64_t(k) * b_in + f * 16 + 4 * g, acc2[mf][f]);
+          }
+#pragma unroll
+          for (int f = 0; f < (PAIR ? NFI : 1); ++f) acc2[mf][f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
     if (!S.last) return;
@@ -360,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   };
 
   // ---- software pipeline over NSET register sets
-  u32x4_t wr[NSET][NWL];
+  u32x4_t wr[NSET][NT][NWL];
   Run<__bf16> br[NSET][KH][MF];
   Step S[NSET];
 #pragma unroll
@@ -703,7 +758,10 @@ DataSplit data_split(const aa_plan_s& plan, int64_t M) {
   if (d.mt_count < 1) d.mt_count = 1;
   const int nb = plan.law == AA_LAW_QQ ? 2 * plan.q - 1 : 9;
   d.units = int64_t(plan.q) * d.mt_count * nb;
-  const int64_t per = (d.units + 256) / 512;
+  // Q_q items with pairs cover about 2R units (a range of R own-group blocks
+  // and the one-block leaves of the same range), without them R units
+  const bool pair = plan.law == AA_LAW_QQ && nfi <= 8;
+  const int64_t per = pair ? (d.units + 512) / 1024 : (d.units + 256) / 512;
   d.R = plan.law == AA_LAW_QQ ? int(per < 2 ? 2 : (per > 4 ? 4 : per)) : 4;
   const int len = plan.law == AA_LAW_QQ ? plan.q : 4;
   d.nparts = len > d.R ? (len + d.R - 1) / d.R : 1;
@@ -775,21 +833,30 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
   P.R = dsp.R;
   P.nb = plan.law == AA_LAW_QQ ? 2 * plan.q - 1 : 9;
   const int nfi = int(plan.b_in / 16);
-  const int KS = nfi <= 8 ? 4 : 2;   // strips per step
+  const bool pair = plan.law == AA_LAW_QQ && nfi <= 8;
+  P.pair = pair ? 1 : 0;
+  const int KS = !pair && nfi <= 8 ? 4 : 2;   // strips per step (Q_q steps carry two weight tiles)
   P.ksb = int32_t((plan.b_out / 16 + KS - 1) / KS);
   const int MF = dsp.mf;
   P.mt_count = dsp.mt_count;
   P.units = dsp.units;
   if (P.units >= (int64_t(1) << 31)) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_data: too many rows per type");
-  const size_t lds = size_t(2) * KS * (plan.b_in / 8) * 160 * 2;
+  const size_t lds = size_t(2) * (pair ? 2 : 1) * KS * (plan.b_in / 8) * 160 * 2;
   int grid = device_cu_count() * 2;
   grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
   const bool f32 = plan.out_dtype == AA_F32;
   auto go = [&](auto nfi_c, auto mf_c, auto nset_c) {
     constexpr int NFIc = decltype(nfi_c)::value, MFc = decltype(mf_c)::value, NS = decltype(nset_c)::value;
+    if constexpr (NFIc <= 8) {
+      if (pair) {
+        if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, 2, NS, true>), dim3(grid), dim3(256), lds, stream, P);
+        else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, 2, NS, true>), dim3(grid), dim3(256), lds, stream, P);
+        return;
+      }
+    }
     constexpr int KSc = NFIc <= 8 ? 4 : 2;
-    if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, KSc, NS>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, KSc, NS>), dim3(grid), dim3(256), lds, stream, P);
+    if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, KSc, NS, false>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, KSc, NS, false>), dim3(grid), dim3(256), lds, stream, P);
   };
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
