@@ -149,7 +149,7 @@ aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_byt
   if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: plan is NULL");
   if (M < 0) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: M is negative");
   if (data_bytes) *data_bytes = aa::bwd_data_workspace_bytes(*plan, M);
-  if (weight_bytes) *weight_bytes = aa::bwd_weight_workspace_bytes(*plan);
+  if (weight_bytes) *weight_bytes = aa::bwd_weight_workspace_bytes(*plan, M);
   return AA_OK;
 }
 
@@ -200,7 +200,7 @@ aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY,
   const size_t wb = size_t(plan->d_in * plan->d_out) * elem_size(plan->out_dtype);
   if (overlaps(dW_packed, wb, X, xb) || overlaps(dW_packed, wb, dY, yb))
     return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: dW_packed overlaps X or dY");
-  const size_t need = aa::bwd_weight_workspace_bytes(*plan);
+  const size_t need = aa::bwd_weight_workspace_bytes(*plan, M);
   if (workspace_bytes < need)
     return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_weight: workspace smaller than aa_project_bwd_workspace reports");
   if (need > 0 && (st = check_ptr(workspace, "workspace", fn)) != AA_OK) return st;

@@ -462,13 +462,13 @@ struct BwdWeightParams {
   const __bf16* X;    // M x ldx
   const __bf16* dY;   // M x ldy
   void* dW;           // packed (Tout)
-  float* ws;          // ntg > 1: [type group][k][packed block] fp32 partial diagonal blocks
+  float* ws;          // reduce kernel: [part][k][packed block] fp32 partial diagonal blocks
   int64_t M, ldx, ldy;
   int32_t q, b_in, b_out, law, kind, off_mod_q;
   int64_t rows_per_type;
   int32_t nchunks;    // column chunks of NC strips per output group
   int32_t ndin;       // row chunks of 64 NFW input features per block
-  int32_t ntg;        // type groups (Q_q only): partial diagonal blocks, added by a second kernel
+  int32_t nparts;     // reduce kernel: partial sums per diagonal block
   int32_t ldsx, ldsy; // LDS row pitch (elements) of the X and dY tiles
 };
 
@@ -478,15 +478,16 @@ struct BwdWeightParams {
 // eight different 32-byte bank windows.
 __device__ inline int tile_row(int t) { return t ^ ((((t >> 2) ^ (t >> 3)) & 1) * 12); }
 
-// Accumulator slots: Q_q uses slot 0 for block (i, k) of the current type and
-// slot 1 for the diagonal block (k, k); Q2 x Q2 uses slot j for block (j, k).
-// A step is 64 tokens of one type i and one input group j (two MFMA k-steps).
-template <typename Tout, bool QQ, int NFW, int NC, int NSET>
+// The Q2 x Q2 weight gradient: a workgroup owns a column chunk of output
+// group k (and a chunk of input features) and walks every row type; the four
+// blocks (j, k) of the column stay in four accumulator slots to the end.  A
+// step is 64 tokens of one type i and one input group j (two MFMA k-steps).
+template <typename Tout, int NFW, int NC, int NSET>
 __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   constexpr int NTHR = 256;
   constexpr int TK = 64;                         // tokens per step
   constexpr int DIN = 64 * NFW;                  // input features per workgroup
-  constexpr int NSLOT = QQ ? 2 : 4;
+  constexpr int NSLOT = 4;
   constexpr int XCPR = DIN / 8;                  // 16-byte chunks of an X tile row
   constexpr int NXL = TK * XCPR / NTHR;          // X loads per thread
   constexpr int NYL = (TK * 2 * NC + NTHR - 1) / NTHR;
@@ -504,9 +505,9 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   Tout* __restrict__ dW = static_cast<Tout*>(P.dW);
   const int64_t blk = int64_t(b_in) * P.b_out;
 
-  // ---- item (output group k, type group tg, column chunk c, row chunk dc);
-  // each XCD takes a contiguous run, so one group's items share its L2
-  const int64_t n_items = int64_t(q) * P.ntg * P.nchunks * P.ndin;
+  // ---- item (output group k, column chunk c, row chunk dc); each XCD takes
+  // a contiguous run, so one group's items share its L2
+  const int64_t n_items = int64_t(q) * P.nchunks * P.ndin;
   const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
   const int64_t xlo = n_items * xcd / kNumXcd, xhi = n_items * (xcd + 1) / kNumXcd;
   int64_t item = xlo + slot;
@@ -514,33 +515,29 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   const int dc = int(item % P.ndin);
   item /= P.ndin;
   const int c = int(item % P.nchunks);
-  item /= P.nchunks;
-  const int tg = int(item % P.ntg);
-  const int k = int(item / P.ntg);
+  const int k = int(item / P.nchunks);
   const int col0 = c * NC * 16;   // first column of the chunk inside group k
   const int row0 = dc * DIN;      // first input feature of the chunk inside a block
-  const int t_begin = tg * q / P.ntg, t_end = (tg + 1) * q / P.ntg;
   const TypeMap tmap(P.kind, q, P.off_mod_q, P.M, P.rows_per_type);
 
-  // steps: every type of the group, every 64-token chunk of it (at least one,
-  // so that a type without rows still writes its zero block), every j with
-  // (i, j, k) in T
+  // steps: every type, every 64-token chunk of it (at least one, so that the
+  // step structure does not depend on empty types), every j with (i, j, k) in T
   auto chunks_of = [&](int i) __attribute__((always_inline)) {
     const int64_t n = tmap.rows(i).count;
     return n > 0 ? int((n + TK - 1) / TK) : 1;
   };
   int n_steps = 0;
-  for (int i = t_begin; i < t_end; ++i) {
+  for (int i = 0; i < q; ++i) {
     int gl[4];
     n_steps += chunks_of(i) * device_leaf_groups(P.law, i, k, gl);
   }
 
   struct Step {
-    int i, tc, j, slot;
-    bool live, flush0;   // flush0 (Q_q): the type's last step, block (i, k) done
+    int i, tc, j;
+    bool live;
     TypeRows tr;
   };
-  int cur_i = t_begin, cur_tc = 0, cur_jx = 0, issued = 0;
+  int cur_i = 0, cur_tc = 0, cur_jx = 0, issued = 0;
   auto setup = [&](Step& S) __attribute__((always_inline)) {
     S.live = issued < n_steps;
     int gl[4];
@@ -549,8 +546,6 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     S.i = cur_i;
     S.tc = cur_tc;
     S.j = gl[cur_jx];
-    S.slot = QQ ? (S.j == k ? 1 : 0) : S.j;
-    S.flush0 = QQ && S.live && cur_i != k && cur_tc == nch - 1 && cur_jx == ng - 1;
     S.tr = tmap.rows(cur_i);
     if (S.live) {
       ++issued;
@@ -625,10 +620,9 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     fofs[a] = fok[a] ? f * 16 : 0;
   }
 
-  // Store slot sl as block (j, k): lane (column r, g) holds rows 4g .. 4g+3 of
-  // each of its fragments, half of a packed run.  To the workspace when the
-  // block is a partial sum over this workgroup's types.
-  auto flush = [&](int sl, int j, bool partial) __attribute__((always_inline)) {
+  // Store slot sl as block (sl, k): lane (column r, g) holds rows 4g .. 4g+3
+  // of each of its fragments, half of a packed run.
+  auto flush = [&](int sl) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < NFW; ++a) {
       if (fok[a]) {
@@ -638,8 +632,7 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
           const int st = c * NC + b;
           if (st < nstrips) {
             const int64_t o = int64_t(st) * (b_in * 16) + (row >> 3) * 128 + r * 8 + (row & 7);
-            if (partial) store4(P.ws + (int64_t(tg) * q + k) * blk + o, acc[sl][a][b]);
-            else store4(dW + (int64_t(j) * q + k) * blk + o, acc[sl][a][b]);
+            store4(dW + (int64_t(sl) * q + k) * blk + o, acc[sl][a][b]);
           }
         }
       }
@@ -665,7 +658,7 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
     }
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
-      if (S.slot == sl) {
+      if (S.j == sl) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -673,13 +666,6 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
 #pragma unroll
             for (int b = 0; b < NC; ++b) acc[sl][a][b] = mma(av[h][a], bv[h][b], acc[sl][a][b]);
       }
-    }
-    if (QQ && S.flush0) {
-      flush(0, S.i, false);
-#pragma unroll
-      for (int a = 0; a < NFW; ++a)
-#pragma unroll
-        for (int b = 0; b < NC; ++b) acc[0][a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
 
@@ -704,16 +690,11 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
       load(S[sn], xr[sn], yr[sn]);
     }
   }
-  if (QQ) {
-    // the diagonal block: a type group's partial sum, or the whole of it
-    flush(1, k, P.ntg > 1);
-  } else {
 #pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl) flush(sl, sl, false);
-  }
+  for (int sl = 0; sl < NSLOT; ++sl) flush(sl);
 }
 
-// Add the type groups' partial diagonal blocks (Q_q) into dW.
+// Add the parts' partial diagonal blocks (Q_q) into dW.
 template <typename Tout>
 __global__ __launch_bounds__(256) void bwd_weight_reduce_kernel(BwdWeightParams P) {
   const int64_t blk = int64_t(P.b_in) * P.b_out;
@@ -723,8 +704,238 @@ __global__ __launch_bounds__(256) void bwd_weight_reduce_kernel(BwdWeightParams 
     const int64_t e = e4 * 4;
     const int64_t k = e / blk, o = e - k * blk;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    for (int tg = 0; tg < P.ntg; ++tg) s += *reinterpret_cast<const f32x4_t*>(P.ws + int64_t(tg) * P.q * blk + e);
+    for (int pt = 0; pt < P.nparts; ++pt) s += *reinterpret_cast<const f32x4_t*>(P.ws + int64_t(pt) * P.q * blk + e);
     store4(dW + (k * P.q + k) * blk + o, s);
+  }
+}
+
+// ------------------------------------------- weight gradient, large tiles ---
+//
+// Q_q with input blocks of at most 128 features per chunk: a workgroup's
+// output tile is 128 input features by 128 columns of one block, the four
+// waves in a 2 x 2 arrangement (64 x 64 each), so that every 64-token step
+// brings 16 KB of X and 16 KB of dY for 32 MFMAs per wave.  Work items:
+//   off-diagonal block (i, k), i != k: the rows of type i (kept only there);
+//   diagonal block (k, k): all rows, cut into P token ranges whose fp32
+//   partial sums a second kernel adds when P > 1.
+// Items are numbered by output group k (diagonal parts first), and every
+// workgroup takes a contiguous, step-balanced range inside its XCD's run.
+
+struct WTileParams {
+  const __bf16* X;    // M x ldx
+  const __bf16* dY;   // M x ldy
+  void* dW;           // packed (Tout)
+  float* ws;          // P > 1: [part][k][packed block] fp32 partial diagonal blocks
+  int64_t M, ldx, ldy;
+  int32_t q, b_in, b_out, kind, off_mod_q;
+  int64_t rows_per_type;
+  int32_t nch, ndc;   // 128-column chunks, 128-feature chunks of a block
+  int32_t P, SB, SA;  // diagonal parts, steps per part, steps per off-diagonal item
+  int64_t UB, Uk;     // units (steps) of the diagonal items of a group, of a group
+  int64_t units;      // q * Uk
+};
+
+struct WItem {
+  int64_t gu;
+  int k, j, c, dc, part, nsteps;
+  bool diag;
+};
+
+__device__ inline WItem witem_at(const WTileParams& P, int64_t g) {
+  WItem it;
+  const uint32_t kk = uint32_t(g / P.Uk);
+  const int64_t u = g - int64_t(kk) * P.Uk;
+  const int tiles = P.nch * P.ndc;
+  it.k = int(kk);
+  int tile;
+  if (u < P.UB) {
+    const int idx = int(u / P.SB);
+    tile = idx / P.P;
+    it.part = idx - tile * P.P;
+    it.j = it.k;
+    it.diag = true;
+    it.nsteps = P.SB;
+    it.gu = int64_t(kk) * P.Uk + int64_t(idx) * P.SB;
+  } else {
+    const int idx = int((u - P.UB) / P.SA);
+    const int ii = idx / tiles;
+    tile = idx - ii * tiles;
+    it.j = ii < it.k ? ii : ii + 1;
+    it.part = 0;
+    it.diag = false;
+    it.nsteps = P.SA;
+    it.gu = int64_t(kk) * P.Uk + P.UB + int64_t(idx) * P.SA;
+  }
+  it.c = tile / P.ndc;
+  it.dc = tile - it.c * P.ndc;
+  return it;
+}
+
+template <typename Tout>
+__global__ __launch_bounds__(256, 2) void bwd_weight_tile_kernel(WTileParams P) {
+  constexpr int NTHR = 256, TK = 64, NSET = 2;
+  constexpr int RP = 128;                 // LDS row pitch (elements): 256 bytes, chunks XOR-swizzled
+  constexpr int TILE = TK * RP;           // elements of one staged tile
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __bf16* lds = reinterpret_cast<__bf16*>(smem);
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int g = lane >> 4, r = lane & 15;
+  const int dh = wave & 1, chh = wave >> 1;   // this wave's 64-feature and 64-column halves
+  const int b_in = P.b_in, q = P.q;
+  const int nstrips = P.b_out / 16;
+  const int64_t blk = int64_t(b_in) * P.b_out;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+  Tout* __restrict__ dW = static_cast<Tout*>(P.dW);
+  const TypeMap tmap(P.kind, q, P.off_mod_q, P.M, P.rows_per_type);
+
+  const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int64_t S8 = gridDim.x / kNumXcd;
+  const int64_t xlo = P.units * xcd / kNumXcd, xhi = P.units * (xcd + 1) / kNumXcd;
+  const int64_t lo = xlo + (xhi - xlo) * slot / S8, hi = xlo + (xhi - xlo) * (slot + 1) / S8;
+  if (lo >= hi) return;
+  WItem first = witem_at(P, lo);
+  if (first.gu < lo) first = witem_at(P, first.gu + first.nsteps);
+  if (first.gu >= hi) return;
+  int n_steps = 0;
+  for (WItem it = first;;) {
+    n_steps += it.nsteps;
+    const int64_t nx = it.gu + it.nsteps;
+    if (nx >= hi || nx >= P.units) break;
+    it = witem_at(P, nx);
+  }
+
+  struct Step {
+    WItem it;
+    int st;
+    bool live, last;
+    TypeRows tr;       // the item's rows: type j's (off-diagonal) or all rows (diagonal)
+  };
+  WItem cur = first;
+  int cur_st = 0, issued = 0;
+  auto setup = [&](Step& S) __attribute__((always_inline)) {
+    S.live = issued < n_steps;
+    S.it = cur;
+    S.st = cur_st;
+    S.last = S.live && cur_st == cur.nsteps - 1;
+    if (cur.diag) {
+      S.tr.first = int64_t(cur.part) * P.SB * TK;
+      S.tr.stride = 1;
+      S.tr.count = P.M - S.tr.first;
+    } else {
+      S.tr = tmap.rows(cur.j);
+    }
+    if (S.live) {
+      ++issued;
+      if (++cur_st == cur.nsteps) {
+        cur_st = 0;
+        if (issued < n_steps) cur = witem_at(P, cur.gu + cur.nsteps);
+      }
+    }
+  };
+
+  // Thread t stages chunks t + 256 l (l < 4) of each tile: token ch / 16,
+  // 16-byte chunk ch mod 16 of the row.
+  auto load = [&](const Step& S, u32x4_t (&xr)[4], u32x4_t (&yr)[4]) __attribute__((always_inline)) {
+    const int xw = b_in - S.it.dc * 128 < 128 ? b_in - S.it.dc * 128 : 128;
+    const int yw = P.b_out - S.it.c * 128 < 128 ? P.b_out - S.it.c * 128 : 128;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch >> 4, cc = ch & 15;
+      const int64_t tt = int64_t(S.st) * TK + tk;
+      const bool rok = tt < S.tr.count;
+      const int64_t row = S.tr.first + tt * S.tr.stride;
+      const __bf16* xs = rok && cc * 8 < xw ? P.X + row * P.ldx + int64_t(S.it.j) * b_in + S.it.dc * 128 + cc * 8 : zero;
+      const __bf16* ys =
+          rok && cc * 8 < yw ? P.dY + row * P.ldy + int64_t(S.it.k) * P.b_out + S.it.c * 128 + cc * 8 : zero;
+      xr[l] = *reinterpret_cast<const u32x4_t*>(xs);
+      yr[l] = *reinterpret_cast<const u32x4_t*>(ys);
+    }
+  };
+  int sofs[4];   // LDS offset of the thread's chunks (row-permuted, XOR-swizzled)
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    const int ch = l * NTHR + int(threadIdx.x);
+    const int tk = ch >> 4, cc = ch & 15;
+    const int R = tile_row(tk);
+    sofs[l] = R * RP + (((cc >> 1) ^ (R & 7)) << 4) + (cc & 1) * 8;
+  }
+  auto store_tiles = [&](const u32x4_t (&xr)[4], const u32x4_t (&yr)[4], int buf) __attribute__((always_inline)) {
+    __bf16* base = lds + buf * 2 * TILE;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      *reinterpret_cast<u32x4_t*>(base + sofs[l]) = xr[l];
+      *reinterpret_cast<u32x4_t*>(base + TILE + sofs[l]) = yr[l];
+    }
+  };
+
+  // Transposing reads: tokens 8g + r/4 (+ 4: 8 rows on) of k-step h (32 h
+  // rows on), 4 consecutive features / columns at 4 (r mod 4) of 32-byte
+  // chunk c32, which sits at c32 XOR (row mod 8).
+  const int rbase = 16 * (g >> 1) + 4 * (g & 1) + (r >> 2);   // = tile_row(8g + r/4)
+  const int rsw = rbase & 7;
+  auto rd = [&](__bf16* tile, int h, int c32) __attribute__((always_inline)) {
+    __bf16* p = tile + (32 * h + rbase) * RP + ((c32 ^ rsw) << 4) + 4 * (r & 3);
+    return lds_run_tr(p, p + 8 * RP);
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Step& S, int buf) __attribute__((always_inline)) {
+    if (!S.live) return;
+    __bf16* xt = lds + buf * 2 * TILE;
+    __bf16* yt = xt + TILE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      Run<__bf16> av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = rd(xt, h, 4 * dh + a);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bv[b] = rd(yt, h, 4 * chh + b);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mma(av[a], bv[b], acc[a][b]);
+    }
+    if (!S.last) return;
+    // lane (column r, g) holds rows 4g .. 4g+3 of each fragment: half a packed run
+    const bool partial = S.it.diag && P.P > 1;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int row = S.it.dc * 128 + 64 * dh + 16 * a + 4 * g;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int st = 8 * S.it.c + 4 * chh + b;
+        if (row < b_in && st < nstrips) {
+          const int64_t o = int64_t(st) * (b_in * 16) + (row >> 3) * 128 + r * 8 + (row & 7);
+          if (partial) store4(P.ws + (int64_t(S.it.part) * q + S.it.k) * blk + o, acc[a][b]);
+          else store4(dW + (int64_t(S.it.j) * q + S.it.k) * blk + o, acc[a][b]);
+        }
+        acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  u32x4_t xr[NSET][4], yr[NSET][4];
+  Step S[NSET];
+  setup(S[0]);
+  load(S[0], xr[0], yr[0]);
+  const int rounds = (n_steps + NSET - 1) / NSET;
+  for (int rdn = 0; rdn < rounds; ++rdn) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      store_tiles(xr[s], yr[s], s);
+      __syncthreads();
+      const int sn = (s + 1) % NSET;
+      setup(S[sn]);
+      load(S[sn], xr[sn], yr[sn]);
+      compute(S[s], s);
+    }
   }
 }
 
@@ -739,6 +950,33 @@ int64_t max_rows_per_type(const aa_plan_s& plan, int64_t M) {
   if (plan.type_kind == AA_TYPES_BLOCK_ROWS) return M / plan.q;
   return (M + plan.q - 1) / plan.q;
 }
+
+// Work split of the large-tile weight gradient (Q_q): P token ranges of SB
+// steps for each diagonal tile, chosen so that a diagonal part is about 1.5x
+// the average work per workgroup (at most 8 parts).
+struct TileSplit {
+  int nch, ndc, P, SB, SA;
+  int64_t UB, Uk, units;
+};
+TileSplit tile_split(const aa_plan_s& plan, int64_t M) {
+  TileSplit t;
+  t.nch = int((plan.b_out + 127) / 128);
+  t.ndc = int((plan.b_in + 127) / 128);
+  const int tiles = t.nch * t.ndc;
+  const int64_t sbt = (M + 63) / 64 > 0 ? (M + 63) / 64 : 1;
+  const int64_t rpt = max_rows_per_type(plan, M);
+  t.SA = int((rpt + 63) / 64 > 0 ? (rpt + 63) / 64 : 1);
+  const double avg = double(plan.q) * tiles * (double(sbt) + double(plan.q - 1) * t.SA) / 512.0;
+  int P = int((double(sbt) + 1.5 * avg - 1.0) / (1.5 * avg > 1.0 ? 1.5 * avg : 1.0));
+  P = P < 1 ? 1 : (P > 8 ? 8 : P);
+  t.SB = int((sbt + P - 1) / P);
+  t.P = int((sbt + t.SB - 1) / t.SB);
+  t.UB = int64_t(tiles) * t.P * t.SB;
+  t.Uk = t.UB + int64_t(plan.q - 1) * tiles * t.SA;
+  t.units = int64_t(plan.q) * t.Uk;
+  return t;
+}
+
 
 // Blocks per part of a split data-gradient leaf.  Q_q's own-group leaf has q
 // blocks and every other leaf one.  Parts of R blocks keep work items within a
@@ -768,35 +1006,21 @@ DataSplit data_split(const aa_plan_s& plan, int64_t M) {
   return d;
 }
 
-// Work split of the weight gradient: NFW row fragments per wave (64 NFW input
-// features per workgroup), NC strips per column chunk, and for Q_q type groups
-// whose partial diagonal blocks a second kernel adds (only while the other
-// splits leave fewer than 384 workgroups, and at most q / 2 groups, which keeps
-// the partial sums within the size of dW).
+// Work split of the Q2 x Q2 weight gradient: NFW row fragments per wave (64
+// NFW input features per workgroup) and 2 strips per column chunk.
 struct WeightShape {
-  bool qq;
-  int nfw, nc, nchunks, ndin, ntg;
+  int nfw, nc, nchunks, ndin;
 };
 WeightShape weight_shape(const aa_plan_s& plan) {
   WeightShape s;
-  s.qq = plan.law == AA_LAW_QQ;
   const int nstrips = int(plan.b_out / 16);
-  // Q_q: 128 features by 2 strips, or 64 by 4 (the register budget of two
-  // workgroups per CU); Q2 x Q2 keeps four accumulator slots, so 2 strips.
-  auto nc_of = [&](int nfw) { return s.qq && nfw == 1 ? 4 : 2; };
-  auto items = [&](int nfw) {
-    const int nc = nc_of(nfw);
-    return int64_t(plan.q) * ((nstrips + nc - 1) / nc) * ((plan.b_in + 64 * nfw - 1) / (64 * nfw));
-  };
-  s.nfw = plan.b_in >= 128 && items(2) >= 128 ? 2 : 1;
-  s.nc = nc_of(s.nfw);
+  s.nc = 2;
   s.nchunks = (nstrips + s.nc - 1) / s.nc;
+  const int64_t items2 = int64_t(plan.q) * s.nchunks * ((plan.b_in + 127) / 128);
+  s.nfw = plan.b_in >= 128 && items2 >= 128 ? 2 : 1;
   s.ndin = int((plan.b_in + 64 * s.nfw - 1) / (64 * s.nfw));
-  s.ntg = 1;
-  while (s.qq && items(s.nfw) * s.ntg < 384 && s.ntg * 2 <= plan.q / 2) s.ntg *= 2;
   return s;
 }
-
 
 }  // namespace
 
@@ -806,10 +1030,11 @@ size_t bwd_data_workspace_bytes(const aa_plan_s& plan, int64_t M) {
   return size_t(d.nparts) * size_t(M) * size_t(plan.b_in) * sizeof(float);
 }
 
-size_t bwd_weight_workspace_bytes(const aa_plan_s& plan) {
-  const WeightShape sh = weight_shape(plan);
-  if (sh.ntg == 1) return 0;
-  return size_t(sh.ntg) * size_t(plan.q) * size_t(plan.b_in) * size_t(plan.b_out) * sizeof(float);
+size_t bwd_weight_workspace_bytes(const aa_plan_s& plan, int64_t M) {
+  if (plan.law != AA_LAW_QQ) return 0;
+  const int parts = tile_split(plan, M).P;
+  if (parts == 1) return 0;
+  return size_t(parts) * size_t(plan.q) * size_t(plan.b_in) * size_t(plan.b_out) * sizeof(float);
 }
 
 aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W, void* dX, int64_t M,
@@ -890,6 +1115,52 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
 
 aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
                               int64_t pos_offset, void* ws, hipStream_t stream) {
+  const bool f32 = plan.out_dtype == AA_F32;
+  if (plan.law == AA_LAW_QQ) {
+    const TileSplit ts = tile_split(plan, M);
+    if (ts.units >= (int64_t(1) << 31)) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_weight: too many rows");
+    WTileParams T{};
+    T.X = static_cast<const __bf16*>(X);
+    T.dY = static_cast<const __bf16*>(dY);
+    T.dW = dW;
+    T.ws = static_cast<float*>(ws);
+    T.M = M;
+    T.ldx = plan.d_in;
+    T.ldy = plan.d_out;
+    T.q = plan.q;
+    T.b_in = int32_t(plan.b_in);
+    T.b_out = int32_t(plan.b_out);
+    T.kind = plan.type_kind;
+    T.off_mod_q = int32_t(pos_offset % plan.q);
+    T.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
+    T.nch = ts.nch;
+    T.ndc = ts.ndc;
+    T.P = ts.P;
+    T.SB = ts.SB;
+    T.SA = ts.SA;
+    T.UB = ts.UB;
+    T.Uk = ts.Uk;
+    T.units = ts.units;
+    int grid = device_cu_count() * 2;
+    grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
+    const size_t lds = size_t(2) * 2 * 64 * 128 * 2;
+    if (f32) hipLaunchKernelGGL((bwd_weight_tile_kernel<float>), dim3(grid), dim3(256), lds, stream, T);
+    else hipLaunchKernelGGL((bwd_weight_tile_kernel<__bf16>), dim3(grid), dim3(256), lds, stream, T);
+    aa_status_t st = after_launch(stream, "bwd_weight_tile");
+    if (st != AA_OK || ts.P == 1) return st;
+    BwdWeightParams R{};
+    R.dW = dW;
+    R.ws = static_cast<float*>(ws);
+    R.q = plan.q;
+    R.b_in = int32_t(plan.b_in);
+    R.b_out = int32_t(plan.b_out);
+    R.nparts = ts.P;
+    const int64_t n4 = int64_t(plan.q) * plan.b_in * plan.b_out / 4;
+    const int blocks = int(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
+    if (f32) hipLaunchKernelGGL((bwd_weight_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, R);
+    else hipLaunchKernelGGL((bwd_weight_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, R);
+    return after_launch(stream, "bwd_weight_reduce");
+  }
   const WeightShape sh = weight_shape(plan);
   BwdWeightParams P{};
   P.X = static_cast<const __bf16*>(X);
@@ -908,37 +1179,20 @@ aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* 
   P.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
   P.nchunks = sh.nchunks;
   P.ndin = sh.ndin;
-  P.ntg = sh.ntg;
   P.ldsx = lds_pitch(64 * sh.nfw);
   P.ldsy = lds_pitch(16 * sh.nc);
   const size_t lds = size_t(2) * 64 * (P.ldsx + P.ldsy) * 2;
-  const int64_t n_items = int64_t(plan.q) * sh.ntg * sh.nchunks * sh.ndin;
+  const int64_t n_items = int64_t(plan.q) * sh.nchunks * sh.ndin;
   const int grid = int((n_items + kNumXcd - 1) / kNumXcd * kNumXcd);
-  const bool f32 = plan.out_dtype == AA_F32;
-  auto go = [&](auto qq_c, auto nfw_c, auto nc_c) {
-    constexpr bool QQc = decltype(qq_c)::value;
-    constexpr int NFWc = decltype(nfw_c)::value, NCc = decltype(nc_c)::value;
-    constexpr int NS = 4;   // six sets measured slower: the weight gradient is bound by L2 reads, not latency
-    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, QQc, NFWc, NCc, NS>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, QQc, NFWc, NCc, NS>), dim3(grid), dim3(256), lds, stream, P);
-  };
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  using C4 = std::integral_constant<int, 4>;
-  if (sh.qq) {
-    if (sh.nfw == 2) go(std::true_type{}, C2{}, C2{});
-    else go(std::true_type{}, C1{}, C4{});
+  // four register sets (six measured slower: in-flight data beyond L2)
+  if (sh.nfw == 2) {
+    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, 2, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, 2, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
   } else {
-    if (sh.nfw == 2) go(std::false_type{}, C2{}, C2{});
-    else go(std::false_type{}, C1{}, C2{});
+    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, 1, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
+    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, 1, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
   }
-  aa_status_t st = after_launch(stream, "bwd_weight");
-  if (st != AA_OK || sh.ntg == 1) return st;
-  const int64_t n4 = int64_t(plan.q) * plan.b_in * plan.b_out / 4;
-  const int blocks = int(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
-  if (f32) hipLaunchKernelGGL((bwd_weight_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, P);
-  else hipLaunchKernelGGL((bwd_weight_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, P);
-  return after_launch(stream, "bwd_weight_reduce");
+  return after_launch(stream, "bwd_weight");
 }
 
 }  // namespace aa

@@ -63,7 +63,7 @@ bool decode_swiglu_ok(const aa_plan_s& plan);
 // Gradients (bf16 operands, position or block-row typing).  Each needs the
 // device workspace its *_workspace_bytes reports (0: none).
 size_t bwd_data_workspace_bytes(const aa_plan_s& plan, int64_t M);
-size_t bwd_weight_workspace_bytes(const aa_plan_s& plan);
+size_t bwd_weight_workspace_bytes(const aa_plan_s& plan, int64_t M);
 aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W, void* dX, int64_t M,
                             int64_t pos_offset, void* ws, hipStream_t stream);
 aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,

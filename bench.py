@@ -448,6 +448,9 @@ def bench_backward(args, torch, inp, aa, dev, which):
         dense["step_ms"] = round(t_total, 5)
         dense["speedup_step"] = round(t_total / ms_step, 3)
     big = max(parts.items(), key=lambda kv: kv[1]["ms"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_backward(args, torch, inp, sets[0], shapes, q, M)
     return {"metric": f"dense-equiv TFLOP/s + % roofline, {which} (dX and dW of each projection) bf16",
             "value": round(dense_flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
@@ -456,7 +459,41 @@ def bench_backward(args, torch, inp, aa, dev, which):
                        "projections": [{"name": n, "d_in": di, "d_out": do} for n, di, do in shapes],
                        "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
             "roofline": big[1]["roofline"], "roofline_kernel": big[0], "parts": parts, "dense": dense,
-            "kernel_source": kernel_source_hash()}
+            "cpu_baseline": cpu, "kernel_source": kernel_source_hash()}
+
+
+def cpu_baseline_backward(args, torch, inp, st, shapes, q, M):
+    """The fp64 oracle's gradients on the host, on a bounded sample: the rows
+    of the first s row types of every projection (dX of those rows and their
+    contribution to dW), s grown to about --cpu-seconds of work.  Reported in
+    the metric's unit (dense-equivalent TFLOP/s of the sampled rows)."""
+    import numpy as np
+    import oracle
+    host = {}
+    for j, (n, di, do) in enumerate(shapes):
+        W = inp.gaussian((di, do), 1000 + 10 * j + 1, di ** -0.5, torch.bfloat16, "cuda").float().cpu().numpy()
+        host[n] = (st[n]["X"].float().cpu().numpy(), st[n]["dY"].float().cpu().numpy(), W)
+    types = oracle.types_pos_mod(M, q)
+
+    def sample(s):
+        rows = np.nonzero(types < s)[0]
+        for n, _, _ in shapes:
+            X, dY, W = host[n]
+            oracle.project_grad_input(dY[rows], W, "Qq", q, types[rows])
+            oracle.project_grad_weight(X[rows], dY[rows], "Qq", q, types[rows])
+        return len(rows)
+
+    t0 = time.perf_counter()
+    sample(1)
+    t_one = time.perf_counter() - t0
+    s = int(max(1, min(q, args.cpu_seconds / max(t_one, 1e-6))))
+    t0 = time.perf_counter()
+    n = sample(s)
+    t = time.perf_counter() - t0
+    dense = sum(2 * 2.0 * n * di * do for _, di, do in shapes)
+    return {"value": round(dense / t / 1e12, 5), "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"dX and dW of rows of row types 0..{s - 1} ({n} of {M} tokens) for every projection, "
+                      f"fp64 numpy, {t:.2f} s", "seconds": round(t, 3)}
 
 
 def decode_single_token(torch, aa, plan, sets, pos0, n_tok, D, F, q, dense_set=None, reps=20):

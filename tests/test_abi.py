@@ -179,9 +179,10 @@ def test_gradients_validate_before_launch(lib):
     sp = aa.aa_plan_create("Qq", 16, 2048, 768)
     nws = aa.aa_project_bwd_workspace(sp, 2048)[1]
     assert nws > 0
-    assert _raw(lib, "aa_project_bwd_weight", sp.handle, g, 2 * g, 3 * g, 64, 0, None, 4 * g, nws - 16, None) == \
+    G = 0x100000000
+    assert _raw(lib, "aa_project_bwd_weight", sp.handle, G, 2 * G, 3 * G, 2048, 0, None, 4 * G, nws - 16, None) == \
         aa.AA_ERR_INVALID_ARG
-    assert _raw(lib, "aa_project_bwd_weight", sp.handle, g, 2 * g, 3 * g, 64, 0, None, None, nws, None) == \
+    assert _raw(lib, "aa_project_bwd_weight", sp.handle, G, 2 * G, 3 * G, 2048, 0, None, None, nws, None) == \
         aa.AA_ERR_INVALID_ARG
     # unsupported: fp32 operands, explicit type lists, blocks too wide
     f32 = aa.aa_plan_create("Qq", 4, 256, 256, "pos_mod", 0, "f32", "f32")
