@@ -76,6 +76,11 @@ def _run(law, q, M, d_in, d_out, out_dt="f32", kind="pos_mod", pos_offset=0, per
     ("Q2xQ2 down shape", "Q2xQ2", 4, 1100, 1536, 768, "pos_mod", 2, 1536),
     ("Q2xQ2 block rows", "Q2xQ2", 4, 256, 256, 128, "block_rows", 0, 0),
     ("wide input blocks (b_in 384)", "Qq", 32, 900, 12288, 4096, "pos_mod", 9, 0),
+    ("q = 1 (dense gradients)", "Qq", 1, 300, 64, 96, "pos_mod", 0, 0),
+    ("one row", "Qq", 8, 1, 512, 512, "pos_mod", 11, 0),
+    ("b = 16, q = 256 block rows", "Qq", 256, 2048, 4096, 4096, "block_rows", 0, 0),
+    ("q = 3", "Qq", 3, 700, 384, 576, "pos_mod", 1, 0),
+    ("Qwen3-30B-A3B expert gate", "Qq", 16, 2048, 2048, 768, "pos_mod", 0, 0),
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_gradients_match_oracle(name, law, q, M, d_in, d_out, kind, pos_offset, period, out_dt):

@@ -102,6 +102,8 @@ def test_pack_roundtrip_and_layout(law, q, d_in, d_out, dt):
     ("Qq", 8, 1024, 256, 256, "block_rows", "bf16"),
     ("Qq", 2, 256, 64, 64, "pos_mod", "f32"),
     ("Qq", 1, 40, 64, 48, "pos_mod", "bf16"),
+    ("Qq", 3, 700, 384, 576, "pos_mod", "bf16"),       # q = 3 (a law the pages plan next)
+    ("Qq", 5, 333, 320, 160, "pos_mod", "bf16"),       # q = 5, 64 x 32 blocks
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_integer_exact(law, q, M, d_in, d_out, kind, in_dt, out_dt):
@@ -127,6 +129,8 @@ def test_integer_exact(law, q, M, d_in, d_out, kind, in_dt, out_dt):
     ("Qq", 32, 2048, 2048, 6144, "pos_mod"),     # the Qwen3-1.7B-shaped projection (64 x 192 blocks)
     ("Q2xQ2", 4, 4100, 768, 1536, "pos_mod"),
     ("Qq", 64, 8192, 8192, 8192, "block_rows"),  # full product, 128 x 128 blocks
+    ("Qq", 3, 3000, 768, 2304, "pos_mod"),       # q = 3: 256 x 768 blocks, 1000 rows per type
+    ("Qq", 4, 2050, 1024, 4096, "pos_mod"),      # q = 4: 256 x 1024 blocks
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_project_parity(law, q, M, d_in, d_out, kind, out_dt):
