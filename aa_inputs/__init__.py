@@ -94,4 +94,7 @@ WORKLOADS = {
     # public configuration (hidden 2048, intermediate 6144)
     6: Workload(6, "qwen3_1p7b_q32", "Qq", 32, 2048, 2048, 6144, "project", "bf16", "pos_mod",
                 notes="Qwen3-1.7B FFN shape, M=2048, q=32 (blocks 64 x 192)"),
+    # the down projection of the Qwen3-8B SwiGLU FFN on its own
+    7: Workload(7, "qwen3_8b_down_q32", "Qq", 32, 2048, 12288, 4096, "project", "bf16", "pos_mod",
+                notes="Qwen3-8B FFN down projection, M=2048, q=32 (blocks 384 x 128)"),
 }

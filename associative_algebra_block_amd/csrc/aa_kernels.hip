@@ -2174,6 +2174,9 @@ int choose_kstream(const aa_plan_s& plan, int64_t M, bool swiglu) {
   // 128-wide input groups go to the job and persistent kernels; wider ones
   // (a SwiGLU down projection) are streamed in K chunks here.
   if (plan.b_in == 128) return -1;
+  // 128-wide tiles when they divide the output groups (the Qwen3-8B down
+  // projection: 39.4 vs 41.6 us for the 64-wide ones); 64-wide otherwise
+  if (!swiglu && plan.b_out % 128 == 0 && fits(0)) return 0;
   return fits(2) ? 2 : -1;
 }
 

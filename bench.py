@@ -44,8 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
-                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "backward_qwen3_8b",
-                             "backward_expert"])
+                    choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
+                             "backward_qwen3_8b", "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -85,6 +85,8 @@ def main():
         res = bench_qwen3(args, torch, inp, aa, dev)
     elif args.workload == "qwen3_1p7b":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[6])
+    elif args.workload == "qwen3_8b_down":
+        res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[7])
     elif args.workload.startswith("backward_"):
         res = bench_backward(args, torch, inp, aa, dev, args.workload)
     elif args.workload == "square":
