@@ -28,21 +28,26 @@
 // under Q2 x Q2 one, two or four.  A work item is (type i, token tile, j, part
 // of K(i, j)); long lists (Q_q's own group) are cut into parts of R blocks
 // whose fp32 partial sums go to a workspace and are added by a second kernel.
-// Per item the kernel computes dX^T = W_jk dY^T: the A operand (16 input
+// Under Q_q an item also carries the one-block leaves (i, k) of its range of
+// k, which read the same dY blocks (so each is read once).  Per item the
+// kernel computes dX^T = W_jk dY^T: the A operand (16 input
 // features x 32 output features of W_jk) is a two-strip piece of the packed
 // block copied to LDS as it is (the packed octets of 8 rows already hold the
 // m index contiguous) and read transposed; the B operand is 16 bytes of a dY
 // row, loaded straight from HBM.
 //
-// Weight gradient.  One workgroup owns a column chunk of one output group k
-// and walks every row type i: each 32-token chunk of type i adds
-// X[rows, j]^T dY[rows, k] to the accumulator of block (j, k) for every j with
-// (i, j, k) in T.  Under Q_q those are j = i (block (i, k), complete after
-// type i) and j = k (the diagonal block, complete after the last type); under
-// Q2 x Q2 the four blocks of column k stay in registers to the end.  Both MFMA
-// operands (X^T and dY, contracted over tokens) come from LDS tiles read
-// transposed; the result lands in the packed layout directly (a lane holds
-// four consecutive rows of one column, half of a packed run).
+// Weight gradient.  Under Q_q an off-diagonal block W_ik is reached only by
+// rows of type i and a diagonal block W_kk by all rows, so the work items are
+// (block (i, k), rows of type i) and (block (k, k), a token range of all
+// rows); a workgroup computes a 128 x 128 tile of the block with its waves in
+// a 2 x 2 arrangement, and the token ranges of a diagonal block leave fp32
+// partial sums that a second kernel adds.  Under Q2 x Q2 a workgroup owns a
+// column chunk of output group k and walks every row type i, adding
+// X[rows, j]^T dY[rows, k] into the block (j, k) of each kept j; the four
+// blocks of the column stay in registers to the end.  Both MFMA operands
+// (X^T and dY, contracted over tokens) come from LDS tiles read transposed;
+// the result lands in the packed layout directly (a lane holds four
+// consecutive rows of one column, half of a packed run).
 //
 // Both kernels keep the forward kernels' pipeline discipline: NSET rotating
 // register sets, loads of step e + NSET - 1 issued after step e's multiplies,
