@@ -21,7 +21,7 @@ __all__ = [
     "AA_ERR_HIP", "AAError", "Plan", "lib_path", "load",
     "aa_plan_create", "aa_plan_destroy", "aa_plan_info", "aa_pack_weights", "aa_unpack_weights",
     "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_decode_gemv", "aa_project_bwd_workspace",
-    "aa_project_bwd_data", "aa_project_bwd_weight", "aa_status_string", "aa_last_error",
+    "aa_project_bwd_data", "aa_project_bwd_weight", "aa_set_kernel_events", "aa_status_string", "aa_last_error",
 ]
 
 AA_LAW_QQ, AA_LAW_Q2XQ2 = 0, 1
@@ -58,6 +58,7 @@ _SIGNATURES = {
                                            _c_p]),
     "aa_project_bwd_weight": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, ctypes.c_size_t,
                                              _c_p]),
+    "aa_set_kernel_events": (ctypes.c_int, [_c_p, _c_p]),
     "aa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "aa_last_error": (ctypes.c_char_p, []),
 }
@@ -264,6 +265,24 @@ def aa_project_bwd_weight(plan: Plan, X, dY, dW_packed, M=None, pos_offset=0, ro
         _ptr(dW_packed, "dW_packed", plan.out_torch_dtype, plan.d_in * plan.d_out), M, int(pos_offset),
         _ptr(row_types, "row_types", torch.int32, M), _ptr(workspace, "workspace"), int(workspace_bytes),
         _stream(stream)), "aa_project_bwd_weight")
+
+
+def _event(ev):
+    if ev is None:
+        return None
+    if isinstance(ev, torch.cuda.Event):
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("aa_set_kernel_events: a torch.cuda.Event exists only after its first record()")
+        return h
+    return int(ev)
+
+
+def aa_set_kernel_events(start=None, stop=None):
+    """Hand the next kernel launched from this thread the start event and every
+    later one the stop event (torch.cuda.Event with timing, or raw handles);
+    (None, None) switches this off."""
+    _check(load().aa_set_kernel_events(_event(start), _event(stop)), "aa_set_kernel_events")
 
 
 # ----------------------------------------------------------- conveniences ---

@@ -1079,14 +1079,14 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
     constexpr int NFIc = decltype(nfi_c)::value, MFc = decltype(mf_c)::value, NS = decltype(nset_c)::value;
     if constexpr (NFIc <= 8) {
       if (pair) {
-        if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, 2, NS, true>), dim3(grid), dim3(256), lds, stream, P);
-        else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, 2, NS, true>), dim3(grid), dim3(256), lds, stream, P);
+        if (f32) launch((bwd_data_kernel<float, NFIc, MFc, 2, NS, true>), dim3(grid), dim3(256), lds, stream, P);
+        else launch((bwd_data_kernel<__bf16, NFIc, MFc, 2, NS, true>), dim3(grid), dim3(256), lds, stream, P);
         return;
       }
     }
     constexpr int KSc = NFIc <= 8 ? 4 : 2;
-    if (f32) hipLaunchKernelGGL((bwd_data_kernel<float, NFIc, MFc, KSc, NS, false>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_data_kernel<__bf16, NFIc, MFc, KSc, NS, false>), dim3(grid), dim3(256), lds, stream, P);
+    if (f32) launch((bwd_data_kernel<float, NFIc, MFc, KSc, NS, false>), dim3(grid), dim3(256), lds, stream, P);
+    else launch((bwd_data_kernel<__bf16, NFIc, MFc, KSc, NS, false>), dim3(grid), dim3(256), lds, stream, P);
   };
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
@@ -1111,8 +1111,8 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
     const int nparts = dsp.nparts;
     const int64_t n = M * (plan.b_in / 4);
     const int blocks = int(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
-    if (f32) hipLaunchKernelGGL((bwd_data_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, P, nparts);
-    else hipLaunchKernelGGL((bwd_data_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, P, nparts);
+    if (f32) launch((bwd_data_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, P, nparts);
+    else launch((bwd_data_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, P, nparts);
     st = after_launch(stream, "bwd_data_reduce");
   }
   return st;
@@ -1149,8 +1149,8 @@ aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* 
     int grid = device_cu_count() * 2;
     grid = (grid + kNumXcd - 1) / kNumXcd * kNumXcd;
     const size_t lds = size_t(2) * 2 * 64 * 128 * 2;
-    if (f32) hipLaunchKernelGGL((bwd_weight_tile_kernel<float>), dim3(grid), dim3(256), lds, stream, T);
-    else hipLaunchKernelGGL((bwd_weight_tile_kernel<__bf16>), dim3(grid), dim3(256), lds, stream, T);
+    if (f32) launch((bwd_weight_tile_kernel<float>), dim3(grid), dim3(256), lds, stream, T);
+    else launch((bwd_weight_tile_kernel<__bf16>), dim3(grid), dim3(256), lds, stream, T);
     aa_status_t st = after_launch(stream, "bwd_weight_tile");
     if (st != AA_OK || ts.P == 1) return st;
     BwdWeightParams R{};
@@ -1162,8 +1162,8 @@ aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* 
     R.nparts = ts.P;
     const int64_t n4 = int64_t(plan.q) * plan.b_in * plan.b_out / 4;
     const int blocks = int(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
-    if (f32) hipLaunchKernelGGL((bwd_weight_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, R);
-    else hipLaunchKernelGGL((bwd_weight_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, R);
+    if (f32) launch((bwd_weight_reduce_kernel<float>), dim3(blocks), dim3(256), 0, stream, R);
+    else launch((bwd_weight_reduce_kernel<__bf16>), dim3(blocks), dim3(256), 0, stream, R);
     return after_launch(stream, "bwd_weight_reduce");
   }
   const WeightShape sh = weight_shape(plan);
@@ -1191,11 +1191,11 @@ aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* 
   const int grid = int((n_items + kNumXcd - 1) / kNumXcd * kNumXcd);
   // four register sets (six measured slower: in-flight data beyond L2)
   if (sh.nfw == 2) {
-    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, 2, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, 2, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
+    if (f32) launch((bwd_weight_kernel<float, 2, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
+    else launch((bwd_weight_kernel<__bf16, 2, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
   } else {
-    if (f32) hipLaunchKernelGGL((bwd_weight_kernel<float, 1, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
-    else hipLaunchKernelGGL((bwd_weight_kernel<__bf16, 1, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
+    if (f32) launch((bwd_weight_kernel<float, 1, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
+    else launch((bwd_weight_kernel<__bf16, 1, 2, 4>), dim3(grid), dim3(256), lds, stream, P);
   }
   return after_launch(stream, "bwd_weight");
 }

@@ -6,6 +6,9 @@
 
 #include <string>
 
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
 #include "aa.h"
 
 // Host-side plan: immutable after aa_plan_create.
@@ -68,6 +71,23 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
                             int64_t pos_offset, void* ws, hipStream_t stream);
 aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
                               int64_t pos_offset, void* ws, hipStream_t stream);
+
+// Dispatch events set by aa_set_kernel_events for the calling thread: the
+// start event is handed out once (to the next launch), the stop event to every
+// launch until the events are set again.
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+KernelEvents take_kernel_events();
+
+// Every kernel of the library is launched through here, so that the timing
+// events reach the dispatch itself (hipExtLaunchKernel records them from the
+// kernel's own start and end).  Errors are picked up by after_launch.
+template <typename... Args, typename F = void (*)(Args...)>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream, Args... args) {
+  const KernelEvents ev = take_kernel_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev.start, ev.stop, 0u, args...);
+}
 
 // Compute units of the current device.
 int device_cu_count();

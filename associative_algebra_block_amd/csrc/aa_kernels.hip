@@ -1810,7 +1810,7 @@ struct Variant {
 
 template <typename Tin, typename Tout, int WN, int WM, int NF, int MF, bool SW, int ST>
 void launch_variant(LeafParams p, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_gemm_kernel<Tin, Tout, WN, WM, NF, MF, SW, ST>), grid, block, 0, s, p);
+  launch((leaf_gemm_kernel<Tin, Tout, WN, WM, NF, MF, SW, ST>), grid, block, 0, s, p);
 }
 
 #define AA_VARIANT(ID, WN, WM, NF, MF, ST)                                                        \
@@ -1851,7 +1851,7 @@ struct StreamVariant {
 
 template <int WN, int WM, int NF, int MF, int CK, int GC, bool DB, bool SW, typename Tout>
 void launch_stream(LeafParams p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_stream_kernel<WN, WM, NF, MF, CK, GC, DB, SW, Tout>), grid, block, lds, s, p);
+  launch((leaf_stream_kernel<WN, WM, NF, MF, CK, GC, DB, SW, Tout>), grid, block, lds, s, p);
 }
 
 // SwiGLU instances hold two weight streams, so they use half the group.
@@ -1891,7 +1891,7 @@ struct PersistVariant {
 
 template <int NF, int MF, int CK, int NCH, bool SW, int POL, typename Tout>
 void launch_persist(LeafParams p, dim3 grid, dim3 block, size_t, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_persist_kernel<NF, MF, CK, NCH, SW, POL, Tout>), grid, block, 0, s, p);
+  launch((leaf_persist_kernel<NF, MF, CK, NCH, SW, POL, Tout>), grid, block, 0, s, p);
 }
 
 #define AA_PL(NF, MF, CK, NCH, SW, T)                                                            \
@@ -1932,7 +1932,7 @@ struct JobVariant {
 
 template <int NF, int MF, int CK, int NSET, bool SW, int POL, typename Tout>
 void launch_job(JobParams p, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_job_kernel<NF, MF, CK, NSET, SW, POL, Tout>), grid, block, 0, s, p);
+  launch((leaf_job_kernel<NF, MF, CK, NSET, SW, POL, Tout>), grid, block, 0, s, p);
 }
 
 #define AA_JL(NF, MF, CK, NSET, SW, T)                                                               \
@@ -1976,7 +1976,7 @@ struct KStreamVariant {
 
 template <int NF, int MF, int CK, int NSET, bool SW, int POL, typename Tout>
 void launch_kstream(LeafParams p, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((leaf_kstream_kernel<NF, MF, CK, NSET, SW, POL, Tout>), grid, block, 0, s, p);
+  launch((leaf_kstream_kernel<NF, MF, CK, NSET, SW, POL, Tout>), grid, block, 0, s, p);
 }
 
 #define AA_KL(NF, MF, CK, NSET, SW, T)                                                                       \
@@ -2217,11 +2217,11 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
     const dim3 grid{uint32_t(n_tiles), 1, 1}, block{256, 1, 1};
     const bool fout = plan.out_dtype == AA_F32;
     if (call.swiglu) {
-      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<true, 3, float>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((leaf_tile_kernel<true, 3, __bf16>), grid, block, 0, stream, p);
+      if (fout) launch((leaf_tile_kernel<true, 3, float>), grid, block, 0, stream, p);
+      else launch((leaf_tile_kernel<true, 3, __bf16>), grid, block, 0, stream, p);
     } else {
-      if (fout) hipLaunchKernelGGL((leaf_tile_kernel<false, 3, float>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((leaf_tile_kernel<false, 3, __bf16>), grid, block, 0, stream, p);
+      if (fout) launch((leaf_tile_kernel<false, 3, float>), grid, block, 0, stream, p);
+      else launch((leaf_tile_kernel<false, 3, __bf16>), grid, block, 0, stream, p);
     }
     return after_launch(stream, call.swiglu ? "leaf_tile(swiglu)" : "leaf_tile");
   }
@@ -2403,11 +2403,11 @@ aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool 
   if (n_runs == 0) return AA_OK;
   const dim3 block{256, 1, 1}, grid{uint32_t((n_runs + 255) / 256), 1, 1};
   if (plan.in_dtype == AA_BF16)
-    hipLaunchKernelGGL(pack_kernel<__bf16>, grid, block, 0, stream, static_cast<const __bf16*>(src),
+    launch(pack_kernel<__bf16>, grid, block, 0, stream, static_cast<const __bf16*>(src),
                        static_cast<__bf16*>(dst), plan.q, int32_t(plan.b_in), int32_t(plan.b_out), plan.d_out,
                        n_runs, unpack);
   else
-    hipLaunchKernelGGL(pack_kernel<float>, grid, block, 0, stream, static_cast<const float*>(src),
+    launch(pack_kernel<float>, grid, block, 0, stream, static_cast<const float*>(src),
                        static_cast<float*>(dst), plan.q, int32_t(plan.b_in), int32_t(plan.b_out), plan.d_out,
                        n_runs, unpack);
   return after_launch(stream, unpack ? "unpack" : "pack");
@@ -2445,17 +2445,17 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, c
     if (W1 != nullptr) {   // SwiGLU gate/up (bf16 input; the caller checked KF <= 8)
       if constexpr (KFc <= 8) {
         if (fin) return false;
-        if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float, TGc, KFc, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((decode_kernel<__bf16, __bf16, TGc, KFc, true>), grid, block, 0, stream, p);
+        if (fout) launch((decode_kernel<__bf16, float, TGc, KFc, true>), grid, block, 0, stream, p);
+        else launch((decode_kernel<__bf16, __bf16, TGc, KFc, true>), grid, block, 0, stream, p);
         return true;
       } else {
         return false;
       }
     }
-    if (fin && fout) hipLaunchKernelGGL((decode_kernel<float, float, TGc, KFc>), grid, block, 0, stream, p);
-    else if (fin) hipLaunchKernelGGL((decode_kernel<float, __bf16, TGc, KFc>), grid, block, 0, stream, p);
-    else if (fout) hipLaunchKernelGGL((decode_kernel<__bf16, float, TGc, KFc>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<__bf16, __bf16, TGc, KFc>), grid, block, 0, stream, p);
+    if (fin && fout) launch((decode_kernel<float, float, TGc, KFc>), grid, block, 0, stream, p);
+    else if (fin) launch((decode_kernel<float, __bf16, TGc, KFc>), grid, block, 0, stream, p);
+    else if (fout) launch((decode_kernel<__bf16, float, TGc, KFc>), grid, block, 0, stream, p);
+    else launch((decode_kernel<__bf16, __bf16, TGc, KFc>), grid, block, 0, stream, p);
     return true;
   };
   using I1 = std::integral_constant<int, 1>;

@@ -19,6 +19,14 @@ namespace aa {
 
 static thread_local std::string g_last_error;
 
+static thread_local KernelEvents g_kernel_events = {nullptr, nullptr};
+
+KernelEvents take_kernel_events() {
+  const KernelEvents ev = g_kernel_events;
+  g_kernel_events.start = nullptr;
+  return ev;
+}
+
 void set_error(const std::string& msg) { g_last_error = msg; }
 void clear_error() { g_last_error.clear(); }
 aa_status_t fail(aa_status_t st, const std::string& msg) {
@@ -66,6 +74,12 @@ const char* aa_status_string(aa_status_t s) {
 }
 
 const char* aa_last_error(void) { return aa::g_last_error.c_str(); }
+
+aa_status_t aa_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
+  aa::g_kernel_events.start = start;
+  aa::g_kernel_events.stop = stop;
+  return AA_OK;
+}
 
 aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in, int64_t d_out,
                            aa_type_kind_t type_kind, int64_t period, aa_dtype_t in_dtype,

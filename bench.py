@@ -13,12 +13,17 @@ cannot hold a step's working set (a flushed-cache measurement).
 
 Printed (one JSON line): dense-equivalent TFLOP/s of the step (2 M d_in d_out
 per dense projection counted for every projection in the step), the roofline of
-the projection kernel (algorithmic HBM bytes / its event-timed duration), the
-same for every call, a dense bf16 torch.matmul comparator timed in the same
-run, and the fp64 oracle timed on the host on a bounded sample.
+the projection kernel (algorithmic HBM bytes / its duration), the same for
+every call, a dense bf16 torch.matmul comparator timed in the same run, and the
+fp64 oracle timed on the host on a bounded sample.  Call durations come from HIP
+events that the library records from the kernels' own dispatches
+(aa_set_kernel_events) inside the timed steps, so they match a kernel trace;
+the step time comes from events around the K steps and includes the gaps
+between kernels.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
-                    [--workload qwen3_8b_q32|square|pilot_ffn|expert_ffn|qwen3_1p7b]
+                    [--workload qwen3_8b_q32|square|pilot_ffn|expert_ffn|qwen3_1p7b|qwen3_8b_down|
+                                backward_qwen3_8b|backward_expert]
 """
 from __future__ import annotations
 
@@ -49,6 +54,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="Qwen3-8B step and projections: skip the one-token and back-to-back measurements "
+                         "(a kernel trace then holds only the warmup and timed calls)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a 1 GiB device-to-device copy (reference kernel for HBM byte counters)")
@@ -100,6 +108,44 @@ def main():
 
 def _ev(torch):
     return torch.cuda.Event(enable_timing=True)
+
+
+class KernelTimer:
+    """Durations of library calls taken from their own kernel dispatches
+    (aa_set_kernel_events): the start event is a marker recorded just before
+    the call's first dispatch, the stop event is recorded by its last kernel,
+    so the queue time between calls is not counted.  An armed launch costs the
+    host about 13 us more than a plain one, so one call per step is armed, in
+    turn (step s times call s mod calls), which keeps small-kernel steps from
+    waiting on the host.  Events are recorded once at creation because torch
+    creates an event at its first record."""
+
+    def __init__(self, torch, aa, steps, calls):
+        if steps < calls:
+            raise SystemExit(f"--steps must be at least {calls} here (one call of the step is timed per step)")
+        self.aa, self.calls, self.armed = aa, calls, False
+        self.ev = [(_ev(torch), _ev(torch)) for _ in range(steps)]
+        for pair in self.ev:
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
+
+    def arm(self, step, call):
+        if step % self.calls == call:
+            self.aa.aa_set_kernel_events(*self.ev[step])
+            self.armed = True
+        else:
+            self.disarm()
+
+    def disarm(self):
+        if self.armed:
+            self.aa.aa_set_kernel_events(None, None)
+            self.armed = False
+
+    def ms(self, call):
+        """Mean duration of the call over the steps that timed it, in ms."""
+        t = [a.elapsed_time(b) for s, (a, b) in enumerate(self.ev) if s % self.calls == call]
+        return sum(t) / len(t) if t else float("nan")
 
 
 def kernel_source_hash():
@@ -198,37 +244,35 @@ def bench_qwen3(args, torch, inp, aa, dev):
     torch.cuda.synchronize()
     pos_dec = 4096  # decode positions 4096 .. 4127: one token of every type
 
-    def step(st, evs=None):
-        if evs is not None:
-            evs[0].record()
+    def step(st, kt=None, s=0):
+        if kt:
+            kt.arm(s, 0)
         aa.aa_project_fwd(plan, st["X"], st["Wp"], st["Y"])
-        if evs is not None:
-            evs[1].record()
+        if kt:
+            kt.arm(s, 1)
         aa.aa_swiglu_ffn_fwd(plan, down, st["X"], st["Wgp"], st["Wup"], st["Wdp"], st["H"], st["Y2"])
-        if evs is not None:
-            evs[2].record()
+        if kt:
+            kt.arm(s, 2)
         aa.aa_decode_gemv(plan, st["x"], st["Wp"], st["y"], None, pos_dec)
-        if evs is not None:
-            evs[3].record()
+        if kt:
+            kt.disarm()
 
     for w in range(args.warmup):
         step(sets[w % n_sets])
     torch.cuda.synchronize()
     K = args.steps
-    evs = [[_ev(torch) for _ in range(4)] for _ in range(K)]
+    kt = KernelTimer(torch, aa, K, 3)
     t0e, t1e = _ev(torch), _ev(torch)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0e.record()
     for s in range(K):
-        step(sets[s % n_sets], evs[s])
+        step(sets[s % n_sets], kt, s)
     t1e.record()
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
     ms_step = t0e.elapsed_time(t1e) / K
-    ms_proj = sum(e[0].elapsed_time(e[1]) for e in evs) / K
-    ms_swi = sum(e[1].elapsed_time(e[2]) for e in evs) / K
-    ms_dec = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    ms_proj, ms_swi, ms_dec = kt.ms(0), kt.ms(1), kt.ms(2)
 
     dense_flops = {"project": 2.0 * M * D * F, "swiglu": 3 * 2.0 * M * D * F, "decode": 2.0 * n_dec * D * F}
     total_dense = sum(dense_flops.values())
@@ -268,10 +312,12 @@ def bench_qwen3(args, torch, inp, aa, dev):
                  "speedup_step": round((t_p + t_s + t_d) / ms_step, 3)}
         del Wd1, Wd2, Wd3
 
-    dec1 = decode_single_token(torch, aa, plan, sets, pos_dec, n_dec, D, F, q,
-                               None if dense is None else sets[0])
-    ffn1 = ffn_single_token(torch, aa, plan, down, sets, pos_dec, n_dec, D, F, q, dense is not None)
-    alone = projection_alone(torch, aa, plan, [(st["X"], st["Wp"], st["Y"]) for st in sets], b_proj)
+    dec1 = ffn1 = alone = None
+    if not args.no_extras:
+        dec1 = decode_single_token(torch, aa, plan, sets, pos_dec, n_dec, D, F, q,
+                                   None if dense is None else sets[0])
+        ffn1 = ffn_single_token(torch, aa, plan, down, sets, pos_dec, n_dec, D, F, q, dense is not None)
+        alone = projection_alone(torch, aa, plan, [(st["X"], st["Wp"], st["Y"]) for st in sets], b_proj)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -287,6 +333,9 @@ def bench_qwen3(args, torch, inp, aa, dev):
                    "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
         "roofline": parts["project"]["roofline"],
         "roofline_kernel": "aa_project_fwd at the Qwen3-8B shape (leaf_persist_kernel)",
+        "timing": "parts: kernel dispatch events of each call (first kernel start to last kernel end); "
+                  "ms_per_step: events around the K steps",
+        "ms_between_kernels": round(ms_step - ms_proj - ms_swi - ms_dec, 5),
         "parts": parts, "projection_alone": alone, "decode_single_token": dec1, "ffn_single_token": ffn1,
         "dense": dense,
         "cpu_baseline": cpu,
@@ -339,29 +388,36 @@ def bench_projection(args, torch, inp, aa, dev, wl):
         aa.aa_project_fwd(plan, X, Wp, Y)
     torch.cuda.synchronize()
     K = args.steps
+    kt = KernelTimer(torch, aa, K, 1)
     a, b = _ev(torch), _ev(torch)
     a.record()
     for s in range(K):
         X, Wp, Y = sets[s % n_sets]
+        kt.arm(s, 0)
         aa.aa_project_fwd(plan, X, Wp, Y)
+    kt.disarm()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / K
-    alone = projection_alone(torch, aa, plan, sets, per_set)
+    ms_k = kt.ms(0)
+    alone = None if args.no_extras else projection_alone(torch, aa, plan, sets, per_set)
     dense = None
     if not args.no_dense:
         Wd = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
         X0 = sets[0][0]
         t = dense_timer(torch, lambda: torch.matmul(X0, Wd))
         dense = {"kind": "torch.matmul bf16 (hipBLASLt), hot cache", "ms": round(t, 5),
-                 "speedup_flushed": round(t / ms, 3), "speedup_hot": round(t / alone["hot"]["ms"], 3)}
+                 "speedup_flushed": round(t / ms, 3)}
+        if alone:
+            dense["speedup_hot"] = round(t / alone["hot"]["ms"], 3)
     return {"metric": f"dense-equiv TFLOP/s + % roofline, {wl.name} projection bf16",
             "value": round(2.0 * M * D * F / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": wl.name, "M": M, "d_in": D, "d_out": F, "q": q, "law": wl.law,
                        "type_map": "pos mod q", "input_sets": n_sets},
-            "roofline": roofline(per_set, ms), "projection_alone": alone, "dense": dense,
+            "roofline": roofline(per_set, ms_k), "kernel_ms": round(ms_k, 5), "projection_alone": alone,
+            "dense": dense,
             "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / (ms * 1e-3) / 1e12, 2),
             "kernel_source": kernel_source_hash()}
 
@@ -402,35 +458,35 @@ def bench_backward(args, torch, inp, aa, dev, which):
     torch.cuda.synchronize()
     calls = [(n, kind) for n, _, _ in shapes for kind in ("dX", "dW")]
 
-    def step(st, evs=None):
+    def step(st, kt=None, s=0):
         for c, (n, kind) in enumerate(calls):
-            if evs is not None:
-                evs[c].record()
+            if kt:
+                kt.arm(s, c)
             b = st[n]
             if kind == "dX":
                 aa.aa_project_bwd_data(plans[n], b["dY"], b["Wp"], b["dX"], None, 0, None, b["wsd"], b["nd"])
             else:
                 aa.aa_project_bwd_weight(plans[n], b["X"], b["dY"], b["dWp"], None, 0, None, b["wsw"], b["nw"])
-        if evs is not None:
-            evs[len(calls)].record()
+        if kt:
+            kt.disarm()
 
     for w in range(args.warmup):
         step(sets[w % n_sets])
     torch.cuda.synchronize()
     K = args.steps
-    evs = [[_ev(torch) for _ in range(len(calls) + 1)] for _ in range(K)]
+    kt = KernelTimer(torch, aa, K, len(calls))
     a, b = _ev(torch), _ev(torch)
     torch.cuda.synchronize()
     a.record()
     for s_ in range(K):
-        step(sets[s_ % n_sets], evs[s_])
+        step(sets[s_ % n_sets], kt, s_)
     b.record()
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / K
     dims = {n: (di, do) for n, di, do in shapes}
     parts = {}
     for c, (n, kind) in enumerate(calls):
-        ms = sum(e[c].elapsed_time(e[c + 1]) for e in evs) / K
+        ms = kt.ms(c)
         di, do = dims[n]
         parts[f"{n}_{kind}"] = {"ms": round(ms, 5), "roofline": roofline(2 * (M * di + di * do + M * do), ms),
                                 "exec_tflops": round(exec_flops(M, di, do, "Qq", q) / (ms * 1e-3) / 1e12, 2)}
@@ -461,6 +517,8 @@ def bench_backward(args, torch, inp, aa, dev, which):
                        "projections": [{"name": n, "d_in": di, "d_out": do} for n, di, do in shapes],
                        "input_sets": n_sets, "cache": "flushed (rotating input sets)"},
             "roofline": big[1]["roofline"], "roofline_kernel": big[0], "parts": parts, "dense": dense,
+            "timing": "parts: kernel dispatch events of each call (its main kernel and partial-sum reduction); "
+                      "ms_per_step: events around the K steps",
             "cpu_baseline": cpu, "kernel_source": kernel_source_hash()}
 
 
@@ -673,13 +731,17 @@ def bench_square(args, torch, inp, aa, dev):
         aa.aa_project_fwd(plan, X, Wp, Y)
     torch.cuda.synchronize()
     K = args.steps
+    kt = KernelTimer(torch, aa, K, 1)
     a, b = _ev(torch), _ev(torch)
     a.record()
-    for _ in range(K):
+    for s in range(K):
+        kt.arm(s, 0)
         aa.aa_project_fwd(plan, X, Wp, Y)
+    kt.disarm()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / K
+    ms_k = kt.ms(0)
     dense = 2.0 * n ** 3
     by = proj_bytes(n, n, n)
     res = {"metric": "dense-equiv TFLOP/s + % roofline, square n=32768 b=128 q=256 bf16",
@@ -687,7 +749,7 @@ def bench_square(args, torch, inp, aa, dev):
            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "square_n32768_b128_q256", "n": n, "q": q, "law": "Qq", "type_map": "block rows"},
-           "roofline": roofline(by, ms, traffic_for("project_square_n32768")),
+           "roofline": roofline(by, ms_k, traffic_for("project_square_n32768")), "kernel_ms": round(ms_k, 5),
            "exec_tflops": round(exec_flops(n, n, n, "Qq", q) / ms / 1e9, 2),
            "kernel_source": kernel_source_hash()}
     if not args.no_dense:

@@ -73,6 +73,20 @@ def pmc(d, counter):
 
 
 
+def bench_durations(log):
+    """Per-call durations (ms) from the JSON line bench.py printed."""
+    rec = None
+    with open(log) as f:
+        for line in f:
+            if line.startswith('{"metric"'):
+                rec = json.loads(line)
+    if rec is None:
+        raise SystemExit(f"no bench.py result line in {log}")
+    if "parts" in rec:
+        return {k: v["ms"] for k, v in rec["parts"].items()}
+    return {"projection": rec["kernel_ms"]} if "kernel_ms" in rec else {}
+
+
 def is_calibration_copy(name):
     return "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name
 
@@ -88,6 +102,9 @@ def main():
     ap.add_argument("--key", default=None, help="traffic.json key for the projection kernel")
     ap.add_argument("--alg-bytes", type=float, default=None, help="algorithmic bytes per projection launch")
     ap.add_argument("--match", default="leaf_", help="substring naming the projection kernel instance")
+    ap.add_argument("--bench-log", default=None,
+                    help="output of the same bench.py command run without the tracer just before")
+    ap.add_argument("--bench-log-traced", default=None, help="output of the traced bench.py run")
     a = ap.parse_args()
     os.makedirs(PROFILES, exist_ok=True)
     src = kernel_source_hash()
@@ -101,6 +118,20 @@ def main():
     for k in ks:
         lines.append(f"| `{short(k['name'])}` | {k['grid']} | {k['calls']} | {k['avg_us']:.2f} | "
                      f"{k['min_us']:.2f} | {k['max_us']:.2f} | {k['pct']:.1f} |")
+    if a.bench_log or a.bench_log_traced:
+        plain = bench_durations(a.bench_log) if a.bench_log else {}
+        traced = bench_durations(a.bench_log_traced) if a.bench_log_traced else {}
+        lines += ["", "bench.py's own durations of each call, mean over its timed calls (HIP events: the start "
+                      "event is a marker recorded just before the call's first dispatch, the stop event is "
+                      "recorded by its last kernel).  Under the tracer every dispatch starts 4-5 us after the "
+                      "marker before it, a gap the trace's kernel durations do not contain; without the tracer "
+                      "the same command gives the first column.  The trace's averages above also hold the "
+                      "warmup calls.", "",
+                      "| call | bench.py, no tracer (same command, run just before) | bench.py in the traced run |",
+                      "|---|---|---|"]
+        for k in sorted(set(plain) | set(traced), key=lambda k: list(plain or traced).index(k)):
+            f = lambda d: f"{d[k] * 1e3:.2f} us" if k in d else "-"
+            lines.append(f"| {k} | {f(plain)} | {f(traced)} |")
     with open(os.path.join(PROFILES, f"{a.name}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines[:14]))

@@ -183,6 +183,20 @@ aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY,
                                   int64_t pos_offset, const int32_t* row_types, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* Kernel timing, for measurement only (no part of the method).  After
+ * aa_set_kernel_events(start, stop) the next kernel that a call of this
+ * library launches from the calling thread records `start` at the beginning
+ * of its own dispatch, and every kernel launched from this thread after that
+ * records `stop` at the end of its dispatch, until the next
+ * aa_set_kernel_events call; (NULL, NULL) switches this off.  Once the stream
+ * has passed the call, hipEventElapsedTime(start, stop) is the time from the
+ * start of its first kernel to the end of its last one, without the queue
+ * time before the first kernel.  The events must have been created with
+ * timing enabled on the device that runs the kernels and stay owned by the
+ * caller; either may be NULL.  The setting is per thread.  Always returns
+ * AA_OK and makes no HIP call. */
+aa_status_t aa_set_kernel_events(hipEvent_t start, hipEvent_t stop);
+
 /* A static English name of a status code. */
 const char* aa_status_string(aa_status_t status);
 

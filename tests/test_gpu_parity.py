@@ -307,6 +307,36 @@ def test_deterministic_and_pos_shift():
     assert_parity(host(outs[3]), ref, True, "shift by one")
 
 
+def test_kernel_events_time_the_dispatch():
+    """aa_set_kernel_events: the events are recorded by the kernel's own
+    dispatch, so the time is positive and no longer than marker events around
+    the call; switching them off leaves later calls untimed; results do not
+    change."""
+    law, q, M, d_in, d_out = "Qq", 32, 2048, 4096, 12288
+    say("kernel events", law, q, M, d_in, d_out)
+    plan, X, W = _make(law, q, M, d_in, d_out, "bf16", "bf16", seed=71)
+    Wp = aa.pack(plan, W)
+    Ys = [torch.empty(M, d_out, dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    aa.aa_project_fwd(plan, X, Wp, Ys[0])
+    ks, ke, a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(5))
+    ks.record()
+    ke.record()
+    torch.cuda.synchronize()
+    a.record()
+    aa.aa_set_kernel_events(ks, ke)
+    aa.aa_project_fwd(plan, X, Wp, Ys[1])
+    aa.aa_set_kernel_events(None, None)
+    b.record()
+    aa.aa_project_fwd(plan, X, Wp, Ys[2])
+    c.record()
+    torch.cuda.synchronize()
+    tk, tm, tm2 = ks.elapsed_time(ke), a.elapsed_time(b), a.elapsed_time(c)
+    say("kernel events ms", tk, tm, tm2)
+    assert 0.0 < tk <= tm + 1e-3, (tk, tm)
+    assert tk < 0.75 * tm2, (tk, tm2)
+    assert torch.equal(Ys[0], Ys[1]) and torch.equal(Ys[0], Ys[2])
+
+
 def test_period_and_empty():
     law, q, M, d_in, d_out = "Q2xQ2", 4, 3 * 24, 256, 512
     say("period", law, q, M)
