@@ -862,12 +862,24 @@ __global__ __launch_bounds__(256, 2) void leaf_job_kernel(JobParams p) {
     w = r2 % base;
     s_job = base;
   }
-  const int tiles = q * p.mt_count;
-  // (Contiguous ranges measure better than dealing the tiles in turn: with
-  // every workgroup on the same row type at once, the traffic concentrates
-  // on one row block of X, W and Y at a time.)
-  const int u_begin = int(int64_t(tiles) * w / s_job);
-  const int u_end = int(int64_t(tiles) * (w + 1) / s_job);
+  // Tiles of the job are (type, m-tile) pairs, type-major.  When the job's
+  // workgroups are a multiple of its m-tiles, each takes one m-tile over a
+  // contiguous range of types, so the m-tiles of a type are multiplied at
+  // the same time on different workgroups and its own weight strip W_ik
+  // comes from HBM once (read one tile apart by one workgroup, it was often
+  // evicted from L2 in between: the square product read 1.096x its
+  // algorithmic bytes that way, 1.018x this way).  Otherwise each
+  // takes a contiguous range of the (type, m-tile) order.  (Contiguous
+  // ranges measure better than dealing the tiles in turn: with every
+  // workgroup on the same row type at once, the traffic concentrates on one
+  // row block of X, W and Y at a time.)
+  const bool by_mt = p.mt_count > 1 && s_job % p.mt_count == 0;
+  const int n_sub = by_mt ? s_job / p.mt_count : s_job;
+  const int w_sub = by_mt ? w / p.mt_count : w;
+  const int my_mt = by_mt ? w % p.mt_count : 0;
+  const int tiles = by_mt ? q : q * p.mt_count;
+  const int u_begin = int(int64_t(tiles) * w_sub / n_sub);
+  const int u_end = int(int64_t(tiles) * (w_sub + 1) / n_sub);
   const int n_my = u_end - u_begin;
   if (n_my <= 0) return;
 
@@ -911,8 +923,8 @@ __global__ __launch_bounds__(256, 2) void leaf_job_kernel(JobParams p) {
   auto setup = [&](int u, Tile& T) __attribute__((always_inline)) {
     T.valid = u < n_my;
     const int ug = u_begin + (T.valid ? u : 0);
-    T.i = p.mt_count == 1 ? ug : ug / p.mt_count;
-    const int mt = ug - T.i * p.mt_count;
+    T.i = by_mt || p.mt_count == 1 ? ug : ug / p.mt_count;
+    const int mt = by_mt ? my_mt : ug - T.i * p.mt_count;
     int64_t count;
     if (p.kind == AA_TYPES_BLOCK_ROWS) {
       T.first = int64_t(T.i) * p.rows_per_type;

@@ -142,10 +142,20 @@ class KernelTimer:
             self.aa.aa_set_kernel_events(None, None)
             self.armed = False
 
+    def samples(self, call):
+        return [a.elapsed_time(b) for s, (a, b) in enumerate(self.ev) if s % self.calls == call]
+
     def ms(self, call):
         """Mean duration of the call over the steps that timed it, in ms."""
-        t = [a.elapsed_time(b) for s, (a, b) in enumerate(self.ev) if s % self.calls == call]
-        return sum(t) / len(t) if t else float("nan")
+        t = self.samples(call)
+        return sum(t) / len(t)
+
+    def spread(self, call):
+        """Median, 10th and 90th percentile of the call's durations (ms)."""
+        t = sorted(self.samples(call))
+        q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+        return {"median_ms": round(q(0.5), 5), "p10_ms": round(q(0.1), 5), "p90_ms": round(q(0.9), 5),
+                "samples": len(t)}
 
 
 def kernel_source_hash():
@@ -283,13 +293,16 @@ def bench_qwen3(args, torch, inp, aa, dev):
     b_dec = 2 * (n_dec * D + D * F + n_dec * F)
     ex_proj = exec_flops(M, D, F, law, q)
     parts = {
-        "project": {"ms": round(ms_proj, 5), "dense_equiv_tflops": round(dense_flops["project"] / ms_proj / 1e9, 2),
+        "project": {"ms": round(ms_proj, 5), **kt.spread(0),
+                    "dense_equiv_tflops": round(dense_flops["project"] / ms_proj / 1e9, 2),
                     "exec_tflops": round(ex_proj / ms_proj / 1e9, 2),
                     "roofline": roofline(b_proj, ms_proj, traffic_for("project_qwen3_8b_q32"))},
-        "swiglu": {"ms": round(ms_swi, 5), "dense_equiv_tflops": round(dense_flops["swiglu"] / ms_swi / 1e9, 2),
+        "swiglu": {"ms": round(ms_swi, 5), **kt.spread(1),
+                   "dense_equiv_tflops": round(dense_flops["swiglu"] / ms_swi / 1e9, 2),
                    "exec_tflops": round(3 * ex_proj / ms_swi / 1e9, 2),
                    "roofline": roofline(b_swi, ms_swi)},
-        "decode32": {"ms": round(ms_dec, 5), "dense_equiv_tflops": round(dense_flops["decode"] / ms_dec / 1e9, 3),
+        "decode32": {"ms": round(ms_dec, 5), **kt.spread(2),
+                     "dense_equiv_tflops": round(dense_flops["decode"] / ms_dec / 1e9, 3),
                      "roofline": roofline(b_dec, ms_dec)},
     }
 
@@ -416,7 +429,8 @@ def bench_projection(args, torch, inp, aa, dev, wl):
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": wl.name, "M": M, "d_in": D, "d_out": F, "q": q, "law": wl.law,
                        "type_map": "pos mod q", "input_sets": n_sets},
-            "roofline": roofline(per_set, ms_k), "kernel_ms": round(ms_k, 5), "projection_alone": alone,
+            "roofline": roofline(per_set, ms_k), "kernel_ms": round(ms_k, 5), "kernel_spread": kt.spread(0),
+            "projection_alone": alone,
             "dense": dense,
             "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / (ms * 1e-3) / 1e12, 2),
             "kernel_source": kernel_source_hash()}
@@ -488,7 +502,8 @@ def bench_backward(args, torch, inp, aa, dev, which):
     for c, (n, kind) in enumerate(calls):
         ms = kt.ms(c)
         di, do = dims[n]
-        parts[f"{n}_{kind}"] = {"ms": round(ms, 5), "roofline": roofline(2 * (M * di + di * do + M * do), ms),
+        parts[f"{n}_{kind}"] = {"ms": round(ms, 5), **kt.spread(c),
+                                "roofline": roofline(2 * (M * di + di * do + M * do), ms),
                                 "exec_tflops": round(exec_flops(M, di, do, "Qq", q) / (ms * 1e-3) / 1e12, 2)}
     dense_flops = sum(2 * 2.0 * M * di * do for _, di, do in shapes)
     dense = None
@@ -750,6 +765,7 @@ def bench_square(args, torch, inp, aa, dev):
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "square_n32768_b128_q256", "n": n, "q": q, "law": "Qq", "type_map": "block rows"},
            "roofline": roofline(by, ms_k, traffic_for("project_square_n32768")), "kernel_ms": round(ms_k, 5),
+           "kernel_spread": kt.spread(0),
            "exec_tflops": round(exec_flops(n, n, n, "Qq", q) / ms / 1e9, 2),
            "kernel_source": kernel_source_hash()}
     if not args.no_dense:

@@ -73,8 +73,7 @@ def pmc(d, counter):
 
 
 
-def bench_durations(log):
-    """Per-call durations (ms) from the JSON line bench.py printed."""
+def bench_record(log):
     rec = None
     with open(log) as f:
         for line in f:
@@ -82,6 +81,25 @@ def bench_durations(log):
                 rec = json.loads(line)
     if rec is None:
         raise SystemExit(f"no bench.py result line in {log}")
+    return rec
+
+
+def last_calls(d, match, n):
+    """Name, count and mean duration (us) of the last n dispatches of the
+    longest-running kernel whose name contains `match`."""
+    c = _db(d)
+    names = [r[0] for r in c.execute("select name, sum(end - start) s from kernels group by name order by s desc")
+             if match in r[0]]
+    if not names:
+        return None
+    durs = [r[0] for r in c.execute("select end - start from kernels where name = ? order by start", (names[0],))]
+    tail = durs[-n:]
+    return names[0], len(tail), sum(tail) / len(tail) / 1e3
+
+
+def bench_durations(log):
+    """Per-call durations (ms) from the JSON line bench.py printed."""
+    rec = bench_record(log)
     if "parts" in rec:
         return {k: v["ms"] for k, v in rec["parts"].items()}
     return {"projection": rec["kernel_ms"]} if "kernel_ms" in rec else {}
@@ -132,6 +150,11 @@ def main():
         for k in sorted(set(plain) | set(traced), key=lambda k: list(plain or traced).index(k)):
             f = lambda d: f"{d[k] * 1e3:.2f} us" if k in d else "-"
             lines.append(f"| {k} | {f(plain)} | {f(traced)} |")
+        if a.bench_log_traced and a.match:
+            lc = last_calls(a.trace, a.match, int(bench_record(a.bench_log_traced)["steps"]))
+            if lc:
+                lines += ["", f"Trace average of `{short(lc[0], 60)}` over its last {lc[1]} dispatches (the "
+                              f"timed steps, one call each): {lc[2]:.2f} us."]
     with open(os.path.join(PROFILES, f"{a.name}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines[:14]))
@@ -162,10 +185,10 @@ def main():
             w = wr.get(n, 0) * 1024 * w_fac
             lines.append(f"| `{short(n)}` | {fe.get(n, 0):.0f} | {wr.get(n, 0):.0f} | {r / 1e6:.2f} | "
                          f"{w / 1e6:.2f} | {(r + w) / 1e6:.2f} |")
-            if a.match in n:
+            if a.match in n and not traffic:   # the largest matching kernel
                 traffic = {"read_bytes": r, "write_bytes": w, "hbm_bytes_per_launch": r + w, "kernel": n}
         if traffic and a.alg_bytes:
-            lines += ["", f"Projection kernel: {traffic['hbm_bytes_per_launch'] / 1e6:.2f} MB measured per launch "
+            lines += ["", f"`{short(traffic['kernel'], 60)}`: {traffic['hbm_bytes_per_launch'] / 1e6:.2f} MB measured per launch "
                           f"against {a.alg_bytes / 1e6:.2f} MB algorithmic "
                           f"({traffic['hbm_bytes_per_launch'] / a.alg_bytes:.3f}x)."]
         with open(os.path.join(PROFILES, f"{a.name}_hbm_traffic.md"), "w") as f:
