@@ -162,6 +162,7 @@ def test_every_tile_variant_agrees():
     (8, 20, 1024, 1536, "pos_mod"),        # fewer tiles than pipeline stages
     (16, 2048, 2048, 768, "pos_mod"),      # 48-wide output blocks (ragged strips)
     (64, 8192, 8192, 8192, "block_rows"),  # several m-tiles per leaf
+    (16, 2048, 2048, 6144, "block_rows"),  # jobs of 11 and 10 workgroups over 2 m-tiles: both tile splits
 ])
 def test_job_kernel_variants(q, M, d_in, d_out, kind):
     """Each pipelined job-kernel variant, bf16 output, against the oracle."""
