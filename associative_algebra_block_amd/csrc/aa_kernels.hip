@@ -1439,24 +1439,27 @@ __global__ __launch_bounds__(256, 2) void leaf_tile_kernel(LeafParams p) {
   const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
   Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
 
-  // ---- tile: leaf (in order of decreasing input-group count), m-tile, n-tile
-  const int per_leaf = p.mt_count * p.nt_count;
-  const int lo = int(blockIdx.x) / per_leaf;
-  const int rem = int(blockIdx.x) - lo * per_leaf;
-  const int mt = rem / p.nt_count, nt = rem - mt * p.nt_count;
-  int i, k;
-  if (p.law == AA_LAW_QQ) {
-    if (lo < q * (q - 1)) {   // off-diagonal leaves (two groups) first
-      i = lo / (q - 1);
-      const int j = lo - i * (q - 1);
-      k = j < i ? j : j + 1;
-    } else {
-      i = k = lo - q * (q - 1);
-    }
-  } else {   // Q2 x Q2: i ^ k = 3 (four groups), then 2 and 1 (two), then 0 (one)
-    i = lo & 3;
-    k = i ^ (3 - (lo >> 2));
-  }
+  // ---- tile, XCD-aware: XCD x (blockIdx % 8) owns the m-tiles mt = x, x + 8,
+  // ... of every leaf, and its workgroups (blockIdx / 8, in dispatch order)
+  // walk them leaf class by leaf class (most input groups first, so that the
+  // long tiles start first), then row type, m-tile and n-tile.  An XCD thus
+  // keeps re-reading its own activation m-tiles and the weight strips of a
+  // few leaves from its L2; dealing the tiles over all XCDs in leaf order
+  // had them re-read from beyond L2 (pilot FFN gate/up: L2 hit rate 54% ->
+  // 81%, 62.3 -> 58.9 us; walking row type before leaf class reached 85% but
+  // let long tiles start last, and the down projection lost 9 us).
+  const int xcd = int(blockIdx.x % kNumXcd), slot = int(blockIdx.x / kNumXcd);
+  const int mt_x = (p.mt_count - xcd + kNumXcd - 1) / kNumXcd;   // m-tiles of this XCD
+  const int per_leaf = mt_x * p.nt_count;
+  if (slot >= q * q * per_leaf) return;
+  const int li = slot / (q * per_leaf);
+  const int rem = slot - li * q * per_leaf;
+  const int i = rem / per_leaf;
+  const int rem2 = rem - i * per_leaf;
+  const int mt = xcd + (rem2 / p.nt_count) * kNumXcd, nt = rem2 - (rem2 / p.nt_count) * p.nt_count;
+  int k;
+  if (p.law == AA_LAW_QQ) k = li == q - 1 ? i : (li < i ? li : li + 1);   // off-diagonal leaves first
+  else k = i ^ (3 - li);   // Q2 x Q2: i ^ k = 3 (four groups), then 2 and 1 (two), then 0 (one)
   int segs[4] = {0, 0, 0, 0};
   const int nseg = device_leaf_groups(p.law, i, k, segs);
   const uint32_t gpack = uint32_t(segs[0]) | (uint32_t(segs[1]) << 2) | (uint32_t(segs[2]) << 4) | (uint32_t(segs[3]) << 6);
@@ -2224,9 +2227,11 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
     const int tn = call.swiglu ? 64 : 128;   // output columns per workgroup
     p.nt_count = int32_t((plan.b_out + tn - 1) / tn);
     if (p.mt_count < 1) return AA_OK;
-    const int64_t n_tiles = int64_t(plan.q) * plan.q * p.mt_count * p.nt_count;
-    if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
-    const dim3 grid{uint32_t(n_tiles), 1, 1}, block{256, 1, 1};
+    // every XCD gets the same number of workgroups; those past its own tiles
+    // (when the m-tiles do not divide by the XCDs) exit at once
+    const int64_t n_slots = int64_t(plan.q) * plan.q * ((p.mt_count + kNumXcd - 1) / kNumXcd) * p.nt_count;
+    if (n_slots * kNumXcd > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+    const dim3 grid{uint32_t(n_slots * kNumXcd), 1, 1}, block{256, 1, 1};
     const bool fout = plan.out_dtype == AA_F32;
     if (call.swiglu) {
       if (fout) launch((leaf_tile_kernel<true, 3, float>), grid, block, 0, stream, p);
