@@ -101,6 +101,10 @@ def main():
         res = bench_square(args, torch, inp, aa, dev)
     else:
         res = bench_ffn(args, torch, inp, aa, dev, args.workload)
+    if not args.no_extras and isinstance(res.get("roofline"), dict) and res["roofline"].get("bound") == "hbm":
+        copy = copy_bandwidth(torch, dev)
+        res["achievable_hbm"] = {**copy, "roofline_kernel_frac_of_copy":
+                                 round(res["roofline"]["achieved"] / copy["GBs"], 4)}
     print(json.dumps(res), flush=True)
 
 
@@ -209,6 +213,28 @@ def dense_timer(torch, fn, iters=20, warm=5):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / iters
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+    """What a plain device-to-device copy reaches on this GPU in the same run
+    (torch copy_ of 1 GiB, two buffer pairs alternating so that the 256 MB
+    Infinity Cache holds neither): read plus write bytes per second.  A
+    secondary, achievable reference beside the datasheet peak."""
+    bufs = [torch.empty(nbytes // 2, dtype=torch.int16, device=dev) for _ in range(4)]
+    for t in bufs:
+        t.zero_()
+    for r in range(3):
+        bufs[2 * (r % 2) + 1].copy_(bufs[2 * (r % 2)])
+    torch.cuda.synchronize()
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for r in range(reps):
+        bufs[2 * (r % 2) + 1].copy_(bufs[2 * (r % 2)])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del bufs
+    return {"kind": "torch copy_ of 1 GiB, device to device, hot loop of 10", "GBs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def cpu_threads():
