@@ -38,11 +38,46 @@ LAW_Q2XQ2 = "Q2xQ2"
 LAWS = (LAW_QQ, LAW_Q2XQ2)
 
 
+class Digraph:
+    """The multiplication table of a directed graph on q vertices.
+
+    [review], multiplication-table paragraph: the table comes from a directed
+    graph whose vertices are the diagonal slots and whose edges are the kept
+    off-diagonal slots; a product of two edges is zero, and the complete graph
+    gives Q_q.  So with an edge set E (pairs (i, k), i != k):
+        C_ii = A_ii B_ii,  C_ik = A_ii B_ik + A_ik B_kk for (i, k) in E,
+    and a slot (i, k) that is not an edge holds nothing: C_ik = 0, and the
+    blocks A_ik, B_ik of such slots take part in no product.
+    An instance is passed wherever a law is expected.
+    """
+
+    def __init__(self, q: int, edges):
+        self.q = int(q)
+        es = set()
+        for i, k in edges:
+            i, k = int(i), int(k)
+            if not (0 <= i < self.q and 0 <= k < self.q):
+                raise ValueError("edge outside the vertex range")
+            if i != k:
+                es.add((i, k))
+        self.edges = frozenset(es)
+
+    def has(self, i: int, k: int) -> bool:
+        return (i, k) in self.edges
+
+    def __repr__(self) -> str:
+        return f"Digraph({self.q}, {sorted(self.edges)})"
+
+
 # --------------------------------------------------------------------------
 # The interaction table
 # --------------------------------------------------------------------------
 
-def _check_law(law: str, q: int) -> None:
+def _check_law(law, q: int) -> None:
+    if isinstance(law, Digraph):
+        if law.q != q:
+            raise ValueError("the digraph has a different number of vertices")
+        return
     if law not in LAWS:
         raise ValueError(f"unknown law {law!r}")
     if q < 1:
@@ -67,6 +102,12 @@ def in_table(law: str, q: int, i: int, j: int, k: int) -> bool:
     it is kept in each factor separately.
     """
     _check_law(law, q)
+    if isinstance(law, Digraph):
+        # vertex slot: its own diagonal pair; edge slot: source diagonal times
+        # the edge, edge times target diagonal; any other slot: nothing
+        if k == i:
+            return j == i
+        return law.has(i, k) and (j == i or j == k)
     if law == LAW_QQ:
         return j == i or j == k
     a, b = divmod(i, 2)

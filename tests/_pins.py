@@ -398,4 +398,102 @@ def pin_executed_flops(orc):
     assert orc.executed_flops([4] * 4, 8, 8, "Q2xQ2", 4) == Fraction(2 * 16 * 8 * 8 * 9, 16)
 
 
+# ------------------------------------------------------------- digraphs ---
+#
+# [review], multiplication-table paragraph: the table of a directed graph
+# keeps the vertex slots and the edge slots, edge times edge is zero, and the
+# complete graph is Q_q.
+
+def _upper(A, q):
+    """Zero the blocks below the block diagonal."""
+    A = np.array(A, dtype=np.float64)
+    r, c = A.shape[0] // q, A.shape[1] // q
+    for i in range(q):
+        for k in range(i):
+            A[i * r:(i + 1) * r, k * c:(k + 1) * c] = 0
+    return A
+
+
+def _support(C, q, edges):
+    """Keep the diagonal blocks and the blocks of the edges; zero the rest."""
+    C = np.array(C, dtype=np.float64)
+    r, c = C.shape[0] // q, C.shape[1] // q
+    for i in range(q):
+        for k in range(q):
+            if i != k and (i, k) not in edges:
+                C[i * r:(i + 1) * r, k * c:(k + 1) * c] = 0
+    return C
+
+
+def pin_digraph_two_vertex_chain(orc):
+    """One edge 0 -> 1 on two vertices: the algebra of block upper-triangular
+    matrices, whose product is the ordinary matrix product."""
+    g = orc.Digraph(2, [(0, 1)])
+    rng = _rng(31)
+    A, B = rng.standard_normal((6, 4)), rng.standard_normal((4, 10))
+    _close(orc.star(A, B, g, 2), _upper(A, 2) @ _upper(B, 2))
+    X, W = rng.standard_normal((7, 4)), rng.standard_normal((4, 10))
+    types = np.array([0, 1, 1, 0, 1, 0, 0])
+    Y = orc.project(X, W, g, 2, types)
+    Wu = _upper(W, 2)
+    for t in range(7):
+        x = X[t].copy()
+        if types[t] == 1:
+            x[:2] = 0                 # a type-1 row has only its own group ...
+        y = x @ Wu
+        if types[t] == 1:
+            y[:5] = 0                 # ... and nothing in output group 0
+        _close(Y[t], y)
+
+
+def pin_digraph_masked_closed_form(orc):
+    """A digraph product is Q_q's closed form A B - off(A) off(B) restricted
+    to the vertex and edge slots; a row of type i is x W - off_i(x) off(W) with
+    the groups k of non-edges (i, k) set to zero."""
+    q = 5
+    rng = _rng(32)
+    edges = {(i, k) for i in range(q) for k in range(q) if i != k and rng.random() < 0.45}
+    g = orc.Digraph(q, edges)
+    A, B = rng.standard_normal((10, 15)), rng.standard_normal((15, 20))
+    want = _support(A @ B - _off_qq(A, q) @ _off_qq(B, q), q, edges)
+    _close(orc.star(A, B, g, q), want)
+    X, W = rng.standard_normal((23, 15)), rng.standard_normal((15, 20))
+    types = rng.integers(0, q, 23)
+    Y = orc.project(X, W, g, q, types)
+    offW = _off_qq(W, q)
+    for t in range(23):
+        i = int(types[t])
+        xo = X[t].copy()
+        xo[i * 3:(i + 1) * 3] = 0
+        y = X[t] @ W - xo @ offW
+        for k in range(q):
+            if k != i and (i, k) not in edges:
+                y[k * 4:(k + 1) * 4] = 0
+        _close(Y[t], y)
+
+
+def pin_digraph_special_cases(orc):
+    """The empty graph gives the block-diagonal product, the complete graph
+    Q_q; one full product has q + 2 |E| block products."""
+    q = 4
+    rng = _rng(33)
+    A, B = rng.standard_normal((8, 8)), rng.standard_normal((8, 12))
+    bd = np.zeros((8, 12))
+    for i in range(q):
+        bd[2 * i:2 * i + 2, 3 * i:3 * i + 3] = A[2 * i:2 * i + 2, 2 * i:2 * i + 2] @ B[2 * i:2 * i + 2, 3 * i:3 * i + 3]
+    _close(orc.star(A, B, orc.Digraph(q, []), q), bd)
+    full = orc.Digraph(q, [(i, k) for i in range(q) for k in range(q)])
+    _close(orc.star(A, B, full, q), A @ B - _off_qq(A, q) @ _off_qq(B, q))
+    edges = [(0, 1), (1, 2), (2, 0), (3, 1), (0, 3)]
+    assert orc.count_block_products(orc.Digraph(q, edges), q) == q + 2 * len(edges)
+
+
+def pin_digraph_associativity(orc):
+    q = 4
+    rng = _rng(34)
+    g = orc.Digraph(q, [(0, 1), (1, 2), (0, 2), (3, 0), (2, 3)])
+    A, B, C = (rng.standard_normal((8, 8)) for _ in range(3))
+    _close(orc.star(orc.star(A, B, g, q), C, g, q), orc.star(A, orc.star(B, C, g, q), g, q), 1e-10)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

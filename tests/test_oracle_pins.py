@@ -59,6 +59,9 @@ MUTANTS = [
     ("grad_weight_wrong_x_group", "+= Xi[:, j * bi:(j + 1) * bi].T @ dYi", "+= Xi[:, k * bi:(k + 1) * bi].T @ dYi"),
     ("grad_weight_overwrites", "dW[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo] += Xi", "dW[j * bi:(j + 1) * bi, k * bo:(k + 1) * bo] = Xi"),
     ("grad_weight_dense", "for j in leaf_groups(law, q, i, k):\n                dW", "for j in range(q):\n                dW"),
+    ("digraph_keeps_every_slot", "return law.has(i, k) and (j == i or j == k)", "return j == i or j == k"),
+    ("digraph_edge_drops_target_diag", "return law.has(i, k) and (j == i or j == k)", "return law.has(i, k) and j == i"),
+    ("digraph_reversed_edges", "return law.has(i, k) and (j == i or j == k)", "return law.has(k, i) and (j == i or j == k)"),
 ]
 
 
