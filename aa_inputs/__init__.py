@@ -47,6 +47,15 @@ def small_integers(shape, seed: int, lo: int = -3, hi: int = 3, dtype=torch.bflo
     return t.to(dtype)
 
 
+def random_edges(q: int, density: float, seed: int) -> list:
+    """Seeded edge set of a directed graph on q vertices: each ordered pair
+    (i, k), i != k, is an edge with probability `density`."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    u = torch.rand((q, q), generator=g)
+    return [(i, k) for i in range(q) for k in range(q) if i != k and float(u[i, k]) < density]
+
+
 def random_types(M: int, q: int, seed: int, device="cpu") -> torch.Tensor:
     """Explicit per-row types, uniform over [0, q)."""
     g = torch.Generator(device=device)

@@ -16,20 +16,21 @@ import os
 import torch  # loaded before libaa.so so that both share torch's HIP runtime
 
 __all__ = [
-    "AA_LAW_QQ", "AA_LAW_Q2XQ2", "AA_TYPES_POS_MOD", "AA_TYPES_BLOCK_ROWS", "AA_TYPES_EXPLICIT",
+    "AA_LAW_QQ", "AA_LAW_Q2XQ2", "AA_LAW_DIGRAPH", "AA_TYPES_POS_MOD", "AA_TYPES_BLOCK_ROWS", "AA_TYPES_EXPLICIT",
     "AA_BF16", "AA_F32", "AA_OK", "AA_ERR_INVALID_ARG", "AA_ERR_SHAPE", "AA_ERR_UNSUPPORTED",
     "AA_ERR_HIP", "AAError", "Plan", "lib_path", "load",
-    "aa_plan_create", "aa_plan_destroy", "aa_plan_info", "aa_pack_weights", "aa_unpack_weights",
+    "aa_plan_create", "aa_plan_create_digraph", "aa_plan_destroy", "aa_plan_info", "aa_pack_weights", "aa_unpack_weights",
     "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_decode_gemv", "aa_project_bwd_workspace",
     "aa_project_bwd_data", "aa_project_bwd_weight", "aa_set_kernel_events", "aa_status_string", "aa_last_error",
 ]
 
-AA_LAW_QQ, AA_LAW_Q2XQ2 = 0, 1
+AA_LAW_QQ, AA_LAW_Q2XQ2, AA_LAW_DIGRAPH = 0, 1, 2
 AA_TYPES_POS_MOD, AA_TYPES_BLOCK_ROWS, AA_TYPES_EXPLICIT = 0, 1, 2
 AA_BF16, AA_F32 = 0, 1
 AA_OK, AA_ERR_INVALID_ARG, AA_ERR_SHAPE, AA_ERR_UNSUPPORTED, AA_ERR_HIP = 0, 1, 2, 3, 4
 
-_LAWS = {"Qq": AA_LAW_QQ, "Q2xQ2": AA_LAW_Q2XQ2, AA_LAW_QQ: AA_LAW_QQ, AA_LAW_Q2XQ2: AA_LAW_Q2XQ2}
+_LAWS = {"Qq": AA_LAW_QQ, "Q2xQ2": AA_LAW_Q2XQ2, "digraph": AA_LAW_DIGRAPH, AA_LAW_QQ: AA_LAW_QQ,
+         AA_LAW_Q2XQ2: AA_LAW_Q2XQ2, AA_LAW_DIGRAPH: AA_LAW_DIGRAPH}
 _KINDS = {"pos_mod": AA_TYPES_POS_MOD, "block_rows": AA_TYPES_BLOCK_ROWS, "explicit": AA_TYPES_EXPLICIT,
           AA_TYPES_POS_MOD: AA_TYPES_POS_MOD, AA_TYPES_BLOCK_ROWS: AA_TYPES_BLOCK_ROWS,
           AA_TYPES_EXPLICIT: AA_TYPES_EXPLICIT}
@@ -44,6 +45,8 @@ _c_i32, _c_i64, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 _SIGNATURES = {
     "aa_plan_create": (ctypes.c_int, [ctypes.POINTER(_c_p), ctypes.c_int, _c_i32, _c_i64, _c_i64, ctypes.c_int,
                                       _c_i64, ctypes.c_int, ctypes.c_int]),
+    "aa_plan_create_digraph": (ctypes.c_int, [ctypes.POINTER(_c_p), _c_i32, ctypes.c_char_p, _c_i64, _c_i64,
+                                              ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int]),
     "aa_plan_destroy": (ctypes.c_int, [_c_p]),
     "aa_plan_info": (ctypes.c_int, [_c_p, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64)]),
     "aa_pack_weights": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
@@ -169,6 +172,27 @@ def aa_plan_create(law, q, d_in, d_out, type_kind="pos_mod", period=0, in_dtype=
     _check(lib.aa_plan_create(ctypes.byref(h), law_, int(q), int(d_in), int(d_out), kind_, int(period), din_,
                               dout_), "aa_plan_create")
     return Plan(h.value, law_, int(q), int(d_in), int(d_out), kind_, int(period), din_, dout_)
+
+
+def aa_plan_create_digraph(q, edges, d_in, d_out, type_kind="pos_mod", period=0, in_dtype="bf16",
+                           out_dtype="bf16") -> Plan:
+    """Plan for the table of a directed graph on q groups; `edges` is an
+    iterable of (i, k) pairs (i -> k) or a q x q 0/1 array."""
+    lib = load()
+    q = int(q)
+    adj = bytearray(q * q)
+    if hasattr(edges, "shape"):
+        for i in range(q):
+            for k in range(q):
+                adj[i * q + k] = 1 if edges[i][k] else 0
+    else:
+        for i, k in edges:
+            adj[int(i) * q + int(k)] = 1
+    h = _c_p()
+    kind_, din_, dout_ = _KINDS[type_kind], _DTYPES[in_dtype], _DTYPES[out_dtype]
+    _check(lib.aa_plan_create_digraph(ctypes.byref(h), q, bytes(adj), int(d_in), int(d_out), kind_, int(period),
+                                      din_, dout_), "aa_plan_create_digraph")
+    return Plan(h.value, AA_LAW_DIGRAPH, q, int(d_in), int(d_out), kind_, int(period), din_, dout_)
 
 
 def aa_plan_destroy(plan: Plan):

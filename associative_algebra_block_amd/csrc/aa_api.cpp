@@ -51,6 +51,8 @@ aa_status_t check_bwd(const aa_plan_s& plan, int64_t M, int64_t pos_offset, cons
   if (plan.type_kind == AA_TYPES_EXPLICIT)
     return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": explicit type lists are not supported by the gradients");
   if (plan.in_dtype != AA_BF16) return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": gradients need bf16 operands");
+  if (plan.law == AA_LAW_DIGRAPH)
+    return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": digraph plans have no gradient kernels");
   return AA_OK;
 }
 
@@ -148,8 +150,9 @@ aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_byt
   aa::clear_error();
   if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: plan is NULL");
   if (M < 0) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: M is negative");
-  if (data_bytes) *data_bytes = aa::bwd_data_workspace_bytes(*plan, M);
-  if (weight_bytes) *weight_bytes = aa::bwd_weight_workspace_bytes(*plan, M);
+  const bool none = plan->law == AA_LAW_DIGRAPH;   // no gradient kernels
+  if (data_bytes) *data_bytes = none ? 0 : aa::bwd_data_workspace_bytes(*plan, M);
+  if (weight_bytes) *weight_bytes = none ? 0 : aa::bwd_weight_workspace_bytes(*plan, M);
   return AA_OK;
 }
 

@@ -106,7 +106,15 @@ __device__ inline void store4_nt(float* p, f32x4_t v) { __builtin_nontemporal_st
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // Input groups of leaf (type i, output group k); returns their count (<= 4).
-__device__ inline int device_leaf_groups(int law, int i, int k, int* g) {
+// For a digraph, adj_row has bit k set for the edges i -> k; a leaf of a
+// non-edge has no groups (its outputs are zero).
+__device__ inline int device_leaf_groups(int law, int i, int k, int* g, uint64_t adj_row = 0) {
+  if (law == AA_LAW_DIGRAPH) {
+    g[0] = i;
+    g[1] = k;
+    if (k == i) return 1;
+    return (adj_row >> k) & 1 ? 2 : 0;
+  }
   if (law == AA_LAW_QQ) {
     g[0] = i;
     g[1] = k;

@@ -25,6 +25,8 @@ struct aa_plan_s {
   int32_t tile_override;     // -1: automatic; else a variant id (tuning only)
   int32_t wg_per_cu;         // persistent kernels: workgroups launched per CU (0: automatic)
   int32_t persist_pol;       // persistent kernels: cache policy bits (-1: automatic; tuning only)
+  uint64_t adj[64];          // AA_LAW_DIGRAPH: bit k of adj[i] = edge i -> k (else all zero)
+  int32_t n_edges;
 };
 
 namespace aa {
@@ -35,8 +37,10 @@ void clear_error();
 aa_status_t fail(aa_status_t st, const std::string& msg);
 
 // Number of block products in the table row of type i that ends in output
-// group k (1 for k == i under Q_q, 2 otherwise; 1, 2 or 4 under Q2 x Q2).
-int leaf_groups(aa_law_t law, int q, int i, int k, int* groups /* up to 4 */);
+// group k (1 for k == i under Q_q, 2 otherwise; 1, 2 or 4 under Q2 x Q2; for a
+// digraph 1 for k == i, 2 for an edge i -> k, else 0).  adj_row: bit k set for
+// the edges i -> k of a digraph.
+int leaf_groups(aa_law_t law, int q, int i, int k, int* groups /* up to 4 */, uint64_t adj_row = 0);
 
 // ---------------------------------------------------------------- launch ---
 

@@ -65,6 +65,7 @@ struct LeafParams {
   int32_t kc;              // output groups per tile-order chunk
   uint32_t n_tiles;
   int32_t cpr;             // streaming kernel: 16-byte LDS chunks per staged activation row
+  uint64_t adj[64];        // general kernel, digraph law: bit k of adj[i] = edge i -> k
 };
 
 // Rows of type i, in order; fills rows[0..TM) for m-tile mt and returns how
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kWave * WN * WM) void leaf_gemm_kernel(LeafParams p
   const int l16 = lane & 15;
 
   int segs[4];
-  const int nseg = device_leaf_groups(p.law, i, k, segs);
+  const int nseg = device_leaf_groups(p.law, i, k, segs, p.law == AA_LAW_DIGRAPH ? p.adj[i] : 0);
   const int KF = (p.b_in + 31) / 32;
   const int nsteps = nseg * KF;
 
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
   const unsigned char* W1 = static_cast<const unsigned char*>(p.W1);
   const Tin* __restrict__ X = static_cast<const Tin*>(p.X);
   Tout* __restrict__ Y = static_cast<Tout*>(p.Y);
-  const bool qq = p.law == AA_LAW_QQ;
+  const bool qq = p.law == AA_LAW_QQ || p.law == AA_LAW_DIGRAPH;   // input groups i, then k
 
   // This workgroup's run of tiles: XCD x owns a contiguous run of the tile
   // order; its G8 workgroups take every G8-th tile of it.
@@ -582,7 +583,7 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
     T.i = int(t % uint32_t(p.q));
     T.k = int(t / uint32_t(p.q)) * p.kc + kk;
     int sg[4] = {0, 0, 0, 0};
-    T.nseg = device_leaf_groups(p.law, T.i, T.k, sg);
+    T.nseg = device_leaf_groups(p.law, T.i, T.k, sg, p.law == AA_LAW_DIGRAPH ? p.adj[T.i] : 0);
     T.gpack = uint32_t(sg[0] & 3) | (uint32_t(sg[1] & 3) << 2) | (uint32_t(sg[2] & 3) << 4) | (uint32_t(sg[3] & 3) << 6);
     T.nchunks = T.nseg;
     int64_t count;
@@ -656,8 +657,9 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int c = ch < T.nchunks ? ch : 0;
-      // a void step re-reads the diagonal block W_kk, which stays in L2
-      const int64_t base = (int64_t(T.live ? seg_of(T, c) : T.k) * p.q + T.k) * blk_bytes;
+      // a void step, and a digraph leaf with no input group, re-read the
+      // diagonal block W_kk, which stays in L2
+      const int64_t base = (int64_t(T.live && T.nchunks > 0 ? seg_of(T, c) : T.k) * p.q + T.k) * blk_bytes;
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -2043,7 +2045,7 @@ size_t stream_lds_bytes(const aa_plan_s& plan, int v) {
 
 // Streaming variant for this call, or -1 for the general kernel.
 int choose_stream(const aa_plan_s& plan, int64_t M, bool swiglu) {
-  if (plan.in_dtype != AA_BF16 || plan.type_kind == AA_TYPES_EXPLICIT) return -1;
+  if (plan.in_dtype != AA_BF16 || plan.type_kind == AA_TYPES_EXPLICIT || plan.law == AA_LAW_DIGRAPH) return -1;
   auto fits = [&](int v) {
     return stream_lds_bytes(plan, v) <= kStreamLdsMax && plan.b_in % (32 * kStream[v].ck) == 0;
   };
@@ -2197,7 +2199,7 @@ int choose_kstream(const aa_plan_s& plan, int64_t M, bool swiglu) {
 
 // Large-tile kernel for leaves with many rows per type (override 500).
 bool choose_tile(const aa_plan_s& plan, int64_t M) {
-  if (plan.in_dtype != AA_BF16) return false;
+  if (plan.in_dtype != AA_BF16 || plan.law == AA_LAW_DIGRAPH) return false;
   if (plan.type_kind != AA_TYPES_POS_MOD && plan.type_kind != AA_TYPES_BLOCK_ROWS) return false;
   if (plan.b_in % 64) return false;
   if (plan.tile_override == 500) return true;
@@ -2324,6 +2326,7 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
   if (pid >= 0) {
     const PersistVariant& pv = kPersist[pid];
     LeafParams p{};
+    for (int r = 0; r < 64; ++r) p.adj[r] = plan.adj[r];
     p.X = call.X;
     p.W0 = call.W0;
     p.W1 = call.W1;
@@ -2358,7 +2361,7 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
     int pol = (p.mt_count == 1 ? kPolWOwn : 0) | kPolYNt;
     // the last staged column block is the own activation block x_k when the
     // two input groups of a Q_q leaf fill the staged K exactly
-    if (p.nt_count == 1 && plan.law == AA_LAW_QQ && plan.q > 1 && pv.nch == 2) pol |= kPolXOwn;
+    if (p.nt_count == 1 && plan.law != AA_LAW_Q2XQ2 && plan.q > 1 && pv.nch == 2) pol |= kPolXOwn;
     if (plan.persist_pol >= 0) pol = plan.persist_pol;
     auto fn = call.swiglu ? (fout ? pv.swi_f[pol] : pv.swi_b[pol]) : (fout ? pv.plain_f[pol] : pv.plain_b[pol]);
     fn(p, grid, block, 0, stream);
@@ -2382,6 +2385,7 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
   p.b_in = int32_t(plan.b_in);
   p.b_out = int32_t(plan.b_out);
   p.law = plan.law;
+  for (int r = 0; r < 64; ++r) p.adj[r] = plan.adj[r];
   p.kind = plan.type_kind;
   p.off_mod_q = int32_t(call.pos_offset % plan.q);
   p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
@@ -2430,10 +2434,20 @@ aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool 
   return after_launch(stream, unpack ? "unpack" : "pack");
 }
 
-bool decode_swiglu_ok(const aa_plan_s& plan) { return plan.in_dtype == AA_BF16 && plan.b_in <= 256; }
+bool decode_swiglu_ok(const aa_plan_s& plan) {
+  return plan.in_dtype == AA_BF16 && plan.b_in <= 256 && plan.law != AA_LAW_DIGRAPH;
+}
 
 aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,
                           int64_t n, int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  if (plan.law == AA_LAW_DIGRAPH) {
+    // the decode of a digraph plan is its row-typed projection of the new
+    // rows, typed by position (or by the given types)
+    aa_plan_s dp = plan;
+    dp.type_kind = row_types ? AA_TYPES_EXPLICIT : AA_TYPES_POS_MOD;
+    const LeafCall c{x, W, W1, y, n, pos_offset, row_types, W1 != nullptr};
+    return launch_leaf_gemm(dp, c, stream);
+  }
   DecodeParams p{};
   p.x = x;
   p.W = W;

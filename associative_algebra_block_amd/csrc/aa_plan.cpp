@@ -34,7 +34,13 @@ aa_status_t fail(aa_status_t st, const std::string& msg) {
   return st;
 }
 
-int leaf_groups(aa_law_t law, int q, int i, int k, int* groups) {
+int leaf_groups(aa_law_t law, int q, int i, int k, int* groups, uint64_t adj_row) {
+  if (law == AA_LAW_DIGRAPH) {
+    groups[0] = i;
+    groups[1] = k;
+    if (k == i) return 1;
+    return (adj_row >> k) & 1 ? 2 : 0;
+  }
   if (law == AA_LAW_QQ) {
     groups[0] = i;
     if (k == i) return 1;
@@ -81,14 +87,14 @@ aa_status_t aa_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
   return AA_OK;
 }
 
-aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in, int64_t d_out,
-                           aa_type_kind_t type_kind, int64_t period, aa_dtype_t in_dtype,
-                           aa_dtype_t out_dtype) {
-  aa::clear_error();
-  if (!out) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: out is NULL");
-  *out = nullptr;
-  if (law != AA_LAW_QQ && law != AA_LAW_Q2XQ2)
-    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown law");
+}  // extern "C"
+
+namespace {
+
+// Validation and construction shared by both creation calls; adjacency is
+// non-null exactly for AA_LAW_DIGRAPH.
+aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjacency, int64_t d_in, int64_t d_out,
+                   aa_type_kind_t type_kind, int64_t period, aa_dtype_t in_dtype, aa_dtype_t out_dtype) {
   if (type_kind != AA_TYPES_POS_MOD && type_kind != AA_TYPES_BLOCK_ROWS && type_kind != AA_TYPES_EXPLICIT)
     return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown type map");
   if ((in_dtype != AA_BF16 && in_dtype != AA_F32) || (out_dtype != AA_BF16 && out_dtype != AA_F32))
@@ -112,6 +118,16 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
 
   aa_plan_s* p = new (std::nothrow) aa_plan_s;
   if (!p) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: out of host memory");
+  p->n_edges = 0;
+  for (int i = 0; i < 64; ++i) p->adj[i] = 0;
+  if (adjacency) {
+    for (int i = 0; i < q; ++i)
+      for (int k = 0; k < q; ++k)
+        if (k != i && adjacency[int64_t(i) * q + k]) {
+          p->adj[i] |= uint64_t(1) << k;
+          ++p->n_edges;
+        }
+  }
   p->law = law;
   p->q = q;
   p->d_in = d_in;
@@ -125,7 +141,7 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
   int64_t n = 0;
   int groups[4];
   for (int i = 0; i < q; ++i)
-    for (int k = 0; k < q; ++k) n += aa::leaf_groups(law, q, i, k, groups);
+    for (int k = 0; k < q; ++k) n += aa::leaf_groups(law, q, i, k, groups, i < 64 ? p->adj[i] : 0);
   p->n_block_products = n;
   p->n_leaves = int64_t(q) * q;
   p->tile_override = -1;
@@ -149,6 +165,34 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
   }
   *out = p;
   return AA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in, int64_t d_out,
+                           aa_type_kind_t type_kind, int64_t period, aa_dtype_t in_dtype,
+                           aa_dtype_t out_dtype) {
+  aa::clear_error();
+  if (!out) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: out is NULL");
+  *out = nullptr;
+  if (law == AA_LAW_DIGRAPH)
+    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: digraph plans are made by aa_plan_create_digraph");
+  if (law != AA_LAW_QQ && law != AA_LAW_Q2XQ2)
+    return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown law");
+  return create(out, law, q, nullptr, d_in, d_out, type_kind, period, in_dtype, out_dtype);
+}
+
+aa_status_t aa_plan_create_digraph(aa_plan_t* out, int32_t q, const uint8_t* adjacency, int64_t d_in,
+                                   int64_t d_out, aa_type_kind_t type_kind, int64_t period,
+                                   aa_dtype_t in_dtype, aa_dtype_t out_dtype) {
+  aa::clear_error();
+  if (!out) return fail(AA_ERR_INVALID_ARG, "aa_plan_create_digraph: out is NULL");
+  *out = nullptr;
+  if (!adjacency) return fail(AA_ERR_INVALID_ARG, "aa_plan_create_digraph: adjacency is NULL");
+  if (q > 64) return fail(AA_ERR_UNSUPPORTED, "aa_plan_create_digraph: q above 64");
+  return create(out, AA_LAW_DIGRAPH, q, adjacency, d_in, d_out, type_kind, period, in_dtype, out_dtype);
 }
 
 aa_status_t aa_plan_destroy(aa_plan_t plan) {

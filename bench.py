@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
                     choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
+                             "digraph_qwen3_8b",
                              "backward_qwen3_8b", "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,6 +96,8 @@ def main():
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[6])
     elif args.workload == "qwen3_8b_down":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[7])
+    elif args.workload == "digraph_qwen3_8b":
+        res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[3], digraph_density=0.5)
     elif args.workload.startswith("backward_"):
         res = bench_backward(args, torch, inp, aa, dev, args.workload)
     elif args.workload == "square":
@@ -407,13 +410,22 @@ def projection_alone(torch, aa, plan, sets, bytes_alg, reps=50):
     return out
 
 
-def bench_projection(args, torch, inp, aa, dev, wl):
+def bench_projection(args, torch, inp, aa, dev, wl, digraph_density=None):
     """A single row-typed projection shape (position typing), flushed cache
     (rotating input sets of >= 1 GB in total) and hot cache, with a dense bf16
-    comparator of the same shape."""
+    comparator of the same shape.  With digraph_density the table is that of
+    a seeded random directed graph on the q groups (each ordered pair an edge
+    with that probability); the weight blocks of non-edges are read by no row,
+    so the algorithmic bytes count only the q diagonal and |E| edge blocks."""
     M, D, F, q = wl.M, wl.d_in, wl.d_out, wl.q
-    plan = aa.aa_plan_create(wl.law, q, D, F, "pos_mod", 0, "bf16", "bf16")
-    per_set = 2 * (M * D + D * F + M * F)
+    edges = None
+    if digraph_density is None:
+        plan = aa.aa_plan_create(wl.law, q, D, F, "pos_mod", 0, "bf16", "bf16")
+        per_set = 2 * (M * D + D * F + M * F)
+    else:
+        edges = inp.random_edges(q, digraph_density, inp.seed_for(inp.ROLE_TYPES, wl.index))
+        plan = aa.aa_plan_create_digraph(q, edges, D, F, "pos_mod", 0, "bf16", "bf16")
+        per_set = 2 * (M * D + (q + len(edges)) * (D // q) * (F // q) + M * F)
     n_sets = args.sets or max(2, math.ceil(1.0e9 / per_set))
     sets = []
     for s in range(n_sets):
@@ -449,16 +461,19 @@ def bench_projection(args, torch, inp, aa, dev, wl):
                  "speedup_flushed": round(t / ms, 3)}
         if alone:
             dense["speedup_hot"] = round(t / alone["hot"]["ms"], 3)
-    return {"metric": f"dense-equiv TFLOP/s + % roofline, {wl.name} projection bf16",
+    name = wl.name if edges is None else f"{wl.name} digraph ({len(edges)} of {q * (q - 1)} edges)"
+    return {"metric": f"dense-equiv TFLOP/s + % roofline, {name} projection bf16",
             "value": round(2.0 * M * D * F / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": wl.name, "M": M, "d_in": D, "d_out": F, "q": q, "law": wl.law,
-                       "type_map": "pos mod q", "input_sets": n_sets},
+            "config": {"workload": name, "M": M, "d_in": D, "d_out": F, "q": q,
+                       "law": wl.law if edges is None else "digraph", "type_map": "pos mod q", "input_sets": n_sets,
+                       **({} if edges is None else {"edges": len(edges)})},
             "roofline": roofline(per_set, ms_k), "kernel_ms": round(ms_k, 5), "kernel_spread": kt.spread(0),
             "projection_alone": alone,
             "dense": dense,
-            "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / (ms * 1e-3) / 1e12, 2),
+            "exec_tflops": round((exec_flops(M, D, F, wl.law, q) if edges is None else
+                                  2.0 * (M // q) * (D // q) * (F // q) * (q + 2 * len(edges))) / (ms * 1e-3) / 1e12, 2),
             "kernel_source": kernel_source_hash()}
 
 

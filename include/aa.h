@@ -55,8 +55,12 @@ extern "C" {
 typedef struct aa_plan_s* aa_plan_t;
 
 /* The multiplication law.  AA_LAW_Q2XQ2 requires q == 4 (the tensor square of
- * the two-group law; agihunt.info review, pilot-law paragraph). */
-typedef enum { AA_LAW_QQ = 0, AA_LAW_Q2XQ2 = 1 } aa_law_t;
+ * the two-group law; agihunt.info review, pilot-law paragraph).
+ * AA_LAW_DIGRAPH is the table of a directed graph on the q groups (same
+ * review, multiplication-table paragraph: the vertices are the diagonal slots,
+ * the edges the kept off-diagonal slots, and an edge times an edge is zero;
+ * Q_q is the complete graph); such plans come from aa_plan_create_digraph. */
+typedef enum { AA_LAW_QQ = 0, AA_LAW_Q2XQ2 = 1, AA_LAW_DIGRAPH = 2 } aa_law_t;
 
 /* How a row's type is found (agihunt.info review, row-typing paragraph: by
  * the token's absolute position).
@@ -93,12 +97,27 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
                            aa_type_kind_t type_kind, int64_t period,
                            aa_dtype_t in_dtype, aa_dtype_t out_dtype);
 
+/* Create a plan for the table of a directed graph on q groups.  adjacency is
+ * a host array of q * q bytes read during the call (not kept):
+ * adjacency[i * q + k] != 0 with i != k makes i -> k an edge; the diagonal is
+ * ignored.  A row of type i then computes, for output group k,
+ *     y_i = x_i W_ii,   y_k = x_i W_ik + x_k W_kk  if i -> k is an edge,
+ *     y_k = 0           otherwise
+ * (weight blocks W_ik of non-edges are read by no call).  Everything else is
+ * as for aa_plan_create; aa_plan_create itself rejects AA_LAW_DIGRAPH.
+ * Limits of this implementation: 1 <= q <= 64; the calls run the general
+ * leaf-GEMM kernel; the gradient calls return AA_ERR_UNSUPPORTED. */
+aa_status_t aa_plan_create_digraph(aa_plan_t* out, int32_t q, const uint8_t* adjacency, int64_t d_in,
+                                   int64_t d_out, aa_type_kind_t type_kind, int64_t period,
+                                   aa_dtype_t in_dtype, aa_dtype_t out_dtype);
+
 /* Free a plan.  NULL is accepted and ignored. */
 aa_status_t aa_plan_destroy(aa_plan_t plan);
 
 /* Query a plan.  Any output pointer may be NULL.
  *  n_block_products  block products of one full product: 2q^2 - q for Q_q,
- *                    36 for Q2 x Q2 (agihunt.info review, rank paragraph);
+ *                    36 for Q2 x Q2 (agihunt.info review, rank paragraph),
+ *                    q + 2 |E| for a digraph with edge set E;
  *  n_leaves          (row type, output group) pairs, q^2;
  *  packed_elems      elements of a packed weight, equal to d_in * d_out. */
 aa_status_t aa_plan_info(aa_plan_t plan, int64_t* n_block_products, int64_t* n_leaves,

@@ -69,6 +69,34 @@ def test_plan_rejects(lib, args, status):
     assert aa.aa_last_error()
 
 
+def test_digraph_plans(lib):
+    """aa_plan_create_digraph: q + 2 |E| block products, the diagonal of the
+    adjacency ignored, argument checks; no gradients."""
+    p = aa.aa_plan_create_digraph(5, [(0, 1), (1, 2), (2, 0), (4, 3), (3, 3)], 80, 160)
+    assert aa.aa_plan_info(p) == (5 + 2 * 4, 25, 80 * 160)
+    full = aa.aa_plan_create_digraph(6, [(i, k) for i in range(6) for k in range(6)], 96, 96)
+    assert aa.aa_plan_info(full)[0] == 2 * 36 - 6                 # the complete graph is Q_6
+    assert aa.aa_plan_info(aa.aa_plan_create_digraph(4, [], 64, 64))[0] == 4
+    adj = (ctypes.c_uint8 * 4)(0, 1, 0, 0)
+    out = ctypes.c_void_p()
+    assert lib.aa_plan_create_digraph(ctypes.byref(out), 2, None, 64, 64, 0, 0, 0, 0) == aa.AA_ERR_INVALID_ARG
+    assert lib.aa_plan_create_digraph(None, 2, ctypes.cast(adj, ctypes.c_char_p), 64, 64, 0, 0, 0, 0) == \
+        aa.AA_ERR_INVALID_ARG
+    assert lib.aa_plan_create_digraph(ctypes.byref(out), 65, ctypes.cast(adj, ctypes.c_char_p), 65 * 16, 65 * 16,
+                                      0, 0, 0, 0) == aa.AA_ERR_UNSUPPORTED
+    assert lib.aa_plan_create_digraph(ctypes.byref(out), 2, ctypes.cast(adj, ctypes.c_char_p), 48, 64,
+                                      0, 0, 0, 0) == aa.AA_ERR_UNSUPPORTED   # b_in = 24
+    with pytest.raises(aa.AAError) as e:
+        aa.aa_plan_create("digraph", 2, 64, 64)
+    assert e.value.status == aa.AA_ERR_INVALID_ARG
+    assert aa.aa_project_bwd_workspace(p, 100) == (0, 0)
+    g = 0x1000000
+    assert _raw(lib, "aa_project_bwd_data", p.handle, g, 2 * g, 3 * g, 100, 0, None, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
+    assert _raw(lib, "aa_project_bwd_weight", p.handle, g, 2 * g, 3 * g, 100, 0, None, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
+
+
 def test_plan_create_null_out(lib):
     assert lib.aa_plan_create(None, 0, 2, 64, 64, 0, 0, 0, 0) == aa.AA_ERR_INVALID_ARG
 

@@ -1,0 +1,141 @@
+"""Parity of digraph plans (aa_plan_create_digraph) with the fp64 oracle.
+
+The table of a directed graph keeps the vertex slots and the edge slots and
+sets edge times edge to zero; Q_q is the complete graph.  Every test needs an
+MI355X and goes through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import aa_inputs as inp
+import associative_algebra_block_amd as aa
+import oracle
+from tests._gpu_util import MAX_RMS, REL_FRO, assert_parity, host, metrics, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    aa.load()
+
+
+def _graph(name, q, seed):
+    if name == "chain":
+        return [(i, i + 1) for i in range(q - 1)]
+    if name == "ring":
+        return [(i, (i + 1) % q) for i in range(q)]
+    if name == "empty":
+        return []
+    if name == "complete":
+        return [(i, k) for i in range(q) for k in range(q) if i != k]
+    return inp.random_edges(q, float(name), seed)
+
+
+def _types(kind, M, q, pos_offset, seed):
+    if kind == "block_rows":
+        return oracle.types_block_rows(M, q), None
+    if kind == "explicit":
+        t = inp.random_types(M, q, seed, DEV)
+        return t.cpu().numpy(), t
+    return oracle.types_pos_mod(M, q, pos_offset), None
+
+
+@pytest.mark.parametrize("graph,q,M,d_in,d_out,kind,pos_offset", [
+    ("chain", 2, 300, 128, 256, "pos_mod", 1),
+    ("0.5", 4, 1000, 512, 768, "pos_mod", 0),
+    ("ring", 8, 777, 1024, 1024, "pos_mod", 3),
+    ("0.3", 32, 2048, 4096, 12288, "pos_mod", 0),
+    ("0.4", 8, 333, 512, 256, "explicit", 0),
+    ("0.5", 4, 512, 256, 512, "block_rows", 0),
+    ("empty", 4, 200, 256, 256, "pos_mod", 2),
+    ("complete", 8, 500, 1024, 512, "pos_mod", 5),
+])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_digraph_projection_matches_oracle(graph, q, M, d_in, d_out, kind, pos_offset, out_dt):
+    say("digraph", graph, q, M, d_in, d_out, kind, pos_offset, out_dt)
+    edges = _graph(graph, q, 7 * q + M)
+    plan = aa.aa_plan_create_digraph(q, edges, d_in, d_out, kind, 0, "bf16", out_dt)
+    X = inp.gaussian((M, d_in), 11 + q, 1.0, torch.bfloat16, DEV)
+    W = inp.gaussian((d_in, d_out), 12 + q, d_in ** -0.5, torch.bfloat16, DEV)
+    types, dev_types = _types(kind, M, q, pos_offset, 13 + q)
+    Y = torch.empty(M, d_out, dtype=TD[out_dt], device=DEV)
+    aa.aa_project_fwd(plan, X, aa.pack(plan, W), Y, None, pos_offset, dev_types)
+    torch.cuda.synchronize()
+    ref = oracle.project(host(X), host(W), oracle.Digraph(q, edges), q, types)
+    assert_parity(host(Y), ref, out_dt == "bf16", f"digraph {graph} q={q}")
+
+
+def test_digraph_integer_exact():
+    """Small integers with a distinct power-of-two scale per weight block: bit
+    for bit, so a block read from a non-edge slot or a misrouted type shows."""
+    q, M, d_in, d_out = 8, 400, 512, 256
+    say("digraph int", q, M)
+    edges = inp.random_edges(q, 0.4, 5)
+    plan = aa.aa_plan_create_digraph(q, edges, d_in, d_out, "pos_mod", 0, "bf16", "f32")
+    X = inp.small_integers((M, d_in), 21, dtype=torch.bfloat16, device=DEV)
+    W = inp.small_integers((d_in, d_out), 22, dtype=torch.bfloat16, device=DEV)
+    bi, bo = d_in // q, d_out // q
+    scale = torch.tensor([[2.0 ** ((5 * j + 3 * k) % 7) for k in range(q)] for j in range(q)], device=DEV)
+    W = (W.float().view(q, bi, q, bo) * scale.view(q, 1, q, 1)).view(d_in, d_out).to(torch.bfloat16)
+    Y = torch.empty(M, d_out, dtype=torch.float32, device=DEV)
+    aa.aa_project_fwd(plan, X, aa.pack(plan, W), Y, None, 9)
+    torch.cuda.synchronize()
+    ref = oracle.project(host(X), host(W), oracle.Digraph(q, edges), q, oracle.types_pos_mod(M, q, 9))
+    assert np.array_equal(host(Y), ref), float(np.max(np.abs(host(Y) - ref)))
+
+
+@pytest.mark.parametrize("M", [2048, 5])
+def test_digraph_swiglu_matches_oracle(M):
+    """SwiGLU FFN with both plans on one digraph (M = 5: the few-token path).
+
+    H is stored in bf16 (the reading of the pages' FFN the library follows),
+    and a sparse graph leaves many output groups zero, which lowers rms(Y);
+    so the max-error bound on Y adds the error that storing the exact H in
+    bf16 alone causes, computed by the oracle (as the bf16 output floor is)."""
+    q, D, F = 16, 2048, 768
+    say("digraph swiglu", q, M, D, F)
+    edges = inp.random_edges(q, 0.3, 17)
+    up = aa.aa_plan_create_digraph(q, edges, D, F, "pos_mod", 0, "bf16", "bf16")
+    down = aa.aa_plan_create_digraph(q, edges, F, D, "pos_mod", 0, "bf16", "f32")
+    X = inp.gaussian((M, D), 31, 1.0, torch.bfloat16, DEV)
+    Wg = inp.gaussian((D, F), 32, D ** -0.5, torch.bfloat16, DEV)
+    Wu = inp.gaussian((D, F), 33, D ** -0.5, torch.bfloat16, DEV)
+    Wd = inp.gaussian((F, D), 34, F ** -0.5, torch.bfloat16, DEV)
+    H = torch.empty(M, F, dtype=torch.bfloat16, device=DEV)
+    Y = torch.empty(M, D, dtype=torch.float32, device=DEV)
+    aa.aa_swiglu_ffn_fwd(up, down, X, aa.pack(up, Wg), aa.pack(up, Wu), aa.pack(down, Wd), H, Y, None, 4)
+    torch.cuda.synchronize()
+    g, types = oracle.Digraph(q, edges), oracle.types_pos_mod(M, q, 4)
+    H_ref, Y_ref = oracle.swiglu_ffn(host(X), host(Wg), host(Wu), host(Wd), g, q, types)
+    assert_parity(host(H), H_ref, True, "digraph H")
+    Hb = torch.from_numpy(H_ref).to(torch.bfloat16).double().numpy()
+    _, floor = metrics(oracle.project(Hb, host(Wd), g, q, types), Y_ref)
+    rel_fro, max_rms = metrics(host(Y), Y_ref)
+    say(f"digraph Y: rel_fro={rel_fro:.3e} max/rms={max_rms:.3e} bf16-H floor={floor:.3e}")
+    assert rel_fro <= REL_FRO, rel_fro
+    assert max_rms <= MAX_RMS + floor, (max_rms, floor)
+
+
+def test_digraph_decode_matches_oracle():
+    """Decode of n new tokens by position and by explicit types."""
+    q, D, F, n = 8, 1024, 2048, 11
+    say("digraph decode", q, n)
+    edges = inp.random_edges(q, 0.5, 41)
+    plan = aa.aa_plan_create_digraph(q, edges, D, F, "pos_mod", 0, "bf16", "f32")
+    x = inp.gaussian((n, D), 42, 1.0, torch.bfloat16, DEV)
+    W = inp.gaussian((D, F), 43, D ** -0.5, torch.bfloat16, DEV)
+    Wp = aa.pack(plan, W)
+    y = torch.empty(n, F, dtype=torch.float32, device=DEV)
+    aa.aa_decode_gemv(plan, x, Wp, y, None, 1003)
+    types = inp.random_types(n, q, 44, DEV)
+    y2 = torch.empty(n, F, dtype=torch.float32, device=DEV)
+    aa.aa_decode_gemv(plan, x, Wp, y2, None, 0, types)
+    torch.cuda.synchronize()
+    g = oracle.Digraph(q, edges)
+    assert_parity(host(y), oracle.decode(host(x), host(W), g, q, 1003 + np.arange(n)), False, "decode by position")
+    assert_parity(host(y2), oracle.project(host(x), host(W), g, q, types.cpu().numpy()), False, "decode by types")
