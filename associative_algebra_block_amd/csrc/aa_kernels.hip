@@ -2440,9 +2440,15 @@ bool decode_swiglu_ok(const aa_plan_s& plan) {
 
 aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,
                           int64_t n, int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
-  if (plan.law == AA_LAW_DIGRAPH) {
-    // the decode of a digraph plan is its row-typed projection of the new
-    // rows, typed by position (or by the given types)
+  // The decode of a digraph plan, and a decode of at least 2q position-typed
+  // or 8q explicitly typed tokens, run as the row-typed projection of the new
+  // rows (typed by position, or by the given types): the matrix-vector
+  // kernel reads each token's own blocks once per token group, so its time
+  // grows with the tokens, while the leaf kernels read every block once
+  // (Qwen3-8B shape, by position: 32.7 against 29.9 us at 64 tokens, 441
+  // against 32.7 us at 1024; explicit types: 154 against 77 us at 512, the
+  // general kernel's ballot scan of the types costing more per token).
+  if (plan.law == AA_LAW_DIGRAPH || (W1 == nullptr && n >= (row_types ? 8 : 2) * int64_t(plan.q))) {
     aa_plan_s dp = plan;
     dp.type_kind = row_types ? AA_TYPES_EXPLICIT : AA_TYPES_POS_MOD;
     const LeafCall c{x, W, W1, y, n, pos_offset, row_types, W1 != nullptr};

@@ -381,10 +381,12 @@ def test_row_locality():
     ("Qq", 32, 4096, 12288, 32, "bf16"), ("Qq", 32, 4096, 12288, 1, "bf16"),
     ("Q2xQ2", 4, 768, 1536, 7, "bf16"), ("Qq", 16, 768, 2048, 20, "bf16"),
     ("Qq", 32, 12288, 4096, 5, "bf16"), ("Qq", 2, 64, 64, 9, "f32"), ("Qq", 4, 320, 64, 6, "bf16"),
-    ("Qq", 8, 1024, 1536, 2, "bf16"), ("Q2xQ2", 4, 768, 1536, 1, "bf16"), ("Qq", 16, 6144, 2048, 2, "bf16")])
+    ("Qq", 8, 1024, 1536, 2, "bf16"), ("Q2xQ2", 4, 768, 1536, 1, "bf16"), ("Qq", 16, 6144, 2048, 2, "bf16"),
+    # many tokens: from 2q (by position) and 8q (explicit types) on, the leaf kernels
+    ("Qq", 8, 1024, 1536, 64, "bf16"), ("Qq", 32, 4096, 12288, 300, "bf16"), ("Q2xQ2", 4, 768, 1536, 40, "bf16")])
 def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n, dt):
     say("decode", law, q, d_in, d_out, n, dt)
-    plan, X, W = _make(law, q, 64, d_in, d_out, dt, "f32", seed=81)
+    plan, X, W = _make(law, q, max(64, n), d_in, d_out, dt, "f32", seed=81)
     Wp = aa.pack(plan, W)
     pos0 = 1000 + 3
     x = X[:n].contiguous()
