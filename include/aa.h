@@ -212,8 +212,9 @@ aa_status_t aa_project_bwd_weight(aa_plan_t plan, const void* X, const void* dY,
  * start of its first kernel to the end of its last one, without the queue
  * time before the first kernel.  The events must have been created with
  * timing enabled on the device that runs the kernels and stay owned by the
- * caller; either may be NULL.  The setting is per thread.  Always returns
- * AA_OK and makes no HIP call. */
+ * caller; either may be NULL.  The setting is per thread.  Leave it off (NULL,
+ * NULL) for calls captured into a HIP graph.  Always returns AA_OK and makes
+ * no HIP call. */
 aa_status_t aa_set_kernel_events(hipEvent_t start, hipEvent_t stop);
 
 /* A static English name of a status code. */
