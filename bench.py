@@ -21,7 +21,7 @@ events that the library records from the kernels' own dispatches
 the step time comes from events around the K steps and includes the gaps
 between kernels.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 300] [--warmup 10]
                     [--workload qwen3_8b_q32|square|pilot_ffn|expert_ffn|qwen3_1p7b|qwen3_8b_down|
                                 backward_qwen3_8b|backward_expert]
 """
@@ -46,7 +46,9 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=300,
+                    help="timed steps; the calls of a step take turns being timed by their kernel events, so each "
+                         "call gets steps / calls samples (100 for the Qwen3-8B projection by default)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
                     choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
