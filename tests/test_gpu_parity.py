@@ -262,6 +262,48 @@ def test_decode_single_tokens_in_a_graph_replay():
         assert torch.equal(y_graph, y_eager), f"replay {r}"
 
 
+def test_step_in_a_graph_replay():
+    """The Qwen3-8B-shaped step (projection, SwiGLU FFN, a 32-token decode)
+    captured in one HIP graph: the persistent, K-stream and decode kernels
+    replay with eager work and synchronisations between replays, and every
+    replay equals the eager calls bit for bit."""
+    q, M, D, F = 32, 2048, 4096, 12288
+    say("step graph", q, M, D, F)
+    up = aa.aa_plan_create("Qq", q, D, F, "pos_mod", 0, "bf16", "bf16")
+    down = aa.aa_plan_create("Qq", q, F, D, "pos_mod", 0, "bf16", "bf16")
+    X = inp.gaussian((M, D), 91, 1.0, torch.bfloat16, DEV)
+    Wp = aa.pack(up, inp.gaussian((D, F), 92, D ** -0.5, torch.bfloat16, DEV))
+    Wg = aa.pack(up, inp.gaussian((D, F), 93, D ** -0.5, torch.bfloat16, DEV))
+    Wu = aa.pack(up, inp.gaussian((D, F), 94, D ** -0.5, torch.bfloat16, DEV))
+    Wd = aa.pack(down, inp.gaussian((F, D), 95, F ** -0.5, torch.bfloat16, DEV))
+    x = X[:32].clone()
+
+    def outs():
+        return (torch.empty(M, F, dtype=torch.bfloat16, device=DEV), torch.empty(M, F, dtype=torch.bfloat16, device=DEV),
+                torch.empty(M, D, dtype=torch.bfloat16, device=DEV), torch.empty(32, F, dtype=torch.bfloat16, device=DEV))
+
+    def step(o):
+        aa.aa_project_fwd(up, X, Wp, o[0])
+        aa.aa_swiglu_ffn_fwd(up, down, X, Wg, Wu, Wd, o[1], o[2])
+        aa.aa_decode_gemv(up, x, Wp, o[3], None, 4096)
+
+    eager, graph = outs(), outs()
+    step(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(graph)
+    Y_other = torch.empty(M, F, dtype=torch.bfloat16, device=DEV)
+    for r in range(3):
+        for t in graph:
+            t.fill_(float("nan"))
+        g.replay()
+        aa.aa_project_fwd(up, inp.gaussian((M, D), 96 + r, 1.0, torch.bfloat16, DEV), Wg, Y_other)
+        torch.cuda.synchronize()
+        for a, b in zip(eager, graph):
+            assert torch.equal(a, b), f"replay {r}"
+
+
 def test_config1_q2_f32_full_product_and_associativity():
     """Q_2 in fp32: row-typed projection, the full 64 x 64 product, and
     (X * W1) * W2 == X * (W1 * W2) computed on the GPU."""
