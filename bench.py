@@ -356,12 +356,33 @@ def bench_qwen3(args, torch, inp, aa, dev):
                  "speedup_step": round((t_p + t_s + t_d) / ms_step, 3)}
         del Wd1, Wd2, Wd3
 
-    dec1 = ffn1 = alone = None
+    dec1 = ffn1 = alone = graph_step = None
     if not args.no_extras:
         dec1 = decode_single_token(torch, aa, plan, sets, pos_dec, n_dec, D, F, q,
                                    None if dense is None else sets[0])
         ffn1 = ffn_single_token(torch, aa, plan, down, sets, pos_dec, n_dec, D, F, q, dense is not None)
         alone = projection_alone(torch, aa, plan, [(st["X"], st["Wp"], st["Y"]) for st in sets], b_proj)
+        # the same step replayed from HIP graphs (one per input set): no host
+        # launch work and no queue gaps between its four kernels
+        graphs = []
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st)
+            graphs.append(g)
+        for w in range(3):
+            graphs[w % n_sets].replay()
+        torch.cuda.synchronize()
+        a, b = _ev(torch), _ev(torch)
+        a.record()
+        for s_ in range(K):
+            graphs[s_ % n_sets].replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms_g = a.elapsed_time(b) / K
+        graph_step = {"ms": round(ms_g, 5), "dense_equiv_tflops": round(total_dense / (ms_g * 1e-3) / 1e12, 2),
+                      "kind": "the step captured in one HIP graph per input set, graphs replayed in turn"}
+        del graphs
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -380,7 +401,8 @@ def bench_qwen3(args, torch, inp, aa, dev):
         "timing": "parts: kernel dispatch events of each call (first kernel start to last kernel end); "
                   "ms_per_step: events around the K steps",
         "ms_between_kernels": round(ms_step - ms_proj - ms_swi - ms_dec, 5),
-        "parts": parts, "projection_alone": alone, "decode_single_token": dec1, "ffn_single_token": ffn1,
+        "parts": parts, "projection_alone": alone, "graph_step": graph_step, "decode_single_token": dec1,
+        "ffn_single_token": ffn1,
         "dense": dense,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall1 - wall0, 4),
