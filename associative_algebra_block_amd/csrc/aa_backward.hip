@@ -444,6 +444,23 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
   }
 }
 
+// Sum of n partial sums spaced `stride` floats apart, added in part order.
+// The loads go out eight at a time before any add, so a thread waits for
+// memory once per eight parts rather than once per part.
+__device__ inline f32x4_t sum_parts(const float* src, int64_t stride, int n) {
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  int p = 0;
+  for (; p + 8 <= n; p += 8) {
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(src + int64_t(p + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; p < n; ++p) s += *reinterpret_cast<const f32x4_t*>(src + int64_t(p) * stride);
+  return s;
+}
+
 // Sum the partial sums of the split leaves into dX: Q_q's own group, row by
 // row (row t of type i gets input group i).
 template <typename Tout>
@@ -455,8 +472,7 @@ __global__ __launch_bounds__(256) void bwd_data_reduce_kernel(BwdDataParams P, i
     const int64_t t = e / cpr;
     const int c = int(e - t * cpr) * 4;
     const int i = P.kind == AA_TYPES_BLOCK_ROWS ? int(t / P.rows_per_type) : int((P.off_mod_q + t) % P.q);
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < nparts; ++p) s += *reinterpret_cast<const f32x4_t*>(P.ws + (int64_t(p) * P.M + t) * P.b_in + c);
+    const f32x4_t s = sum_parts(P.ws + t * P.b_in + c, P.M * P.b_in, nparts);
     store4(dX + t * P.ldx + int64_t(i) * P.b_in + c, s);
   }
 }
@@ -708,8 +724,7 @@ __global__ __launch_bounds__(256) void bwd_weight_reduce_kernel(BwdWeightParams 
   for (int64_t e4 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e4 < n4; e4 += int64_t(gridDim.x) * blockDim.x) {
     const int64_t e = e4 * 4;
     const int64_t k = e / blk, o = e - k * blk;
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    for (int pt = 0; pt < P.nparts; ++pt) s += *reinterpret_cast<const f32x4_t*>(P.ws + int64_t(pt) * P.q * blk + e);
+    const f32x4_t s = sum_parts(P.ws + e, int64_t(P.q) * blk, P.nparts);
     store4(dW + (k * P.q + k) * blk + o, s);
   }
 }
