@@ -240,3 +240,13 @@ def test_last_error_is_thread_local(lib):
     t.start()
     t.join()
     assert mine and seen == [""]
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libaa.so every entry point raises: there is no fallback path."""
+    monkeypatch.setattr(aa, "_LIB", None)
+    monkeypatch.setattr(aa, "lib_path", lambda: str(tmp_path / "libaa.so"))
+    with pytest.raises(RuntimeError, match="is not built"):
+        aa.load()
+    with pytest.raises(RuntimeError, match="is not built"):
+        aa.aa_plan_create("Qq", 4, 64, 64)
