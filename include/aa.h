@@ -34,6 +34,13 @@
  *    returns AA_ERR_HIP.  With the environment variable AA_DEBUG=1 every call
  *    synchronises its stream after launching and reports asynchronous faults
  *    as AA_ERR_HIP.
+ *  - Kernel selection is automatic.  For tuning experiments only, the
+ *    environment variables AA_TILE (force one kernel variant), AA_WG_PER_CU
+ *    (workgroups per compute unit of the persistent kernels) and
+ *    AA_PERSIST_POL (their cache-policy bits) are read once, when a plan is
+ *    created, and stay fixed for that plan; a forced variant that does not
+ *    fit the plan falls back to the general kernel.  Results do not depend on
+ *    them beyond fp32 summation order.
  *  - Device pointers must be 16-byte aligned.
  *  - A plan is immutable after creation and may be shared between threads
  *    and streams.  aa_plan_create and aa_plan_info make no HIP calls.
