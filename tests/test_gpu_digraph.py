@@ -54,6 +54,8 @@ def _types(kind, M, q, pos_offset, seed):
     ("0.5", 4, 512, 256, 512, "block_rows", 0),
     ("empty", 4, 200, 256, 256, "pos_mod", 2),
     ("complete", 8, 500, 1024, 512, "pos_mod", 5),
+    ("0.2", 64, 640, 1024, 2048, "pos_mod", 1),      # q = 64, the widest adjacency row: 16 x 32 blocks
+    ("0.1", 64, 320, 8192, 8192, "pos_mod", 0),      # q = 64 with 128 x 128 blocks (persistent kernel)
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_digraph_projection_matches_oracle(graph, q, M, d_in, d_out, kind, pos_offset, out_dt):
