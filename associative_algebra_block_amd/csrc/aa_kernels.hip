@@ -1775,6 +1775,71 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Decode under Q2 x Q2: a token's leaf (type i, output group k) has one, two
+// or four input groups ([review], pilot-law paragraph), so a workgroup takes
+// one 16-column strip of output group k for one token and its wave w the
+// leaf's w-th input group: every weight run a wave needs is requested before
+// the first multiply, no wave waits on another's loads, and the grid has a
+// workgroup per strip (96 for the pilot's gate/up instead of 24 with a
+// 64-column chunk per workgroup).  The waves' partial sums meet in LDS and
+// are added in input-group order.
+template <typename Tout, int KF, bool SWIGLU>
+__global__ __launch_bounds__(256) void decode_q2_kernel(DecodeParams p) {
+  using Tin = __bf16;
+  __shared__ f32x4_t part[4][SWIGLU ? 2 : 1][kWave];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int k = blockIdx.x / p.nstrips;
+  const int strip = blockIdx.x % p.nstrips;
+  const int64_t r = blockIdx.y;
+  int ty = p.row_types ? p.row_types[r] : int((p.off_mod_q + r) % p.q);
+  if (ty < 0 || ty >= p.q) return;   // a row the call leaves unwritten (whole workgroup)
+  int sg[4];
+  const int ns = device_leaf_groups(p.law, ty, k, sg);
+  const bool live = wave < ns;
+  const int j = live ? sg[wave] : k;
+  const Tin* __restrict__ W = static_cast<const Tin*>(p.W);
+  const Tin* __restrict__ Wu = static_cast<const Tin*>(p.W1);
+  const Tin* __restrict__ x = static_cast<const Tin*>(p.x);
+  const int64_t base = (int64_t(j) * p.q + k) * (int64_t(p.b_in) * p.b_out) + int64_t(strip) * 16 * p.b_in + lane * 8;
+  // Slabs past b_in (KF rounded up, or the upper half of a half-width last
+  // slab) re-read the strip's first run and meet a zero activation.
+  Run<Tin> w[KF], u[SWIGLU ? KF : 1], b[KF];
+#pragma unroll
+  for (int kf = 0; kf < KF; ++kf) {
+    const bool in_blk = kf * 32 + g * 8 < p.b_in;
+    const int64_t o = base + (in_blk ? kf * 512 : 0);
+    w[kf] = Run<Tin>::load(W + o);
+    if (SWIGLU) u[kf] = Run<Tin>::load(Wu + o);
+    b[kf] = Run<Tin>::zero();
+    if (live && l16 == 0 && in_blk) b[kf] = Run<Tin>::load_cached(x + r * p.ldx + int64_t(j) * p.b_in + kf * 32 + g * 8);
+  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+#pragma unroll
+    for (int kf = 0; kf < KF; ++kf) {
+      acc = mma(w[kf], b[kf], acc);
+      if (SWIGLU) acc1 = mma(u[kf], b[kf], acc1);
+    }
+  }
+  part[wave][0][lane] = acc;
+  if (SWIGLU) part[wave][SWIGLU ? 1 : 0][lane] = acc1;
+  __syncthreads();
+  if (wave != 0 || l16 != 0) return;
+  // lane (g, 0) holds the token's strip columns g*4 .. g*4+3
+  f32x4_t s = part[0][0][lane], s1 = SWIGLU ? part[0][SWIGLU ? 1 : 0][lane] : s;
+  for (int v = 1; v < ns; ++v) {
+    s += part[v][0][lane];
+    if (SWIGLU) s1 += part[v][SWIGLU ? 1 : 0][lane];
+  }
+  if (SWIGLU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = silu_mul(s[e], s1[e]);
+  }
+  store4(static_cast<Tout*>(p.y) + r * p.ldy + int64_t(k) * p.b_out + strip * 16 + g * 4, s);
+}
+
 // ----------------------------------------------------------------- pack ---
 
 // Thread c moves one run of 8 elements: packed elements [8c, 8c + 8) from/to
@@ -2476,6 +2541,26 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, c
   // blocks so that (TG + 1) * KF weight runs fit the registers.
   const int kf = int((plan.b_in + 31) / 32);
   const bool fin = plan.in_dtype == AA_F32, fout = plan.out_dtype == AA_F32;
+  if (plan.law == AA_LAW_Q2XQ2 && !fin && kf <= 12) {
+    // one workgroup per (output strip, token), one wave per input group
+    const dim3 grid{uint32_t(plan.q * p.nstrips), uint32_t(n), 1}, block{256, 1, 1};
+    auto q2 = [&](auto kf_c) {
+      constexpr int KFc = decltype(kf_c)::value;
+      if (W1 != nullptr) {
+        if (fout) launch((decode_q2_kernel<float, KFc, true>), grid, block, 0, stream, p);
+        else launch((decode_q2_kernel<__bf16, KFc, true>), grid, block, 0, stream, p);
+      } else {
+        if (fout) launch((decode_q2_kernel<float, KFc, false>), grid, block, 0, stream, p);
+        else launch((decode_q2_kernel<__bf16, KFc, false>), grid, block, 0, stream, p);
+      }
+    };
+    if (kf <= 2) q2(std::integral_constant<int, 2>{});
+    else if (kf <= 4) q2(std::integral_constant<int, 4>{});
+    else if (kf <= 6) q2(std::integral_constant<int, 6>{});
+    else if (kf <= 8) q2(std::integral_constant<int, 8>{});
+    else q2(std::integral_constant<int, 12>{});
+    return after_launch(stream, W1 ? "decode_q2(swiglu)" : "decode_q2");
+  }
   auto go = [&](auto tg_c, auto kf_c) {
     constexpr int TGc = decltype(tg_c)::value, KFc = decltype(kf_c)::value;
     const int64_t groups = (n + TGc - 1) / TGc;

@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
                     choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
-                             "digraph_qwen3_8b",
+                             "digraph_qwen3_8b", "pilot_decode_stack",
                              "backward_qwen3_8b", "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -102,6 +102,8 @@ def main():
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[3], digraph_density=0.5)
     elif args.workload.startswith("backward_"):
         res = bench_backward(args, torch, inp, aa, dev, args.workload)
+    elif args.workload == "pilot_decode_stack":
+        res = bench_decode_stack(args, torch, inp, aa, dev)
     elif args.workload == "square":
         res = bench_square(args, torch, inp, aa, dev)
     else:
@@ -881,6 +883,127 @@ def bench_ffn(args, torch, inp, aa, dev, which):
         t = dense_timer(torch, lambda: torch.matmul(
             torch.nn.functional.silu(torch.matmul(X, Wd1)) * torch.matmul(X, Wd2), Wd3))
         res["dense"] = {"kind": "torch.matmul bf16 x3 + silu*mul", "ms": round(t, 5), "speedup": round(t / ms, 3)}
+    return res
+
+
+STACK_LAYERS = 12   # decoder blocks of the 110M pilot model
+
+
+def decode_stack_weights(torch, inp, aa, up, down, D, F, dev):
+    """Seeded synthetic weights of the FFN stack, packed: one (gate, up,
+    down) triple per layer, N(0, 1/fan_in)."""
+    wl = inp.WORKLOADS[2]
+    out = []
+    for layer in range(STACK_LAYERS):
+        off = 10 * (layer + 1)
+        out.append((aa.pack(up, inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, wl.index) + off, D ** -0.5,
+                                             torch.bfloat16, dev)),
+                    aa.pack(up, inp.gaussian((D, F), inp.seed_for(inp.ROLE_WU, wl.index) + off, D ** -0.5,
+                                             torch.bfloat16, dev)),
+                    aa.pack(down, inp.gaussian((F, D), inp.seed_for(inp.ROLE_WD, wl.index) + off, F ** -0.5,
+                                               torch.bfloat16, dev))))
+    return out
+
+
+def bench_decode_stack(args, torch, inp, aa, dev):
+    """Fixed-length generation through the FFN stack of the 110M pilot model
+    (12 blocks, width 768, SwiGLU 1536, Q2xQ2 law, context 1536): one new
+    token per call, each token through all 12 FFNs in turn (layer l reads
+    layer l - 1's output).  Attention, norms, the LM head and sampling are not
+    in this path, so the rate is that of the FFN share of decoding only.  A
+    HIP graph holds q = 4 consecutive tokens (every row type once; with the
+    context a multiple of q the same graph serves every later group of 4
+    positions) and is replayed for the whole length.  The dense comparator
+    is the same stack with torch.matmul (three GEMVs and silu * mul per
+    layer), one token per graph, replayed as often."""
+    wl = inp.WORKLOADS[2]
+    D, F, q, law = wl.d_in, wl.d_out, wl.q, wl.law
+    period = wl.extra.get("period", 0)
+    L = 256   # generated tokens per timed step
+    up = aa.aa_plan_create(law, q, D, F, "pos_mod", period, "bf16", "bf16")
+    down = aa.aa_plan_create(law, q, F, D, "pos_mod", period, "bf16", "bf16")
+    W = decode_stack_weights(torch, inp, aa, up, down, D, F, dev)
+    x = inp.gaussian((q, D), inp.seed_for(inp.ROLE_X, wl.index), 1.0, torch.bfloat16, dev)
+    H = torch.empty(q, F, dtype=torch.bfloat16, device=dev)
+    Ys = [torch.empty(q, D, dtype=torch.bfloat16, device=dev) for _ in range(STACK_LAYERS)]
+
+    def tokens():   # positions 0 .. q - 1, one call per token and layer
+        for j in range(q):
+            src = x[j:j + 1]
+            for layer, (g, u, d) in enumerate(W):
+                aa.aa_swiglu_ffn_fwd(up, down, src, g, u, d, H[j:j + 1], Ys[layer][j:j + 1], None, j)
+                src = Ys[layer][j:j + 1]
+
+    for _ in range(3):
+        tokens()
+    torch.cuda.synchronize()
+    reps = L // q
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for _ in range(reps):
+        tokens()
+    b.record()
+    torch.cuda.synchronize()
+    eager_us = a.elapsed_time(b) * 1e3 / L
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tokens()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    a.record()
+    for _ in range(K):
+        for _ in range(reps):
+            g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K            # one step = L tokens
+    us_tok = ms * 1e3 / L
+    # a token reads its row type's 9 of the 16 blocks of each of the 36 weights
+    per_tok = STACK_LAYERS * 2 * (3 * 9 * (D // q) * (F // q) + 2 * D + 2 * F)
+    res = {"metric": "FFN-stack decode tokens/s, pilot 110M shape (12 SwiGLU blocks, Q2xQ2), no attention",
+           "value": round(L / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "pilot_decode_stack", "layers": STACK_LAYERS, "D": D, "F": F, "q": q,
+                      "law": law, "period": period, "tokens_per_step": L, "batch": 1,
+                      "graph": f"{q} tokens x {STACK_LAYERS} layers per replay"},
+           "us_per_token": round(us_tok, 3), "eager_us_per_token": round(eager_us, 3),
+           "bytes_per_token": per_tok, "GBs": round(per_tok / us_tok / 1e3, 1),
+           "weights_resident": f"{STACK_LAYERS * 3 * D * F * 2 / 1e6:.0f} MB of weights, inside the 256 MB "
+                               "Infinity Cache across tokens",
+           "kernel_source": kernel_source_hash()}
+    if not args.no_dense:
+        dw = [[torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(0.0, shape[0] ** -0.5)
+               for shape in ((D, F), (D, F), (F, D))] for _ in range(STACK_LAYERS)]
+        x1 = x[:1].clone()
+
+        def dense_token():
+            h = x1
+            for Wg, Wu, Wd in dw:
+                h = torch.matmul(torch.nn.functional.silu(torch.matmul(h, Wg)) * torch.matmul(h, Wu), Wd)
+            return h
+
+        for _ in range(3):
+            dense_token()
+        torch.cuda.synchronize()
+        dg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(dg):
+            dense_token()
+        for _ in range(3):
+            dg.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(L):
+            dg.replay()
+        b.record()
+        torch.cuda.synchronize()
+        dense_us = a.elapsed_time(b) * 1e3 / L
+        res["dense"] = {"kind": "torch.matmul bf16, 3 GEMVs + silu*mul per layer, one token per HIP graph",
+                        "us_per_token": round(dense_us, 3), "tokens_per_s": round(1e6 / dense_us, 1),
+                        "speedup": round(dense_us / us_tok, 3)}
+        del dw
     return res
 
 
