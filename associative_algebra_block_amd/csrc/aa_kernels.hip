@@ -1775,17 +1775,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 }
 
-// Decode under Q2 x Q2: a token's leaf (type i, output group k) has one, two
-// or four input groups ([review], pilot-law paragraph), so a workgroup takes
-// one 16-column strip of output group k for one token and its wave w the
-// leaf's w-th input group: every weight run a wave needs is requested before
-// the first multiply, no wave waits on another's loads, and the grid has a
-// workgroup per strip (96 for the pilot's gate/up instead of 24 with a
-// 64-column chunk per workgroup).  The waves' partial sums meet in LDS and
-// are added in input-group order.
-template <typename Tout, int KF, bool SWIGLU>
-__global__ __launch_bounds__(256) void decode_q2_kernel(DecodeParams p) {
+// Decode of one token per workgroup: a workgroup takes one 16-column strip
+// of output group k for one token, and its four waves split the leaf's
+// (input group, 32-row slab) pairs between them - a Q_q leaf has one or two
+// input groups, a Q2 x Q2 leaf one, two or four ([review], multiplication-
+// table and pilot-law paragraphs).  Every weight run a wave needs is requested
+// before its first multiply, no wave waits on another's loads, and the grid
+// has a workgroup per strip and token (the pilot's single-token gate/up: 96
+// workgroups instead of 24 with a 64-column chunk per workgroup; the Qwen3-8B
+// down projection: 256 instead of 64).  The waves' partial sums meet in LDS
+// and are added in wave order.
+template <typename Tout, int KF, int NSMAX, bool SWIGLU>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
   using Tin = __bf16;
+  constexpr int UPW = (NSMAX * KF + 3) / 4;   // (group, slab) units per wave
   __shared__ f32x4_t part[4][SWIGLU ? 2 : 1][kWave];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -1797,47 +1800,50 @@ __global__ __launch_bounds__(256) void decode_q2_kernel(DecodeParams p) {
   if (ty < 0 || ty >= p.q) return;   // a row the call leaves unwritten (whole workgroup)
   int sg[4];
   const int ns = device_leaf_groups(p.law, ty, k, sg);
-  const bool live = wave < ns;
-  const int j = live ? sg[wave] : k;
   const Tin* __restrict__ W = static_cast<const Tin*>(p.W);
   const Tin* __restrict__ Wu = static_cast<const Tin*>(p.W1);
   const Tin* __restrict__ x = static_cast<const Tin*>(p.x);
-  const int64_t base = (int64_t(j) * p.q + k) * (int64_t(p.b_in) * p.b_out) + int64_t(strip) * 16 * p.b_in + lane * 8;
-  // Slabs past b_in (KF rounded up, or the upper half of a half-width last
-  // slab) re-read the strip's first run and meet a zero activation.
-  Run<Tin> w[KF], u[SWIGLU ? KF : 1], b[KF];
+  const int64_t blk = int64_t(p.b_in) * p.b_out;
+  const int64_t sofs = int64_t(strip) * 16 * p.b_in + lane * 8;
+  // Unit t of this wave is u = wave + 4 t: input group sg[u / KF], slab
+  // u % KF.  Units past the leaf, slabs past b_in (KF rounded up) and the
+  // upper half of a half-width last slab re-read a valid run and meet a zero
+  // activation.
+  Run<Tin> w[UPW], u[SWIGLU ? UPW : 1], b[UPW];
 #pragma unroll
-  for (int kf = 0; kf < KF; ++kf) {
-    const bool in_blk = kf * 32 + g * 8 < p.b_in;
-    const int64_t o = base + (in_blk ? kf * 512 : 0);
-    w[kf] = Run<Tin>::load(W + o);
-    if (SWIGLU) u[kf] = Run<Tin>::load(Wu + o);
-    b[kf] = Run<Tin>::zero();
-    if (live && l16 == 0 && in_blk) b[kf] = Run<Tin>::load_cached(x + r * p.ldx + int64_t(j) * p.b_in + kf * 32 + g * 8);
+  for (int t = 0; t < UPW; ++t) {
+    const int un = wave + 4 * t;
+    const int s = un / KF, kf = un - s * KF;
+    const bool live = s < ns && kf * 32 + g * 8 < p.b_in;
+    const int j = s < ns ? sg[s] : k;
+    const int64_t o = (int64_t(j) * p.q + k) * blk + sofs + (live ? kf * 512 : 0);
+    w[t] = Run<Tin>::load(W + o);
+    if (SWIGLU) u[t] = Run<Tin>::load(Wu + o);
+    b[t] = Run<Tin>::zero();
+    if (live && l16 == 0) b[t] = Run<Tin>::load_cached(x + r * p.ldx + int64_t(j) * p.b_in + kf * 32 + g * 8);
   }
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  if (live) {
 #pragma unroll
-    for (int kf = 0; kf < KF; ++kf) {
-      acc = mma(w[kf], b[kf], acc);
-      if (SWIGLU) acc1 = mma(u[kf], b[kf], acc1);
-    }
+  for (int t = 0; t < UPW; ++t) {
+    acc = mma(w[t], b[t], acc);
+    if (SWIGLU) acc1 = mma(u[t], b[t], acc1);
   }
   part[wave][0][lane] = acc;
   if (SWIGLU) part[wave][SWIGLU ? 1 : 0][lane] = acc1;
   __syncthreads();
   if (wave != 0 || l16 != 0) return;
   // lane (g, 0) holds the token's strip columns g*4 .. g*4+3
-  f32x4_t s = part[0][0][lane], s1 = SWIGLU ? part[0][SWIGLU ? 1 : 0][lane] : s;
-  for (int v = 1; v < ns; ++v) {
-    s += part[v][0][lane];
-    if (SWIGLU) s1 += part[v][SWIGLU ? 1 : 0][lane];
+  f32x4_t sum = part[0][0][lane], sum1 = part[0][SWIGLU ? 1 : 0][lane];
+#pragma unroll
+  for (int v = 1; v < 4; ++v) {
+    sum += part[v][0][lane];
+    if (SWIGLU) sum1 += part[v][SWIGLU ? 1 : 0][lane];
   }
   if (SWIGLU) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] = silu_mul(s[e], s1[e]);
+    for (int e = 0; e < 4; ++e) sum[e] = silu_mul(sum[e], sum1[e]);
   }
-  store4(static_cast<Tout*>(p.y) + r * p.ldy + int64_t(k) * p.b_out + strip * 16 + g * 4, s);
+  store4(static_cast<Tout*>(p.y) + r * p.ldy + int64_t(k) * p.b_out + strip * 16 + g * 4, sum);
 }
 
 // ----------------------------------------------------------------- pack ---
@@ -2541,25 +2547,31 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, c
   // blocks so that (TG + 1) * KF weight runs fit the registers.
   const int kf = int((plan.b_in + 31) / 32);
   const bool fin = plan.in_dtype == AA_F32, fout = plan.out_dtype == AA_F32;
-  if (plan.law == AA_LAW_Q2XQ2 && !fin && kf <= 12) {
-    // one workgroup per (output strip, token), one wave per input group
+  // One token per workgroup (the waves splitting its leaf): every Q2 x Q2
+  // decode, and Q_q generation (one token per call).
+  const bool split = !fin && kf <= 12 && (plan.law == AA_LAW_Q2XQ2 || (plan.law == AA_LAW_QQ && n == 1));
+  if (split) {
     const dim3 grid{uint32_t(plan.q * p.nstrips), uint32_t(n), 1}, block{256, 1, 1};
-    auto q2 = [&](auto kf_c) {
-      constexpr int KFc = decltype(kf_c)::value;
+    auto go_split = [&](auto kf_c, auto ns_c) {
+      constexpr int KFc = decltype(kf_c)::value, NSc = decltype(ns_c)::value;
       if (W1 != nullptr) {
-        if (fout) launch((decode_q2_kernel<float, KFc, true>), grid, block, 0, stream, p);
-        else launch((decode_q2_kernel<__bf16, KFc, true>), grid, block, 0, stream, p);
+        if (fout) launch((decode_split_kernel<float, KFc, NSc, true>), grid, block, 0, stream, p);
+        else launch((decode_split_kernel<__bf16, KFc, NSc, true>), grid, block, 0, stream, p);
       } else {
-        if (fout) launch((decode_q2_kernel<float, KFc, false>), grid, block, 0, stream, p);
-        else launch((decode_q2_kernel<__bf16, KFc, false>), grid, block, 0, stream, p);
+        if (fout) launch((decode_split_kernel<float, KFc, NSc, false>), grid, block, 0, stream, p);
+        else launch((decode_split_kernel<__bf16, KFc, NSc, false>), grid, block, 0, stream, p);
       }
     };
-    if (kf <= 2) q2(std::integral_constant<int, 2>{});
-    else if (kf <= 4) q2(std::integral_constant<int, 4>{});
-    else if (kf <= 6) q2(std::integral_constant<int, 6>{});
-    else if (kf <= 8) q2(std::integral_constant<int, 8>{});
-    else q2(std::integral_constant<int, 12>{});
-    return after_launch(stream, W1 ? "decode_q2(swiglu)" : "decode_q2");
+    auto by_kf = [&](auto ns_c) {
+      if (kf <= 2) go_split(std::integral_constant<int, 2>{}, ns_c);
+      else if (kf <= 4) go_split(std::integral_constant<int, 4>{}, ns_c);
+      else if (kf <= 6) go_split(std::integral_constant<int, 6>{}, ns_c);
+      else if (kf <= 8) go_split(std::integral_constant<int, 8>{}, ns_c);
+      else go_split(std::integral_constant<int, 12>{}, ns_c);
+    };
+    if (plan.law == AA_LAW_Q2XQ2) by_kf(std::integral_constant<int, 4>{});
+    else by_kf(std::integral_constant<int, 2>{});
+    return after_launch(stream, W1 ? "decode_split(swiglu)" : "decode_split");
   }
   auto go = [&](auto tg_c, auto kf_c) {
     constexpr int TGc = decltype(tg_c)::value, KFc = decltype(kf_c)::value;
