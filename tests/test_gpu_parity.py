@@ -424,6 +424,9 @@ def test_row_locality():
     ("Q2xQ2", 4, 768, 1536, 7, "bf16"), ("Qq", 16, 768, 2048, 20, "bf16"),
     ("Qq", 32, 12288, 4096, 5, "bf16"), ("Qq", 2, 64, 64, 9, "f32"), ("Qq", 4, 320, 64, 6, "bf16"),
     ("Qq", 8, 1024, 1536, 2, "bf16"), ("Q2xQ2", 4, 768, 1536, 1, "bf16"), ("Qq", 16, 6144, 2048, 2, "bf16"),
+    # one token per workgroup: a half-width last slab (b_in = 80), q = 1, 384-wide blocks, Q2 x Q2 tails
+    ("Qq", 4, 320, 64, 1, "bf16"), ("Qq", 1, 64, 48, 1, "bf16"), ("Qq", 32, 12288, 4096, 1, "bf16"),
+    ("Q2xQ2", 4, 320, 512, 3, "bf16"), ("Q2xQ2", 4, 1536, 768, 2, "f32"),
     # many tokens: from 2q (by position) and 8q (explicit types) on, the leaf kernels
     ("Qq", 8, 1024, 1536, 64, "bf16"), ("Qq", 32, 4096, 12288, 300, "bf16"), ("Q2xQ2", 4, 768, 1536, 40, "bf16")])
 def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n, dt):
