@@ -620,7 +620,9 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 #pragma unroll
     for (int jb = 0; jb < JPB; ++jb) {
       const int r = jb * (NTHR / XCB) + x_r0;
-      rowofs[jb] = (T.nrows > 0 ? T.first + int64_t(r < T.nrows ? r : 0) * T.stride : 0) * p.ldx;
+      // a digraph leaf with no input group (it stores zeros) re-reads row 0,
+      // which stays in L1, instead of fetching rows nothing will use
+      rowofs[jb] = (T.nrows > 0 && T.nchunks > 0 ? T.first + int64_t(r < T.nrows ? r : 0) * T.stride : 0) * p.ldx;
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
@@ -664,7 +666,9 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int kl = 0; kl < CK; ++kl) {
-          const int64_t o = base + ((nfrag0 + f) * 16 < p.b_out ? wl + f * fstride : int64_t(lane) * 16) + kl * 1024;
+          // (with no input group, every load re-reads the block's first 1 KiB)
+          const int64_t o = T.nchunks == 0 ? base + int64_t(lane) * 16
+                                           : base + ((nfrag0 + f) * 16 < p.b_out ? wl + f * fstride : int64_t(lane) * 16) + kl * 1024;
           if ((POL & kPolWOwn) && ch == 0) {
             a0[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
             if (SWIGLU) a1[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o));
