@@ -620,13 +620,14 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 #pragma unroll
     for (int jb = 0; jb < JPB; ++jb) {
       const int r = jb * (NTHR / XCB) + x_r0;
-      // a digraph leaf with no input group (it stores zeros) re-reads row 0,
-      // which stays in L1, instead of fetching rows nothing will use
-      rowofs[jb] = (T.nrows > 0 && T.nchunks > 0 ? T.first + int64_t(r < T.nrows ? r : 0) * T.stride : 0) * p.ldx;
+      // a void step, and a digraph leaf with no input group (it stores
+      // zeros), re-read row 0, which stays in L1, instead of fetching rows
+      // nothing will use
+      rowofs[jb] = (T.live && T.nrows > 0 && T.nchunks > 0 ? T.first + int64_t(r < T.nrows ? r : 0) * T.stride : 0) * p.ldx;
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      // a void step re-reads the type's own group, which stays in L2
+      // a void step reads the own group's first columns of row 0
       const int colofs = ch < T.nchunks ? seg_of(T, T.live ? ch : 0) * p.b_in + x_cc * 8 : 0;
 #pragma unroll
       for (int jb = 0; jb < JPB; ++jb) {
@@ -659,15 +660,15 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int c = ch < T.nchunks ? ch : 0;
-      // a void step, and a digraph leaf with no input group, re-read the
-      // diagonal block W_kk, which stays in L2
+      // a void step, and a digraph leaf with no input group, address the
+      // diagonal block W_kk (and re-read its first 1 KiB only, below)
       const int64_t base = (int64_t(T.live && T.nchunks > 0 ? seg_of(T, c) : T.k) * p.q + T.k) * blk_bytes;
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int kl = 0; kl < CK; ++kl) {
-          // (with no input group, every load re-reads the block's first 1 KiB)
-          const int64_t o = T.nchunks == 0 ? base + int64_t(lane) * 16
+          // (a void step, or no input group: every load re-reads the block's first 1 KiB)
+          const int64_t o = !T.live || T.nchunks == 0 ? base + int64_t(lane) * 16
                                            : base + ((nfrag0 + f) * 16 < p.b_out ? wl + f * fstride : int64_t(lane) * 16) + kl * 1024;
           if ((POL & kPolWOwn) && ch == 0) {
             a0[ch][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o));
@@ -752,8 +753,9 @@ __global__ __launch_bounds__(256, 2) void leaf_persist_kernel(LeafParams p) {
   if (t0 >= run_end) return;
   const int n_my = int((run_end - t0 + G8 - 1) / G8);
   const uint32_t t_last = t0 + uint32_t(n_my - 1) * G8;
-  // Step u of this workgroup; steps past its last tile are void: they
-  // re-read data of the last tile that stays in L2 and store nothing.  No
+  // Step u of this workgroup; steps past its last tile are void: all their
+  // loads re-read one 1 KiB run and one activation row, which stay in L1,
+  // and they store nothing.  No
   // load is ever skipped by a branch, and the loop exits only after whole
   // rounds of two steps, so every step sees the same queue of pending loads
   // and the waits before the multiplies never drain the prefetch.
