@@ -1230,9 +1230,10 @@ __global__ __launch_bounds__(256, 2) void leaf_kstream_kernel(LeafParams p) {
   };
 
   // ---- loads of one step.  Slot 0: x_i chunk j and W_ik chunk j; slot 1:
-  // x_k chunk j and W_kk chunk j (a diagonal leaf or a void step re-reads the
-  // cached data of slot 0 / of W_kk).  Activations: chunk x_cc of rows
-  // x_r0 + jb (NTHR / XCB); rows past the tile re-read its first row.
+  // x_k chunk j and W_kk chunk j (a diagonal leaf re-reads the cached data of
+  // slot 0; a void step re-reads one 1 KiB run and one row start).
+  // Activations: chunk x_cc of rows x_r0 + jb (NTHR / XCB); rows past the
+  // tile re-read its first row.
   const int x_cc = int(threadIdx.x) % XCB, x_r0 = int(threadIdx.x) / XCB;
   auto load = [&](const Step& S, Run<Tin> (&xr)[2 * JPB], Run<Tin> (&wr)[2][CK][NF],
                   Run<Tin> (&wu)[2][CK][NF]) __attribute__((always_inline)) {
@@ -1242,7 +1243,9 @@ __global__ __launch_bounds__(256, 2) void leaf_kstream_kernel(LeafParams p) {
 #pragma unroll
     for (int jb = 0; jb < JPB; ++jb) {
       const int rr = jb * (NTHR / XCB) + x_r0;
-      rowofs[jb] = uint32_t(rr < S.nrows ? rr : 0) * rstep + uint32_t(S.j * 32 * CK + x_cc * 8);
+      // a void step reads the first columns of the tile's first row only
+      rowofs[jb] = S.live ? uint32_t(rr < S.nrows ? rr : 0) * rstep + uint32_t(S.j * 32 * CK + x_cc * 8)
+                          : uint32_t(x_cc * 8);
     }
     const Tin* x0 = xt + S.i * p.b_in;
     const Tin* x1 = (S.live && !S.diag) ? xt + S.k * p.b_in : x0;
@@ -1263,7 +1266,9 @@ __global__ __launch_bounds__(256, 2) void leaf_kstream_kernel(LeafParams p) {
       const int64_t so = int64_t(sl) * strip_bytes + lo;
 #pragma unroll
       for (int kl = 0; kl < CK; ++kl) {
-        const int64_t o0 = b0 + so + kl * 1024, o1 = kkb + so + kl * 1024;
+        // a void step re-reads the first 1 KiB of W_kk, which stays in L1
+        const int64_t o0 = S.live ? b0 + so + kl * 1024 : kkb + lane * 16;
+        const int64_t o1 = S.live ? kkb + so + kl * 1024 : kkb + lane * 16;
         if (POL & kPolWOwn) {
           wr[0][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W0 + o0));
           if (SWIGLU) wu[0][kl][f] = Run<Tin>::load(reinterpret_cast<const Tin*>(W1 + o0));
