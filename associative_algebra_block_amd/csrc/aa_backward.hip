@@ -51,7 +51,7 @@
 //
 // Both kernels keep the forward kernels' pipeline discipline: NSET rotating
 // register sets, loads of step e + NSET - 1 issued after step e's multiplies,
-// void steps past the end re-reading valid addresses, whole rounds only.
+// void steps past the end reading one zero run (it stays in L1), whole rounds only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
 #pragma unroll
       for (int c = 0; c < NWL; ++c) {
         const int ch = c * NTHR + int(threadIdx.x);
-        const __bf16* src = ch < nvalid ? wt + ch * 8 : zero;
+        const __bf16* src = S.live && ch < nvalid ? wt + ch * 8 : zero;   // a void step reads zeros (L1)
         wr[t][c] = *reinterpret_cast<const u32x4_t*>(src);
       }
     }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void bwd_data_kernel(BwdDataParams P) {
 #pragma unroll
       for (int mf = 0; mf < MF; ++mf) {
         const int64_t tt = int64_t(S.it.mt) * TM + (wave * MF + mf) * 16 + r;
-        const bool ok = kok && tt < S.tr.count;
+        const bool ok = S.live && kok && tt < S.tr.count;
         const __bf16* src =
             ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + st0 * 16 + h * 32 + g * 8
                : zero;
@@ -864,7 +864,7 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_tile_kernel(WTileParams P) 
       const int ch = l * NTHR + int(threadIdx.x);
       const int tk = ch >> 4, cc = ch & 15;
       const int64_t tt = int64_t(S.st) * TK + tk;
-      const bool rok = tt < S.tr.count;
+      const bool rok = S.live && tt < S.tr.count;   // a void step reads zeros (L1)
       const int64_t row = S.tr.first + tt * S.tr.stride;
       const __bf16* xs = rok && cc * 8 < xw ? P.X + row * P.ldx + int64_t(S.it.j) * b_in + S.it.dc * 128 + cc * 8 : zero;
       const __bf16* ys =
