@@ -370,11 +370,3 @@ def executed_flops(M_per_type, d_in: int, d_out: int, law: str, q: int) -> int:
     bi, bo = d_in // q, d_out // q
     return int(sum(2 * int(m) * bi * bo * count_row_block_products(law, q, i)
                    for i, m in enumerate(M_per_type)))
-
-
-def row_mac_ratio(law: str, q: int) -> float:
-    """Fraction of a dense row's block products that a row of each type performs."""
-    vals = {count_row_block_products(law, q, i) for i in range(q)}
-    if len(vals) != 1:
-        raise ValueError("types differ")
-    return vals.pop() / (q * q)

@@ -233,6 +233,31 @@ def pin_rowtyped_equals_full_rows(orc):
             _close(orc.project(x, B, law, q, [i]), full[[i]])
 
 
+def pin_project_block_row(orc):
+    # Block-row i of a full product A * B, computed from that block-row of A
+    # alone, equals block-row i of the product given by the closed forms
+    # through library matrix products (Q_q: A B - off(A) off(B); Q2 x Q2: the
+    # inclusion-exclusion form).  The weight may also be any 2-D sliceable
+    # (the tests pass a lazy view of a device tensor).
+    rng = _rng(31)
+    Pa = lambda A: _proj_q2xq2(A, lambda a, b, a1, b1: a != a1)
+    Pb = lambda A: _proj_q2xq2(A, lambda a, b, a1, b1: b != b1)
+    Pab = lambda A: _proj_q2xq2(A, lambda a, b, a1, b1: a != a1 and b != b1)
+    for law, q, (ra, ca, cb) in [("Qq", 3, (2, 2, 3)), ("Qq", 5, (1, 3, 2)), ("Q2xQ2", 4, (3, 2, 2))]:
+        A = rng.standard_normal((q * ra, q * ca))
+        B = rng.standard_normal((q * ca, q * cb))
+        if law == "Qq":
+            full = A @ B - _off_qq(A, q) @ _off_qq(B, q)
+        else:
+            full = A @ B - Pa(A) @ Pa(B) - Pb(A) @ Pb(B) + Pab(A) @ Pab(B)
+        for i in range(q):
+            rows = slice(i * ra, (i + 1) * ra)
+            _close(orc.project_block_row(A[rows], B, law, q, i), full[rows])
+            # a subset of the block-row's rows (one row, in the middle)
+            r = i * ra + ra // 2
+            _close(orc.project_block_row(A[r:r + 1], B, law, q, i), full[r:r + 1])
+
+
 def pin_row_locality(orc):
     rng = _rng(9)
     q = 4

@@ -61,6 +61,10 @@ MUTANTS = [
     ("grad_weight_dense", "for j in leaf_groups(law, q, i, k):\n                dW", "for j in range(q):\n                dW"),
     ("digraph_keeps_every_slot", "return law.has(i, k) and (j == i or j == k)", "return j == i or j == k"),
     ("digraph_edge_drops_target_diag", "return law.has(i, k) and (j == i or j == k)", "return law.has(i, k) and j == i"),
+    ("block_row_next_type", "np.full(X_rows.shape[0], i, dtype=np.int64)",
+     "np.full(X_rows.shape[0], (i + 1) % q, dtype=np.int64)"),
+    ("block_row_type_zero", "np.full(X_rows.shape[0], i, dtype=np.int64)",
+     "np.zeros(X_rows.shape[0], dtype=np.int64)"),
     ("digraph_reversed_edges", "return law.has(i, k) and (j == i or j == k)", "return law.has(k, i) and (j == i or j == k)"),
 ]
 
