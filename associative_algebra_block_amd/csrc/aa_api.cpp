@@ -56,6 +56,54 @@ aa_status_t check_bwd(const aa_plan_s& plan, int64_t M, int64_t pos_offset, cons
   return AA_OK;
 }
 
+// Checks shared by the two SwiGLU calls (everything but the hidden buffer).
+aa_status_t check_swiglu(aa_plan_t up, aa_plan_t down, const void* X, const void* Wg_packed, const void* Wu_packed,
+                         const void* Wd_packed, const void* Y, int64_t M, int64_t pos_offset,
+                         const int32_t* row_types, const char* fn) {
+  if (!up || !down) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": plan is NULL");
+  if (up->law != down->law || up->q != down->q)
+    return fail(AA_ERR_SHAPE, std::string(fn) + ": up and down plans use different laws or q");
+  if (up->type_kind != down->type_kind || up->period != down->period)
+    return fail(AA_ERR_SHAPE, std::string(fn) + ": up and down plans use different type maps");
+  if (up->d_out != down->d_in || up->d_in != down->d_out)
+    return fail(AA_ERR_SHAPE, std::string(fn) + ": up must map D -> F and down F -> D");
+  if (down->in_dtype != up->out_dtype)
+    return fail(AA_ERR_SHAPE, std::string(fn) + ": down's input dtype must be up's output dtype (H)");
+  aa_status_t st;
+  if ((st = check_rows(*up, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if (M == 0) return AA_OK;
+  if ((st = check_ptr(X, "X", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Wg_packed, "Wg_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Wu_packed, "Wu_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Wd_packed, "Wd_packed", fn)) != AA_OK) return st;
+  if ((st = check_ptr(Y, "Y", fn)) != AA_OK) return st;
+  const size_t yb = size_t(M * down->d_out) * elem_size(down->out_dtype);
+  const size_t xb = size_t(M * up->d_in) * elem_size(up->in_dtype);
+  if (overlaps(Y, yb, X, xb)) return fail(AA_ERR_INVALID_ARG, std::string(fn) + ": X and Y must not overlap");
+  return AA_OK;
+}
+
+// The two launches of a SwiGLU FFN, after the checks.
+aa_status_t run_swiglu(const aa_plan_s& up, const aa_plan_s& down, const void* X, const void* Wg_packed,
+                       const void* Wu_packed, const void* Wd_packed, void* H, void* Y, int64_t M,
+                       int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  aa_status_t st;
+  // A few tokens (at most one per row type on average: generation decodes one
+  // new position per call) take the matrix-vector kernels, which read each
+  // token's 2q - 1 blocks once; the leaf GEMMs would pad them to full tiles.
+  // The down projection's decode falls back to the leaf kernels itself when
+  // its blocks are too wide for the matrix-vector kernels.
+  if (M <= up.q && up.type_kind != AA_TYPES_BLOCK_ROWS && aa::decode_swiglu_ok(up)) {
+    if ((st = aa::launch_decode(up, X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, stream)) != AA_OK)
+      return st;
+    return aa::launch_decode(down, H, Wd_packed, nullptr, Y, M, pos_offset, row_types, stream);
+  }
+  aa::LeafCall gate_up{X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, true};
+  if ((st = aa::launch_leaf_gemm(up, gate_up, stream)) != AA_OK) return st;
+  aa::LeafCall proj_down{H, Wd_packed, nullptr, Y, M, pos_offset, row_types, false};
+  return aa::launch_leaf_gemm(down, proj_down, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,41 +157,17 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
                               int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
   aa::clear_error();
   static const char* fn = "aa_swiglu_ffn_fwd";
-  if (!up || !down) return fail(AA_ERR_INVALID_ARG, "aa_swiglu_ffn_fwd: plan is NULL");
-  if (up->law != down->law || up->q != down->q)
-    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: up and down plans use different laws or q");
-  if (up->type_kind != down->type_kind || up->period != down->period)
-    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: up and down plans use different type maps");
-  if (up->d_out != down->d_in || up->d_in != down->d_out)
-    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: up must map D -> F and down F -> D");
-  if (down->in_dtype != up->out_dtype)
-    return fail(AA_ERR_SHAPE, "aa_swiglu_ffn_fwd: down's input dtype must be up's output dtype (H)");
   aa_status_t st;
-  if ((st = check_rows(*up, M, pos_offset, row_types, fn)) != AA_OK) return st;
+  if ((st = check_swiglu(up, down, X, Wg_packed, Wu_packed, Wd_packed, Y, M, pos_offset, row_types, fn)) != AA_OK)
+    return st;
   if (M == 0) return AA_OK;
-  if ((st = check_ptr(X, "X", fn)) != AA_OK) return st;
-  if ((st = check_ptr(Wg_packed, "Wg_packed", fn)) != AA_OK) return st;
-  if ((st = check_ptr(Wu_packed, "Wu_packed", fn)) != AA_OK) return st;
-  if ((st = check_ptr(Wd_packed, "Wd_packed", fn)) != AA_OK) return st;
   if ((st = check_ptr(H, "H", fn)) != AA_OK) return st;
-  if ((st = check_ptr(Y, "Y", fn)) != AA_OK) return st;
   const size_t hb = size_t(M * up->d_out) * elem_size(up->out_dtype);
   const size_t yb = size_t(M * down->d_out) * elem_size(down->out_dtype);
   const size_t xb = size_t(M * up->d_in) * elem_size(up->in_dtype);
-  if (overlaps(H, hb, Y, yb) || overlaps(H, hb, X, xb) || overlaps(Y, yb, X, xb))
+  if (overlaps(H, hb, Y, yb) || overlaps(H, hb, X, xb))
     return fail(AA_ERR_INVALID_ARG, "aa_swiglu_ffn_fwd: X, H and Y must not overlap");
-  // A few tokens (at most one per row type on average: generation decodes one
-  // new position per call) take the matrix-vector kernels, which read each
-  // token's 2q - 1 blocks once; the leaf GEMMs would pad them to full tiles.
-  if (M <= up->q && up->type_kind != AA_TYPES_BLOCK_ROWS && aa::decode_swiglu_ok(*up)) {
-    if ((st = aa::launch_decode(*up, X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, stream)) != AA_OK)
-      return st;
-    return aa::launch_decode(*down, H, Wd_packed, nullptr, Y, M, pos_offset, row_types, stream);
-  }
-  aa::LeafCall gate_up{X, Wg_packed, Wu_packed, H, M, pos_offset, row_types, true};
-  if ((st = aa::launch_leaf_gemm(*up, gate_up, stream)) != AA_OK) return st;
-  aa::LeafCall proj_down{H, Wd_packed, nullptr, Y, M, pos_offset, row_types, false};
-  return aa::launch_leaf_gemm(*down, proj_down, stream);
+  return run_swiglu(*up, *down, X, Wg_packed, Wu_packed, Wd_packed, H, Y, M, pos_offset, row_types, stream);
 }
 
 aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_bytes, size_t* weight_bytes) {

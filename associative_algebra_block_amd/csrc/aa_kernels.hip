@@ -2212,6 +2212,7 @@ int device_cu_count() {
 
 // ------------------------------------------------------------ launchers ---
 
+
 aa_status_t after_launch(hipStream_t stream, const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(AA_ERR_HIP, std::string(what) + ": launch failed: " + hipGetErrorString(e));
@@ -2542,7 +2543,13 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, c
   // (Qwen3-8B shape, by position: 32.7 against 29.9 us at 64 tokens, 441
   // against 32.7 us at 1024; explicit types: 154 against 77 us at 512, the
   // general kernel's ballot scan of the types costing more per token).
-  if (plan.law == AA_LAW_DIGRAPH || (W1 == nullptr && n >= (row_types ? 8 : 2) * int64_t(plan.q))) {
+  //
+  // Blocks wider than the matrix-vector kernels take (input blocks above 512
+  // features; above 256 for the SwiGLU gate/up pair) also run as the
+  // projection of the new rows, so that every plan the leaf kernels accept
+  // decodes, whatever the token count.
+  const bool too_wide = plan.b_in > 512 || (W1 != nullptr && !decode_swiglu_ok(plan));
+  if (plan.law == AA_LAW_DIGRAPH || too_wide || (W1 == nullptr && n >= (row_types ? 8 : 2) * int64_t(plan.q))) {
     aa_plan_s dp = plan;
     dp.type_kind = row_types ? AA_TYPES_EXPLICIT : AA_TYPES_POS_MOD;
     const LeafCall c{x, W, W1, y, n, pos_offset, row_types, W1 != nullptr};

@@ -105,6 +105,24 @@ def test_gradients_integer_exact(law, q, M, d_in, d_out, kind):
     assert np.array_equal(dW, dW_ref), np.max(np.abs(dW - dW_ref))
 
 
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_grad_input_widest_blocks(out_dt):
+    """dX at the widest input blocks it takes (b_in = 512; dW stops at 384)."""
+    q, M, d_in, d_out = 8, 1000, 4096, 1024
+    say("bwd dX b_in 512", q, M, d_in, d_out, out_dt)
+    plan = aa.aa_plan_create("Qq", q, d_in, d_out, "pos_mod", 0, "bf16", out_dt)
+    W = inp.gaussian((d_in, d_out), 402, d_in ** -0.5, torch.bfloat16, DEV)
+    dY = inp.gaussian((M, d_out), 403, 1.0, torch.bfloat16, DEV)
+    Wp = aa.pack(plan, W)
+    dX = torch.full((M, d_in), float("nan"), dtype=TD[out_dt], device=DEV)
+    nd, _ = aa.aa_project_bwd_workspace(plan, M)
+    wsd = torch.empty(max(nd, 1), dtype=torch.uint8, device=DEV)
+    aa.aa_project_bwd_data(plan, dY, Wp, dX, None, 5, None, wsd if nd else None, nd)
+    torch.cuda.synchronize()
+    ref = oracle.project_grad_input(host(dY), host(W), "Qq", q, oracle.types_pos_mod(M, q, 5))
+    assert_parity(host(dX), ref, out_dt == "bf16", "dX b_in 512")
+
+
 def test_gradients_qwen3_8b_shape():
     """M = 2048, 4096 -> 12288, Q_32, bf16 outputs: the benchmark's launch configuration."""
     say("bwd qwen3-8b")

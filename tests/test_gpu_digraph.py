@@ -11,7 +11,7 @@ import torch
 import aa_inputs as inp
 import associative_algebra_block_amd as aa
 import oracle
-from tests._gpu_util import MAX_RMS, REL_FRO, assert_parity, host, metrics, say
+from tests._gpu_util import REL_FRO, assert_parity, host, metrics, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -95,10 +95,10 @@ def test_digraph_integer_exact():
 def test_digraph_swiglu_matches_oracle(M):
     """SwiGLU FFN with both plans on one digraph (M = 5: the few-token path).
 
-    H is stored in bf16 (the reading of the pages' FFN the library follows),
-    and a sparse graph leaves many output groups zero, which lowers rms(Y);
-    so the max-error bound on Y adds the error that storing the exact H in
-    bf16 alone causes, computed by the oracle (as the bf16 output floor is)."""
+    H is the bf16 output of the gate/up launch and is checked as such against
+    the oracle's H.  Y is the down projection of that stored H, so it is
+    compared, at the plain bounds, with the oracle's projection of the GPU's
+    own bf16 H."""
     q, D, F = 16, 2048, 768
     say("digraph swiglu", q, M, D, F)
     edges = inp.random_edges(q, 0.3, 17)
@@ -115,12 +115,12 @@ def test_digraph_swiglu_matches_oracle(M):
     g, types = oracle.Digraph(q, edges), oracle.types_pos_mod(M, q, 4)
     H_ref, Y_ref = oracle.swiglu_ffn(host(X), host(Wg), host(Wu), host(Wd), g, q, types)
     assert_parity(host(H), H_ref, True, "digraph H")
-    Hb = torch.from_numpy(H_ref).to(torch.bfloat16).double().numpy()
-    _, floor = metrics(oracle.project(Hb, host(Wd), g, q, types), Y_ref)
+    assert_parity(host(Y), oracle.project(host(H), host(Wd), g, q, types), False, "digraph Y (from the GPU's H)")
+    # and the end to end error against the exact FFN, reported only: storing
+    # H in bf16 is part of the method's reading, not a kernel error
     rel_fro, max_rms = metrics(host(Y), Y_ref)
-    say(f"digraph Y: rel_fro={rel_fro:.3e} max/rms={max_rms:.3e} bf16-H floor={floor:.3e}")
+    say(f"digraph Y vs exact FFN: rel_fro={rel_fro:.3e} max/rms={max_rms:.3e}")
     assert rel_fro <= REL_FRO, rel_fro
-    assert max_rms <= MAX_RMS + floor, (max_rms, floor)
 
 
 def test_digraph_decode_matches_oracle():

@@ -13,7 +13,7 @@ import torch
 import aa_inputs as inp
 import associative_algebra_block_amd as aa
 import oracle
-from tests._gpu_util import LazyRows, assert_parity, host, say
+from tests._gpu_util import MAX_RMS, REL_FRO, LazyRows, assert_parity, bf16_floor, host, metrics, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -428,7 +428,9 @@ def test_row_locality():
     ("Qq", 4, 320, 64, 1, "bf16"), ("Qq", 1, 64, 48, 1, "bf16"), ("Qq", 32, 12288, 4096, 1, "bf16"),
     ("Q2xQ2", 4, 320, 512, 3, "bf16"), ("Q2xQ2", 4, 1536, 768, 2, "f32"),
     # many tokens: from 2q (by position) and 8q (explicit types) on, the leaf kernels
-    ("Qq", 8, 1024, 1536, 64, "bf16"), ("Qq", 32, 4096, 12288, 300, "bf16"), ("Q2xQ2", 4, 768, 1536, 40, "bf16")])
+    ("Qq", 8, 1024, 1536, 64, "bf16"), ("Qq", 32, 4096, 12288, 300, "bf16"), ("Q2xQ2", 4, 768, 1536, 40, "bf16"),
+    # input blocks wider than the matrix-vector kernels take (b_in = 768): the leaf kernels at any count
+    ("Qq", 16, 12288, 4096, 1, "bf16"), ("Qq", 16, 12288, 4096, 3, "f32")])
 def test_decode_matches_oracle_and_prefill(law, q, d_in, d_out, n, dt):
     say("decode", law, q, d_in, d_out, n, dt)
     plan, X, W = _make(law, q, max(64, n), d_in, d_out, dt, "f32", seed=81)
@@ -491,6 +493,10 @@ def test_swiglu_parity(name, law, q, M, D, F, period, out_dt):
     ("pilot Q2xQ2 one token", "Q2xQ2", 4, 1, 768, 1536, 1536, 1535, "f32"),
     ("pilot Q2xQ2 three tokens", "Q2xQ2", 4, 3, 768, 1536, 1536, 2, "bf16"),
     ("Qwen3-30B-A3B expert, five tokens", "Qq", 16, 5, 2048, 768, 0, 13, "bf16"),
+    # the Qwen3-8B widths at q = 16: gate/up blocks 256 wide (matrix-vector),
+    # down blocks 768 wide (leaf kernels)
+    ("Qwen3-8B widths at q = 16, one token", "Qq", 16, 1, 4096, 12288, 0, 9, "bf16"),
+    ("Qwen3-8B widths at q = 16, one token per type", "Qq", 16, 16, 4096, 12288, 0, 3, "f32"),
 ])
 def test_swiglu_few_tokens_matches_oracle(name, law, q, M, D, F, period, pos_offset, out_dt):
     """At most q tokens: the FFN runs as a fused gate/up matrix-vector kernel
@@ -554,29 +560,56 @@ def test_swiglu_single_token_in_a_graph_replay():
         assert torch.equal(Hg, He) and torch.equal(Yg, Ye), f"replay {r}"
 
 
-# ------------------------------------------- full square product (sampled) ---
+# ------------------------------------------------- full square product ---
 
-def test_square_product_full_size_sampled():
-    """n = 32768, b = 128, q = 256, every block-row computed on the GPU in the
-    benchmark's launch configuration; the oracle checks sampled block-rows in
-    full and a sample of single rows elsewhere."""
+def test_square_product_full_size():
+    """n = 32768, b = 128, q = 256: the whole X * W on the GPU in the
+    benchmark's launch configuration, with fp32 and with bf16 output.
+
+    fp32 output, at the plain bounds: three whole block-rows (first, middle,
+    last) and four seeded rows of every other block-row against the oracle,
+    which reads only the weight blocks the row's type names.  bf16 output: the
+    same rows against the oracle (bf16 output floor), and, over all 2^30
+    outputs, equality with the fp32 result rounded to bf16 (both outputs come
+    from the same summation; only the final conversion differs)."""
     n, q = 32768, 256
+    b = n // q
     say("square", n, q)
-    plan = aa.aa_plan_create("Qq", q, n, n, "block_rows", 0, "bf16", "bf16")
+    planf = aa.aa_plan_create("Qq", q, n, n, "block_rows", 0, "bf16", "f32")
+    planb = aa.aa_plan_create("Qq", q, n, n, "block_rows", 0, "bf16", "bf16")
     X = inp.gaussian((n, n), inp.seed_for(inp.ROLE_X, 5), 1.0, torch.bfloat16, DEV)
     W = inp.gaussian((n, n), inp.seed_for(inp.ROLE_W, 5), n ** -0.5, torch.bfloat16, DEV)
-    Wp = aa.pack(plan, W)
-    Y = torch.empty(n, n, dtype=torch.bfloat16, device=DEV)
-    aa.aa_project_fwd(plan, X, Wp, Y)
+    Wp = aa.pack(planf, W)
+    Yf = torch.empty(n, n, dtype=torch.float32, device=DEV)
+    aa.aa_project_fwd(planf, X, Wp, Yf)
+    Yb = torch.empty(n, n, dtype=torch.bfloat16, device=DEV)
+    aa.aa_project_fwd(planb, X, Wp, Yb)
     torch.cuda.synchronize()
-    Wl = LazyRows(W)
-    b = n // q
-    for i in (0, 137, 255):
-        rows = slice(i * b, (i + 1) * b)
-        ref = oracle.project_block_row(host(X[rows]), Wl, "Qq", q, i)
-        assert_parity(host(Y[rows]), ref, True, f"square block-row {i}")
+    del Wp
+    mism = 0
+    for r0 in range(0, n, 4096):
+        mism += int((Yf[r0:r0 + 4096].to(torch.bfloat16).view(torch.int16) !=
+                     Yb[r0:r0 + 4096].view(torch.int16)).sum())
+    say(f"square: bf16 outputs differing from bf16(fp32 outputs): {mism}")
+    assert mism == 0
+    Wl = LazyRows(W.cpu())
     rng = np.random.default_rng(5)
-    for r in rng.integers(0, n, 6):
-        i = int(r) // b
-        ref = oracle.project_block_row(host(X[int(r):int(r) + 1]), Wl, "Qq", q, i)
-        assert_parity(host(Y[int(r):int(r) + 1]), ref, True, f"square row {int(r)}")
+    worst_f = worst_b = 0.0
+    for i in range(q):
+        if i in (0, 137, 255):
+            rows = np.arange(i * b, (i + 1) * b)
+        else:
+            rows = i * b + np.sort(rng.choice(b, 4, replace=False))
+        idx = torch.from_numpy(rows).to(DEV)
+        ref = oracle.project_block_row(host(X[idx]), Wl, "Qq", q, i)
+        got_f, got_b = host(Yf[idx]), host(Yb[idx])
+        if rows.size == b:
+            assert_parity(got_f, ref, False, f"square block-row {i} (whole, fp32)")
+            assert_parity(got_b, ref, True, f"square block-row {i} (whole, bf16)")
+        rel_f, max_f = metrics(got_f, ref)
+        rel_b, max_b = metrics(got_b, ref)
+        floor = bf16_floor(ref)
+        assert rel_f <= REL_FRO and max_f <= MAX_RMS, (i, rel_f, max_f)
+        assert rel_b <= REL_FRO and max_b <= MAX_RMS + floor, (i, rel_b, max_b, floor)
+        worst_f, worst_b = max(worst_f, max_f), max(worst_b, max_b)
+    say(f"square: 256 block-rows checked; worst max/rms fp32 {worst_f:.3e}, bf16 {worst_b:.3e}")
