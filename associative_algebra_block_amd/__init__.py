@@ -19,7 +19,8 @@ __all__ = [
     "AA_LAW_QQ", "AA_LAW_Q2XQ2", "AA_LAW_DIGRAPH", "AA_TYPES_POS_MOD", "AA_TYPES_BLOCK_ROWS", "AA_TYPES_EXPLICIT",
     "AA_BF16", "AA_F32", "AA_OK", "AA_ERR_INVALID_ARG", "AA_ERR_SHAPE", "AA_ERR_UNSUPPORTED",
     "AA_ERR_HIP", "AAError", "Plan", "lib_path", "load",
-    "aa_plan_create", "aa_plan_create_digraph", "aa_plan_destroy", "aa_plan_info", "aa_pack_weights", "aa_unpack_weights",
+    "aa_plan_create", "aa_plan_create_digraph", "aa_plan_destroy", "aa_plan_info", "aa_packed_layout_version",
+    "aa_pack_weights", "aa_unpack_weights",
     "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_decode_gemv", "aa_project_bwd_workspace",
     "aa_project_bwd_data", "aa_project_bwd_weight", "aa_set_kernel_events", "aa_status_string", "aa_last_error",
 ]
@@ -49,6 +50,7 @@ _SIGNATURES = {
                                               ctypes.c_int, _c_i64, ctypes.c_int, ctypes.c_int]),
     "aa_plan_destroy": (ctypes.c_int, [_c_p]),
     "aa_plan_info": (ctypes.c_int, [_c_p, ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64), ctypes.POINTER(_c_i64)]),
+    "aa_packed_layout_version": (ctypes.c_int, [_c_p, ctypes.POINTER(_c_i32)]),
     "aa_pack_weights": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     "aa_unpack_weights": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     "aa_project_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
@@ -205,6 +207,12 @@ def aa_plan_info(plan: Plan):
     a, b, c = _c_i64(), _c_i64(), _c_i64()
     _check(load().aa_plan_info(plan.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "aa_plan_info")
     return a.value, b.value, c.value
+
+
+def aa_packed_layout_version(plan: Plan) -> int:
+    v = _c_i32()
+    _check(load().aa_packed_layout_version(plan.handle, ctypes.byref(v)), "aa_packed_layout_version")
+    return int(v.value)
 
 
 def aa_pack_weights(plan: Plan, W_rowmajor, W_packed, stream=None):

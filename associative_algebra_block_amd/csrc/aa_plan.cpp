@@ -12,6 +12,7 @@
 
 #include <new>
 #include <string>
+#include <type_traits>
 
 #include "aa_internal.h"
 
@@ -66,10 +67,25 @@ int leaf_groups(aa_law_t law, int q, int i, int k, int* groups, uint64_t adj_row
 
 using aa::fail;
 
+namespace {
+
+// The integer a C caller passed for an enum argument.  A C caller may pass
+// any int; reading a value outside the enumerators through the enum type is
+// undefined in C++, so the checks look at its representation instead.
+template <typename E>
+int32_t raw(const E& e) {
+  static_assert(std::is_enum<E>::value && sizeof(E) == sizeof(int32_t), "enum arguments are 32-bit");
+  int32_t v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* aa_status_string(aa_status_t s) {
-  switch (s) {
+  switch (raw(s)) {
     case AA_OK: return "AA_OK";
     case AA_ERR_INVALID_ARG: return "AA_ERR_INVALID_ARG";
     case AA_ERR_SHAPE: return "AA_ERR_SHAPE";
@@ -94,11 +110,14 @@ namespace {
 // Validation and construction shared by both creation calls; adjacency is
 // non-null exactly for AA_LAW_DIGRAPH.
 aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjacency, int64_t d_in, int64_t d_out,
-                   aa_type_kind_t type_kind, int64_t period, aa_dtype_t in_dtype, aa_dtype_t out_dtype) {
-  if (type_kind != AA_TYPES_POS_MOD && type_kind != AA_TYPES_BLOCK_ROWS && type_kind != AA_TYPES_EXPLICIT)
+                   int32_t kind_raw, int64_t period, int32_t in_raw, int32_t out_raw) {
+  if (kind_raw != AA_TYPES_POS_MOD && kind_raw != AA_TYPES_BLOCK_ROWS && kind_raw != AA_TYPES_EXPLICIT)
     return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown type map");
-  if ((in_dtype != AA_BF16 && in_dtype != AA_F32) || (out_dtype != AA_BF16 && out_dtype != AA_F32))
+  if ((in_raw != AA_BF16 && in_raw != AA_F32) || (out_raw != AA_BF16 && out_raw != AA_F32))
     return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown dtype");
+  // valid enumerators from here on
+  const aa_type_kind_t type_kind = static_cast<aa_type_kind_t>(kind_raw);
+  const aa_dtype_t in_dtype = static_cast<aa_dtype_t>(in_raw), out_dtype = static_cast<aa_dtype_t>(out_raw);
   if (q < 1) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: q must be >= 1");
   if (q > 65536) return fail(AA_ERR_UNSUPPORTED, "aa_plan_create: q above 65536");
   if (law == AA_LAW_Q2XQ2 && q != 4)
@@ -144,6 +163,7 @@ aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjac
     for (int k = 0; k < q; ++k) n += aa::leaf_groups(law, q, i, k, groups, i < 64 ? p->adj[i] : 0);
   p->n_block_products = n;
   p->n_leaves = int64_t(q) * q;
+  p->layout_version = 1;
   p->tile_override = -1;
   p->wg_per_cu = 0;
   p->persist_pol = -1;
@@ -177,11 +197,13 @@ aa_status_t aa_plan_create(aa_plan_t* out, aa_law_t law, int32_t q, int64_t d_in
   aa::clear_error();
   if (!out) return fail(AA_ERR_INVALID_ARG, "aa_plan_create: out is NULL");
   *out = nullptr;
-  if (law == AA_LAW_DIGRAPH)
+  const int32_t law_raw = raw(law);
+  if (law_raw == AA_LAW_DIGRAPH)
     return fail(AA_ERR_INVALID_ARG, "aa_plan_create: digraph plans are made by aa_plan_create_digraph");
-  if (law != AA_LAW_QQ && law != AA_LAW_Q2XQ2)
+  if (law_raw != AA_LAW_QQ && law_raw != AA_LAW_Q2XQ2)
     return fail(AA_ERR_INVALID_ARG, "aa_plan_create: unknown law");
-  return create(out, law, q, nullptr, d_in, d_out, type_kind, period, in_dtype, out_dtype);
+  return create(out, static_cast<aa_law_t>(law_raw), q, nullptr, d_in, d_out, raw(type_kind), period, raw(in_dtype),
+                raw(out_dtype));
 }
 
 aa_status_t aa_plan_create_digraph(aa_plan_t* out, int32_t q, const uint8_t* adjacency, int64_t d_in,
@@ -192,12 +214,21 @@ aa_status_t aa_plan_create_digraph(aa_plan_t* out, int32_t q, const uint8_t* adj
   *out = nullptr;
   if (!adjacency) return fail(AA_ERR_INVALID_ARG, "aa_plan_create_digraph: adjacency is NULL");
   if (q > 64) return fail(AA_ERR_UNSUPPORTED, "aa_plan_create_digraph: q above 64");
-  return create(out, AA_LAW_DIGRAPH, q, adjacency, d_in, d_out, type_kind, period, in_dtype, out_dtype);
+  return create(out, AA_LAW_DIGRAPH, q, adjacency, d_in, d_out, raw(type_kind), period, raw(in_dtype),
+                raw(out_dtype));
 }
 
 aa_status_t aa_plan_destroy(aa_plan_t plan) {
   aa::clear_error();
   delete plan;
+  return AA_OK;
+}
+
+aa_status_t aa_packed_layout_version(aa_plan_t plan, int32_t* version) {
+  aa::clear_error();
+  if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_packed_layout_version: plan is NULL");
+  if (!version) return fail(AA_ERR_INVALID_ARG, "aa_packed_layout_version: version is NULL");
+  *version = plan->layout_version;
   return AA_OK;
 }
 

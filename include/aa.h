@@ -130,6 +130,13 @@ aa_status_t aa_plan_destroy(aa_plan_t plan);
 aa_status_t aa_plan_info(aa_plan_t plan, int64_t* n_block_products, int64_t* n_leaves,
                          int64_t* packed_elems);
 
+/* The version of the packed weight layout a plan's calls read and write (the
+ * format a caller stores packed weights in; see aa_pack_weights).  Every plan
+ * of this library uses version 1.  Packed weights written under one version
+ * are only valid for plans that report the same version and the same law, q,
+ * d_in, d_out and in_dtype. */
+aa_status_t aa_packed_layout_version(aa_plan_t plan, int32_t* version);
+
 /* Rearrange a row-major d_in x d_out weight into the block-packed layout the
  * compute calls read, and back.  The packed weight has exactly d_in * d_out
  * elements of the plan's in_dtype; the two calls are inverse permutations

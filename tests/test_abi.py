@@ -53,6 +53,13 @@ def test_plan_counts(lib, law, q, n):
     aa.aa_plan_destroy(p)
 
 
+def test_packed_layout_version(lib):
+    for law, q in [("Qq", 32), ("Q2xQ2", 4), ("Qq", 1)]:
+        assert aa.aa_packed_layout_version(aa.aa_plan_create(law, q, 16 * q, 32 * q)) == 1
+    assert aa.aa_packed_layout_version(aa.aa_plan_create_digraph(3, [(0, 1)], 48, 48)) == 1
+    assert _raw(lib, "aa_packed_layout_version", None, None) == aa.AA_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("args,status", [
     (("Qq", 0, 64, 64), aa.AA_ERR_INVALID_ARG),
     (("Q2xQ2", 2, 64, 64), aa.AA_ERR_INVALID_ARG),
