@@ -13,6 +13,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -29,7 +30,7 @@ ARCH = "gfx950"
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function",
 ]
 
 
@@ -44,13 +45,16 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libaa.so.  Returns the library path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="aa_build_") as tmp:
-        objs = []
+        objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *HIP_FLAGS, *lang, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
-            _run(cmd, verbose)
+            cmds.append([cc, *HIP_FLAGS, *lang, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
             objs.append(obj)
+        # the translation units are independent: compile them side by side
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
         vscript = os.path.join(tmp, "aa.map")
         with open(vscript, "w") as f:
             f.write("{ global: aa_*; local: *; };\n")

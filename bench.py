@@ -245,13 +245,30 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
 
 
 def cpu_threads():
+    """Host threads the oracle's BLAS may use: the cores this process may run
+    on (its affinity set), capped by OMP_NUM_THREADS when that is set (a
+    shared host's share of cores)."""
+    n = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        n = max((d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"), default=1)
-        return int(n)
-    except Exception:
-        return os.cpu_count() or 1
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
+
+
+def timed_oracle(fn):
+    """Run fn() with the BLAS pool pinned to cpu_threads(); returns (fn's
+    result, the BLAS thread count actually in effect, the affinity size)."""
+    n = cpu_threads()
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        with threadpool_limits(limits=n, user_api="blas"):
+            used = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"),
+                       default=1)
+            out = fn()
+    except ImportError:
+        used, out = n, fn()
+    return out, int(used), len(os.sched_getaffinity(0))
 
 
 # ---------------------------------------------------- Qwen3-8B-shaped step ---
@@ -632,17 +649,20 @@ def cpu_baseline_backward(args, torch, inp, st, shapes, q, M):
             oracle.project_grad_weight(X[rows], dY[rows], "Qq", q, types[rows])
         return len(rows)
 
-    t0 = time.perf_counter()
-    sample(1)
-    t_one = time.perf_counter() - t0
-    s = int(max(1, min(q, args.cpu_seconds / max(t_one, 1e-6))))
-    t0 = time.perf_counter()
-    n = sample(s)
-    t = time.perf_counter() - t0
+    def run():
+        t0 = time.perf_counter()
+        sample(1)
+        t_one = time.perf_counter() - t0
+        s = int(max(1, min(q, args.cpu_seconds / max(t_one, 1e-6))))
+        t0 = time.perf_counter()
+        n = sample(s)
+        return s, n, time.perf_counter() - t0
+
+    (s, n, t), used, aff = timed_oracle(run)
     dense = sum(2 * 2.0 * n * di * do for _, di, do in shapes)
-    return {"value": round(dense / t / 1e12, 5), "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+    return {"value": round(dense / t / 1e12, 5), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
             "sample": f"dX and dW of rows of row types 0..{s - 1} ({n} of {M} tokens) for every projection, "
-                      f"fp64 numpy, {t:.2f} s", "seconds": round(t, 3)}
+                      f"fp64 numpy, {t:.2f} s", "seconds": round(t, 3), "affinity_cores": aff}
 
 
 def decode_single_token(torch, aa, plan, sets, pos0, n_tok, D, F, q, dense_set=None, reps=20):
@@ -775,34 +795,41 @@ def cpu_baseline_qwen3(args, torch, inp, st, wl):
     gen = lambda role, shape, fan: inp.gaussian(shape, inp.seed_for(role, 3), fan ** -0.5, torch.bfloat16,
                                                 "cuda").float().cpu().numpy()
     W, Wu, Wdn = gen(inp.ROLE_W, (D, F), D), gen(inp.ROLE_WU, (D, F), D), gen(inp.ROLE_WD, (F, D), F)
+    # the step's gate weight is its own tensor (seed offset 50, as in the step)
+    Wg = inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, 3) + 50, D ** -0.5, torch.bfloat16,
+                      "cuda").float().cpu().numpy()
     types = oracle.types_pos_mod(M, q)
 
     def sample(s):
         rows = np.nonzero(types < s)[0]
         oracle.project(X[rows], W, "Qq", q, types[rows])
-        oracle.swiglu_ffn(X[rows], W, Wu, Wdn, "Qq", q, types[rows])
+        oracle.swiglu_ffn(X[rows], Wg, Wu, Wdn, "Qq", q, types[rows])
         oracle.decode(X[:s], W, "Qq", q, np.arange(s))
         return len(rows)
 
-    t0 = time.perf_counter()
-    sample(1)
-    t_one = time.perf_counter() - t0
-    s = int(max(1, min(q, args.cpu_seconds / max(t_one, 1e-6))))
-    reps = 1
-    t0 = time.perf_counter()
-    n = sample(s)
-    t = time.perf_counter() - t0
-    if s == q and t < args.cpu_seconds / 2:
-        reps = max(1, int(args.cpu_seconds / max(t, 1e-6)))
+    def run():
         t0 = time.perf_counter()
-        for _ in range(reps):
-            sample(s)
-        t = (time.perf_counter() - t0) / reps
+        sample(1)
+        t_one = time.perf_counter() - t0
+        s = int(max(1, min(q, args.cpu_seconds / max(t_one, 1e-6))))
+        reps = 1
+        t0 = time.perf_counter()
+        n = sample(s)
+        t = time.perf_counter() - t0
+        if s == q and t < args.cpu_seconds / 2:
+            reps = max(1, int(args.cpu_seconds / max(t, 1e-6)))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                sample(s)
+            t = (time.perf_counter() - t0) / reps
+        return s, n, t, reps
+
+    (s, n, t, reps), used, aff = timed_oracle(run)
     dense = 2.0 * n * D * F * 4 + 2.0 * s * D * F
-    return {"value": round(dense / t / 1e12, 5), "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
+    return {"value": round(dense / t / 1e12, 5), "unit": "TFLOP/s", "cores": used, "kind": "oracle",
             "sample": f"rows of row types 0..{s - 1} ({n} of {M} tokens) through the projection and the SwiGLU "
                       f"FFN plus {s} decode tokens, fp64 numpy, {t:.2f} s per pass, {reps} pass(es)",
-            "seconds": round(t * reps, 3)}
+            "seconds": round(t * reps, 3), "affinity_cores": aff}
 
 
 # ----------------------------------------------------- other workloads ------
