@@ -21,7 +21,7 @@ __all__ = [
     "AA_ERR_HIP", "AAError", "Plan", "lib_path", "load",
     "aa_plan_create", "aa_plan_create_digraph", "aa_plan_destroy", "aa_plan_info", "aa_packed_layout_version",
     "aa_pack_weights", "aa_unpack_weights",
-    "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_decode_gemv", "aa_project_bwd_workspace",
+    "aa_project_fwd", "aa_swiglu_ffn_fwd", "aa_swiglu_ffn_fwd_noalloc", "aa_decode_gemv", "aa_project_bwd_workspace",
     "aa_project_bwd_data", "aa_project_bwd_weight", "aa_set_kernel_events", "aa_status_string", "aa_last_error",
 ]
 
@@ -56,6 +56,8 @@ _SIGNATURES = {
     "aa_project_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "aa_swiglu_ffn_fwd": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p,
                                          _c_p]),
+    "aa_swiglu_ffn_fwd_noalloc": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64,
+                                                 _c_p, _c_p]),
     "aa_decode_gemv": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "aa_project_bwd_workspace": (ctypes.c_int, [_c_p, _c_i64, ctypes.POINTER(ctypes.c_size_t),
                                                 ctypes.POINTER(ctypes.c_size_t)]),
@@ -254,6 +256,23 @@ def aa_swiglu_ffn_fwd(up: Plan, down: Plan, X, Wg_packed, Wu_packed, Wd_packed, 
         _ptr(Wd_packed, "Wd_packed", down.in_torch_dtype, down.d_in * down.d_out),
         _ptr(H, "H", up.out_torch_dtype, M * up.d_out), _ptr(Y, "Y", down.out_torch_dtype, M * down.d_out),
         M, int(pos_offset), _ptr(row_types, "row_types", torch.int32, M), _stream(stream)), "aa_swiglu_ffn_fwd")
+
+
+def aa_swiglu_ffn_fwd_noalloc(up: Plan, down: Plan, X, Wg_packed, Wu_packed, Wd_packed, Y, M=None, pos_offset=0,
+                              row_types=None, stream=None):
+    """aa_swiglu_ffn_fwd with the hidden activation in the library's static
+    device scratch (no H argument; at most AA_NOALLOC_SCRATCH_BYTES of it)."""
+    M = _rows_of(X, M)
+    nw = up.d_in * up.d_out
+    _check(load().aa_swiglu_ffn_fwd_noalloc(
+        up.handle, down.handle, _ptr(X, "X", up.in_torch_dtype, M * up.d_in),
+        _ptr(Wg_packed, "Wg_packed", up.in_torch_dtype, nw), _ptr(Wu_packed, "Wu_packed", up.in_torch_dtype, nw),
+        _ptr(Wd_packed, "Wd_packed", down.in_torch_dtype, down.d_in * down.d_out),
+        _ptr(Y, "Y", down.out_torch_dtype, M * down.d_out), M, int(pos_offset),
+        _ptr(row_types, "row_types", torch.int32, M), _stream(stream)), "aa_swiglu_ffn_fwd_noalloc")
+
+
+AA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def aa_decode_gemv(plan: Plan, x, W_packed, y, n=None, pos_offset=0, row_types=None, stream=None):

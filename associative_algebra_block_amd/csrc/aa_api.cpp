@@ -170,6 +170,25 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
   return run_swiglu(*up, *down, X, Wg_packed, Wu_packed, Wd_packed, H, Y, M, pos_offset, row_types, stream);
 }
 
+aa_status_t aa_swiglu_ffn_fwd_noalloc(aa_plan_t up, aa_plan_t down, const void* X, const void* Wg_packed,
+                                      const void* Wu_packed, const void* Wd_packed, void* Y, int64_t M,
+                                      int64_t pos_offset, const int32_t* row_types, hipStream_t stream) {
+  aa::clear_error();
+  static const char* fn = "aa_swiglu_ffn_fwd_noalloc";
+  aa_status_t st;
+  if ((st = check_swiglu(up, down, X, Wg_packed, Wu_packed, Wd_packed, Y, M, pos_offset, row_types, fn)) != AA_OK)
+    return st;
+  if (M == 0) return AA_OK;
+  const size_t hb = size_t(M) * size_t(up->d_out) * elem_size(up->out_dtype);
+  if (hb > aa::kNoAllocScratchBytes)
+    return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": the hidden activation (" + std::to_string(hb) +
+                                        " bytes) exceeds the library's static scratch (" +
+                                        std::to_string(aa::kNoAllocScratchBytes) + " bytes)");
+  void* H = nullptr;
+  if ((st = aa::noalloc_scratch(&H)) != AA_OK) return st;
+  return run_swiglu(*up, *down, X, Wg_packed, Wu_packed, Wd_packed, H, Y, M, pos_offset, row_types, stream);
+}
+
 aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_bytes, size_t* weight_bytes) {
   aa::clear_error();
   if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: plan is NULL");

@@ -77,6 +77,12 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
 aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
                               int64_t pos_offset, void* ws, hipStream_t stream);
 
+// Allocation-free SwiGLU: the hidden activation goes to a static device
+// array of this many bytes (one per GPU); noalloc_scratch returns its address
+// on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(AA_NOALLOC_SCRATCH_BYTES);
+aa_status_t noalloc_scratch(void** ptr);
+
 // Dispatch events set by aa_set_kernel_events for the calling thread: the
 // start event is handed out once (to the next launch), the stop event to every
 // launch until the events are set again.

@@ -33,11 +33,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <string>
 #include <type_traits>
 
 #include "aa_device.h"
 #include "aa_internal.h"
+
+// Device memory of the allocation-free SwiGLU call (aa_swiglu_ffn_fwd_noalloc):
+// its hidden activation H lives here instead of in a caller buffer.  Every
+// GPU the library runs on holds its own copy from module load to process
+// exit.  Host code never passes this name to a kernel (on the host it is only
+// a stand-in); it uses the device address noalloc_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[aa::kNoAllocScratchBytes];
 
 namespace aa {
 namespace {
@@ -2211,6 +2219,28 @@ int device_cu_count() {
 }
 
 // ------------------------------------------------------------ launchers ---
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+aa_status_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(AA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(AA_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(AA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return AA_OK;
+}
 
 
 aa_status_t after_launch(hipStream_t stream, const char* what) {

@@ -174,6 +174,24 @@ aa_status_t aa_swiglu_ffn_fwd(aa_plan_t up, aa_plan_t down, const void* X, const
                               int64_t M, int64_t pos_offset, const int32_t* row_types,
                               hipStream_t stream);
 
+/* The SwiGLU feed-forward of aa_swiglu_ffn_fwd without the caller's hidden
+ * buffer, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The call itself allocates nothing: the hidden activation H (M x F of up's
+ * out_dtype) goes to a static device array of AA_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends.
+ * Arguments, checks, kernels and results are those of aa_swiglu_ffn_fwd with
+ * H dropped; a call whose H would exceed the array returns
+ * AA_ERR_UNSUPPORTED and launches nothing.  The first call on a device looks
+ * the array's address up (a HIP call, made once per device; make one call
+ * before capturing a graph).  All calls on one GPU share its array, which
+ * keeps the last call's H: calls that overlap in time on one GPU (several
+ * streams or threads) race and must be serialised by the caller. */
+#define AA_NOALLOC_SCRATCH_BYTES (64u << 20)
+aa_status_t aa_swiglu_ffn_fwd_noalloc(aa_plan_t up, aa_plan_t down, const void* X, const void* Wg_packed,
+                                      const void* Wu_packed, const void* Wd_packed, void* Y, int64_t M,
+                                      int64_t pos_offset, const int32_t* row_types, hipStream_t stream);
+
 /* Decode: n new tokens, each computing only its own table row by a
  * matrix-vector kernel (agihunt.info review: decoding computes only the new
  * position's row, leaves the KV cache as it is, and is a separate

@@ -117,6 +117,11 @@ int main() {
                    AA_ERR_INVALID_ARG);
   EXPECT(aa_swiglu_ffn_fwd(up, down, P(1), P(2), P(3), P(4), P(5), P(6), 2048, 0, nullptr, nullptr), AA_OK);
   EXPECT(aa_swiglu_ffn_fwd(up, down, P(1), P(2), P(3), P(4), P(5), P(6), 3, 7, nullptr, nullptr), AA_OK);
+  EXPECT_NO_LAUNCH(aa_swiglu_ffn_fwd_noalloc(up, down, P(1), P(2), P(3), P(4), P(1), 8, 0, nullptr, nullptr),
+                   AA_ERR_INVALID_ARG);
+  EXPECT_NO_LAUNCH(aa_swiglu_ffn_fwd_noalloc(up, down, P(1), P(2), P(3), P(4), P(6), 4096, 0, nullptr, nullptr),
+                   AA_ERR_UNSUPPORTED);
+  EXPECT(aa_swiglu_ffn_fwd_noalloc(up, down, P(1), P(2), P(3), P(4), P(6), 2048, 0, nullptr, nullptr), AA_OK);
 
   // ---- decode
   EXPECT_NO_LAUNCH(aa_decode_gemv(p, P(1), P(2), P(1), 4, 0, nullptr, nullptr), AA_ERR_INVALID_ARG);

@@ -34,5 +34,9 @@ aa_status_t launch_bwd_weight(const aa_plan_s&, const void*, const void*, void*,
   ++g_launches;
   return AA_OK;
 }
+aa_status_t noalloc_scratch(void** ptr) {
+  *ptr = reinterpret_cast<void*>(uintptr_t(1) << 44);
+  return AA_OK;
+}
 
 }  // namespace aa

@@ -172,6 +172,25 @@ def test_swiglu_plan_mismatch(lib):
         assert r == st, aa.aa_last_error()
 
 
+def test_noalloc_swiglu_validates_before_launch(lib):
+    """The allocation-free SwiGLU call checks like the other one and refuses a
+    hidden activation larger than its static scratch, all before any HIP call."""
+    up = aa.aa_plan_create("Qq", 4, 1024, 4096)
+    down = aa.aa_plan_create("Qq", 4, 4096, 1024, "pos_mod", 0, "bf16", "f32")
+    bad_down = aa.aa_plan_create("Qq", 2, 4096, 1024)
+    g = 0x100000
+    fn = "aa_swiglu_ffn_fwd_noalloc"
+    assert _raw(lib, fn, up.handle, bad_down.handle, g, 2 * g, 3 * g, 4 * g, 6 * g, 8, 0, None, None) == \
+        aa.AA_ERR_SHAPE
+    assert _raw(lib, fn, up.handle, down.handle, None, 2 * g, 3 * g, 4 * g, 6 * g, 8, 0, None, None) == \
+        aa.AA_ERR_INVALID_ARG
+    assert _raw(lib, fn, up.handle, down.handle, g, 2 * g, 3 * g, 4 * g, 6 * g, 0, 0, None, None) == aa.AA_OK
+    too_many = aa.AA_NOALLOC_SCRATCH_BYTES // (2 * 4096) + 1
+    assert _raw(lib, fn, up.handle, down.handle, g, 2 * g, 3 * g, 4 * g, 1 << 40, too_many, 0, None, None) == \
+        aa.AA_ERR_UNSUPPORTED
+    assert "scratch" in aa.aa_last_error()
+
+
 def test_gradients_validate_before_launch(lib):
     import ctypes
     g = 0x1000000
