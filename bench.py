@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="Qwen3-8B step: skip the other configurations (pilot FFN, expert FFN, square product) "
+                         "that the default line also reports")
     ap.add_argument("--no-extras", action="store_true",
                     help="Qwen3-8B step and projections: skip the one-token and back-to-back measurements "
                          "(a kernel trace then holds only the warmup and timed calls)")
@@ -407,6 +410,20 @@ def bench_qwen3(args, torch, inp, aa, dev):
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_qwen3(args, torch, inp, sets[0], wl)
 
+    configs = None
+    if not args.no_configs:
+        # the other configurations of the workload list, each against its own
+        # binding roofline (after the step's own buffers are released)
+        del sets
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        configs = {
+            "pilot_ffn_q2xq2": ffn_part(torch, inp, aa, dev, "pilot_ffn", 60, 5, not args.no_dense),
+            "qwen3_30b_a3b_expert_ffn_q16": ffn_part(torch, inp, aa, dev, "expert_ffn", 100, 10,
+                                                     not args.no_dense),
+            "square_n32768_b128": square_part(torch, inp, aa, dev, 20, 2, not args.no_dense),
+        }
+
     return {
         "metric": "dense-equiv TFLOP/s + % roofline (HBM/MFMA), Qwen3-8B-shape q=32 M=2048 bf16",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -424,6 +441,7 @@ def bench_qwen3(args, torch, inp, aa, dev):
         "ffn_single_token": ffn1,
         "dense": dense,
         "cpu_baseline": cpu,
+        "configs": configs,
         "wall_s_timed": round(wall1 - wall0, 4),
         "kernel_source": kernel_source_hash(),
     }
@@ -834,8 +852,10 @@ def cpu_baseline_qwen3(args, torch, inp, st, wl):
 
 # ----------------------------------------------------- other workloads ------
 
-def bench_square(args, torch, inp, aa, dev):
-    """Fixed-block square product n = 32768, b = 128, q = 256 (block-row typing)."""
+def square_part(torch, inp, aa, dev, steps, warmup, dense=True):
+    """Fixed-block square product n = 32768, b = 128, q = 256 (block-row
+    typing): K launches on one resident input set (6.4 GB, far above the 256
+    MB Infinity Cache), each timed by its own kernel dispatch events."""
     n, q = 32768, 256
     plan = aa.aa_plan_create("Qq", q, n, n, "block_rows", 0, "bf16", "bf16")
     X = inp.gaussian((n, n), inp.seed_for(inp.ROLE_X, 5), 1.0, torch.bfloat16, dev)
@@ -843,74 +863,135 @@ def bench_square(args, torch, inp, aa, dev):
     Wp = aa.pack(plan, W)
     del W
     Y = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         aa.aa_project_fwd(plan, X, Wp, Y)
     torch.cuda.synchronize()
-    K = args.steps
-    kt = KernelTimer(torch, aa, K, 1)
+    kt = KernelTimer(torch, aa, steps, 1)
     a, b = _ev(torch), _ev(torch)
     a.record()
-    for s in range(K):
-        kt.arm(s, 0)
+    for s_ in range(steps):
+        kt.arm(s_, 0)
         aa.aa_project_fwd(plan, X, Wp, Y)
     kt.disarm()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / K
+    ms = a.elapsed_time(b) / steps
     ms_k = kt.ms(0)
-    dense = 2.0 * n ** 3
-    by = proj_bytes(n, n, n)
-    res = {"metric": "dense-equiv TFLOP/s + % roofline, square n=32768 b=128 q=256 bf16",
-           "value": round(dense / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "square_n32768_b128_q256", "n": n, "q": q, "law": "Qq", "type_map": "block rows"},
-           "roofline": roofline(by, ms_k, traffic_for("project_square_n32768")), "kernel_ms": round(ms_k, 5),
-           "kernel_spread": kt.spread(0),
-           "exec_tflops": round(exec_flops(n, n, n, "Qq", q) / ms / 1e9, 2),
-           "kernel_source": kernel_source_hash()}
-    if not args.no_dense:
+    dense_fl = 2.0 * n ** 3
+    part = {"workload": "square_n32768_b128_q256: full X * W, every block-row, block-row typing", "n": n, "q": q,
+            "steps": steps, "ms": round(ms_k, 5), **kt.spread(0), "ms_per_call": round(ms, 5),
+            "dense_equiv_tflops": round(dense_fl / ms_k / 1e9, 2),
+            "exec_tflops": round(exec_flops(n, n, n, "Qq", q) / ms_k / 1e9, 2),
+            "roofline": roofline(proj_bytes(n, n, n), ms_k, traffic_for("project_square_n32768"))}
+    if dense:
+        del Wp
         Wd = inp.gaussian((n, n), 999, n ** -0.5, torch.bfloat16, dev)
         t = dense_timer(torch, lambda: torch.matmul(X, Wd), iters=3, warm=1)
-        res["dense"] = {"kind": "torch.matmul bf16", "ms": round(t, 4), "speedup": round(t / ms, 3)}
-    return res
+        part["dense"] = {"kind": "torch.matmul bf16 (hipBLASLt), same run", "ms": round(t, 4),
+                         "speedup": round(t / ms_k, 3)}
+        del Wd
+    del X, Y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return part
 
 
-def bench_ffn(args, torch, inp, aa, dev, which):
+def bench_square(args, torch, inp, aa, dev):
+    """The square product as its own workload (one JSON line)."""
+    part = square_part(torch, inp, aa, dev, args.steps, args.warmup, not args.no_dense)
+    return {"metric": "dense-equiv TFLOP/s + % roofline, square n=32768 b=128 q=256 bf16",
+            "value": round(2.0 * part["n"] ** 3 / part["ms_per_call"] / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": part["ms_per_call"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "square_n32768_b128_q256", "n": part["n"], "q": part["q"], "law": "Qq",
+                       "type_map": "block rows"},
+            "roofline": part["roofline"], "kernel_ms": part["ms"],
+            "kernel_spread": {k: part[k] for k in ("median_ms", "p10_ms", "p90_ms", "samples")},
+            "exec_tflops": part["exec_tflops"], "dense": part.get("dense"), "kernel_source": kernel_source_hash()}
+
+
+def ffn_part(torch, inp, aa, dev, which, steps, warmup, dense=True):
+    """SwiGLU FFN forward (gate/up launch + down launch) at the pilot
+    (Q2 x Q2, M = 12288, 768 -> 1536 -> 768) or the Qwen3-30B-A3B expert
+    (Q_16, M = 2048, 2048 -> 768 -> 2048) shape.  Input sets of at least 1 GB
+    rotate between calls (flushed cache); each call is timed by its kernels'
+    dispatch events.  The pilot FFN is bound by the bf16 MFMA rate (its
+    executed FLOPs over its bytes exceed the chip's FLOP/byte balance), the
+    expert FFN by HBM."""
     wl = inp.WORKLOADS[2 if which == "pilot_ffn" else 4]
     M, D, F, q, law = wl.M, wl.d_in, wl.d_out, wl.q, wl.law
     period = wl.extra.get("period", 0)
     up = aa.aa_plan_create(law, q, D, F, "pos_mod", period, "bf16", "bf16")
     down = aa.aa_plan_create(law, q, F, D, "pos_mod", period, "bf16", "bf16")
-    X = inp.gaussian((M, D), inp.seed_for(inp.ROLE_X, wl.index), 1.0, torch.bfloat16, dev)
-    Wg = aa.pack(up, inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, wl.index), D ** -0.5, torch.bfloat16, dev))
-    Wu = aa.pack(up, inp.gaussian((D, F), inp.seed_for(inp.ROLE_WU, wl.index), D ** -0.5, torch.bfloat16, dev))
-    Wd = aa.pack(down, inp.gaussian((F, D), inp.seed_for(inp.ROLE_WD, wl.index), F ** -0.5, torch.bfloat16, dev))
-    H = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
-    Y = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
-    f = lambda: aa.aa_swiglu_ffn_fwd(up, down, X, Wg, Wu, Wd, H, Y)
-    ms = dense_timer(torch, f, iters=args.steps, warm=args.warmup)
-    dense = 3 * 2.0 * M * D * F
+    set_bytes = 2 * (M * D + 3 * D * F + M * F + M * D)
+    n_sets = max(2, math.ceil(1.0e9 / set_bytes))
+    sets = []
+    for s_ in range(n_sets):
+        off = 100 * s_
+        g = lambda role, shape, fan: inp.gaussian(shape, inp.seed_for(role, wl.index) + off, fan ** -0.5,
+                                                  torch.bfloat16, dev)
+        sets.append({"X": inp.gaussian((M, D), inp.seed_for(inp.ROLE_X, wl.index) + off, 1.0, torch.bfloat16, dev),
+                     "Wg": aa.pack(up, g(inp.ROLE_W, (D, F), D)), "Wu": aa.pack(up, g(inp.ROLE_WU, (D, F), D)),
+                     "Wd": aa.pack(down, g(inp.ROLE_WD, (F, D), F)),
+                     "H": torch.empty(M, F, dtype=torch.bfloat16, device=dev),
+                     "Y": torch.empty(M, D, dtype=torch.bfloat16, device=dev)})
+    call = lambda st: aa.aa_swiglu_ffn_fwd(up, down, st["X"], st["Wg"], st["Wu"], st["Wd"], st["H"], st["Y"])
+    for w in range(warmup):
+        call(sets[w % n_sets])
+    torch.cuda.synchronize()
+    kt = KernelTimer(torch, aa, steps, 1)
+    a, b = _ev(torch), _ev(torch)
+    a.record()
+    for s_ in range(steps):
+        kt.arm(s_, 0)
+        call(sets[s_ % n_sets])
+    kt.disarm()
+    b.record()
+    torch.cuda.synchronize()
+    ms_call = a.elapsed_time(b) / steps
+    ms = kt.ms(0)
+    dense_fl = 3 * 2.0 * M * D * F
     ex = 3 * exec_flops(M, D, F, law, q)
     by = 2 * (M * D + 2 * D * F + M * F) + 2 * (M * F + F * D + M * D)
-    res = {"metric": f"dense-equiv TFLOP/s, {wl.name} SwiGLU forward bf16",
-           "value": round(dense / ms / 1e9, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": wl.name, "M": M, "D": D, "F": F, "q": q, "law": law},
-           "exec_tflops": round(ex / ms / 1e9, 2),
-           "roofline_hbm": roofline(by, ms),
-           "roofline_mfma": {"bound": "mfma", "achieved": round(ex / ms / 1e9, 2), "peak": BF16_PEAK_TFLOPS,
-                             "unit": "TFLOP/s", "frac": round(ex / ms / 1e9 / BF16_PEAK_TFLOPS, 4)},
-           "kernel_source": kernel_source_hash()}
-    if not args.no_dense:
+    mfma = {"bound": "mfma", "achieved": round(ex / ms / 1e9, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ex / ms / 1e9 / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    hbm = roofline(by, ms)
+    pilot = which == "pilot_ffn"
+    part = {"workload": f"{wl.name}: SwiGLU FFN forward (gate/up + down), {wl.notes}", "M": M, "D": D, "F": F,
+            "q": q, "law": law, "input_sets": n_sets, "steps": steps, "ms": round(ms, 5), **kt.spread(0),
+            "ms_per_call": round(ms_call, 5), "dense_equiv_tflops": round(dense_fl / ms / 1e9, 2),
+            "exec_tflops": round(ex / ms / 1e9, 2),
+            "roofline": mfma if pilot else hbm, "roofline_other": hbm if pilot else mfma}
+    if dense:
+        X = sets[0]["X"]
         Wd1 = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
         Wd2 = inp.gaussian((D, F), 998, D ** -0.5, torch.bfloat16, dev)
         Wd3 = inp.gaussian((F, D), 997, F ** -0.5, torch.bfloat16, dev)
         t = dense_timer(torch, lambda: torch.matmul(
             torch.nn.functional.silu(torch.matmul(X, Wd1)) * torch.matmul(X, Wd2), Wd3))
-        res["dense"] = {"kind": "torch.matmul bf16 x3 + silu*mul", "ms": round(t, 5), "speedup": round(t / ms, 3)}
-    return res
+        part["dense"] = {"kind": "torch.matmul bf16 x3 + silu*mul (hipBLASLt), hot cache, same run",
+                         "ms": round(t, 5), "speedup": round(t / ms, 3)}
+        del Wd1, Wd2, Wd3
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return part
+
+
+def bench_ffn(args, torch, inp, aa, dev, which):
+    """One FFN workload as its own JSON line."""
+    part = ffn_part(torch, inp, aa, dev, which, args.steps, args.warmup, not args.no_dense)
+    wl = inp.WORKLOADS[2 if which == "pilot_ffn" else 4]
+    return {"metric": f"dense-equiv TFLOP/s, {wl.name} SwiGLU forward bf16",
+            "value": round(3 * 2.0 * part["M"] * part["D"] * part["F"] / part["ms_per_call"] / 1e9, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": part["ms_per_call"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": wl.name, "M": part["M"], "D": part["D"], "F": part["F"], "q": part["q"],
+                       "law": part["law"], "input_sets": part["input_sets"]},
+            "kernel_ms": part["ms"], "exec_tflops": part["exec_tflops"], "roofline": part["roofline"],
+            "roofline_other": part["roofline_other"], "dense": part.get("dense"),
+            "kernel_source": kernel_source_hash()}
 
 
 STACK_LAYERS = 12   # decoder blocks of the 110M pilot model
