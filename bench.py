@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
                     choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
-                             "digraph_qwen3_8b", "pilot_decode_stack",
+                             "digraph_qwen3_8b", "pilot_decode_stack", "pilot_generate",
                              "backward_qwen3_8b", "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -107,6 +107,8 @@ def main():
         res = bench_backward(args, torch, inp, aa, dev, args.workload)
     elif args.workload == "pilot_decode_stack":
         res = bench_decode_stack(args, torch, inp, aa, dev)
+    elif args.workload == "pilot_generate":
+        res = bench_generate(args, torch, aa, dev)
     elif args.workload == "square":
         res = bench_square(args, torch, inp, aa, dev)
     else:
@@ -1113,6 +1115,86 @@ def bench_decode_stack(args, torch, inp, aa, dev):
                         "speedup": round(dense_us / us_tok, 3)}
         del dw
     return res
+
+
+def generate_timing(torch, gen, prompt, n_new, reps):
+    """Fixed-length generation: the prompt in one prefill pass, then n_new
+    decode steps, each replayed from one HIP graph of a decode step (device
+    position, so one graph serves every position).  Returns (prefill ms,
+    decode ms per token), medians over reps sequences."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gen.prefill(prompt)
+        for _ in range(3):
+            gen.decode_step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gen.decode_step()
+    pre, dec = [], []
+    for _ in range(reps + 1):
+        a, b, c = _ev(torch), _ev(torch), _ev(torch)
+        a.record()
+        gen.prefill(prompt)
+        b.record()
+        for _ in range(n_new):
+            g.replay()
+        c.record()
+        torch.cuda.synchronize()
+        pre.append(a.elapsed_time(b))
+        dec.append(b.elapsed_time(c) / n_new)
+    med = lambda v: sorted(v[1:])[len(v[1:]) // 2]   # the first sequence warms up
+    del g
+    return med(pre), med(dec)
+
+
+def bench_generate(args, torch, aa, dev):
+    """Fixed-length greedy generation with a decoder stack shaped like the
+    pilot 110M model (12 layers, width 768, 32 heads, context 1536, GPT-2
+    vocabulary, tied LM head, 110,631,168 parameters), once with a dense
+    SwiGLU FFN (torch.matmul) and once with the algebra FFN (Q2 x Q2 through
+    aa_swiglu_ffn_fwd), on the same synthetic weights: a 128-token prompt and
+    256 new tokens per sequence, batch 1 and batch 8.  Attention over the KV
+    cache, LayerNorms, the LM head and argmax run in torch in both models.
+    value = the algebra model's decode tokens/s at batch 1."""
+    from associative_algebra_block_amd.pilot_stack import PilotConfig, PilotGenerator, make_weights
+    cfg = PilotConfig()
+    w = make_weights(cfg, 0, dev)
+    P, G, reps = 128, 256, max(3, min(args.steps, 10))
+    runs = {}
+    for B in (1, 8):
+        g = torch.Generator(device="cpu")
+        g.manual_seed(7 + B)
+        prompt = torch.randint(0, cfg.vocab, (B, P), generator=g).to(dev)
+        for ffn in ("dense", "algebra"):
+            gen = PilotGenerator(cfg, w, ffn, B, dev)
+            pre, dec = generate_timing(torch, gen, prompt, G, reps)
+            runs[(B, ffn)] = {"prefill_ms": round(pre, 4), "decode_ms_per_step": round(dec, 5),
+                              "decode_tokens_per_s": round(B / (dec * 1e-3), 1),
+                              "sequence_tokens_per_s": round(B * G / ((pre + G * dec) * 1e-3), 1)}
+            del gen
+            torch.cuda.synchronize()
+    out = {}
+    for B in (1, 8):
+        d, a = runs[(B, "dense")], runs[(B, "algebra")]
+        out[f"batch{B}"] = {"dense_ffn": d, "algebra_ffn": a,
+                            "decode_speedup": round(a["decode_tokens_per_s"] / d["decode_tokens_per_s"], 4),
+                            "sequence_speedup": round(a["sequence_tokens_per_s"] / d["sequence_tokens_per_s"], 4),
+                            "prefill_speedup": round(d["prefill_ms"] / a["prefill_ms"], 4)}
+    a1 = runs[(1, "algebra")]
+    return {"metric": "fixed-length generation tokens/s, pilot 110M-shaped decoder, algebra FFN vs dense FFN",
+            "value": a1["decode_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": reps,
+            "warmup": 1, "ms_per_step": a1["decode_ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random weights and prompts)",
+            "config": {"workload": "pilot_generate", "layers": cfg.layers, "d": cfg.d, "heads": cfg.heads,
+                       "ffn": cfg.ffn, "ctx": cfg.ctx, "vocab": cfg.vocab, "params": cfg.parameter_count(),
+                       "law": "Q2xQ2", "prompt": P, "new_tokens": G, "batches": [1, 8],
+                       "decode": "one HIP graph per decode step, replayed"},
+            "runs": out,
+            "pages": "generation gain of the pilot models: +6.2 to +7.8% tokens/s (tokenization and sampling "
+                     "included, hardware not stated)",
+            "kernel_source": kernel_source_hash()}
 
 
 if __name__ == "__main__":
