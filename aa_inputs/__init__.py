@@ -106,4 +106,8 @@ WORKLOADS = {
     # the down projection of the Qwen3-8B SwiGLU FFN on its own
     7: Workload(7, "qwen3_8b_down_q32", "Qq", 32, 2048, 12288, 4096, "project", "bf16", "pos_mod",
                 notes="Qwen3-8B FFN down projection, M=2048, q=32 (blocks 384 x 128)"),
+    # the Qwen3-32B row of the pages' projection table; widths from the
+    # model's public configuration (hidden 5120, intermediate 25600)
+    8: Workload(8, "qwen3_32b_q256", "Qq", 256, 32768, 5120, 25600, "project", "bf16", "pos_mod",
+                notes="Qwen3-32B FFN shape, M=32768, q=256 (blocks 20 x 100, packed layout 2)"),
 }

@@ -53,6 +53,8 @@ aa_status_t check_bwd(const aa_plan_s& plan, int64_t M, int64_t pos_offset, cons
   if (plan.in_dtype != AA_BF16) return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": gradients need bf16 operands");
   if (plan.law == AA_LAW_DIGRAPH)
     return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": digraph plans have no gradient kernels");
+  if (plan.layout_version != 1)
+    return fail(AA_ERR_UNSUPPORTED, std::string(fn) + ": blocks that are not multiples of 16 have no gradient kernels");
   return AA_OK;
 }
 
@@ -193,7 +195,7 @@ aa_status_t aa_project_bwd_workspace(aa_plan_t plan, int64_t M, size_t* data_byt
   aa::clear_error();
   if (!plan) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: plan is NULL");
   if (M < 0) return fail(AA_ERR_INVALID_ARG, "aa_project_bwd_workspace: M is negative");
-  const bool none = plan->law == AA_LAW_DIGRAPH;   // no gradient kernels
+  const bool none = plan->law == AA_LAW_DIGRAPH || plan->layout_version != 1;   // no gradient kernels
   if (data_bytes) *data_bytes = none ? 0 : aa::bwd_data_workspace_bytes(*plan, M);
   if (weight_bytes) *weight_bytes = none ? 0 : aa::bwd_weight_workspace_bytes(*plan, M);
   return AA_OK;
@@ -268,6 +270,8 @@ aa_status_t aa_decode_gemv(aa_plan_t plan, const void* x, const void* W_packed, 
     return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: row_types is required unless the plan uses position typing");
   if (row_types && (reinterpret_cast<uintptr_t>(row_types) & 3u))
     return fail(AA_ERR_INVALID_ARG, "aa_decode_gemv: row_types is not 4-byte aligned");
+  if (row_types && plan->layout_version != 1)
+    return fail(AA_ERR_UNSUPPORTED, "aa_decode_gemv: per-token types with blocks that are not multiples of 16");
   if (n == 0) return AA_OK;
   aa_status_t st;
   if ((st = check_ptr(x, "x", fn)) != AA_OK) return st;

@@ -62,6 +62,14 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
 aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool unpack,
                         hipStream_t stream);
 
+// Plans whose block sides are not both multiples of 16 use packed layout 2
+// and the small-block kernel (aa_small.hip).  small_layout_ok is the shape
+// rule plan creation applies to them: bf16 weights, Q_q or a digraph,
+// position or block-row typing, b_in and b_out multiples of 4 and at most 128.
+bool small_layout_ok(aa_law_t law, aa_type_kind_t kind, aa_dtype_t in_dtype, int64_t b_in, int64_t b_out);
+aa_status_t launch_small_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream);
+aa_status_t launch_pack_v2(const aa_plan_s& plan, const void* src, void* dst, bool unpack, hipStream_t stream);
+
 // W1 non-null: SwiGLU gate/up (W gate, W1 up, y = silu(x W) * (x W1)); bf16
 // input and input blocks of at most 256 rows (decode_swiglu_ok).
 aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,

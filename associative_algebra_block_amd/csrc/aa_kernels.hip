@@ -2333,6 +2333,7 @@ bool choose_tile(const aa_plan_s& plan, int64_t M) {
 }
 
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  if (plan.layout_version == 2) return launch_small_gemm(plan, call, stream);
   if (choose_tile(plan, call.M)) {
     LeafParams p{};
     p.X = call.X;
@@ -2545,6 +2546,7 @@ aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStr
 }
 
 aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool unpack, hipStream_t stream) {
+  if (plan.layout_version == 2) return launch_pack_v2(plan, src, dst, unpack, stream);
   const int64_t n_runs = plan.d_in * plan.d_out / 8;
   if (n_runs == 0) return AA_OK;
   const dim3 block{256, 1, 1}, grid{uint32_t((n_runs + 255) / 256), 1, 1};
@@ -2560,7 +2562,7 @@ aa_status_t launch_pack(const aa_plan_s& plan, const void* src, void* dst, bool 
 }
 
 bool decode_swiglu_ok(const aa_plan_s& plan) {
-  return plan.in_dtype == AA_BF16 && plan.b_in <= 256 && plan.law != AA_LAW_DIGRAPH;
+  return plan.in_dtype == AA_BF16 && plan.b_in <= 256 && plan.law != AA_LAW_DIGRAPH && plan.layout_version == 1;
 }
 
 aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,
@@ -2575,10 +2577,10 @@ aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, c
   // general kernel's ballot scan of the types costing more per token).
   //
   // Blocks wider than the matrix-vector kernels take (input blocks above 512
-  // features; above 256 for the SwiGLU gate/up pair) also run as the
-  // projection of the new rows, so that every plan the leaf kernels accept
-  // decodes, whatever the token count.
-  const bool too_wide = plan.b_in > 512 || (W1 != nullptr && !decode_swiglu_ok(plan));
+  // features; above 256 for the SwiGLU gate/up pair), and blocks of packed
+  // layout 2, also run as the projection of the new rows, so that every plan
+  // the leaf kernels accept decodes, whatever the token count.
+  const bool too_wide = plan.b_in > 512 || (W1 != nullptr && !decode_swiglu_ok(plan)) || plan.layout_version != 1;
   if (plan.law == AA_LAW_DIGRAPH || too_wide || (W1 == nullptr && n >= (row_types ? 8 : 2) * int64_t(plan.q))) {
     aa_plan_s dp = plan;
     dp.type_kind = row_types ? AA_TYPES_EXPLICIT : AA_TYPES_POS_MOD;

@@ -63,6 +63,11 @@ int leaf_groups(aa_law_t law, int q, int i, int k, int* groups, uint64_t adj_row
   return n;
 }
 
+bool small_layout_ok(aa_law_t law, aa_type_kind_t kind, aa_dtype_t in_dtype, int64_t b_in, int64_t b_out) {
+  return in_dtype == AA_BF16 && law != AA_LAW_Q2XQ2 && kind != AA_TYPES_EXPLICIT && b_in % 4 == 0 &&
+         b_out % 4 == 0 && b_in <= 128 && b_out <= 128;
+}
+
 }  // namespace aa
 
 using aa::fail;
@@ -130,8 +135,14 @@ aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjac
     return fail(AA_ERR_UNSUPPORTED,
                 "aa_plan_create: a period that q does not divide needs AA_TYPES_EXPLICIT");
   const int64_t b_in = d_in / q, b_out = d_out / q;
-  if (b_in % 16 || b_out % 16)
-    return fail(AA_ERR_UNSUPPORTED, "aa_plan_create: block sides d_in/q and d_out/q must be multiples of 16");
+  // blocks whose sides are multiples of the 16-wide MFMA fragment use packed
+  // layout 1; narrower ones layout 2 and the small-block kernel, in the
+  // shapes that kernel takes
+  const bool layout1 = b_in % 16 == 0 && b_out % 16 == 0;
+  if (!layout1 && !aa::small_layout_ok(law, type_kind, in_dtype, b_in, b_out))
+    return fail(AA_ERR_UNSUPPORTED,
+                "aa_plan_create: block sides d_in/q and d_out/q must be multiples of 16, or multiples of 4 "
+                "up to 128 with bf16 weights, position or block-row typing and the Q_q or digraph law");
   if (d_in > (int64_t(1) << 31) || d_out > (int64_t(1) << 31))
     return fail(AA_ERR_UNSUPPORTED, "aa_plan_create: widths above 2^31");
 
@@ -163,7 +174,7 @@ aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjac
     for (int k = 0; k < q; ++k) n += aa::leaf_groups(law, q, i, k, groups, i < 64 ? p->adj[i] : 0);
   p->n_block_products = n;
   p->n_leaves = int64_t(q) * q;
-  p->layout_version = 1;
+  p->layout_version = layout1 ? 1 : 2;
   p->tile_override = -1;
   p->wg_per_cu = 0;
   p->persist_pol = -1;

@@ -1,0 +1,414 @@
+// HIP kernels (gfx950) for plans whose weight blocks are narrower than the
+// 16-wide MFMA fragment the main packed layout is built from: block sides
+// b_in and b_out that are multiples of 4 but not both of 16, such as the
+// Qwen3-32B FFN shape of the projection table in the agihunt.info review of
+// "Change the Product, Keep the Parameters" (5120 -> 25600 features, q = 256:
+// 20 x 100 blocks).  The operation is the same row-typed projection: a row of
+// type i produces output group k as the sum over the table's input groups j
+// of x_j W_jk (Q_q: j in {i, k}; a digraph: {i, k} for an edge i -> k, {i}
+// for k = i, nothing otherwise).
+//
+// Packed layout version 2 (aa_pack_weights for such plans).  Blocks W_jk in
+// row-major block order, each b_in * b_out elements.  Inside a block, runs of
+// 4 elements: run (kq, n) holds rows 4 kq .. 4 kq + 3 of column n.  Columns
+// are taken 16 at a time (a fragment); inside a fragment the runs go kq-major,
+// then n.  The last fragment of a block may be narrower (b_out mod 16
+// columns, same order).  The element count is exactly b_in * b_out.
+//
+// Formulation.  As in the main kernels, Y^T = W^T X^T with
+// v_mfma_f32_16x16x32_bf16: each lane supplies 8 consecutive k of the A
+// operand (weights) and of the B operand (activations).  The K axis of a leaf
+// is the concatenation of its input groups, b_in each; since b_in is a
+// multiple of 4, a lane's 8 k are two runs of 4 that may come from different
+// input groups (blocks), so every lane loads its two 8-byte halves from its
+// own addresses.  K past the leaf's end and columns past b_out read zeros.
+//
+// Work split.  A workgroup (4 waves) computes, for one row type i and one
+// m-tile of 64 MF of its rows, a run of kc consecutive output groups, and NF
+// of the blocks' 16-column fragments (blockIdx.y picks which, when a block
+// has more fragments than one workgroup's registers hold); each
+// wave owns MF 16-row fragments and walks the output groups, with the loads
+// of the next output group in flight while it multiplies the current one
+// (NSET = 2).  Outputs are stored straight from the accumulators: a lane holds
+// 4 consecutive columns of one row.  Tiles are dealt so that each XCD runs a
+// contiguous part of the (type, m-tile, output-group run) order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "aa_device.h"
+#include "aa_internal.h"
+
+namespace aa {
+namespace {
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+struct SmallParams {
+  const __bf16* X;
+  const __bf16* W0;
+  const __bf16* W1;
+  void* Y;
+  int64_t M;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t q;
+  int32_t b_in;
+  int32_t b_out;
+  int32_t law;
+  int32_t kind;            // position or block-row typing
+  int32_t off_mod_q;
+  int64_t rows_per_type;   // block-row typing
+  int32_t mt_count;        // m-tiles per row type
+  int32_t kc;              // output groups per tile
+  int32_t kchunks;         // tiles per (row type, m-tile)
+  uint32_t n_tiles;
+  uint64_t adj[64];        // digraph: bit k of adj[i] = edge i -> k
+};
+
+// Element offset of run (kq, n) inside a block of the version-2 layout.
+__device__ __host__ inline int64_t v2_run(int b_in, int b_out, int kq, int n) {
+  const int nfull = b_out >> 4;
+  const int f = n >> 4;
+  if (f < nfull) return int64_t(f) * 16 * b_in + kq * 64 + (n & 15) * 4;
+  const int w = b_out - nfull * 16;
+  return int64_t(nfull) * 16 * b_in + int64_t(kq) * 4 * w + (n - nfull * 16) * 4;
+}
+
+__device__ inline u32x2_t load8(const __bf16* p) { return *reinterpret_cast<const u32x2_t*>(p); }
+__device__ inline Run<__bf16> join(u32x2_t lo, u32x2_t hi) {
+  Run<__bf16> r;
+  r.v = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  return r;
+}
+
+// Output store modes (tuning): 0 and 1 store each lane's four columns straight
+// from the accumulators (nontemporal / cached); 2 and 3 first stage the
+// wave's rows in LDS and store them as consecutive 4-column runs along each
+// row (cached / nontemporal), so that one store instruction covers whole
+// stretches of a few rows instead of 32-byte pieces of 16 rows.
+template <int S, int NF, int MF, int NSET, bool SWIGLU, typename Tout, int STORE>
+__global__ __launch_bounds__(256) void leaf_small_kernel(SmallParams p) {
+  constexpr int NW = 4;
+  constexpr int SROW = NF * 16 + 4;   // staged row stride (elements)
+  __shared__ __attribute__((aligned(16))) Tout stage[STORE >= 2 ? NW * 16 * MF * SROW : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+
+  // this workgroup's tile: XCD x (blockIdx mod 8) takes a contiguous run of
+  // the tile order (row type, m-tile, run of output groups)
+  const uint32_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int chunk = int(t % uint32_t(p.kchunks));
+  t /= uint32_t(p.kchunks);
+  const int mt = int(t % uint32_t(p.mt_count));
+  const int i = int(t / uint32_t(p.mt_count));
+  const int f0 = int(blockIdx.y) * NF;   // this launch row's first 16-column fragment
+  const int k0 = chunk * p.kc;
+  const int k1 = k0 + p.kc < p.q ? k0 + p.kc : p.q;
+  if (k0 >= k1) return;
+
+  // rows of type i in closed form
+  int64_t first, stride, count;
+  if (p.kind == AA_TYPES_BLOCK_ROWS) {
+    first = int64_t(i) * p.rows_per_type;
+    stride = 1;
+    count = p.rows_per_type;
+  } else {
+    int64_t r0 = int64_t(i) - p.off_mod_q;
+    if (r0 < 0) r0 += p.q;
+    first = r0;
+    stride = p.q;
+    count = r0 < p.M ? (p.M - r0 + p.q - 1) / p.q : 0;
+  }
+  int64_t xoff[MF], yoff[MF];
+  bool rv[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    const int64_t r = (int64_t(mt) * NW * MF + wave * MF + mf) * 16 + l16;
+    rv[mf] = r < count;
+    const int64_t row = rv[mf] ? first + r * stride : 0;   // rows past the type's last re-read row 0
+    xoff[mf] = row * p.ldx;
+    yoff[mf] = row * p.ldy;
+  }
+
+  // K position of each of this lane's runs: step s, half h covers leaf k
+  // 32 s + 8 g + 4 h .. + 3, which lies in input-group slot si at offset lk
+  int si[S][2], lk[S][2];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 32 * s + 8 * g + 4 * h;
+      si[s][h] = kk / p.b_in;
+      lk[s][h] = kk - si[s][h] * p.b_in;
+    }
+  const uint64_t adj_row = p.law == AA_LAW_DIGRAPH ? p.adj[i] : 0;
+  const int64_t blk_elems = int64_t(p.b_in) * p.b_out;
+
+  struct Set {
+    u32x2_t a0[S][NF][2], a1[S][NF][2], b[S][MF][2];
+  };
+  auto load = [&](int k, Set& st) __attribute__((always_inline)) {
+    int sg[4] = {0, 0, 0, 0};
+    const int nseg = device_leaf_groups(p.law, i, k, sg, adj_row);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool kv = si[s][h] < nseg;
+        const int seg = si[s][h] == 0 ? sg[0] : sg[1];
+        const __bf16* wblk0 = p.W0 + (int64_t(seg) * p.q + k) * blk_elems;
+        const __bf16* wblk1 = SWIGLU ? p.W1 + (int64_t(seg) * p.q + k) * blk_elems : nullptr;
+        const int kq = lk[s][h] >> 2;
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+          st.b[s][mf][h] = load8(kv ? p.X + xoff[mf] + int64_t(seg) * p.b_in + lk[s][h] : zero);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int n = (f0 + f) * 16 + l16;
+          const bool ok = kv && n < p.b_out;
+          const int64_t o = ok ? v2_run(p.b_in, p.b_out, kq, n) : 0;
+          st.a0[s][f][h] = load8(ok ? wblk0 + o : zero);
+          if (SWIGLU) st.a1[s][f][h] = load8(ok ? wblk1 + o : zero);
+        }
+      }
+  };
+  auto compute_store = [&](int k, const Set& st, bool live) __attribute__((always_inline)) {
+    f32x4_t acc0[NF][MF], acc1[NF][MF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        acc0[f][mf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1[f][mf] = acc0[f][mf];
+      }
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        const Run<__bf16> xb = join(st.b[s][mf][0], st.b[s][mf][1]);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          acc0[f][mf] = mma(join(st.a0[s][f][0], st.a0[s][f][1]), xb, acc0[f][mf]);
+          if (SWIGLU) acc1[f][mf] = mma(join(st.a1[s][f][0], st.a1[s][f][1]), xb, acc1[f][mf]);
+        }
+      }
+    if (!live) return;
+    Tout* Y = static_cast<Tout*>(p.Y);
+    const int64_t col0 = int64_t(k) * p.b_out + f0 * 16;
+    Tout* st_w = stage + wave * 16 * MF * SROW;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) {
+        f32x4_t v = acc0[f][mf];
+        if (SWIGLU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc0[f][mf][e], acc1[f][mf][e]);
+        }
+        if constexpr (STORE >= 2) {
+          store4(st_w + (mf * 16 + l16) * SROW + f * 16 + 4 * g, v);
+        } else {
+          // b_out is a multiple of 4: a lane's four columns are all in or all out
+          if (rv[mf] && (f0 + f) * 16 + 4 * g < p.b_out) {
+            if (STORE == 0) store4_nt(Y + yoff[mf] + col0 + f * 16 + 4 * g, v);
+            else store4(Y + yoff[mf] + col0 + f * 16 + 4 * g, v);
+          }
+        }
+      }
+    if constexpr (STORE >= 2) {
+      // this wave's staged rows back out as runs of 4 columns along each row
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+      const int ncol = p.b_out - f0 * 16 < NF * 16 ? p.b_out - f0 * 16 : NF * 16;
+      const int cpr = ncol >> 2;
+      const int total = 16 * MF * cpr;
+      for (int e = lane; e < total; e += 64) {
+        const int r = e / cpr, c = (e - r * cpr) * 4;
+        const int64_t rr = (int64_t(mt) * NW * MF + wave * MF) * 16 + r;
+        if (rr < count) {
+          Tout* dst = Y + (first + rr * stride) * p.ldy + col0 + c;
+          const Tout* src = st_w + r * SROW + c;
+          if constexpr (sizeof(Tout) == 2) {
+            const u32x2_t val = *reinterpret_cast<const u32x2_t*>(src);
+            if (STORE == 3) __builtin_nontemporal_store(val, reinterpret_cast<u32x2_t*>(dst));
+            else *reinterpret_cast<u32x2_t*>(dst) = val;
+          } else {
+            const u32x4_t val = *reinterpret_cast<const u32x4_t*>(src);
+            if (STORE == 3) __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(dst));
+            else *reinterpret_cast<u32x4_t*>(dst) = val;
+          }
+        }
+      }
+    }
+  };
+
+  // Output groups k0 .. k1 - 1, two per round with the next one's loads in
+  // flight (NSET = 2); a step past k1 - 1 re-loads the last group and stores
+  // nothing, so no load sits behind a branch.
+  const int nk = k1 - k0;
+  if (NSET == 1) {
+    Set A;
+    for (int u = 0; u < nk; ++u) {
+      load(k0 + u, A);
+      compute_store(k0 + u, A, true);
+    }
+  } else {
+    Set A, B;
+    load(k0, A);
+    for (int u = 0; u < nk; u += 2) {
+      load(k0 + u + 1 < k1 ? k0 + u + 1 : k1 - 1, B);
+      compute_store(k0 + u, A, true);
+      load(k0 + u + 2 < k1 ? k0 + u + 2 : k1 - 1, A);
+      compute_store(k0 + u + 1, B, u + 1 < nk);
+    }
+  }
+}
+
+// Thread c moves run c (4 elements) of the version-2 layout from or to the
+// row-major weight.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_v2_kernel(const T* __restrict__ src, T* __restrict__ dst, int32_t q,
+                                                      int32_t b_in, int32_t b_out, int64_t d_out, int64_t n_runs,
+                                                      bool unpack) {
+  const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= n_runs) return;
+  const int64_t runs_per_blk = int64_t(b_in) * b_out / 4;
+  const int64_t blk = c / runs_per_blk;
+  const int64_t w = c - blk * runs_per_blk;
+  const int64_t j = blk / q, kb = blk % q;
+  const int64_t nfull = b_out / 16, full_runs = nfull * 4 * b_in;
+  int64_t kq, n;
+  if (w < full_runs) {
+    const int64_t f = w / (4 * b_in), r = w - f * 4 * b_in;
+    kq = r / 16;
+    n = f * 16 + r % 16;
+  } else {
+    const int64_t width = b_out - nfull * 16, r = w - full_runs;
+    kq = r / width;
+    n = nfull * 16 + r % width;
+  }
+  const int64_t row = j * b_in + 4 * kq, col = kb * b_out + n;
+  if (!unpack) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[c * 4 + e] = src[(row + e) * d_out + col];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(row + e) * d_out + col] = src[c * 4 + e];
+  }
+}
+
+template <int S, int NF, int MF, int NSET, bool SW, int STORE>
+void go_small_st(const SmallParams& p, bool fout, dim3 grid, hipStream_t s) {
+  const dim3 block{256, 1, 1};
+  if (fout) launch((leaf_small_kernel<S, NF, MF, NSET, SW, float, STORE>), grid, block, 0, s, p);
+  else launch((leaf_small_kernel<S, NF, MF, NSET, SW, __bf16, STORE>), grid, block, 0, s, p);
+}
+
+// The store mode is a tuning override for the Qwen3-32B-shaped instance
+// (600 + mode); every other instance uses the default mode.
+constexpr int kSmallStoreDefault = 2;
+template <int S, int NF, int MF, int NSET, bool SW>
+void go_small(const SmallParams& p, bool fout, dim3 grid, hipStream_t s, int store) {
+  if constexpr (S == 2 && NF == 8 && !SW) {
+    switch (store) {
+      case 0: return go_small_st<S, NF, MF, NSET, SW, 0>(p, fout, grid, s);
+      case 1: return go_small_st<S, NF, MF, NSET, SW, 1>(p, fout, grid, s);
+      case 3: return go_small_st<S, NF, MF, NSET, SW, 3>(p, fout, grid, s);
+      default: break;
+    }
+  }
+  go_small_st<S, NF, MF, NSET, SW, kSmallStoreDefault>(p, fout, grid, s);
+}
+
+// Instances: S k-steps of 32 (the leaf's K padded), NF fragments per
+// workgroup.  The registers one lane holds grow with S NF (two loaded sets of
+// S NF weight runs for the plain kernel, one set of both weights for the
+// SwiGLU one), so S NF is kept at most 16 (plain) or 8 (SwiGLU) and wider
+// blocks take several launch rows of fragments.
+template <bool SW>
+bool go_small_sn(int S, int NF, const SmallParams& p, bool fout, dim3 grid, hipStream_t s, int store) {
+  constexpr int MF = SW ? 1 : 2, NSET = SW ? 1 : 2;
+#define AA_SMALL(s_, n_)                                \
+  if (S == s_ && NF == n_) {                            \
+    go_small<s_, n_, MF, NSET, SW>(p, fout, grid, s, store);  \
+    return true;                                        \
+  }
+  AA_SMALL(1, 1) AA_SMALL(1, 2) AA_SMALL(1, 4) AA_SMALL(1, 8)
+  AA_SMALL(2, 1) AA_SMALL(2, 2) AA_SMALL(2, 4)
+  AA_SMALL(4, 1) AA_SMALL(4, 2)
+  AA_SMALL(8, 1)
+  if constexpr (!SW) {
+    AA_SMALL(2, 8) AA_SMALL(4, 4) AA_SMALL(8, 2)
+  }
+#undef AA_SMALL
+  return false;
+}
+
+}  // namespace
+
+aa_status_t launch_small_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
+  // plan creation admits layout-2 plans only in the shapes handled here
+  if (!small_layout_ok(plan.law, plan.type_kind, plan.in_dtype, plan.b_in, plan.b_out))
+    return fail(AA_ERR_UNSUPPORTED, "this plan's block shape has no kernel");
+  SmallParams p{};
+  p.X = static_cast<const __bf16*>(call.X);
+  p.W0 = static_cast<const __bf16*>(call.W0);
+  p.W1 = static_cast<const __bf16*>(call.W1);
+  p.Y = call.Y;
+  p.M = call.M;
+  p.ldx = plan.d_in;
+  p.ldy = plan.d_out;
+  p.q = plan.q;
+  p.b_in = int32_t(plan.b_in);
+  p.b_out = int32_t(plan.b_out);
+  p.law = plan.law;
+  p.kind = plan.type_kind;
+  p.off_mod_q = int32_t(call.pos_offset % plan.q);
+  p.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : 0;
+  for (int r = 0; r < 64; ++r) p.adj[r] = plan.adj[r];
+  const int mf = call.swiglu ? 1 : 2;
+  const int64_t mi = plan.type_kind == AA_TYPES_BLOCK_ROWS ? call.M / plan.q : (call.M + plan.q - 1) / plan.q;
+  p.mt_count = int32_t((mi + 64 * mf - 1) / (64 * mf));
+  if (p.mt_count < 1) return AA_OK;
+  // runs of output groups: enough tiles for about eight workgroups per CU
+  const int64_t base = int64_t(plan.q) * p.mt_count;
+  const int64_t want = int64_t(device_cu_count()) * 8;
+  int64_t chunks = (want + base - 1) / base;
+  if (chunks > plan.q) chunks = plan.q;
+  p.kc = int32_t((plan.q + chunks - 1) / chunks);
+  p.kchunks = int32_t((plan.q + p.kc - 1) / p.kc);
+  const int64_t n_tiles = base * p.kchunks;
+  if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+  p.n_tiles = uint32_t(n_tiles);
+  const int nseg_max = plan.q > 1 ? 2 : 1;
+  const int steps = int((nseg_max * plan.b_in + 31) / 32);
+  const int S = steps <= 1 ? 1 : steps <= 2 ? 2 : steps <= 4 ? 4 : 8;
+  const int nf = int((plan.b_out + 15) / 16);
+  const int budget = (call.swiglu ? 8 : 16) / S;
+  int NF = 1;
+  while (NF < nf && NF * 2 <= budget) NF *= 2;
+  const dim3 grid{uint32_t(n_tiles), uint32_t((nf + NF - 1) / NF), 1};
+  const bool fout = plan.out_dtype == AA_F32;
+  const int store = plan.tile_override >= 600 && plan.tile_override < 604 ? plan.tile_override - 600
+                                                                         : kSmallStoreDefault;
+  const bool ok = call.swiglu ? go_small_sn<true>(S, NF, p, fout, grid, stream, store)
+                              : go_small_sn<false>(S, NF, p, fout, grid, stream, store);
+  if (!ok) return fail(AA_ERR_UNSUPPORTED, "this plan's block shape has no kernel");
+  return after_launch(stream, call.swiglu ? "leaf_small(swiglu)" : "leaf_small");
+}
+
+aa_status_t launch_pack_v2(const aa_plan_s& plan, const void* src, void* dst, bool unpack, hipStream_t stream) {
+  const int64_t n_runs = plan.d_in * plan.d_out / 4;
+  if (n_runs == 0) return AA_OK;
+  const dim3 block{256, 1, 1}, grid{uint32_t((n_runs + 255) / 256), 1, 1};
+  // layout-2 plans take bf16 weights only
+  launch(pack_v2_kernel<__bf16>, grid, block, 0, stream, static_cast<const __bf16*>(src),
+         static_cast<__bf16*>(dst), plan.q, int32_t(plan.b_in), int32_t(plan.b_out), plan.d_out, n_runs, unpack);
+  return after_launch(stream, unpack ? "unpack (layout 2)" : "pack (layout 2)");
+}
+
+}  // namespace aa

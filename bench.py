@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
                     choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
+                             "qwen3_32b",
                              "digraph_qwen3_8b", "pilot_decode_stack", "pilot_generate",
                              "backward_qwen3_8b", "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
@@ -101,6 +102,8 @@ def main():
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[6])
     elif args.workload == "qwen3_8b_down":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[7])
+    elif args.workload == "qwen3_32b":
+        res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[8])
     elif args.workload == "digraph_qwen3_8b":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[3], digraph_density=0.5)
     elif args.workload.startswith("backward_"):
@@ -424,6 +427,7 @@ def bench_qwen3(args, torch, inp, aa, dev):
             "qwen3_30b_a3b_expert_ffn_q16": ffn_part(torch, inp, aa, dev, "expert_ffn", 100, 10,
                                                      not args.no_dense),
             "square_n32768_b128": square_part(torch, inp, aa, dev, 20, 2, not args.no_dense),
+            "qwen3_32b_q256": projection_part(torch, inp, aa, dev, inp.WORKLOADS[8], 20, 2, not args.no_dense),
         }
 
     return {
@@ -853,6 +857,47 @@ def cpu_baseline_qwen3(args, torch, inp, st, wl):
 
 
 # ----------------------------------------------------- other workloads ------
+
+def projection_part(torch, inp, aa, dev, wl, steps, warmup, dense=True):
+    """One row-typed projection shape (position typing) as a part of the
+    default line: two input sets alternate (flushed cache when a set exceeds
+    the 256 MB Infinity Cache), each call timed by its kernel dispatch events."""
+    M, D, F, q = wl.M, wl.d_in, wl.d_out, wl.q
+    plan = aa.aa_plan_create(wl.law, q, D, F, "pos_mod", 0, "bf16", "bf16")
+    per_set = proj_bytes(M, D, F)
+    sets = []
+    for s_ in range(2):
+        X = inp.gaussian((M, D), inp.seed_for(inp.ROLE_X, wl.index) + 100 * s_, 1.0, torch.bfloat16, dev)
+        W = inp.gaussian((D, F), inp.seed_for(inp.ROLE_W, wl.index) + 100 * s_, D ** -0.5, torch.bfloat16, dev)
+        sets.append((X, aa.pack(plan, W), torch.empty(M, F, dtype=torch.bfloat16, device=dev)))
+        del W
+    for w in range(warmup):
+        aa.aa_project_fwd(plan, *sets[w % 2])
+    torch.cuda.synchronize()
+    kt = KernelTimer(torch, aa, steps, 1)
+    for s_ in range(steps):
+        kt.arm(s_, 0)
+        aa.aa_project_fwd(plan, *sets[s_ % 2])
+    kt.disarm()
+    torch.cuda.synchronize()
+    ms = kt.ms(0)
+    part = {"workload": f"{wl.name}: {wl.notes}", "M": M, "d_in": D, "d_out": F, "q": q,
+            "layout": aa.aa_packed_layout_version(plan), "steps": steps, "ms": round(ms, 5), **kt.spread(0),
+            "dense_equiv_tflops": round(2.0 * M * D * F / ms / 1e9, 2),
+            "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / ms / 1e9, 2),
+            "roofline": roofline(per_set, ms)}
+    if dense:
+        Wd = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
+        X0 = sets[0][0]
+        t = dense_timer(torch, lambda: torch.matmul(X0, Wd), iters=5, warm=2)
+        part["dense"] = {"kind": "torch.matmul bf16 (hipBLASLt), same run", "ms": round(t, 4),
+                         "speedup": round(t / ms, 3)}
+        del Wd
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return part
+
 
 def square_part(torch, inp, aa, dev, steps, warmup, dense=True):
     """Fixed-block square product n = 32768, b = 128, q = 256 (block-row

@@ -45,8 +45,13 @@
  *  - A plan is immutable after creation and may be shared between threads
  *    and streams.  aa_plan_create and aa_plan_info make no HIP calls.
  *  - Shape limits of this implementation: q >= 1, q divides d_in and d_out,
- *    and the block sides b_in and b_out are multiples of 16 (the MFMA
- *    fragment width).  Other shapes return AA_ERR_UNSUPPORTED.
+ *    and either the block sides b_in and b_out are multiples of 16 (the MFMA
+ *    fragment width; packed layout 1), or they are multiples of 4 of at most
+ *    128 with bf16 weights, the Q_q or digraph law and position or block-row
+ *    typing (packed layout 2, e.g. the Qwen3-32B widths 5120 -> 25600 at
+ *    q = 256: 20 x 100 blocks).  Layout-2 plans have no gradient calls and no
+ *    per-token types in aa_decode_gemv.  Other shapes return
+ *    AA_ERR_UNSUPPORTED.
  */
 #ifndef AA_H_
 #define AA_H_
@@ -131,8 +136,8 @@ aa_status_t aa_plan_info(aa_plan_t plan, int64_t* n_block_products, int64_t* n_l
                          int64_t* packed_elems);
 
 /* The version of the packed weight layout a plan's calls read and write (the
- * format a caller stores packed weights in; see aa_pack_weights).  Every plan
- * of this library uses version 1.  Packed weights written under one version
+ * format a caller stores packed weights in; see aa_pack_weights): 1 when both
+ * block sides are multiples of 16, else 2.  Packed weights written under one version
  * are only valid for plans that report the same version and the same law, q,
  * d_in, d_out and in_dtype. */
 aa_status_t aa_packed_layout_version(aa_plan_t plan, int32_t* version);
@@ -148,7 +153,13 @@ aa_status_t aa_packed_layout_version(aa_plan_t plan, int32_t* version);
  * each other; a slab holds 64 runs of 8 elements, run r covering rows
  * 8 * (r / 16) .. + 7 of the slab in column r mod 16 of the strip.  When b_in
  * is an odd multiple of 16 the last slab of each strip has 16 rows and 32
- * runs. */
+ * runs.
+ *
+ * Packed layout (version 2, blocks whose sides are not both multiples of 16):
+ * the blocks in the same order and size; inside a block, runs of 4 elements,
+ * run (kq, n) covering rows 4 kq .. 4 kq + 3 of column n.  Columns are taken
+ * 16 at a time; inside such a fragment the runs go kq-major, then n; the last
+ * fragment holds the remaining b_out mod 16 columns in the same order. */
 aa_status_t aa_pack_weights(aa_plan_t plan, const void* W_rowmajor, void* W_packed, hipStream_t stream);
 aa_status_t aa_unpack_weights(aa_plan_t plan, const void* W_packed, void* W_rowmajor, hipStream_t stream);
 

@@ -57,6 +57,18 @@ int main() {
   int32_t ver = 0;
   EXPECT(aa_packed_layout_version(p, &ver), AA_OK);
   if (ver != 1) return 7;
+  {
+    aa_plan_t p2 = nullptr;
+    EXPECT(aa_plan_create(&p2, AA_LAW_QQ, 256, 5120, 25600, AA_TYPES_POS_MOD, 0, AA_BF16, AA_BF16), AA_OK);
+    EXPECT(aa_packed_layout_version(p2, &ver), AA_OK);
+    if (ver != 2) return 8;
+    EXPECT(aa_project_fwd(p2, P(1), P(2), P(3), 32768, 0, nullptr, nullptr), AA_OK);
+    EXPECT_NO_LAUNCH(aa_project_bwd_weight(p2, P(1), P(2), P(3), 64, 0, nullptr, nullptr, 0, nullptr),
+                     AA_ERR_UNSUPPORTED);
+    EXPECT_NO_LAUNCH(aa_decode_gemv(p2, P(1), P(2), P(3), 2, 0, static_cast<const int32_t*>(P(4)), nullptr),
+                     AA_ERR_UNSUPPORTED);
+    EXPECT(aa_plan_destroy(p2), AA_OK);
+  }
   EXPECT(aa_packed_layout_version(p, nullptr), AA_ERR_INVALID_ARG);
   EXPECT(aa_plan_info(nullptr, &nb, &nl, &pe), AA_ERR_INVALID_ARG);
   aa_plan_t bad = p;
@@ -65,7 +77,8 @@ int main() {
   if (bad != nullptr) return 3;
   EXPECT(aa_plan_create(&bad, AA_LAW_Q2XQ2, 2, 64, 64, AA_TYPES_POS_MOD, 0, AA_BF16, AA_BF16), AA_ERR_INVALID_ARG);
   EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 3, 64, 96, AA_TYPES_POS_MOD, 0, AA_BF16, AA_BF16), AA_ERR_SHAPE);
-  EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 2, 48, 64, AA_TYPES_POS_MOD, 0, AA_BF16, AA_BF16), AA_ERR_UNSUPPORTED);
+  EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 2, 36, 64, AA_TYPES_POS_MOD, 0, AA_BF16, AA_BF16), AA_ERR_UNSUPPORTED);
+  EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 2, 48, 64, AA_TYPES_EXPLICIT, 0, AA_BF16, AA_BF16), AA_ERR_UNSUPPORTED);
   EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 4, 64, 64, AA_TYPES_POS_MOD, 6, AA_BF16, AA_BF16), AA_ERR_UNSUPPORTED);
   EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 4, 64, 64, AA_TYPES_POS_MOD, -4, AA_BF16, AA_BF16), AA_ERR_INVALID_ARG);
   EXPECT(aa_plan_create(&bad, AA_LAW_QQ, 2, -64, 64, AA_TYPES_POS_MOD, 0, AA_BF16, AA_BF16), AA_ERR_INVALID_ARG);

@@ -58,13 +58,35 @@ def test_packed_layout_version(lib):
         assert aa.aa_packed_layout_version(aa.aa_plan_create(law, q, 16 * q, 32 * q)) == 1
     assert aa.aa_packed_layout_version(aa.aa_plan_create_digraph(3, [(0, 1)], 48, 48)) == 1
     assert _raw(lib, "aa_packed_layout_version", None, None) == aa.AA_ERR_INVALID_ARG
+    # the Qwen3-32B FFN widths at q = 256: 20 x 100 blocks, layout 2
+    p = aa.aa_plan_create("Qq", 256, 5120, 25600)
+    assert aa.aa_packed_layout_version(p) == 2
+    assert aa.aa_plan_info(p) == (2 * 256 * 256 - 256, 256 * 256, 5120 * 25600)
+    assert aa.aa_packed_layout_version(aa.aa_plan_create_digraph(3, [(0, 1)], 36, 60)) == 2
+
+
+def test_layout2_limits_before_launch(lib):
+    """Layout-2 plans: no gradients, no per-token decode types; both refused
+    on the host."""
+    p = aa.aa_plan_create("Qq", 4, 80, 48, "pos_mod", 0, "bf16", "f32")
+    g = 0x1000000
+    assert aa.aa_project_bwd_workspace(p, 100) == (0, 0)
+    assert _raw(lib, "aa_project_bwd_data", p.handle, g, 2 * g, 3 * g, 100, 0, None, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
+    assert _raw(lib, "aa_project_bwd_weight", p.handle, g, 2 * g, 3 * g, 100, 0, None, None, 0, None) == \
+        aa.AA_ERR_UNSUPPORTED
+    assert _raw(lib, "aa_decode_gemv", p.handle, g, 2 * g, 3 * g, 2, 0, 4 * g, None) == aa.AA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("args,status", [
     (("Qq", 0, 64, 64), aa.AA_ERR_INVALID_ARG),
     (("Q2xQ2", 2, 64, 64), aa.AA_ERR_INVALID_ARG),
     (("Qq", 3, 64, 96), aa.AA_ERR_SHAPE),          # 3 does not divide 64
-    (("Qq", 2, 48, 64), aa.AA_ERR_UNSUPPORTED),    # b_in = 24 is not a multiple of 16
+    (("Qq", 2, 36, 64), aa.AA_ERR_UNSUPPORTED),    # b_in = 18 is not a multiple of 4
+    (("Q2xQ2", 4, 96, 64), aa.AA_ERR_UNSUPPORTED),  # 24 x 16 blocks: layout 2 takes Q_q and digraphs
+    (("Qq", 2, 48, 64, "explicit"), aa.AA_ERR_UNSUPPORTED),   # layout 2 without explicit types
+    (("Qq", 2, 48, 64, "pos_mod", 0, "f32", "f32"), aa.AA_ERR_UNSUPPORTED),   # layout 2 takes bf16
+    (("Qq", 2, 264, 64), aa.AA_ERR_UNSUPPORTED),   # b_in = 132: layout 2 stops at 128
     (("Qq", 4, 64, 64, "pos_mod", 6), aa.AA_ERR_UNSUPPORTED),  # period not a multiple of q
     (("Qq", 4, 64, 64, "pos_mod", -4), aa.AA_ERR_INVALID_ARG),
     (("Qq", 2, -64, 64), aa.AA_ERR_INVALID_ARG),
@@ -91,8 +113,8 @@ def test_digraph_plans(lib):
         aa.AA_ERR_INVALID_ARG
     assert lib.aa_plan_create_digraph(ctypes.byref(out), 65, ctypes.cast(adj, ctypes.c_char_p), 65 * 16, 65 * 16,
                                       0, 0, 0, 0) == aa.AA_ERR_UNSUPPORTED
-    assert lib.aa_plan_create_digraph(ctypes.byref(out), 2, ctypes.cast(adj, ctypes.c_char_p), 48, 64,
-                                      0, 0, 0, 0) == aa.AA_ERR_UNSUPPORTED   # b_in = 24
+    assert lib.aa_plan_create_digraph(ctypes.byref(out), 2, ctypes.cast(adj, ctypes.c_char_p), 36, 64,
+                                      0, 0, 0, 0) == aa.AA_ERR_UNSUPPORTED   # b_in = 18
     with pytest.raises(aa.AAError) as e:
         aa.aa_plan_create("digraph", 2, 64, 64)
     assert e.value.status == aa.AA_ERR_INVALID_ARG
