@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_q32",
                     choices=["qwen3_8b_q32", "square", "pilot_ffn", "expert_ffn", "qwen3_1p7b", "qwen3_8b_down",
-                             "qwen3_32b",
+                             "qwen3_32b", "qwen3_8b_proj",
                              "digraph_qwen3_8b", "pilot_decode_stack", "pilot_generate",
                              "backward_qwen3_8b", "backward_expert"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = enough to exceed 1 GB)")
@@ -102,6 +102,8 @@ def main():
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[6])
     elif args.workload == "qwen3_8b_down":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[7])
+    elif args.workload == "qwen3_8b_proj":
+        res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[3])
     elif args.workload == "qwen3_32b":
         res = bench_projection(args, torch, inp, aa, dev, inp.WORKLOADS[8])
     elif args.workload == "digraph_qwen3_8b":
