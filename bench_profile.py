@@ -32,10 +32,11 @@ COPY_BYTES = 1 << 30   # bench.py --calibration-copy copies 2^28 int32
 
 
 def kernel_source_hash():
-    """Hash of the forward kernels' sources (aa_kernels.hip and the device
-    header it includes): stored traffic figures are used only while it matches."""
+    """Hash of the forward kernels' sources (aa_kernels.hip, aa_small.hip and
+    the device header they include): stored traffic figures are used only
+    while it matches."""
     h = hashlib.sha256()
-    for name in ("aa_kernels.hip", "aa_device.h"):
+    for name in ("aa_kernels.hip", "aa_small.hip", "aa_device.h"):
         with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -109,6 +110,41 @@ def is_calibration_copy(name):
     return "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name
 
 
+def write_counters(a, src):
+    """Per-kernel means of the counters of one --pmc run, with the kernel's
+    mean duration and GRBM_GUI_ACTIVE-normalised busy fractions where the
+    counters allow (SQ counters read one of the 32 shader engines: 8 CUs, 32
+    SIMDs; SQ_*_CYCLES wave and busy counters count in units of 4 cycles)."""
+    c = _db(a.counters)
+    rows = c.execute("select name, counter_name, avg(counter_value), avg(duration) from pmc_events "
+                     "group by name, counter_name").fetchall()
+    per = {}
+    for name, cn, v, dur in rows:
+        if a.match and a.match not in name:
+            continue
+        d = per.setdefault(name, {"_us": dur / 1000.0})
+        d[cn] = v
+    names = sorted({cn for d in per.values() for cn in d if not cn.startswith("_")})
+    lines = [f"# Counters: {a.name}", "", f"Command (run from /tmp with TMPDIR=/tmp): `{a.cmd_counters}`", "",
+             f"Forward kernel sources (aa_kernels.hip, aa_small.hip, aa_device.h) sha256[:16]: `{src}`", "",
+             "Mean per dispatch.  SQ counters read one of the 32 shader engines (8 CUs, 32 SIMDs).  "
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (32 x GRBM_GUI_ACTIVE); wait share = SQ_WAIT_INST_ANY / "
+             "SQ_WAVE_CYCLES (waves waiting on their own loads); residency = 4 x SQ_WAVE_CYCLES / "
+             "(SIMDs x waves per SIMD x GRBM_GUI_ACTIVE) is not shown, the occupancy differs per kernel.", "",
+             "| kernel | us | " + " | ".join(names) + " | MFMA busy | wait share |",
+             "|---|---|" + "---|" * len(names) + "---|---|"]
+    for n, d in sorted(per.items(), key=lambda kv: -kv[1]["_us"]):
+        mf = d.get("SQ_VALU_MFMA_BUSY_CYCLES"), d.get("GRBM_GUI_ACTIVE")
+        busy = f"{mf[0] / (32 * mf[1]):.3f}" if mf[0] is not None and mf[1] else "-"
+        wt = d.get("SQ_WAIT_INST_ANY"), d.get("SQ_WAVE_CYCLES")
+        wait = f"{wt[0] / wt[1]:.3f}" if wt[0] is not None and wt[1] else "-"
+        lines.append(f"| `{short(n)}` | {d['_us']:.2f} | " + " | ".join(f"{d.get(k, 0):.0f}" for k in names) +
+                     f" | {busy} | {wait} |")
+    with open(os.path.join(PROFILES, f"{a.name}_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--name", required=True)
@@ -123,14 +159,20 @@ def main():
     ap.add_argument("--bench-log", default=None,
                     help="output of the same bench.py command run without the tracer just before")
     ap.add_argument("--bench-log-traced", default=None, help="output of the traced bench.py run")
+    ap.add_argument("--counters", default=None,
+                    help="a rocprofv3 --pmc output directory: write profiles/<name>_counters.md, the mean of every "
+                         "counter per kernel (only kernels whose name contains --match)")
+    ap.add_argument("--cmd-counters", default="")
     a = ap.parse_args()
     os.makedirs(PROFILES, exist_ok=True)
     src = kernel_source_hash()
+    if a.counters:
+        write_counters(a, src)
 
     ks = kernel_stats(a.trace)
     lines = [f"# Kernel trace: {a.name}", "",
              f"Command (run from /tmp with TMPDIR=/tmp): `{a.cmd_trace}`", "",
-             f"Forward kernel sources (aa_kernels.hip, aa_device.h) sha256[:16]: `{src}`", "",
+             f"Forward kernel sources (aa_kernels.hip, aa_small.hip, aa_device.h) sha256[:16]: `{src}`", "",
              "| kernel | grid (threads) | calls | avg us | min us | max us | % of GPU time |",
              "|---|---|---|---|---|---|---|"]
     for k in ks:
@@ -173,7 +215,7 @@ def main():
         lines = [f"# HBM traffic per launch: {a.name}", "",
                  f"Commands (run from /tmp with TMPDIR=/tmp): `{a.cmd_pmc.replace('PMC', 'FETCH_SIZE')}` and "
                  f"`{a.cmd_pmc.replace('PMC', 'WRITE_SIZE')}`", "",
-                 f"Forward kernel sources (aa_kernels.hip, aa_device.h) sha256[:16]: `{src}`", "",
+                 f"Forward kernel sources (aa_kernels.hip, aa_small.hip, aa_device.h) sha256[:16]: `{src}`", "",
                  f"Calibration: a 1 GiB device copy (`{short(cname, 60)}`, its largest dispatches) reads FETCH_SIZE = {fe[cname]:.0f} KiB "
                  f"and WRITE_SIZE = {wr[cname]:.0f} KiB per launch, so bytes = FETCH_SIZE x 1024 x {f_fac:.4f} "
                  f"and WRITE_SIZE x 1024 x {w_fac:.4f}.", "",
