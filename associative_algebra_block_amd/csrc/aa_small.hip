@@ -268,6 +268,231 @@ __global__ __launch_bounds__(256) void leaf_small_kernel(SmallParams p) {
   }
 }
 
+// ---- LDS-staged variant: plain projections whose leaves are at most 64 deep
+// (b_in <= 32) with blocks of at most 4096 elements, e.g. the Qwen3-32B 20 x 100
+// blocks.  These are bound by how many bytes each compute unit keeps in
+// flight.  The kernel above has every wave load all weight runs of a leaf for
+// itself (16 KB of registers per wave and output group), which limits a CU to
+// two workgroups and one output group of loads in flight each.  Here the four
+// waves of a workgroup (one 16-row fragment each, 64 rows) share one copy of
+// an output group's two weight blocks and activation segments: all 256
+// threads load them (a few 16-byte runs each) two output groups ahead into
+// registers and write them to one of two LDS stage buffers, and each wave
+// reads its MFMA operands from there.  The type's own activation block is
+// staged once per tile.  LDS per workgroup: two stages of 2 b_in b_out + 64
+// b_in bf16 values, the own block (64 b_in), and the outputs staged per wave
+// (16 rows x 16 NF + 4 columns).
+constexpr int kLdsTM = 64;
+
+struct LdsRegions {
+  int w, xd, xo, out, total;   // byte offsets of the regions, total bytes
+};
+__host__ __device__ inline LdsRegions lds_regions(int b_in, int b_out, int nf, int out_bytes) {
+  const int wb = 2 * b_in * b_out * 2, xb = kLdsTM * b_in * 2;
+  LdsRegions r;
+  r.w = 0;
+  r.xd = 2 * wb;
+  r.xo = r.xd + 2 * xb;
+  r.out = (r.xo + xb + 15) / 16 * 16;
+  r.total = r.out + 4 * 16 * (nf * 16 + 4) * out_bytes;
+  return r;
+}
+
+// WPT: 16-byte weight runs per thread and stage (two blocks of up to 1024 WPT
+// bf16 values); XPT: 8-byte activation runs per thread and stage (64 rows of
+// up to 32 k).
+template <int S, int NF, int WPT, typename Tout>
+__global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  constexpr int XPT = 2;
+  constexpr int SROW = NF * 16 + 4;
+  const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+  const LdsRegions R = lds_regions(p.b_in, p.b_out, NF, int(sizeof(Tout)));
+
+  const uint32_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int chunk = int(t % uint32_t(p.kchunks));
+  t /= uint32_t(p.kchunks);
+  const int mt = int(t % uint32_t(p.mt_count));
+  const int i = int(t / uint32_t(p.mt_count));
+  const int f0 = int(blockIdx.y) * NF;
+  const int k0 = chunk * p.kc;
+  const int k1 = k0 + p.kc < p.q ? k0 + p.kc : p.q;
+  if (k0 >= k1) return;
+
+  int64_t first, stride, count;
+  if (p.kind == AA_TYPES_BLOCK_ROWS) {
+    first = int64_t(i) * p.rows_per_type;
+    stride = 1;
+    count = p.rows_per_type;
+  } else {
+    int64_t r0 = int64_t(i) - p.off_mod_q;
+    if (r0 < 0) r0 += p.q;
+    first = r0;
+    stride = p.q;
+    count = r0 < p.M ? (p.M - r0 + p.q - 1) / p.q : 0;
+  }
+  const int64_t m0 = int64_t(mt) * kLdsTM;
+  auto grow = [&](int r) -> int64_t { return m0 + r < count ? first + (m0 + r) * stride : 0; };
+
+  const int blk_el = p.b_in * p.b_out;
+  const int q4n = p.b_in >> 2;                    // 8-byte runs per activation row segment
+  const int n_wc = blk_el * 4 / 16;               // 16-byte runs of the two blocks of a stage
+  const int n_xr = kLdsTM * q4n;                  // 8-byte runs of a stage's activation segments
+  const uint64_t adj_row = p.law == AA_LAW_DIGRAPH ? p.adj[i] : 0;
+
+  // per-thread activation rows of the stage runs (fixed for the tile)
+  int64_t xrow[XPT];
+  int xq[XPT];
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int r = tid + 256 * j;
+    const int row = r < n_xr ? r / q4n : 0;
+    xq[j] = r < n_xr ? r - row * q4n : 0;
+    xrow[j] = grow(row) * p.ldx;
+  }
+
+  struct Set {
+    u32x4_t w[WPT];
+    u32x2_t x[XPT];
+  };
+  // Stage k: blocks (g0, k) and (g1, k) of the leaf's input groups (a diagonal
+  // leaf, or a digraph leaf without an edge, re-reads valid blocks its zero
+  // K masks out), and the rows' activation segment of group k.
+  auto load = [&](int k, Set& st) __attribute__((always_inline)) {
+    int sg[4] = {0, 0, 0, 0};
+    const int nseg = device_leaf_groups(p.law, i, k, sg, adj_row);
+    const int g0 = nseg > 0 ? sg[0] : i, g1 = nseg > 1 ? sg[1] : g0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int c = tid + 256 * j;
+      const int e = c * 8;   // element offset in the stage (8 bf16 per run)
+      const int slot2 = e >= blk_el ? 1 : 0;
+      const __bf16* src = p.W0 + (int64_t(slot2 ? g1 : g0) * p.q + k) * blk_el + (e - slot2 * blk_el);
+      st.w[j] = *reinterpret_cast<const u32x4_t*>(c < n_wc ? src : zero);
+    }
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const __bf16* src = p.X + xrow[j] + int64_t(k) * p.b_in + 4 * xq[j];
+      st.x[j] = *reinterpret_cast<const u32x2_t*>(tid + 256 * j < n_xr ? src : zero);
+    }
+  };
+  auto store = [&](int buf, const Set& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int c = tid + 256 * j;
+      if (c < n_wc) *reinterpret_cast<u32x4_t*>(lds + R.w + buf * blk_el * 4 + c * 16) = st.w[j];
+    }
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int r = tid + 256 * j;
+      if (r < n_xr) *reinterpret_cast<u32x2_t*>(lds + R.xd + buf * kLdsTM * p.b_in * 2 + r * 8) = st.x[j];
+    }
+  };
+
+  // the type's own activation block, once per tile
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int r = tid + 256 * j;
+    const __bf16* src = p.X + xrow[j] + int64_t(i) * p.b_in + 4 * xq[j];
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(r < n_xr ? src : zero);
+    if (r < n_xr) *reinterpret_cast<u32x2_t*>(lds + R.xo + r * 8) = v;
+  }
+
+  // K position of this lane's runs (as in the kernel above)
+  int si[S][2], lk[S][2];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 32 * s + 8 * g + 4 * h;
+      si[s][h] = kk / p.b_in;
+      lk[s][h] = kk - si[s][h] * p.b_in;
+    }
+  const int row_l = wave * 16 + l16;
+  Tout* Y = static_cast<Tout*>(p.Y);
+  Tout* st_w = reinterpret_cast<Tout*>(lds + R.out) + wave * 16 * SROW;
+
+  auto compute_store = [&](int buf, int k, bool live) __attribute__((always_inline)) {
+    int sg[4] = {0, 0, 0, 0};
+    const int nseg = device_leaf_groups(p.law, i, k, sg, adj_row);
+    f32x4_t acc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const unsigned char* wl = lds + R.w + buf * blk_el * 4;
+    const unsigned char* xd = lds + R.xd + buf * kLdsTM * p.b_in * 2;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      u32x2_t xb[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool kv = si[s][h] < nseg;
+        const unsigned char* base = si[s][h] == 0 ? lds + R.xo : xd;
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(base + (row_l * p.b_in + (kv ? lk[s][h] : 0)) * 2);
+        xb[h] = kv ? v : u32x2_t{0u, 0u};
+      }
+      const Run<__bf16> xr = join(xb[0], xb[1]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        u32x2_t a[2];
+        const int n = (f0 + f) * 16 + l16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = si[s][h] < nseg && n < p.b_out;
+          const int64_t o = ok ? int64_t(si[s][h]) * blk_el + v2_run(p.b_in, p.b_out, lk[s][h] >> 2, n) : 0;
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(wl + o * 2);
+          a[h] = ok ? v : u32x2_t{0u, 0u};
+        }
+        acc[f] = mma(join(a[0], a[1]), xr, acc[f]);
+      }
+    }
+    if (!live) return;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) store4(st_w + l16 * SROW + f * 16 + 4 * g, acc[f]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staged rows are written
+    const int ncol = p.b_out - f0 * 16 < NF * 16 ? p.b_out - f0 * 16 : NF * 16;
+    const int cpr = ncol >> 2;
+    const int64_t col0 = int64_t(k) * p.b_out + f0 * 16;
+    for (int e = lane; e < 16 * cpr; e += 64) {
+      const int r = e / cpr, c = (e - r * cpr) * 4;
+      const int64_t rr = m0 + wave * 16 + r;
+      if (rr < count) {
+        Tout* dst = Y + (first + rr * stride) * p.ldy + col0 + c;
+        const Tout* src = st_w + r * SROW + c;
+        if constexpr (sizeof(Tout) == 2) *reinterpret_cast<u32x2_t*>(dst) = *reinterpret_cast<const u32x2_t*>(src);
+        else *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+      }
+    }
+  };
+
+  // Output groups k0 .. k1 - 1: stage u + 1 is in registers (loaded one
+  // step earlier) and stage u + 2 being loaded while stage u is multiplied
+  // from LDS; steps past k1 - 1 re-load the last group and store nothing.
+  const int nk = k1 - k0;
+  auto kat = [&](int u) { return k0 + (u < nk ? u : nk - 1); };
+  Set A, B;
+  load(kat(0), A);
+  load(kat(1), B);
+  store(0, A);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  for (int u = 0; u < nk; u += 2) {
+    load(kat(u + 2), A);
+    compute_store(0, kat(u), true);
+    store(1, B);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    load(kat(u + 3), B);
+    compute_store(1, kat(u + 1), u + 1 < nk);
+    store(0, A);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
 // Thread c moves run c (4 elements) of the version-2 layout from or to the
 // row-major weight.
 template <typename T>
@@ -350,6 +575,65 @@ bool go_small_sn(int S, int NF, const SmallParams& p, bool fout, dim3 grid, hipS
 
 }  // namespace
 
+namespace {
+
+template <int S, int NF>
+void go_small_lds(const SmallParams& p, bool fout, int wpt, dim3 grid, size_t lds, hipStream_t s) {
+  const dim3 block{256, 1, 1};
+  if (wpt <= 2) {
+    if (fout) launch((leaf_small_lds_kernel<S, NF, 2, float>), grid, block, uint32_t(lds), s, p);
+    else launch((leaf_small_lds_kernel<S, NF, 2, __bf16>), grid, block, uint32_t(lds), s, p);
+  } else {
+    if (fout) launch((leaf_small_lds_kernel<S, NF, 4, float>), grid, block, uint32_t(lds), s, p);
+    else launch((leaf_small_lds_kernel<S, NF, 4, __bf16>), grid, block, uint32_t(lds), s, p);
+  }
+}
+
+// Whether the LDS-staged kernel takes a plan: a plain projection, leaves of
+// at most 64 k (b_in <= 32), two blocks per stage within 4 x 256 16-byte runs,
+// and its LDS within the 64 KB a launch gets without an attribute.
+int small_lds_nf(int64_t b_out) {
+  const int nf = int((b_out + 15) / 16);
+  return nf <= 2 ? 2 : nf <= 4 ? 4 : 8;
+}
+bool small_lds_ok(const aa_plan_s& plan, bool swiglu, bool fout) {
+  if (swiglu || plan.b_in > 32 || plan.b_in * plan.b_out > 4096) return false;
+  return lds_regions(int(plan.b_in), int(plan.b_out), small_lds_nf(plan.b_out), fout ? 4 : 2).total <= 65536;
+}
+
+// The LDS-staged kernel: 64-row tiles, runs of output groups for about
+// twelve workgroups per CU in all, fragments split over blockIdx.y by 8.
+aa_status_t launch_small_lds(const aa_plan_s& plan, SmallParams p, int64_t mi, bool fout, hipStream_t stream) {
+  p.mt_count = int32_t((mi + kLdsTM - 1) / kLdsTM);
+  const int64_t base = int64_t(plan.q) * p.mt_count;
+  const int64_t want = int64_t(device_cu_count()) * 12;
+  int64_t chunks = (want + base - 1) / base;
+  if (chunks > plan.q) chunks = plan.q;
+  p.kc = int32_t((plan.q + chunks - 1) / chunks);
+  p.kchunks = int32_t((plan.q + p.kc - 1) / p.kc);
+  const int64_t n_tiles = base * p.kchunks;
+  if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+  p.n_tiles = uint32_t(n_tiles);
+  const int S = plan.q > 1 && 2 * plan.b_in > 32 ? 2 : 1;
+  const int nf = int((plan.b_out + 15) / 16);
+  const int NF = small_lds_nf(plan.b_out);
+  const int wpt = int((plan.b_in * plan.b_out / 4 + 255) / 256);
+  const dim3 grid{uint32_t(n_tiles), uint32_t((nf + NF - 1) / NF), 1};
+  const size_t lds = size_t(lds_regions(int(plan.b_in), int(plan.b_out), NF, fout ? 4 : 2).total);
+  if (S == 1) {
+    if (NF == 2) go_small_lds<1, 2>(p, fout, wpt, grid, lds, stream);
+    else if (NF == 4) go_small_lds<1, 4>(p, fout, wpt, grid, lds, stream);
+    else go_small_lds<1, 8>(p, fout, wpt, grid, lds, stream);
+  } else {
+    if (NF == 2) go_small_lds<2, 2>(p, fout, wpt, grid, lds, stream);
+    else if (NF == 4) go_small_lds<2, 4>(p, fout, wpt, grid, lds, stream);
+    else go_small_lds<2, 8>(p, fout, wpt, grid, lds, stream);
+  }
+  return after_launch(stream, "leaf_small_lds");
+}
+
+}  // namespace
+
 aa_status_t launch_small_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
   // plan creation admits layout-2 plans only in the shapes handled here
   if (!small_layout_ok(plan.law, plan.type_kind, plan.in_dtype, plan.b_in, plan.b_out))
@@ -395,6 +679,11 @@ aa_status_t launch_small_gemm(const aa_plan_s& plan, const LeafCall& call, hipSt
   const bool fout = plan.out_dtype == AA_F32;
   const int store = plan.tile_override >= 600 && plan.tile_override < 604 ? plan.tile_override - 600
                                                                          : kSmallStoreDefault;
+  // plain projections with leaves of at most 64 k and blocks of at most 4096
+  // elements: the LDS-staged kernel (AA_TILE=610 forces the register kernel)
+  if (small_lds_ok(plan, call.swiglu, fout) && plan.tile_override != 610 &&
+      !(plan.tile_override >= 600 && plan.tile_override < 604))
+    return launch_small_lds(plan, p, mi, fout, stream);
   const bool ok = call.swiglu ? go_small_sn<true>(S, NF, p, fout, grid, stream, store)
                               : go_small_sn<false>(S, NF, p, fout, grid, stream, store);
   if (!ok) return fail(AA_ERR_UNSUPPORTED, "this plan's block shape has no kernel");

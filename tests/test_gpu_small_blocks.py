@@ -81,6 +81,7 @@ def _int_case(law, q, M, d_in, d_out, kind, out_dt, seed, edges=None):
     (1, 33, 20, 12, "pos_mod", 0),         # q = 1: a plain product
     (4, 300, 512, 80, "pos_mod", 1),       # 128 x 20 blocks: 256-wide leaves
     (2, 200, 128, 248, "pos_mod", 1),      # 64 x 124 blocks: fragments over two launch rows
+    (4, 150, 128, 512, "pos_mod", 1),      # 32 x 128 blocks: the widest the LDS-staged kernel takes
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_layout2_integer_exact(q, M, d_in, d_out, kind, pos, out_dt):
@@ -97,6 +98,29 @@ def test_layout2_integer_exact(q, M, d_in, d_out, kind, pos, out_dt):
     want = torch.from_numpy(ref).float().to(TD[out_dt])
     iv = torch.int16 if out_dt == "bf16" else torch.int32
     assert torch.equal(Y.cpu().view(iv), want.view(iv))
+
+
+@pytest.mark.parametrize("q,M,d_in,d_out,pos", [(8, 1000, 160, 800, 5), (3, 301, 36, 60, 2), (4, 150, 96, 240, 3)])
+def test_layout2_register_and_lds_kernels_agree(q, M, d_in, d_out, pos, monkeypatch):
+    """Leaves of at most 64 k take the LDS-staged kernel; a plan created with
+    AA_TILE=610 takes the per-wave register kernel instead.  Both sum the same
+    products in the same order, so their outputs are equal bit for bit."""
+    say("layout2 register vs LDS kernel", q, M, d_in, d_out, pos)
+    X = inp.gaussian((M, d_in), 41 + q, 1.0, torch.bfloat16, DEV)
+    W = inp.gaussian((d_in, d_out), 42 + q, d_in ** -0.5, torch.bfloat16, DEV)
+    plan = aa.aa_plan_create("Qq", q, d_in, d_out, "pos_mod", 0, "bf16", "f32")
+    monkeypatch.setenv("AA_TILE", "610")
+    plan_reg = aa.aa_plan_create("Qq", q, d_in, d_out, "pos_mod", 0, "bf16", "f32")
+    monkeypatch.delenv("AA_TILE")
+    P = aa.pack(plan, W)
+    Y = torch.full((M, d_out), float("nan"), device=DEV)
+    Y2 = torch.full((M, d_out), float("nan"), device=DEV)
+    aa.aa_project_fwd(plan, X, P, Y, None, pos)
+    aa.aa_project_fwd(plan_reg, X, P, Y2, None, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+    ref = oracle.project(host(X), host(W), "Qq", q, oracle.types_pos_mod(M, q, pos))
+    assert_parity(host(Y), ref, False, f"layout2 LDS kernel q={q} {d_in}->{d_out}")
 
 
 def test_layout2_digraph_integer_exact():
