@@ -270,8 +270,7 @@ __global__ __launch_bounds__(256) void leaf_small_kernel(SmallParams p) {
 
 // ---- LDS-staged variant: plain projections whose leaves are at most 64 deep
 // (b_in <= 32) with blocks of at most 4096 elements, e.g. the Qwen3-32B 20 x 100
-// blocks.  These are bound by how many bytes each compute unit keeps in
-// flight.  The kernel above has every wave load all weight runs of a leaf for
+// blocks.  The kernel above has every wave load all weight runs of a leaf for
 // itself (16 KB of registers per wave and output group), which limits a CU to
 // two workgroups and one output group of loads in flight each.  Here the four
 // waves of a workgroup (one 16-row fragment each, 64 rows) share one copy of
@@ -280,21 +279,36 @@ __global__ __launch_bounds__(256) void leaf_small_kernel(SmallParams p) {
 // registers and write them to one of two LDS stage buffers, and each wave
 // reads its MFMA operands from there.  The type's own activation block is
 // staged once per tile.  LDS per workgroup: two stages of 2 b_in b_out + 64
-// b_in bf16 values, the own block (64 b_in), and the outputs staged per wave
-// (16 rows x 16 NF + 4 columns).
+// b_in bf16 values, the own block (64 b_in), and each wave's output ring.
+//
+// Outputs leave in whole 128-byte lines.  A workgroup's output groups are
+// consecutive, so its columns of a row form one stretch, written b_out
+// columns per group.  Each wave keeps its 16 rows' unwritten columns in a
+// ring of one line plus b_out columns, and after each group stores only the
+// lines that are complete (after the run's last group, the rest): the memory
+// side then sees no line written in two pieces at different times, which
+// costs a read-modify-write of the line.  Runs of output groups are rounded
+// so that they start on a line where the row length allows.
+//
+// What bounds it at the Qwen3-32B shape: the LDS traffic of the operands
+// (each of the four waves reads both weight blocks of every group) and the
+// store pattern (each wave keeps 16 rows a q apart in progress, a few
+// hundred bytes per row per group), in about equal parts.
 constexpr int kLdsTM = 64;
+
+__host__ __device__ inline int ring_cols(int b_out, int out_bytes) { return 128 / out_bytes + b_out; }
 
 struct LdsRegions {
   int w, xd, xo, out, total;   // byte offsets of the regions, total bytes
 };
-__host__ __device__ inline LdsRegions lds_regions(int b_in, int b_out, int nf, int out_bytes) {
+__host__ __device__ inline LdsRegions lds_regions(int b_in, int b_out, int out_bytes) {
   const int wb = 2 * b_in * b_out * 2, xb = kLdsTM * b_in * 2;
   LdsRegions r;
   r.w = 0;
   r.xd = 2 * wb;
   r.xo = r.xd + 2 * xb;
   r.out = (r.xo + xb + 15) / 16 * 16;
-  r.total = r.out + 4 * 16 * (nf * 16 + 4) * out_bytes;
+  r.total = r.out + 4 * 16 * ring_cols(b_out, out_bytes) * out_bytes;
   return r;
 }
 
@@ -302,14 +316,15 @@ __host__ __device__ inline LdsRegions lds_regions(int b_in, int b_out, int nf, i
 // bf16 values); XPT: 8-byte activation runs per thread and stage (64 rows of
 // up to 32 k).
 template <int S, int NF, int WPT, typename Tout>
-__global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
+__global__ __launch_bounds__(256, WPT == 4 ? 2 : 3) void leaf_small_lds_kernel(SmallParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   constexpr int XPT = 2;
-  constexpr int SROW = NF * 16 + 4;
-  const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  constexpr int LE = 128 / int(sizeof(Tout));   // elements of a 128-byte line
+  const int tid = int(threadIdx.x), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addresses, scalar buffer range
   const int g = lane >> 4, l16 = lane & 15;
   const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
-  const LdsRegions R = lds_regions(p.b_in, p.b_out, NF, int(sizeof(Tout)));
+  const LdsRegions R = lds_regions(p.b_in, p.b_out, int(sizeof(Tout)));
 
   const uint32_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
   const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
@@ -318,8 +333,7 @@ __global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
   t /= uint32_t(p.kchunks);
   const int mt = int(t % uint32_t(p.mt_count));
   const int i = int(t / uint32_t(p.mt_count));
-  const int f0 = int(blockIdx.y) * NF;
-  const int k0 = chunk * p.kc;
+  const int k0 = chunk * p.kc;   // one launch row: NF 16 >= b_out
   const int k1 = k0 + p.kc < p.q ? k0 + p.kc : p.q;
   if (k0 >= k1) return;
 
@@ -414,9 +428,41 @@ __global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
     }
   const int row_l = wave * 16 + l16;
   Tout* Y = static_cast<Tout*>(p.Y);
-  Tout* st_w = reinterpret_cast<Tout*>(lds + R.out) + wave * 16 * SROW;
+  const int RR = ring_cols(p.b_out, int(sizeof(Tout)));
+  Tout* ring = reinterpret_cast<Tout*>(lds + R.out) + wave * 16 * RR;
+  // column c of a row starts a line when (c + ph) is a multiple of LE (rows
+  // whose length is a whole number of lines)
+  const uint32_t ph = uint32_t((reinterpret_cast<uintptr_t>(p.Y) / sizeof(Tout)) % LE);
+  uint32_t written = uint32_t(k0) * uint32_t(p.b_out);   // this wave's rows hold columns < written
+  const int64_t wrow0 = m0 + wave * 16;       // this wave's first row of the tile
+  const int64_t rows_left = count - wrow0;
 
-  auto compute_store = [&](int buf, int k, bool live) __attribute__((always_inline)) {
+  // Write out the complete lines of group k's columns and those before it
+  // (after the run's last group, everything), as runs of 4 columns along
+  // each row.
+  auto flush = [&](int k, bool live) __attribute__((always_inline)) {
+    const uint32_t c0 = uint32_t(k) * uint32_t(p.b_out);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's ring writes are done
+    const uint32_t end = c0 + uint32_t(p.b_out);
+    const uint32_t lb = (end + ph) / LE * LE;
+    const uint32_t upto = !live ? written : k == k1 - 1 ? end : lb >= written + ph ? lb - ph : written;
+    const int runs = int(upto - written) >> 2;
+    const int wbase = int(written % uint32_t(RR));
+    for (int e = lane; e < 16 * runs; e += 64) {
+      const int r = e / runs, c = (e - r * runs) * 4;
+      int slot = wbase + c;
+      slot = slot >= RR ? slot - RR : slot;
+      if (rows_left > r) {
+        Tout* dst = Y + (first + (wrow0 + r) * stride) * p.ldy + written + c;
+        const Tout* src = ring + r * RR + slot;
+        if constexpr (sizeof(Tout) == 2) *reinterpret_cast<u32x2_t*>(dst) = *reinterpret_cast<const u32x2_t*>(src);
+        else *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+      }
+    }
+    written = upto;
+  };
+  // Group k from LDS stage buf: the MFMA products, then the outputs into the ring.
+  auto mma_to_ring = [&](int buf, int k, bool live) __attribute__((always_inline)) {
     int sg[4] = {0, 0, 0, 0};
     const int nseg = device_leaf_groups(p.law, i, k, sg, adj_row);
     f32x4_t acc[NF];
@@ -438,7 +484,7 @@ __global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         u32x2_t a[2];
-        const int n = (f0 + f) * 16 + l16;
+        const int n = f * 16 + l16;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const bool ok = si[s][h] < nseg && n < p.b_out;
@@ -449,28 +495,24 @@ __global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
         acc[f] = mma(join(a[0], a[1]), xr, acc[f]);
       }
     }
-    if (!live) return;
+    // group k's columns c0 .. c0 + b_out - 1 into the ring (slot c mod RR; a
+    // run of 4 never wraps, RR and c0 + n being multiples of 4)
+    const uint32_t c0 = uint32_t(k) * uint32_t(p.b_out);
+    const int base = int(c0 % uint32_t(RR));
 #pragma unroll
-    for (int f = 0; f < NF; ++f) store4(st_w + l16 * SROW + f * 16 + 4 * g, acc[f]);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's staged rows are written
-    const int ncol = p.b_out - f0 * 16 < NF * 16 ? p.b_out - f0 * 16 : NF * 16;
-    const int cpr = ncol >> 2;
-    const int64_t col0 = int64_t(k) * p.b_out + f0 * 16;
-    for (int e = lane; e < 16 * cpr; e += 64) {
-      const int r = e / cpr, c = (e - r * cpr) * 4;
-      const int64_t rr = m0 + wave * 16 + r;
-      if (rr < count) {
-        Tout* dst = Y + (first + rr * stride) * p.ldy + col0 + c;
-        const Tout* src = st_w + r * SROW + c;
-        if constexpr (sizeof(Tout) == 2) *reinterpret_cast<u32x2_t*>(dst) = *reinterpret_cast<const u32x2_t*>(src);
-        else *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
-      }
+    for (int f = 0; f < NF; ++f) {
+      const int n = f * 16 + 4 * g;
+      int slot = base + n;
+      slot = slot >= RR ? slot - RR : slot;
+      if (live && n < p.b_out) store4(ring + l16 * RR + slot, acc[f]);
     }
   };
 
   // Output groups k0 .. k1 - 1: stage u + 1 is in registers (loaded one
   // step earlier) and stage u + 2 being loaded while stage u is multiplied
   // from LDS; steps past k1 - 1 re-load the last group and store nothing.
+  // A group's lines are stored after the barrier that follows its products,
+  // so that the wait for the next stage's loads does not also wait for them.
   const int nk = k1 - k0;
   auto kat = [&](int u) { return k0 + (u < nk ? u : nk - 1); };
   Set A, B;
@@ -481,15 +523,17 @@ __global__ __launch_bounds__(256, 3) void leaf_small_lds_kernel(SmallParams p) {
   __builtin_amdgcn_s_barrier();
   for (int u = 0; u < nk; u += 2) {
     load(kat(u + 2), A);
-    compute_store(0, kat(u), true);
+    mma_to_ring(0, kat(u), true);
     store(1, B);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
+    flush(kat(u), true);
     load(kat(u + 3), B);
-    compute_store(1, kat(u + 1), u + 1 < nk);
+    mma_to_ring(1, kat(u + 1), u + 1 < nk);
     store(0, A);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_s_barrier();
+    flush(kat(u + 1), u + 1 < nk);
   }
 }
 
@@ -597,8 +641,8 @@ int small_lds_nf(int64_t b_out) {
   return nf <= 2 ? 2 : nf <= 4 ? 4 : 8;
 }
 bool small_lds_ok(const aa_plan_s& plan, bool swiglu, bool fout) {
-  if (swiglu || plan.b_in > 32 || plan.b_in * plan.b_out > 4096) return false;
-  return lds_regions(int(plan.b_in), int(plan.b_out), small_lds_nf(plan.b_out), fout ? 4 : 2).total <= 65536;
+  if (swiglu || plan.b_in > 32 || plan.b_out > 128 || plan.b_in * plan.b_out > 4096) return false;
+  return lds_regions(int(plan.b_in), int(plan.b_out), fout ? 4 : 2).total <= 65536;
 }
 
 // The LDS-staged kernel: 64-row tiles, runs of output groups for about
@@ -606,10 +650,21 @@ bool small_lds_ok(const aa_plan_s& plan, bool swiglu, bool fout) {
 aa_status_t launch_small_lds(const aa_plan_s& plan, SmallParams p, int64_t mi, bool fout, hipStream_t stream) {
   p.mt_count = int32_t((mi + kLdsTM - 1) / kLdsTM);
   const int64_t base = int64_t(plan.q) * p.mt_count;
-  const int64_t want = int64_t(device_cu_count()) * 12;
+  const int64_t want = int64_t(device_cu_count()) * (plan.wg_per_cu > 0 ? plan.wg_per_cu : 12);
   int64_t chunks = (want + base - 1) / base;
   if (chunks > plan.q) chunks = plan.q;
   p.kc = int32_t((plan.q + chunks - 1) / chunks);
+  // runs that start on a 128-byte line: kc b_out columns a multiple of a line
+  const int le = fout ? 32 : 64;
+  int gcd = le, b = int(plan.b_out);
+  while (b) {
+    const int t = gcd % b;
+    gcd = b;
+    b = t;
+  }
+  const int step = le / gcd;
+  p.kc = (p.kc + step - 1) / step * step;
+  if (p.kc > plan.q) p.kc = plan.q;
   p.kchunks = int32_t((plan.q + p.kc - 1) / p.kc);
   const int64_t n_tiles = base * p.kchunks;
   if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
@@ -619,7 +674,7 @@ aa_status_t launch_small_lds(const aa_plan_s& plan, SmallParams p, int64_t mi, b
   const int NF = small_lds_nf(plan.b_out);
   const int wpt = int((plan.b_in * plan.b_out / 4 + 255) / 256);
   const dim3 grid{uint32_t(n_tiles), uint32_t((nf + NF - 1) / NF), 1};
-  const size_t lds = size_t(lds_regions(int(plan.b_in), int(plan.b_out), NF, fout ? 4 : 2).total);
+  const size_t lds = size_t(lds_regions(int(plan.b_in), int(plan.b_out), fout ? 4 : 2).total);
   if (S == 1) {
     if (NF == 2) go_small_lds<1, 2>(p, fout, wpt, grid, lds, stream);
     else if (NF == 4) go_small_lds<1, 4>(p, fout, wpt, grid, lds, stream);

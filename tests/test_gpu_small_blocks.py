@@ -81,7 +81,7 @@ def _int_case(law, q, M, d_in, d_out, kind, out_dt, seed, edges=None):
     (1, 33, 20, 12, "pos_mod", 0),         # q = 1: a plain product
     (4, 300, 512, 80, "pos_mod", 1),       # 128 x 20 blocks: 256-wide leaves
     (2, 200, 128, 248, "pos_mod", 1),      # 64 x 124 blocks: fragments over two launch rows
-    (4, 150, 128, 512, "pos_mod", 1),      # 32 x 128 blocks: the widest the LDS-staged kernel takes
+    (4, 150, 128, 384, "pos_mod", 1),      # 32 x 96 blocks: four weight runs a thread in the LDS-staged kernel
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_layout2_integer_exact(q, M, d_in, d_out, kind, pos, out_dt):
