@@ -715,6 +715,213 @@ __global__ __launch_bounds__(256, 2) void bwd_weight_kernel(BwdWeightParams P) {
   for (int sl = 0; sl < NSLOT; ++sl) flush(sl);
 }
 
+// Q_q weight gradient by a walk over the row types.  A workgroup owns a
+// 64-feature by 16 NC-column tile of output group k's blocks and walks every
+// row type i.  The rows of type i reach two blocks of column group k: the
+// diagonal W_kk through their input group k and W_ik through their own group
+// i (for i = k the one leaf is W_kk's).  A step is 64 tokens of one type: the
+// dY tile and both X tiles are staged once and multiplied into two
+// accumulator slots.  The W_kk slot lives to the end of the walk; the W_ik
+// slot is stored when type i's rows are done.  Each dY element is read once,
+// each X element once per column chunk (the group's other chunks, on the
+// same XCD, find it in L2), and no partial sums exist.
+template <typename Tout, int NC, int NSET>
+__global__ __launch_bounds__(256, 2) void bwd_weight_walk_kernel(BwdWeightParams P) {
+  constexpr int NTHR = 256;
+  constexpr int TK = 64;                              // tokens per step
+  constexpr int XCPR = 8;                             // 16-byte chunks of a 64-feature X row
+  constexpr int NXL = TK * XCPR / NTHR;               // loads per X tile and thread
+  constexpr int NYL = (TK * 2 * NC + NTHR - 1) / NTHR;
+  static_assert(NSET % 2 == 0, "set parity is the LDS buffer");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  __bf16* lds = reinterpret_cast<__bf16*>(smem);
+
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int g = lane >> 4, r = lane & 15;
+  const int b_in = P.b_in, q = P.q;
+  const int nstrips = P.b_out / 16;
+  const int x_elems = TK * P.ldsx, y_elems = TK * P.ldsy;
+  const int buf_elems = 2 * x_elems + y_elems;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+  Tout* __restrict__ dW = static_cast<Tout*>(P.dW);
+  const int64_t blk = int64_t(b_in) * P.b_out;
+
+  // item (output group k, column chunk c, feature chunk dc); each XCD takes a
+  // contiguous run, so one group's items share its L2
+  const int64_t n_items = int64_t(q) * P.nchunks * P.ndin;
+  const int64_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int64_t xlo = n_items * xcd / kNumXcd, xhi = n_items * (xcd + 1) / kNumXcd;
+  int64_t item = xlo + slot;
+  if (item >= xhi) return;
+  const int dc = int(item % P.ndin);
+  item /= P.ndin;
+  const int c = int(item % P.nchunks);
+  const int k = int(item / P.nchunks);
+  const int col0 = c * NC * 16;   // first column of the chunk inside group k
+  const int row0 = dc * 64;       // first input feature of the chunk inside a block
+  const TypeMap tmap(P.kind, q, P.off_mod_q, P.M, P.rows_per_type);
+
+  // steps: every type, every 64-token chunk of it (at least one, so that a
+  // type without rows still stores its zero block)
+  auto chunks_of = [&](int i) __attribute__((always_inline)) {
+    const int64_t n = tmap.rows(i).count;
+    return n > 0 ? int((n + TK - 1) / TK) : 1;
+  };
+  int n_steps = 0;
+  for (int i = 0; i < q; ++i) n_steps += chunks_of(i);
+
+  struct Step {
+    int i, tc;
+    bool live, last;   // last: type i's final chunk
+    TypeRows tr;
+  };
+  int cur_i = 0, cur_tc = 0, issued = 0;
+  auto setup = [&](Step& S) __attribute__((always_inline)) {
+    S.live = issued < n_steps;
+    const int nch = chunks_of(cur_i);
+    S.i = cur_i;
+    S.tc = cur_tc;
+    S.last = S.live && cur_tc == nch - 1;
+    S.tr = tmap.rows(cur_i);
+    if (S.live) {
+      ++issued;
+      if (++cur_tc == nch) {
+        cur_tc = 0;
+        if (issued < n_steps) ++cur_i;
+      }
+    }
+  };
+
+  // a void step (past the walk) and the own-group tile of type k read zeros
+  auto load = [&](const Step& S, u32x4_t (&xk)[NXL], u32x4_t (&xi)[NXL], u32x4_t (&yr)[NYL])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int l = 0; l < NXL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / XCPR, cc = ch - tk * XCPR;
+      const int64_t tt = int64_t(S.tc) * TK + tk;
+      const bool ok = S.live && tt < S.tr.count && row0 + cc * 8 < b_in;
+      const __bf16* row = P.X + (S.tr.first + tt * S.tr.stride) * P.ldx + row0 + cc * 8;
+      xk[l] = *reinterpret_cast<const u32x4_t*>(ok ? row + int64_t(k) * b_in : zero);
+      xi[l] = *reinterpret_cast<const u32x4_t*>(ok && S.i != k ? row + int64_t(S.i) * b_in : zero);
+    }
+#pragma unroll
+    for (int l = 0; l < NYL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
+      const int64_t tt = int64_t(S.tc) * TK + tk;
+      const bool ok = S.live && ch < TK * 2 * NC && tt < S.tr.count && col0 + cc * 8 < P.b_out;
+      const __bf16* src =
+          ok ? P.dY + (S.tr.first + tt * S.tr.stride) * P.ldy + int64_t(k) * P.b_out + col0 + cc * 8 : zero;
+      yr[l] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+  };
+  auto store_tiles = [&](const u32x4_t (&xk)[NXL], const u32x4_t (&xi)[NXL], const u32x4_t (&yr)[NYL], int buf)
+      __attribute__((always_inline)) {
+    __bf16* base = lds + buf * buf_elems;
+#pragma unroll
+    for (int l = 0; l < NXL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / XCPR, cc = ch - tk * XCPR;
+      *reinterpret_cast<u32x4_t*>(base + tile_row(tk) * P.ldsx + cc * 8) = xk[l];
+      *reinterpret_cast<u32x4_t*>(base + x_elems + tile_row(tk) * P.ldsx + cc * 8) = xi[l];
+    }
+#pragma unroll
+    for (int l = 0; l < NYL; ++l) {
+      const int ch = l * NTHR + int(threadIdx.x);
+      const int tk = ch / (2 * NC), cc = ch - tk * (2 * NC);
+      if (ch < TK * 2 * NC) *reinterpret_cast<u32x4_t*>(base + 2 * x_elems + tile_row(tk) * P.ldsy + cc * 8) = yr[l];
+    }
+  };
+
+  // slot 0: W_kk, slot 1: W_ik of the current type
+  f32x4_t acc[2][NC];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int b = 0; b < NC; ++b) acc[sl][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Transposing-read offsets as in the Q2 x Q2 kernel above; wave w owns the
+  // 16-feature fragment w of the chunk (a fragment past the block re-reads
+  // fragment 0 and is never stored).
+  const int trow = tile_row(8 * g + (r >> 2));
+  const int xoff = trow * P.ldsx + 4 * (r & 3);
+  const int yoff = trow * P.ldsy + 4 * (r & 3);
+  const bool fok = row0 + wave * 16 < b_in;
+  const int fofs = fok ? wave * 16 : 0;
+
+  // Store slot sl as block (j, k): lane (column r, g) holds rows 4g .. 4g+3
+  // of its fragment, half of a packed run.
+  auto flush = [&](int sl, int j) __attribute__((always_inline)) {
+    if (!fok) return;
+    const int row = row0 + fofs + 4 * g;
+#pragma unroll
+    for (int b = 0; b < NC; ++b) {
+      const int st = c * NC + b;
+      if (st < nstrips) {
+        const int64_t o = int64_t(st) * (b_in * 16) + (row >> 3) * 128 + r * 8 + (row & 7);
+        store4(dW + (int64_t(j) * q + k) * blk + o, acc[sl][b]);
+      }
+    }
+  };
+
+  auto compute = [&](const Step& S, int buf) __attribute__((always_inline)) {
+    if (!S.live) return;
+    __bf16* base = lds + buf * buf_elems;
+    Run<__bf16> bv[2][NC], ak[2], ai[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int b = 0; b < NC; ++b) {
+        __bf16* p = base + 2 * x_elems + yoff + 32 * h * P.ldsy + b * 16;
+        bv[h][b] = lds_run_tr(p, p + 8 * P.ldsy);
+      }
+      __bf16* pk = base + xoff + 32 * h * P.ldsx + fofs;
+      ak[h] = lds_run_tr(pk, pk + 8 * P.ldsx);
+      __bf16* pi = pk + x_elems;
+      ai[h] = lds_run_tr(pi, pi + 8 * P.ldsx);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < NC; ++b) acc[0][b] = mma(ak[h], bv[h][b], acc[0][b]);
+    if (S.i != k) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < NC; ++b) acc[1][b] = mma(ai[h], bv[h][b], acc[1][b]);
+      if (S.last) {
+        flush(1, S.i);
+#pragma unroll
+        for (int b = 0; b < NC; ++b) acc[1][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  u32x4_t xk[NSET][NXL], xi[NSET][NXL], yr[NSET][NYL];
+  Step S[NSET];
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) {
+    setup(S[s]);
+    load(S[s], xk[s], xi[s], yr[s]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int rounds = (n_steps + NSET - 1) / NSET;
+  for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      const int buf = s & 1;   // NSET is even, so set parity = step parity
+      store_tiles(xk[s], xi[s], yr[s], buf);
+      __syncthreads();
+      compute(S[s], buf);
+      const int sn = (s + NSET - 1) % NSET;
+      setup(S[sn]);
+      load(S[sn], xk[sn], xi[sn], yr[sn]);
+    }
+  }
+  flush(0, k);
+}
+
 // Add the parts' partial diagonal blocks (Q_q) into dW.
 template <typename Tout>
 __global__ __launch_bounds__(256) void bwd_weight_reduce_kernel(BwdWeightParams P) {
@@ -1050,8 +1257,21 @@ size_t bwd_data_workspace_bytes(const aa_plan_s& plan, int64_t M) {
   return size_t(d.nparts) * size_t(M) * size_t(plan.b_in) * sizeof(float);
 }
 
+// Q_q weight gradients walk the row types (bwd_weight_walk_kernel) when the
+// walk has a tile per CU or more (64 features x 64 columns of a group each),
+// and otherwise split the diagonal blocks' rows over parts
+// (bwd_weight_tile_kernel).  AA_TILE=630 / 631 force the walk / the parts.
+constexpr int kWalkNC = 4;
+bool weight_walk(const aa_plan_s& plan) {
+  if (plan.law != AA_LAW_QQ) return false;
+  if (plan.tile_override == 630) return true;
+  if (plan.tile_override == 631) return false;
+  const int64_t items = int64_t(plan.q) * ((plan.b_out + 16 * kWalkNC - 1) / (16 * kWalkNC)) * ((plan.b_in + 63) / 64);
+  return items >= device_cu_count();
+}
+
 size_t bwd_weight_workspace_bytes(const aa_plan_s& plan, int64_t M) {
-  if (plan.law != AA_LAW_QQ) return 0;
+  if (plan.law != AA_LAW_QQ || weight_walk(plan)) return 0;
   const int parts = tile_split(plan, M).P;
   if (parts == 1) return 0;
   return size_t(parts) * size_t(plan.q) * size_t(plan.b_in) * size_t(plan.b_out) * sizeof(float);
@@ -1136,6 +1356,32 @@ aa_status_t launch_bwd_data(const aa_plan_s& plan, const void* dY, const void* W
 aa_status_t launch_bwd_weight(const aa_plan_s& plan, const void* X, const void* dY, void* dW, int64_t M,
                               int64_t pos_offset, void* ws, hipStream_t stream) {
   const bool f32 = plan.out_dtype == AA_F32;
+  if (weight_walk(plan)) {
+    BwdWeightParams P{};
+    P.X = static_cast<const __bf16*>(X);
+    P.dY = static_cast<const __bf16*>(dY);
+    P.dW = dW;
+    P.M = M;
+    P.ldx = plan.d_in;
+    P.ldy = plan.d_out;
+    P.q = plan.q;
+    P.b_in = int32_t(plan.b_in);
+    P.b_out = int32_t(plan.b_out);
+    P.law = plan.law;
+    P.kind = plan.type_kind;
+    P.off_mod_q = int32_t(pos_offset % plan.q);
+    P.rows_per_type = plan.type_kind == AA_TYPES_BLOCK_ROWS ? M / plan.q : 0;
+    P.nchunks = int((plan.b_out / 16 + kWalkNC - 1) / kWalkNC);
+    P.ndin = int((plan.b_in + 63) / 64);
+    P.ldsx = lds_pitch(64);
+    P.ldsy = lds_pitch(16 * kWalkNC);
+    const size_t lds = size_t(2) * 64 * (2 * P.ldsx + P.ldsy) * 2;
+    const int64_t n_items = int64_t(plan.q) * P.nchunks * P.ndin;
+    const int grid = int((n_items + kNumXcd - 1) / kNumXcd * kNumXcd);
+    if (f32) launch((bwd_weight_walk_kernel<float, kWalkNC, 4>), dim3(grid), dim3(256), lds, stream, P);
+    else launch((bwd_weight_walk_kernel<__bf16, kWalkNC, 4>), dim3(grid), dim3(256), lds, stream, P);
+    return after_launch(stream, "bwd_weight_walk");
+  }
   if (plan.law == AA_LAW_QQ) {
     const TileSplit ts = tile_split(plan, M);
     if (ts.units >= (int64_t(1) << 31)) return fail(AA_ERR_UNSUPPORTED, "aa_project_bwd_weight: too many rows");

@@ -105,6 +105,26 @@ def test_gradients_integer_exact(law, q, M, d_in, d_out, kind):
     assert np.array_equal(dW, dW_ref), np.max(np.abs(dW - dW_ref))
 
 
+@pytest.mark.parametrize("path", ["630", "631"])
+@pytest.mark.parametrize("q,M,d_in,d_out,kind", [
+    (4, 300, 256, 192, "pos_mod"),
+    (8, 130, 1024, 384, "pos_mod"),
+    (4, 128, 512, 256, "block_rows"),
+    (32, 700, 2048, 4096, "pos_mod"),
+    (8, 5, 512, 512, "pos_mod"),
+])
+def test_weight_gradient_walk_and_parts_integer_exact(path, q, M, d_in, d_out, kind, monkeypatch):
+    """Q_q dW takes one of two kernels: the walk over the row types (one
+    workgroup per 64 x 64 tile of a group, no partial sums) or the parts of
+    the diagonal blocks' rows with a reduction.  AA_TILE=630 / 631 force each
+    on every shape; small integers make both exact, bit for bit."""
+    monkeypatch.setenv("AA_TILE", path)
+    say("bwd dW path", path, q, M, d_in, d_out, kind)
+    _, dW, _, dW_ref = _run("Qq", q, M, d_in, d_out, "f32", kind, 7 if kind == "pos_mod" else 0, 0, seed=9,
+                            ints=True)
+    assert np.array_equal(dW, dW_ref), np.max(np.abs(dW - dW_ref))
+
+
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_grad_input_widest_blocks(out_dt):
     """dX at the widest input blocks it takes (b_in = 512; dW stops at 384)."""
