@@ -537,6 +537,318 @@ __global__ __launch_bounds__(256, WPT == 4 ? 2 : 3) void leaf_small_lds_kernel(S
   }
 }
 
+// ---- 32 x 32 fragments: the same staging for output blocks wider than 64
+// columns (up to 128, e.g. the Qwen3-32B 20 x 100 blocks).  Measured at that
+// shape, the kernel above spends about half its time on LDS operand traffic
+// (each of its four waves reads both weight blocks of every group for 16
+// rows), and its per-group vector arithmetic (addresses, masks, divisions)
+// keeps the SIMDs busy more than half the time.  Here:
+//   - The MFMA is v_mfma_f32_32x32x16_bf16: wave (rh, ch) of a 64-row tile
+//     computes rows 32 rh .. 32 rh + 31 by columns 64 ch .. 64 ch + 63 (two
+//     32-column fragments), so each weight value read from LDS feeds 32 rows.
+//     Lane l of a fragment supplies 8 consecutive k (two runs of 4, k = 16 s +
+//     8 (l / 32)) of column l mod 32 (weights) and of row l mod 32
+//     (activations); register r of the result is column 8 (r / 4) + 4 (l / 32)
+//     + r mod 4 of row l mod 32.
+//   - Every LDS address a lane uses is fixed for the tile.  A stage's second
+//     weight block is staged as zeros when the leaf has fewer input groups
+//     (so no per-group masks), K positions past the leaf read a zero run, and
+//     staging lanes without a run write to a dummy cell.
+//   - The output ring is shared by the two column halves: it holds one line
+//     plus two groups of columns per row, so that a wave may write group u + 1
+//     while another still stores lines of group u.  After each group's
+//     barrier wave w stores the complete lines of rows 16 w .. 16 w + 15, four
+//     rows per store instruction with 16 lanes along each row, so that a store
+//     covers whole lines.
+// Loads run NSET - 1 groups ahead in register sets.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ inline f32x16_t mma32(const Run<__bf16>& a, const Run<__bf16>& b, f32x16_t acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v), __builtin_bit_cast(bf16x8_t, b.v),
+                                                 acc, 0, 0, 0);
+}
+
+// Ring columns: one line plus two groups, padded to 4 times an odd number so
+// that the 32 rows of a fragment's ring writes fall on distinct banks.
+__host__ __device__ inline int ring32_cols(int b_out, int out_bytes) {
+  int rr = (128 / out_bytes + 2 * b_out + 3) / 4 * 4;
+  if ((rr / 4) % 2 == 0) rr += 4;
+  return rr;
+}
+// LDS of the 32 x 32 fragment kernel (bytes): two weight stages, each of the
+// two blocks followed by a 16-byte zero run; two activation stages; the own
+// activation block; a 16-byte zero run and a 16-byte dummy cell; the ring.
+struct T32Regions {
+  int wst, xd, xo, zero, dummy, out, total;
+};
+__host__ __device__ inline T32Regions lds32_regions(int b_in, int b_out, int out_bytes) {
+  const int xb = kLdsTM * b_in * 2;
+  T32Regions r;
+  r.wst = 2 * b_in * b_out * 2 + 16;   // stage stride; stage b starts at b * wst
+  r.xd = 2 * r.wst;
+  r.xo = r.xd + 2 * xb;
+  r.zero = (r.xo + xb + 15) / 16 * 16;
+  r.dummy = r.zero + 16;
+  r.out = r.dummy + 16;
+  r.total = r.out + kLdsTM * ring32_cols(b_out, out_bytes) * out_bytes;
+  return r;
+}
+
+template <int KS, int WPT, int NSET, typename Tout>
+__global__ __launch_bounds__(256, 2) void leaf_small_t32_kernel(SmallParams p) {
+  static_assert(NSET % 2 == 0, "set parity is the LDS buffer");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  constexpr int XPT = 2;
+  constexpr int LE = 128 / int(sizeof(Tout));   // elements of a 128-byte line
+  constexpr int SZ = int(sizeof(Tout));
+  const int tid = int(threadIdx.x), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rh = wave & 1, chh = wave >> 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const __bf16* zero = reinterpret_cast<const __bf16*>(g_zero_runs);
+  const T32Regions R = lds32_regions(p.b_in, p.b_out, SZ);
+
+  const uint32_t xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const uint32_t per = p.n_tiles / kNumXcd, rem = p.n_tiles % kNumXcd;
+  uint32_t t = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  if (t >= p.n_tiles) return;
+  const int chunk = int(t % uint32_t(p.kchunks));
+  t /= uint32_t(p.kchunks);
+  const int mt = int(t % uint32_t(p.mt_count));
+  const int i = int(t / uint32_t(p.mt_count));
+  const int k0 = chunk * p.kc;
+  const int k1 = k0 + p.kc < p.q ? k0 + p.kc : p.q;
+  if (k0 >= k1) return;
+
+  int64_t first, stride, count;
+  if (p.kind == AA_TYPES_BLOCK_ROWS) {
+    first = int64_t(i) * p.rows_per_type;
+    stride = 1;
+    count = p.rows_per_type;
+  } else {
+    int64_t r0 = int64_t(i) - p.off_mod_q;
+    if (r0 < 0) r0 += p.q;
+    first = r0;
+    stride = p.q;
+    count = r0 < p.M ? (p.M - r0 + p.q - 1) / p.q : 0;
+  }
+  const int64_t m0 = int64_t(mt) * kLdsTM;
+  auto grow = [&](int r) -> int64_t { return m0 + r < count ? first + (m0 + r) * stride : 0; };
+
+  const int blk_el = p.b_in * p.b_out;
+  const int q4n = p.b_in >> 2;
+  const int n_wc = blk_el * 4 / 16;          // 16-byte runs of a stage's two blocks
+  const int n_xr = kLdsTM * q4n;             // 8-byte runs of a stage's activation segments
+  const uint64_t adj_row = p.law == AA_LAW_DIGRAPH ? p.adj[i] : 0;
+
+  // ---- staging: each thread's runs, fixed for the tile
+  int w_off[WPT], w_slot[WPT], w_dst[WPT];   // element offset in its block, block slot, LDS byte offset
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int c = tid + 256 * j;
+    const int e = c * 8;
+    w_slot[j] = c < n_wc ? (e >= blk_el ? 1 : 0) : 2;   // 2: no run
+    w_off[j] = c < n_wc ? e - (e >= blk_el ? blk_el : 0) : 0;
+    w_dst[j] = c < n_wc ? c * 16 : -1;
+  }
+  const __bf16* x_src[XPT];                  // the run's row and column inside an activation group
+  int x_dst[XPT];                            // LDS byte offset inside an activation stage
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const int r = tid + 256 * j;
+    const int row = r < n_xr ? r / q4n : 0;
+    const int xq = r < n_xr ? r - row * q4n : 0;
+    x_src[j] = p.X + grow(row) * p.ldx + 4 * xq;
+    x_dst[j] = r < n_xr ? r * 8 : -1;
+  }
+
+  struct Set {
+    u32x4_t w[WPT];
+    u32x2_t x[XPT];
+  };
+  // Group k: blocks (g0, k) and (g1, k) of the leaf's input groups, zeros for
+  // a slot past the leaf's group count, and the rows' activation segment k.
+  auto load = [&](int k, Set& st) __attribute__((always_inline)) {
+    int sg[4] = {0, 0, 0, 0};
+    const int nseg = __builtin_amdgcn_readfirstlane(device_leaf_groups(p.law, i, k, sg, adj_row));
+    // block numbers are the same in every lane: keep their products scalar
+    const int gb0 = __builtin_amdgcn_readfirstlane((nseg > 0 ? sg[0] : i) * p.q + k);
+    const int gb1 = __builtin_amdgcn_readfirstlane((nseg > 1 ? sg[1] : i) * p.q + k);
+    const __bf16* b0 = p.W0 + int64_t(gb0) * blk_el;
+    const __bf16* b1 = p.W0 + int64_t(gb1) * blk_el;
+    const int64_t xk = int64_t(__builtin_amdgcn_readfirstlane(k)) * p.b_in;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const __bf16* src = w_slot[j] < nseg ? (w_slot[j] == 0 ? b0 : b1) + w_off[j] : zero;
+      st.w[j] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const __bf16* src = x_dst[j] >= 0 ? x_src[j] + xk : zero;
+      st.x[j] = *reinterpret_cast<const u32x2_t*>(src);
+    }
+  };
+  auto store = [&](int buf, const Set& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+      *reinterpret_cast<u32x4_t*>(lds + (w_dst[j] >= 0 ? buf * R.wst + w_dst[j] : R.dummy)) = st.w[j];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j)
+      *reinterpret_cast<u32x2_t*>(lds + (x_dst[j] >= 0 ? R.xd + buf * kLdsTM * p.b_in * 2 + x_dst[j] : R.dummy)) =
+          st.x[j];
+  };
+
+  // the zero runs (the weight stages' tails and the activation one) and the
+  // type's own activation block, once per tile
+  if (tid < 3)
+    *reinterpret_cast<u32x4_t*>(lds + (tid < 2 ? tid * R.wst + 2 * blk_el * 2 : R.zero)) = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < XPT; ++j) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(x_dst[j] >= 0 ? x_src[j] + int64_t(i) * p.b_in : zero);
+    *reinterpret_cast<u32x2_t*>(lds + (x_dst[j] >= 0 ? R.xo + x_dst[j] : R.dummy)) = v;
+  }
+
+  // ---- operand addresses (LDS bytes), fixed for the tile: k-step s, half h
+  // covers leaf k 16 s + 8 hi + 4 h .. + 3, in input-group slot si at offset lk.
+  // Weights: relative to the stage; past the leaf's K (si >= 2) or past the
+  // block's columns, the stage's zero tail.  Activations: per stage buffer
+  // (slot 0: the own block, slot 1: the stage's segment, beyond: a zero run).
+  int a_ofs[KS][2][2], b_ofs[2][KS][2];
+  const int row_l = 32 * rh + l32;   // this lane's tile row (B operand and outputs)
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kk = 16 * s + 8 * hi + 4 * h;
+      const int si = kk / p.b_in, lk = kk - si * p.b_in;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int n = 64 * chh + 32 * f + l32;
+        a_ofs[s][h][f] = si < 2 && n < p.b_out ? (si * blk_el + int(v2_run(p.b_in, p.b_out, lk >> 2, n))) * 2
+                                               : 2 * blk_el * 2;
+      }
+      const int xo = (row_l * p.b_in + lk) * 2;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        b_ofs[b][s][h] = si == 0 ? R.xo + xo : si == 1 ? R.xd + b * kLdsTM * p.b_in * 2 + xo : R.zero;
+    }
+
+  // ---- ring: this lane's row for its results; the 8 (fragment, register
+  // quad) column offsets; the dummy cell for columns past the block
+  const int RR = ring32_cols(p.b_out, SZ);
+  const int ring_row = R.out + row_l * RR * SZ;
+  int r_col[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r_col[f][j] = 64 * chh + 32 * f + 8 * j + 4 * hi;
+
+  // ---- stores: row group rg (0..3) of this wave's 16 rows is tile row
+  // 16 wave + 4 rg + lane / 16; lane mod 16 picks the run along the row
+  Tout* Y = static_cast<Tout*>(p.Y);
+  const uint32_t ph = uint32_t((reinterpret_cast<uintptr_t>(p.Y) / sizeof(Tout)) % LE);
+  uint32_t written = uint32_t(k0) * uint32_t(p.b_out);   // every row holds columns < written
+  // ring slots of column `written` and of the next group's first column, kept
+  // by addition (a division per group would cost more than the group's
+  // address arithmetic)
+  uint32_t wbase = written % uint32_t(RR), cbase = wbase;
+  Tout* f_row[4];
+  bool f_ok[4];
+  int f_ring[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    const int tr = 16 * wave + 4 * rg + (lane >> 4);
+    f_ok[rg] = m0 + tr < count;
+    f_row[rg] = Y + (f_ok[rg] ? first + (m0 + tr) * stride : 0) * p.ldy;
+    f_ring[rg] = R.out + tr * RR * SZ;
+  }
+  const int run_l = lane & 15;
+
+  auto flush = [&](int k, bool live) __attribute__((always_inline)) {
+    const uint32_t end = uint32_t(k) * uint32_t(p.b_out) + uint32_t(p.b_out);
+    const uint32_t lb = (end + ph) / LE * LE;
+    const uint32_t upto = !live ? written : k == k1 - 1 ? end : lb >= written + ph ? lb - ph : written;
+    const int runs = int(upto - written) >> 2;
+    for (int m = 0; m < runs; m += 16) {
+      const int run = m + run_l;
+      int sl = int(wbase) + 4 * run;
+      sl = sl >= RR ? sl - RR : sl;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const unsigned char* src = lds + f_ring[rg] + sl * SZ;
+        Tout* dst = f_row[rg] + written + 4 * run;
+        if constexpr (SZ == 2) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
+          if (f_ok[rg] && run < runs) *reinterpret_cast<u32x2_t*>(dst) = v;
+        } else {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
+          if (f_ok[rg] && run < runs) *reinterpret_cast<u32x4_t*>(dst) = v;
+        }
+      }
+    }
+    wbase += upto - written;
+    wbase = wbase >= uint32_t(RR) ? wbase - uint32_t(RR) : wbase;
+    written = upto;
+  };
+  auto mma_to_ring = [&](int buf, int k, bool live) __attribute__((always_inline)) {
+    f32x16_t acc[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
+    const unsigned char* wl = lds + buf * R.wst;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const Run<__bf16> xr = join(*reinterpret_cast<const u32x2_t*>(lds + b_ofs[buf][s][0]),
+                                  *reinterpret_cast<const u32x2_t*>(lds + b_ofs[buf][s][1]));
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const Run<__bf16> ar = join(*reinterpret_cast<const u32x2_t*>(wl + a_ofs[s][0][f]),
+                                    *reinterpret_cast<const u32x2_t*>(wl + a_ofs[s][1][f]));
+        acc[f] = mma32(ar, xr, acc[f]);
+      }
+    }
+    if (!live) return;
+    const int base = int(cbase);
+    cbase += uint32_t(p.b_out);
+    cbase = cbase >= uint32_t(RR) ? cbase - uint32_t(RR) : cbase;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int sl = base + r_col[f][j];
+        sl = sl >= RR ? sl - RR : sl;
+        const int at = r_col[f][j] < p.b_out ? ring_row + sl * SZ : R.dummy;
+        store4(reinterpret_cast<Tout*>(lds + at),
+               f32x4_t{acc[f][4 * j], acc[f][4 * j + 1], acc[f][4 * j + 2], acc[f][4 * j + 3]});
+      }
+  };
+
+  // Output groups k0 .. k1 - 1, NSET per round: stage v is in register set
+  // v mod NSET from NSET - 1 steps before its products and in LDS buffer
+  // v mod 2 from the barrier before them.  Steps past k1 - 1 re-load the
+  // last group and store nothing.
+  const int nk = k1 - k0;
+  auto kat = [&](int u) { return k0 + (u < nk ? u : nk - 1); };
+  Set S[NSET];
+#pragma unroll
+  for (int s = 0; s < NSET - 1; ++s) load(kat(s), S[s]);
+  store(0, S[0]);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  for (int u = 0; u < nk; u += NSET) {
+#pragma unroll
+    for (int s = 0; s < NSET; ++s) {
+      load(kat(u + s + NSET - 1), S[(s + NSET - 1) % NSET]);
+      mma_to_ring(s & 1, kat(u + s), u + s < nk);
+      store((s + 1) & 1, S[(s + 1) % NSET]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      flush(kat(u + s), u + s < nk);
+    }
+  }
+}
+
 // Thread c moves run c (4 elements) of the version-2 layout from or to the
 // row-major weight.
 template <typename T>
@@ -645,6 +957,82 @@ bool small_lds_ok(const aa_plan_s& plan, bool swiglu, bool fout) {
   return lds_regions(int(plan.b_in), int(plan.b_out), fout ? 4 : 2).total <= 65536;
 }
 
+template <typename K>
+void go_t32_one(K kernel, const SmallParams& p, dim3 grid, size_t lds, hipStream_t s) {
+  // beyond 64 KB (the one-workgroup-per-CU tuning mode) the launch needs the attribute
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              int(lds));
+  launch(kernel, grid, dim3{256, 1, 1}, uint32_t(lds), s, p);
+}
+#ifndef AA_T32_NSET
+#define AA_T32_NSET 4
+#endif
+template <int KS>
+void go_small_t32(const SmallParams& p, bool fout, int wpt, dim3 grid, size_t lds, hipStream_t s) {
+  constexpr int NS = AA_T32_NSET;
+  if (wpt <= 2) {
+    if (fout) go_t32_one(leaf_small_t32_kernel<KS, 2, NS, float>, p, grid, lds, s);
+    else go_t32_one(leaf_small_t32_kernel<KS, 2, NS, __bf16>, p, grid, lds, s);
+  } else {
+    if (fout) go_t32_one(leaf_small_t32_kernel<KS, 4, NS, float>, p, grid, lds, s);
+    else go_t32_one(leaf_small_t32_kernel<KS, 4, NS, __bf16>, p, grid, lds, s);
+  }
+}
+
+// The 32 x 32 fragment kernel takes what the LDS-staged one does when the
+// output blocks are wider than 64 columns (AA_TILE=611 keeps those on the
+// 16 x 16 one).
+bool small_t32_ok(const aa_plan_s& plan, bool swiglu, bool fout) {
+  if (swiglu || plan.b_in > 32 || plan.b_out <= 64 || plan.b_out > 128 || plan.b_in * plan.b_out > 4096) return false;
+  if (plan.tile_override == 611) return false;
+  return lds32_regions(int(plan.b_in), int(plan.b_out), fout ? 4 : 2).total <= 65536;
+}
+
+// Runs of output groups that start on a 128-byte line: kc b_out columns a
+// multiple of a line.
+int32_t line_aligned_kc(int32_t kc, int64_t b_out, bool fout, int32_t q) {
+  const int le = fout ? 32 : 64;
+  int gcd = le, b = int(b_out);
+  while (b) {
+    const int t = gcd % b;
+    gcd = b;
+    b = t;
+  }
+  const int step = le / gcd;
+  kc = (kc + step - 1) / step * step;
+  return kc > q ? q : kc;
+}
+
+// The 32 x 32 fragment kernel: 64-row tiles, about four tiles per CU in all
+// (AA_WG_PER_CU sets the count); AA_TILE=612 pads its LDS to hold the grid
+// to one workgroup per CU.
+aa_status_t launch_small_t32(const aa_plan_s& plan, SmallParams p, int64_t mi, bool fout, hipStream_t stream) {
+  p.mt_count = int32_t((mi + kLdsTM - 1) / kLdsTM);
+  const int64_t base = int64_t(plan.q) * p.mt_count;
+  const int64_t want = int64_t(device_cu_count()) * (plan.wg_per_cu > 0 ? plan.wg_per_cu : 4);
+  int64_t chunks = (want + base - 1) / base;
+  if (chunks > plan.q) chunks = plan.q;
+  p.kc = line_aligned_kc(int32_t((plan.q + chunks - 1) / chunks), plan.b_out, fout, plan.q);
+  p.kchunks = int32_t((plan.q + p.kc - 1) / p.kc);
+  const int64_t n_tiles = base * p.kchunks;
+  if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
+  p.n_tiles = uint32_t(n_tiles);
+  const int nseg_max = plan.q > 1 ? 2 : 1;
+  const int KS = int((nseg_max * plan.b_in + 15) / 16);
+  const int wpt = int((plan.b_in * plan.b_out / 4 + 255) / 256);
+  const dim3 grid{uint32_t(n_tiles), 1, 1};
+  size_t lds = size_t(lds32_regions(int(plan.b_in), int(plan.b_out), fout ? 4 : 2).total);
+  if (plan.tile_override == 612) lds = lds < 90 * 1024 ? 90 * 1024 : lds;
+  switch (KS) {
+    case 1: go_small_t32<1>(p, fout, wpt, grid, lds, stream); break;
+    case 2: go_small_t32<2>(p, fout, wpt, grid, lds, stream); break;
+    case 3: go_small_t32<3>(p, fout, wpt, grid, lds, stream); break;
+    default: go_small_t32<4>(p, fout, wpt, grid, lds, stream); break;
+  }
+  return after_launch(stream, "leaf_small_t32");
+}
+
 // The LDS-staged kernel: 64-row tiles, runs of output groups for about
 // twelve workgroups per CU in all, fragments split over blockIdx.y by 8.
 aa_status_t launch_small_lds(const aa_plan_s& plan, SmallParams p, int64_t mi, bool fout, hipStream_t stream) {
@@ -653,18 +1041,7 @@ aa_status_t launch_small_lds(const aa_plan_s& plan, SmallParams p, int64_t mi, b
   const int64_t want = int64_t(device_cu_count()) * (plan.wg_per_cu > 0 ? plan.wg_per_cu : 12);
   int64_t chunks = (want + base - 1) / base;
   if (chunks > plan.q) chunks = plan.q;
-  p.kc = int32_t((plan.q + chunks - 1) / chunks);
-  // runs that start on a 128-byte line: kc b_out columns a multiple of a line
-  const int le = fout ? 32 : 64;
-  int gcd = le, b = int(plan.b_out);
-  while (b) {
-    const int t = gcd % b;
-    gcd = b;
-    b = t;
-  }
-  const int step = le / gcd;
-  p.kc = (p.kc + step - 1) / step * step;
-  if (p.kc > plan.q) p.kc = plan.q;
+  p.kc = line_aligned_kc(int32_t((plan.q + chunks - 1) / chunks), plan.b_out, fout, plan.q);
   p.kchunks = int32_t((plan.q + p.kc - 1) / p.kc);
   const int64_t n_tiles = base * p.kchunks;
   if (n_tiles > int64_t(0x7fffffff)) return fail(AA_ERR_UNSUPPORTED, "aa_project_fwd: too many tiles");
@@ -736,6 +1113,9 @@ aa_status_t launch_small_gemm(const aa_plan_s& plan, const LeafCall& call, hipSt
                                                                          : kSmallStoreDefault;
   // plain projections with leaves of at most 64 k and blocks of at most 4096
   // elements: the LDS-staged kernel (AA_TILE=610 forces the register kernel)
+  if (small_t32_ok(plan, call.swiglu, fout) && plan.tile_override != 610 &&
+      !(plan.tile_override >= 600 && plan.tile_override < 604))
+    return launch_small_t32(plan, p, mi, fout, stream);
   if (small_lds_ok(plan, call.swiglu, fout) && plan.tile_override != 610 &&
       !(plan.tile_override >= 600 && plan.tile_override < 604))
     return launch_small_lds(plan, p, mi, fout, stream);

@@ -100,32 +100,69 @@ def test_layout2_integer_exact(q, M, d_in, d_out, kind, pos, out_dt):
     assert torch.equal(Y.cpu().view(iv), want.view(iv))
 
 
-@pytest.mark.parametrize("q,M,d_in,d_out,pos", [(8, 1000, 160, 800, 5), (3, 301, 36, 60, 2), (4, 150, 96, 240, 3)])
-def test_layout2_register_and_lds_kernels_agree(q, M, d_in, d_out, pos, monkeypatch):
-    """Leaves of at most 64 k take the LDS-staged kernel; a plan created with
-    AA_TILE=610 takes the per-wave register kernel instead.  Both sum the same
-    products in the same order, so their outputs are equal bit for bit."""
-    say("layout2 register vs LDS kernel", q, M, d_in, d_out, pos)
+def _three_paths(q, M, d_in, d_out, pos, X, W, out_dt, monkeypatch):
+    """Y from each kernel a plain layout-2 call can take: the default, the
+    16 x 16 LDS-staged kernel (AA_TILE=611) and the per-wave register kernel
+    (AA_TILE=610).  Plans read AA_TILE when they are created."""
+    outs = []
+    for tile in (None, "611", "610"):
+        if tile is None:
+            monkeypatch.delenv("AA_TILE", raising=False)
+        else:
+            monkeypatch.setenv("AA_TILE", tile)
+        plan = aa.aa_plan_create("Qq", q, d_in, d_out, "pos_mod", 0, "bf16", out_dt)
+        Y = torch.full((M, d_out), float("nan"), dtype=TD[out_dt], device=DEV)
+        aa.aa_project_fwd(plan, X, aa.pack(plan, W), Y, None, pos)
+        outs.append(Y)
+    monkeypatch.delenv("AA_TILE", raising=False)
+    torch.cuda.synchronize()
+    return outs
+
+
+SHAPES_3 = [
+    (8, 1000, 160, 800, 5),   # 20 x 100 blocks (the Qwen3-32B block shape): 32 x 32 fragments by default
+    (3, 301, 36, 252, 2),     # 12 x 84: 32 x 32 fragments, one k-step pair
+    (4, 150, 96, 480, 3),     # 24 x 120
+    (1, 70, 20, 100, 0),      # q = 1
+    (3, 301, 36, 60, 2),      # 12 x 20: the 16 x 16 LDS kernel by default
+    (4, 150, 96, 240, 3),     # 24 x 60
+]
+
+
+@pytest.mark.parametrize("q,M,d_in,d_out,pos", SHAPES_3)
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_layout2_kernels_integer_exact(q, M, d_in, d_out, pos, out_dt, monkeypatch):
+    """Small integers (every sum exact in fp32) through all three kernels:
+    each equals the oracle bit for bit."""
+    say("layout2 three kernels int-exact", q, M, d_in, d_out, pos, out_dt)
+    X = inp.small_integers((M, d_in), 61 + q, dtype=torch.bfloat16, device=DEV)
+    W = inp.small_integers((d_in, d_out), 62 + q, dtype=torch.bfloat16, device=DEV)
+    ref = oracle.project(host(X), host(W), "Qq", q, oracle.types_pos_mod(M, q, pos))
+    want = torch.from_numpy(ref).float().to(TD[out_dt])
+    iv = torch.int16 if out_dt == "bf16" else torch.int32
+    for Y in _three_paths(q, M, d_in, d_out, pos, X, W, out_dt, monkeypatch):
+        assert torch.equal(Y.cpu().view(iv), want.view(iv))
+
+
+@pytest.mark.parametrize("q,M,d_in,d_out,pos", SHAPES_3)
+def test_layout2_kernels_float_parity(q, M, d_in, d_out, pos, monkeypatch):
+    """Gaussian inputs through all three kernels, fp32 output: each within the
+    parity bounds of the oracle; the register and 16 x 16 LDS kernels sum the
+    same products in the same order, so those two agree bit for bit."""
+    say("layout2 three kernels parity", q, M, d_in, d_out, pos)
     X = inp.gaussian((M, d_in), 41 + q, 1.0, torch.bfloat16, DEV)
     W = inp.gaussian((d_in, d_out), 42 + q, d_in ** -0.5, torch.bfloat16, DEV)
-    plan = aa.aa_plan_create("Qq", q, d_in, d_out, "pos_mod", 0, "bf16", "f32")
-    monkeypatch.setenv("AA_TILE", "610")
-    plan_reg = aa.aa_plan_create("Qq", q, d_in, d_out, "pos_mod", 0, "bf16", "f32")
-    monkeypatch.delenv("AA_TILE")
-    P = aa.pack(plan, W)
-    Y = torch.full((M, d_out), float("nan"), device=DEV)
-    Y2 = torch.full((M, d_out), float("nan"), device=DEV)
-    aa.aa_project_fwd(plan, X, P, Y, None, pos)
-    aa.aa_project_fwd(plan_reg, X, P, Y2, None, pos)
-    torch.cuda.synchronize()
-    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
     ref = oracle.project(host(X), host(W), "Qq", q, oracle.types_pos_mod(M, q, pos))
-    assert_parity(host(Y), ref, False, f"layout2 LDS kernel q={q} {d_in}->{d_out}")
+    Yd, Yl, Yr = _three_paths(q, M, d_in, d_out, pos, X, W, "f32", monkeypatch)
+    assert torch.equal(Yl.view(torch.int32), Yr.view(torch.int32))
+    for name, Y in (("default", Yd), ("lds16", Yl), ("register", Yr)):
+        assert_parity(host(Y), ref, False, f"layout2 {name} q={q} {d_in}->{d_out}")
 
 
-def test_layout2_digraph_integer_exact():
-    """A digraph table with 8 x 28 blocks: non-edge output groups are zero."""
-    q, M, d_in, d_out = 6, 250, 48, 168
+@pytest.mark.parametrize("q,M,d_in,d_out", [(6, 250, 48, 168), (4, 300, 64, 400)])
+def test_layout2_digraph_integer_exact(q, M, d_in, d_out):
+    """Digraph tables with 8 x 28 and 16 x 100 blocks (the second on the 32 x
+    32 fragment kernel): non-edge output groups are zero."""
     edges = inp.random_edges(q, 0.4, 23)
     say("layout2 digraph", q, M, d_in, d_out, len(edges))
     plan, X, W = _int_case(None, q, M, d_in, d_out, "pos_mod", "f32", 5, edges)
