@@ -180,11 +180,11 @@ class KernelTimer:
 
 
 def kernel_source_hash():
-    """Hash of the forward kernels' sources (aa_kernels.hip, aa_small.hip and
-    the device header they include): stored traffic figures are used only
-    while it matches."""
+    """Hash of the kernels' sources (aa_kernels.hip, aa_small.hip,
+    aa_backward.hip and the device header they include): stored traffic
+    figures are used only while it matches."""
     h = hashlib.sha256()
-    for name in ("aa_kernels.hip", "aa_small.hip", "aa_device.h"):
+    for name in ("aa_kernels.hip", "aa_small.hip", "aa_backward.hip", "aa_device.h"):
         with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -546,7 +546,8 @@ def bench_projection(args, torch, inp, aa, dev, wl, digraph_density=None):
             "config": {"workload": name, "M": M, "d_in": D, "d_out": F, "q": q,
                        "law": wl.law if edges is None else "digraph", "type_map": "pos mod q", "input_sets": n_sets,
                        **({} if edges is None else {"edges": len(edges)})},
-            "roofline": roofline(per_set, ms_k), "kernel_ms": round(ms_k, 5), "kernel_spread": kt.spread(0),
+            "roofline": roofline(per_set, ms_k, traffic_for(f"project_{wl.name}") if edges is None else None),
+            "kernel_ms": round(ms_k, 5), "kernel_spread": kt.spread(0),
             "projection_alone": alone,
             "dense": dense,
             "exec_tflops": round((exec_flops(M, D, F, wl.law, q) if edges is None else
@@ -620,8 +621,10 @@ def bench_backward(args, torch, inp, aa, dev, which):
     for c, (n, kind) in enumerate(calls):
         ms = kt.ms(c)
         di, do = dims[n]
+        tkey = f"{'bwd_data' if kind == 'dX' else 'bwd_weight'}_{which}" if len(shapes) == 1 else None
         parts[f"{n}_{kind}"] = {"ms": round(ms, 5), **kt.spread(c),
-                                "roofline": roofline(2 * (M * di + di * do + M * do), ms),
+                                "roofline": roofline(2 * (M * di + di * do + M * do), ms,
+                                                     traffic_for(tkey) if tkey else None),
                                 "exec_tflops": round(exec_flops(M, di, do, "Qq", q) / (ms * 1e-3) / 1e12, 2)}
     dense_flops = sum(2 * 2.0 * M * di * do for _, di, do in shapes)
     dense = None
@@ -888,7 +891,7 @@ def projection_part(torch, inp, aa, dev, wl, steps, warmup, dense=True):
             "layout": aa.aa_packed_layout_version(plan), "steps": steps, "ms": round(ms, 5), **kt.spread(0),
             "dense_equiv_tflops": round(2.0 * M * D * F / ms / 1e9, 2),
             "exec_tflops": round(exec_flops(M, D, F, wl.law, q) / ms / 1e9, 2),
-            "roofline": roofline(per_set, ms)}
+            "roofline": roofline(per_set, ms, traffic_for(f"project_{wl.name}"))}
     if dense:
         Wd = inp.gaussian((D, F), 999, D ** -0.5, torch.bfloat16, dev)
         X0 = sets[0][0]
