@@ -104,6 +104,7 @@ def test_pack_roundtrip_and_layout(law, q, d_in, d_out, dt):
     ("Qq", 1, 40, 64, 48, "pos_mod", "bf16"),
     ("Qq", 3, 700, 384, 576, "pos_mod", "bf16"),       # q = 3 (a law the pages plan next)
     ("Qq", 5, 333, 320, 160, "pos_mod", "bf16"),       # q = 5, 64 x 32 blocks
+    ("Qq", 16, 1599, 1024, 3072, "pos_mod", "bf16"),   # 64 x 192 blocks on the persistent kernel, ragged m-tiles
 ])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])
 def test_integer_exact(law, q, M, d_in, d_out, kind, in_dt, out_dt):
