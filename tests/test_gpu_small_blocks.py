@@ -124,6 +124,7 @@ SHAPES_3 = [
     (3, 301, 36, 252, 2),     # 12 x 84: 32 x 32 fragments, one k-step pair
     (4, 150, 96, 480, 3),     # 24 x 120
     (1, 70, 20, 100, 0),      # q = 1
+    (8, 5, 160, 800, 3),      # fewer rows than types: most types empty
     (3, 301, 36, 60, 2),      # 12 x 20: the 16 x 16 LDS kernel by default
     (4, 150, 96, 240, 3),     # 24 x 60
 ]
@@ -157,6 +158,24 @@ def test_layout2_kernels_float_parity(q, M, d_in, d_out, pos, monkeypatch):
     assert torch.equal(Yl.view(torch.int32), Yr.view(torch.int32))
     for name, Y in (("default", Yd), ("lds16", Yl), ("register", Yr)):
         assert_parity(host(Y), ref, False, f"layout2 {name} q={q} {d_in}->{d_out}")
+
+
+@pytest.mark.parametrize("q,M,d_in,d_out,out_dt", [(8, 560, 160, 800, "bf16"), (8, 560, 160, 800, "f32"),
+                                                   (3, 201, 36, 252, "bf16")])
+def test_layout2_block_rows_integer_exact(q, M, d_in, d_out, out_dt):
+    """Block-row typing on the default kernels (the 32 x 32 fragment kernel
+    for bf16 20 x 100 and 12 x 84 blocks; fp32 20 x 100 outputs need more LDS
+    and take the 16 x 16 kernel): contiguous rows per type, ragged m-tiles
+    (70 and 67 rows per type)."""
+    say("layout2 block rows", q, M, d_in, d_out, out_dt)
+    plan, X, W = _int_case("Qq", q, M, d_in, d_out, "block_rows", out_dt, 29)
+    Y = torch.full((M, d_out), float("nan"), dtype=TD[out_dt], device=DEV)
+    aa.aa_project_fwd(plan, X, aa.pack(plan, W), Y, None, 0)
+    torch.cuda.synchronize()
+    ref = oracle.project(host(X), host(W), "Qq", q, oracle.types_block_rows(M, q))
+    want = torch.from_numpy(ref).float().to(TD[out_dt])
+    iv = torch.int16 if out_dt == "bf16" else torch.int32
+    assert torch.equal(Y.cpu().view(iv), want.view(iv))
 
 
 @pytest.mark.parametrize("q,M,d_in,d_out", [(6, 250, 48, 168), (4, 300, 64, 400)])
