@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libaa.so")
 
-SOURCES = ["aa_plan.cpp", "aa_api.cpp", "aa_kernels.hip", "aa_backward.hip", "aa_small.hip"]
+SOURCES = ["aa_plan.cpp", "aa_api.cpp", "aa_kernels.hip", "aa_backward.hip", "aa_small.hip", "aa_tile32.hip"]
 ARCH = "gfx950"
 
 # Device-code flags.  Packed fp32 arithmetic is switched off for every HIP

@@ -70,6 +70,12 @@ bool small_layout_ok(aa_law_t law, aa_type_kind_t kind, aa_dtype_t in_dtype, int
 aa_status_t launch_small_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream);
 aa_status_t launch_pack_v2(const aa_plan_s& plan, const void* src, void* dst, bool unpack, hipStream_t stream);
 
+// SwiGLU gate/up of leaves with many rows per type (aa_tile32.hip): bf16
+// input, Q_q or Q2 x Q2, position or block-row typing, b_in a multiple of 32.
+// rows_max: the rows of the largest row type; taken from 257 rows per type.
+bool tile32_ok(const aa_plan_s& plan, const LeafCall& call, int64_t rows_max);
+aa_status_t launch_tile32(const aa_plan_s& plan, const LeafCall& call, int64_t rows_max, hipStream_t stream);
+
 // W1 non-null: SwiGLU gate/up (W gate, W1 up, y = silu(x W) * (x W1)); bf16
 // input and input blocks of at most 256 rows (decode_swiglu_ok).
 aa_status_t launch_decode(const aa_plan_s& plan, const void* x, const void* W, const void* W1, void* y,

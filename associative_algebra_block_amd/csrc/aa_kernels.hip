@@ -2327,18 +2327,21 @@ int choose_kstream(const aa_plan_s& plan, int64_t M, bool swiglu) {
   return fits(4) ? 4 : (fits(2) ? 2 : -1);
 }
 
-// Large-tile kernel for leaves with many rows per type (override 500).
+// Large-tile kernels for leaves with many rows per type (override 500; 501
+// keeps SwiGLU gate/up on the 16 x 16 tile kernel instead of the 32 x 32 one).
 bool choose_tile(const aa_plan_s& plan, int64_t M) {
   if (plan.in_dtype != AA_BF16 || plan.law == AA_LAW_DIGRAPH) return false;
   if (plan.type_kind != AA_TYPES_POS_MOD && plan.type_kind != AA_TYPES_BLOCK_ROWS) return false;
   if (plan.b_in % 64) return false;
-  if (plan.tile_override == 500) return true;
+  if (plan.tile_override == 500 || plan.tile_override == 501) return true;
   if (plan.tile_override >= 0) return false;
   return rows_per_type_max(plan, M) > 256;
 }
 
 aa_status_t launch_leaf_gemm(const aa_plan_s& plan, const LeafCall& call, hipStream_t stream) {
   if (plan.layout_version == 2) return launch_small_gemm(plan, call, stream);
+  if (tile32_ok(plan, call, rows_per_type_max(plan, call.M)))
+    return launch_tile32(plan, call, rows_per_type_max(plan, call.M), stream);
   if (choose_tile(plan, call.M)) {
     LeafParams p{};
     p.X = call.X;
