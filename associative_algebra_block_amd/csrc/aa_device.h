@@ -103,7 +103,10 @@ __device__ inline void store4_nt(__bf16* p, f32x4_t v) {
 }
 __device__ inline void store4_nt(float* p, f32x4_t v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p)); }
 
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g u / (1 + e^-g), with the hardware exponential and
+// reciprocal (a few ulp of fp32; the correctly rounded division costs about
+// ten instructions per output, which dominated the SwiGLU epilogues).
+__device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
 // Input groups of leaf (type i, output group k); returns their count (<= 4).
 // For a digraph, adj_row has bit k set for the edges i -> k; a leaf of a
