@@ -181,10 +181,10 @@ class KernelTimer:
 
 def kernel_source_hash():
     """Hash of the kernels' sources (aa_kernels.hip, aa_small.hip,
-    aa_backward.hip and the device header they include): stored traffic
-    figures are used only while it matches."""
+    aa_backward.hip, aa_tile32.hip and the device header they include): stored
+    traffic figures are used only while it matches."""
     h = hashlib.sha256()
-    for name in ("aa_kernels.hip", "aa_small.hip", "aa_backward.hip", "aa_device.h"):
+    for name in ("aa_kernels.hip", "aa_small.hip", "aa_backward.hip", "aa_tile32.hip", "aa_device.h"):
         with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

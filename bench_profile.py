@@ -33,10 +33,10 @@ COPY_BYTES = 1 << 30   # bench.py --calibration-copy copies 2^28 int32
 
 def kernel_source_hash():
     """Hash of the kernels' sources (aa_kernels.hip, aa_small.hip,
-    aa_backward.hip and the device header they include): stored traffic
-    figures are used only while it matches."""
+    aa_backward.hip, aa_tile32.hip and the device header they include): stored
+    traffic figures are used only while it matches."""
     h = hashlib.sha256()
-    for name in ("aa_kernels.hip", "aa_small.hip", "aa_backward.hip", "aa_device.h"):
+    for name in ("aa_kernels.hip", "aa_small.hip", "aa_backward.hip", "aa_tile32.hip", "aa_device.h"):
         with open(os.path.join(HERE, "associative_algebra_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -126,7 +126,7 @@ def write_counters(a, src):
         d[cn] = v
     names = sorted({cn for d in per.values() for cn in d if not cn.startswith("_")})
     lines = [f"# Counters: {a.name}", "", f"Command (run from /tmp with TMPDIR=/tmp): `{a.cmd_counters}`", "",
-             f"Kernel sources (aa_kernels.hip, aa_small.hip, aa_backward.hip, aa_device.h) sha256[:16]: `{src}`", "",
+             f"Kernel sources (aa_kernels.hip, aa_small.hip, aa_backward.hip, aa_tile32.hip, aa_device.h) sha256[:16]: `{src}`", "",
              "Mean per dispatch.  SQ counters read one of the 32 shader engines (8 CUs, 32 SIMDs).  "
              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (32 x GRBM_GUI_ACTIVE); wait share = SQ_WAIT_INST_ANY / "
              "SQ_WAVE_CYCLES (waves waiting on their own loads); residency = 4 x SQ_WAVE_CYCLES / "
@@ -172,7 +172,7 @@ def main():
     ks = kernel_stats(a.trace)
     lines = [f"# Kernel trace: {a.name}", "",
              f"Command (run from /tmp with TMPDIR=/tmp): `{a.cmd_trace}`", "",
-             f"Kernel sources (aa_kernels.hip, aa_small.hip, aa_backward.hip, aa_device.h) sha256[:16]: `{src}`", "",
+             f"Kernel sources (aa_kernels.hip, aa_small.hip, aa_backward.hip, aa_tile32.hip, aa_device.h) sha256[:16]: `{src}`", "",
              "| kernel | grid (threads) | calls | avg us | min us | max us | % of GPU time |",
              "|---|---|---|---|---|---|---|"]
     for k in ks:
@@ -215,7 +215,7 @@ def main():
         lines = [f"# HBM traffic per launch: {a.name}", "",
                  f"Commands (run from /tmp with TMPDIR=/tmp): `{a.cmd_pmc.replace('PMC', 'FETCH_SIZE')}` and "
                  f"`{a.cmd_pmc.replace('PMC', 'WRITE_SIZE')}`", "",
-                 f"Kernel sources (aa_kernels.hip, aa_small.hip, aa_backward.hip, aa_device.h) sha256[:16]: `{src}`", "",
+                 f"Kernel sources (aa_kernels.hip, aa_small.hip, aa_backward.hip, aa_tile32.hip, aa_device.h) sha256[:16]: `{src}`", "",
                  f"Calibration: a 1 GiB device copy (`{short(cname, 60)}`, its largest dispatches) reads FETCH_SIZE = {fe[cname]:.0f} KiB "
                  f"and WRITE_SIZE = {wr[cname]:.0f} KiB per launch, so bytes = FETCH_SIZE x 1024 x {f_fac:.4f} "
                  f"and WRITE_SIZE x 1024 x {w_fac:.4f}.", "",
