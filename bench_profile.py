@@ -103,7 +103,9 @@ def bench_durations(log):
     rec = bench_record(log)
     if "parts" in rec:
         return {k: v["ms"] for k, v in rec["parts"].items()}
-    return {"projection": rec["kernel_ms"]} if "kernel_ms" in rec else {}
+    if "kernel_ms" not in rec:
+        return {}
+    return {"swiglu_ffn" if "SwiGLU" in rec.get("metric", "") else "projection": rec["kernel_ms"]}
 
 
 def is_calibration_copy(name):
