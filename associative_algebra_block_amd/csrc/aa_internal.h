@@ -26,6 +26,7 @@ struct aa_plan_s {
   int32_t tile_override;     // -1: automatic; else a variant id (tuning only)
   int32_t wg_per_cu;         // persistent kernels: workgroups launched per CU (0: automatic)
   int32_t persist_pol;       // persistent kernels: cache policy bits (-1: automatic; tuning only)
+  int32_t swiglu_persist;    // 1: SwiGLU gate/up of 128-wide input blocks on the persistent kernel (tuning only)
   uint64_t adj[64];          // AA_LAW_DIGRAPH: bit k of adj[i] = edge i -> k (else all zero)
   int32_t n_edges;
 };

@@ -2111,6 +2111,8 @@ const KStreamVariant kKStream[] = {
     AA_KS_SW(2, 1, 4, 2, 3),   // TN 64,  TM 64 (also a SwiGLU gate/up instance)
     AA_KS(3, 1, 4, 4, 3),      // TN 64,  TM 64, 128-wide K chunks (250 VGPRs: two per CU)
     AA_KS_SW(4, 1, 4, 2, 4),   // TN 64,  TM 64, three steps in flight
+    AA_KS_SW(5, 2, 4, 2, 2),   // TN 128, TM 64, one step in flight
+    AA_KS_SW(6, 2, 4, 1, 3),   // TN 128, TM 64, 32-wide K chunks, two steps in flight (SwiGLU gate/up)
 };
 constexpr int kNumKStream = int(sizeof(kKStream) / sizeof(kKStream[0]));
 
@@ -2325,7 +2327,14 @@ int choose_kstream(const aa_plan_s& plan, int64_t M, bool swiglu) {
   // tiles per workgroup or more (the Qwen3-1.7B shape, 64 x 192 blocks: 15.9
   // against 19.0 us here); wider ones (a SwiGLU down projection) are
   // streamed in K chunks here.
-  if (plan.b_in == 128) return -1;
+  if (plan.b_in == 128) {
+    // except the SwiGLU gate/up with 128-wide output tiles: 32-wide K chunks
+    // keep two weight streams of 128-wide tiles within the register budget
+    // (Qwen3-8B gate/up, weights streamed from HBM: 59.4 against 65.0 us on
+    // the persistent kernel's 64-wide tiles)
+    if (swiglu && !plan.swiglu_persist && plan.b_out % 128 == 0 && fits(6)) return 6;
+    return -1;
+  }
   if (plan.b_in == 64 && !swiglu && choose_persist(plan, M, false) >= 0) return -1;
   // 128-wide tiles when they divide the output groups (the Qwen3-8B down
   // projection: 39.4 vs 41.6 us for the 64-wide ones); 64-wide otherwise,

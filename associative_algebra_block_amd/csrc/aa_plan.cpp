@@ -178,6 +178,7 @@ aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjac
   p->tile_override = -1;
   p->wg_per_cu = 0;
   p->persist_pol = -1;
+  p->swiglu_persist = 0;
   // Tuning overrides, read once here so that a plan stays immutable.
   if (const char* t = getenv("AA_TILE")) {
     char* end = nullptr;
@@ -188,6 +189,9 @@ aa_status_t create(aa_plan_t* out, aa_law_t law, int32_t q, const uint8_t* adjac
     char* end = nullptr;
     long v = strtol(t, &end, 10);
     if (end != t && *end == '\0' && v > 0 && v <= 64) p->wg_per_cu = int32_t(v);
+  }
+  if (const char* t = getenv("AA_SWIGLU_PERSIST")) {
+    if (t[0] == '1' && t[1] == '\0') p->swiglu_persist = 1;
   }
   if (const char* t = getenv("AA_PERSIST_POL")) {
     char* end = nullptr;
