@@ -230,6 +230,35 @@ def test_kstream_swiglu_matches_oracle():
     assert_parity(host(Y), oracle.project(host(H), host(Wd), "Qq", q, types), False, "kstream swiglu Y")
 
 
+@pytest.mark.parametrize("kind,q,M,D,F,off", [
+    ("pos_mod", 8, 999, 1024, 2048, 5),       # ragged second m-tile, two 128-wide n-tiles
+    ("pos_mod", 8, 520, 1024, 3072, 0),       # three n-tiles per leaf (the Qwen3-8B gate/up layout)
+    ("block_rows", 4, 4 * 100, 512, 512, 0),  # block-row typing, 100 rows per type
+])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_kstream_gateup_128_wide(kind, q, M, D, F, off, out_dt):
+    """SwiGLU gate/up of 128-wide input blocks whose output blocks 128 divides
+    takes the K-stream kernel with 128-wide tiles and 32-wide K chunks by
+    default; its H and the down projection against the oracle."""
+    say("kstream gate/up 128-wide", kind, q, M, D, F, off, out_dt)
+    up = aa.aa_plan_create("Qq", q, D, F, kind, 0, "bf16", "bf16")
+    down = aa.aa_plan_create("Qq", q, F, D, kind, 0, "bf16", out_dt)
+    X = inp.gaussian((M, D), 61, 1.0, torch.bfloat16, DEV)
+    Wg = inp.gaussian((D, F), 62, D ** -0.5, torch.bfloat16, DEV)
+    Wu = inp.gaussian((D, F), 63, D ** -0.5, torch.bfloat16, DEV)
+    Wd = inp.gaussian((F, D), 64, F ** -0.5, torch.bfloat16, DEV)
+    H = torch.empty(M, F, dtype=torch.bfloat16, device=DEV)
+    Y = torch.empty(M, D, dtype=TD[out_dt], device=DEV)
+    aa.aa_swiglu_ffn_fwd(up, down, X, aa.pack(up, Wg), aa.pack(up, Wu), aa.pack(down, Wd), H, Y, None, off)
+    torch.cuda.synchronize()
+    types = _types(kind, M, q, off)
+    Href, _ = oracle.swiglu_ffn(host(X), host(Wg), host(Wu), host(Wd), "Qq", q, types)
+    # H is stored in bf16: the rounding floor is allowed on top of the bound
+    assert_parity(host(H), Href, True, "kstream gate/up H")
+    # Y from the GPU's own H, against the oracle's down projection of that H
+    assert_parity(host(Y), oracle.project(host(H), host(Wd), "Qq", q, types), out_dt == "bf16", "kstream gate/up Y")
+
+
 def test_decode_single_tokens_in_a_graph_replay():
     """Single-token decode calls captured in one HIP graph: every replay,
     with eager work and synchronisations between replays, equals the eager
